@@ -1,0 +1,198 @@
+"""Pins of the oracle's speculative-sampling acceptance (CPU only).
+
+Checked against what page 3 ("speculative-decoding-omni") fixes: the worked
+example of section 2, the identities P(accept) = 1 - TV and output == p, the
+chain formula and printed numbers of section 3, and the special cases that
+reduce to greedy acceptance.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import spec_sampling as ss
+from synth.gen import philox_uniforms
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _enumerate_first_token(p, q, n_acc=4096, n_smp=512):
+    """Exact distribution of the first emitted token for k = 1 over a midpoint grid of
+    both uniforms, with the draft x drawn from q by enumeration.  Returns (dist, P(accept)).
+
+    Given a rejection the replacement depends only on the sampling uniform; the grid of
+    that uniform is enumerated under two different rejecting acceptance uniforms, which
+    must agree."""
+    V = len(p)
+    tgt = np.log(np.stack([p, p]))       # softmax(log p) = p
+    drf = np.log(np.asarray(q))[None, :]
+    dist = np.zeros(V)
+    acc = 0.0
+    ua = (np.arange(n_acc) + 0.5) / n_acc
+    us = (np.arange(n_smp) + 0.5) / n_smp
+    for x in range(V):
+        if q[x] == 0:
+            continue
+        rejecting = []
+        for a in ua:
+            n, _, _ = ss.accept_one_sequence(tgt, drf, [x], [a], [0.5, 0.5])
+            if n == 1:
+                dist[x] += q[x] / n_acc
+                acc += q[x] / n_acc
+            else:
+                rejecting.append(a)
+        if rejecting:
+            hists = []
+            for a in (rejecting[0], rejecting[-1]):
+                h = np.zeros(V)
+                for s in us:
+                    _, tok, _ = ss.accept_one_sequence(tgt, drf, [x], [a], [s, 0.5])
+                    h[tok] += 1.0 / n_smp
+                hists.append(h)
+            assert np.array_equal(hists[0], hists[1])
+            dist += q[x] * len(rejecting) / n_acc * hists[0]
+    return dist, acc
+
+
+def test_worked_example_exact():
+    g = _load("p3_worked_example.json")
+    p, q = np.array(g["p"]), np.array(g["q"])
+    assert ss.total_variation(p, q) == pytest.approx(g["tv"], abs=1e-15)
+    dist, acc = _enumerate_first_token(p, q, n_acc=4096, n_smp=64)
+    assert acc == pytest.approx(g["alpha"], abs=1e-12)
+    np.testing.assert_allclose(dist, g["output_distribution"], atol=1e-12)
+    # drafting B: accepted with probability 0.75; the rejected mass all goes to A
+    tgt, drf = np.log(np.stack([p, p])), np.log(q)[None, :]
+    ua = (np.arange(4096) + 0.5) / 4096
+    accB = np.mean([ss.accept_one_sequence(tgt, drf, [1], [a], [0.5, 0.5])[0] for a in ua])
+    assert accB == pytest.approx(g["accept_prob_of_B"], abs=1e-12)
+    for s in (0.01, 0.5, 0.99):
+        n, tok, _ = ss.accept_one_sequence(tgt, drf, [1], [0.9], [s, 0.5])
+        assert n == 0 and tok == 0
+
+
+def test_worked_example_monte_carlo_philox():
+    g = _load("p3_worked_example.json")
+    p, q = np.array(g["p"]), np.array(g["q"])
+    N = 60000
+    u0, u1 = philox_uniforms(1234, np.arange(N), np.zeros(N, dtype=np.int64), stream=0)
+    _, u2 = philox_uniforms(1234, np.arange(N), np.zeros(N, dtype=np.int64), stream=2)
+    # draft x ~ q by inverse transform of an independent uniform
+    xs = np.searchsorted(np.cumsum(q), u2, side="right")
+    tgt, drf = np.log(np.stack([p, p])), np.log(q)[None, :]
+    first = np.empty(N, dtype=np.int64)
+    acc = 0
+    for t in range(N):
+        n, tok, _ = ss.accept_one_sequence(tgt, drf, [int(xs[t])], [u0[t]], [u1[t], 0.5])
+        first[t] = xs[t] if n == 1 else tok
+        acc += n
+    rate = acc / N
+    sigma = math.sqrt(0.9 * 0.1 / N)
+    assert abs(rate - 0.9) < 4 * sigma
+    counts = np.bincount(first, minlength=3)
+    chi2 = float(np.sum((counts - N * p) ** 2 / (N * p)))
+    assert chi2 < 13.8  # chi-square, 2 dof, p = 0.001
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tiny_vocab_output_equals_p_and_accept_is_one_minus_tv(seed):
+    rng = np.random.default_rng(seed)
+    V = 2 + seed % 5
+    p = rng.dirichlet(np.ones(V))
+    q = rng.dirichlet(np.ones(V))
+    dist, acc = _enumerate_first_token(p, q, n_acc=2048, n_smp=1024)
+    # grid quantisation: each uniform is resolved to 1/n
+    assert acc == pytest.approx(1.0 - ss.total_variation(p, q), abs=2.0 / 2048)
+    np.testing.assert_allclose(dist, p, atol=3.0 / 1024)
+
+
+def test_special_cases():
+    rng = np.random.default_rng(7)
+    V = 5
+    p = rng.dirichlet(np.ones(V))
+    # q one-hot at x: the draft is always x and is accepted with probability p(x)
+    x = 3
+    q = np.full(V, 1e-300)
+    q[x] = 1.0
+    tgt, drf = np.log(np.stack([p, p])), np.log(q)[None, :]
+    ua = (np.arange(4096) + 0.5) / 4096
+    acc = np.mean([ss.accept_one_sequence(tgt, drf, [x], [a], [0.5, 0.5])[0] for a in ua])
+    assert acc == pytest.approx(p[x], abs=1.0 / 4096)
+    # p one-hot (temperature -> 0): accept exactly when the draft is p's argmax, and the
+    # replacement is that argmax: greedy acceptance
+    z = np.array([0.0, 5.0, 1.0, -2.0, 0.5]) * 1e4
+    q2 = rng.dirichlet(np.ones(V))
+    for x in range(V):
+        for a in (0.01, 0.5, 0.99):
+            n, tok, _ = ss.accept_one_sequence(np.stack([z, z]), np.log(q2)[None, :], [x], [a], [0.3, 0.3])
+            assert (n == 1) == (x == 1)
+            if n == 0:
+                assert tok == 1
+    # p == q: every draft accepted (ratio 1 > u), then a bonus token from p
+    k = 4
+    zz = rng.standard_normal((k + 1, V))
+    for a in (0.0, 0.999999):
+        n, tok, _ = ss.accept_one_sequence(zz, zz[:k], [0, 1, 2, 3], [a] * k, [0.2] * (k + 1))
+        assert n == k
+        assert tok == int(np.searchsorted(np.cumsum(ss.softmax(zz[k])), 0.2, side="right"))
+
+
+def test_chain_numbers_of_page3():
+    g = _load("p3_chain_numbers.json")
+    a = g["per_position_accept"]
+    # independent product model: sum of products ~ 1.62 accepted tokens
+    assert ss.expected_tokens_per_pass(a) - 1.0 == pytest.approx(g["independent_sum_of_products"], abs=0.005)
+    # constant alpha 0.8 over k = 7 gives accept_len 3.16, i.e. 4.16 tokens per pass
+    k = g["k"]
+    t = ss.expected_tokens_per_pass([g["equivalent_constant_alpha"]] * k)
+    assert t - 1.0 == pytest.approx(g["reported_accept_len"], abs=0.005)
+    alpha = g["equivalent_constant_alpha"]
+    assert t == pytest.approx((1 - alpha ** (k + 1)) / (1 - alpha), rel=1e-12)  # closed form
+    for c, s in g["net_speedup"].items():
+        assert ss.net_speedup(g["tokens_per_pass"], k, float(c)) == pytest.approx(s, abs=0.005)
+    tv = g["tv_vs_accept"]
+    assert 1 - tv["raw_tv"] == pytest.approx(tv["accept_rate_epoch"], abs=1e-12)
+
+
+def test_chain_mean_matches_product_formula():
+    """k positions with fixed (p_i, q_i); drafts drawn from q_i; E[n] = sum_i prod_{j<=i} alpha_j
+    with alpha_j = 1 - TV(p_j, q_j) (the acceptance events are independent here)."""
+    rng = np.random.default_rng(11)
+    V, k, N = 6, 4, 20000
+    zp = rng.standard_normal((k + 1, V)) * 1.5
+    zq = zp[:k] + 0.7 * rng.standard_normal((k, V))
+    alphas = [1 - ss.total_variation(ss.softmax(zp[i]), ss.softmax(zq[i])) for i in range(k)]
+    expect_n = ss.expected_tokens_per_pass(alphas) - 1.0
+    u0, _ = philox_uniforms(99, np.arange(N)[:, None], np.arange(k)[None, :], stream=0)
+    _, u1 = philox_uniforms(99, np.arange(N)[:, None], np.arange(k + 1)[None, :], stream=1)
+    u2, _ = philox_uniforms(99, np.arange(N)[:, None], np.arange(k)[None, :], stream=3)
+    cq = [np.cumsum(ss.softmax(zq[i])) for i in range(k)]
+    tot = 0
+    per_pos_acc = np.zeros(k)
+    per_pos_tries = np.zeros(k)
+    for t in range(N):
+        xs = [min(int(np.searchsorted(cq[i], u2[t, i], side="right")), V - 1) for i in range(k)]
+        n, _, _ = ss.accept_one_sequence(zp, zq, xs, u0[t], u1[t])
+        tot += n
+        per_pos_tries[: min(n + 1, k)] += 1
+        per_pos_acc[:n] += 1
+    mean = tot / N
+    assert abs(mean - expect_n) < 0.03
+    # per position, acceptance given the position was tried equals 1 - TV
+    np.testing.assert_allclose(per_pos_acc / per_pos_tries, alphas, atol=0.02)
+
+
+def test_inverse_cdf_is_smallest_index_over_threshold():
+    w = np.array([0.0, 0.25, 0.0, 0.5, 0.25])
+    assert ss.inverse_cdf(w, 0.0)[0] == 1
+    assert ss.inverse_cdf(w, 0.2)[0] == 1
+    assert ss.inverse_cdf(w, 0.26)[0] == 3
+    assert ss.inverse_cdf(w, 0.76)[0] == 4
+    assert ss.inverse_cdf(w, 0.999999)[0] == 4

@@ -1,0 +1,219 @@
+/*
+ * sdv.h -- C ABI of the single-forward speculative verification library (libsdv.so).
+ *
+ * The operations follow the problem statement of "Decode Before You Hear:
+ * Speculative Listening for Chunk-Interleaved Full-Duplex Speech Language
+ * Models" (page 1, section "Method steps", steps 4 and 6) and the acceptance
+ * rule of "speculative-decoding-omni" (page 3, section 2):
+ *
+ *   sdv_verify_forward  one decoder forward over [audio chunk ; draft (; runner-up
+ *                       branch)] on top of a paged KV cache, yielding every draft
+ *                       position's target distribution as logits plus fused
+ *                       argmax / top-2 margin / log-sum-exp (step 4);
+ *   sdv_accept_greedy   n = min({i-1 : y~_i != argmax p_i} U {gamma}) and the
+ *                       correction argmax p_{n+1}, generalised to a tree walk (step 4);
+ *   sdv_accept_sample   speculative-sampling acceptance: accept x_i with probability
+ *                       min(1, p/q), resample the first rejection from
+ *                       norm(max(0, p - q)), bonus token from p when all pass
+ *                       (step 6; page 3 section 2);
+ *   sdv_kv_rollback     set committed lengths and compact an accepted branch
+ *                       ("roll the KV cache back", step 4).
+ *
+ * Conventions shared by every call
+ *   - All data pointers are DEVICE pointers unless a comment says "host".
+ *   - The caller owns every buffer (weights, cache pages, inputs, outputs and the
+ *     workspace).  The library never allocates or frees device memory, never
+ *     synchronises the stream and keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is
+ *     asynchronous: outputs are valid once the stream reaches that point.
+ *   - Host-checkable problems (NULL pointer, unsupported shape, workspace too small)
+ *     return a negative sdv_status before anything is enqueued; sdv_last_error()
+ *     then returns a message (thread-local, valid until the next call on the thread).
+ *   - Data-dependent problems found on the device (token id outside [0, V), a tree
+ *     parent that is not an earlier row, a cache that would overflow its capacity)
+ *     set bits in the caller's int32 error word for that sequence; that sequence's
+ *     results are then unspecified, other sequences are unaffected, and the kernels
+ *     never read or write outside their buffers.
+ *   - Matrices are row-major [out_features, in_features] (in_features contiguous).
+ *     Storage type: fp32 (SDV_F32) or bf16 (SDV_BF16, raw 16-bit patterns);
+ *     norm gains are always fp32.
+ */
+#ifndef SDV_H
+#define SDV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDV_ABI_VERSION 1
+#define SDV_PAGE 16          /* tokens per KV-cache page */
+#define SDV_MAX_T 128        /* rows per verify pass (chunk + drafts + branches) */
+
+typedef enum {
+  SDV_OK = 0,
+  SDV_ERR_NULL = -1,        /* a required pointer is NULL */
+  SDV_ERR_SHAPE = -2,       /* inconsistent or out-of-range sizes */
+  SDV_ERR_UNSUPPORTED = -3, /* valid but not implemented (e.g. head_dim not 64/128) */
+  SDV_ERR_WORKSPACE = -4,   /* workspace smaller than sdv_*_workspace_size() */
+  SDV_ERR_LAUNCH = -5       /* the HIP runtime rejected a launch */
+} sdv_status;
+
+typedef enum { SDV_F32 = 0, SDV_BF16 = 1 } sdv_dtype;
+
+/* device-side error bits written to the per-sequence error word */
+#define SDV_EBAD_TOKEN    0x1   /* a token id outside [0, vocab) (treated as 0) */
+#define SDV_EBAD_PARENT   0x2   /* parent[j] not in [0, j) for j > 0, or parent[0] != -1 */
+#define SDV_EOVERFLOW     0x4   /* seq_len + T exceeds the cache capacity or max_ctx + T */
+#define SDV_EBAD_MOVE     0x8   /* a rollback move or keep_len outside the capacity */
+#define SDV_EDUP_SIBLING  0x10  /* two children of one tree row carry the same token */
+
+/* One decoder layer: pre-norm attention block and SwiGLU FFN block. */
+typedef struct {
+  const float* attn_norm;  /* [d] RMSNorm gain before attention */
+  const void* wq;          /* [H*dh, d] */
+  const void* wk;          /* [Hkv*dh, d] */
+  const void* wv;          /* [Hkv*dh, d] */
+  const void* wo;          /* [d, H*dh] */
+  const float* ffn_norm;   /* [d] RMSNorm gain before the FFN */
+  const void* wg;          /* [F, d] gate projection */
+  const void* wu;          /* [F, d] up projection */
+  const void* wd;          /* [d, F] down projection */
+} sdv_layer;
+
+/* Decoder: token embedding, n_layers pre-norm blocks, final RMSNorm, untied LM head.
+ * Attention: query head h reads kv head h / (H / Hkv); scale 1/sqrt(dh); rotary
+ * embedding of rotate-half form (element i pairs with i + dh/2, angle
+ * pos * rope_theta^(-2i/dh)) on queries and keys. */
+typedef struct {
+  int32_t n_layers, d, n_heads, n_kv_heads, head_dim, ffn, vocab;
+  int32_t dtype;             /* sdv_dtype of every matrix, the embedding and the KV pages */
+  float eps;                 /* RMSNorm epsilon: x / sqrt(mean(x^2) + eps) * g */
+  float rope_theta;
+  const void* embed;         /* [V, d] */
+  const float* final_norm;   /* [d] */
+  const void* lm_head;       /* [V, d] */
+  const sdv_layer* layers;   /* HOST array of n_layers entries (device pointers inside) */
+} sdv_model;
+
+/* Paged KV cache.  Logical slot s of sequence b lives in physical page
+ * block_table[b * max_blocks + s / 16] at offset s % 16.
+ *   k_pages: [n_layers][n_blocks][Hkv][16][dh]   (token-major within a page)
+ *   v_pages: [n_layers][n_blocks][Hkv][dh][16]   (transposed within a page)
+ * seq_len[b] is the committed length C_b; capacity is max_blocks * 16 slots. */
+typedef struct {
+  void* k_pages;
+  void* v_pages;
+  const int32_t* block_table;  /* [B, max_blocks] */
+  int32_t* seq_len;            /* [B] */
+  int32_t n_blocks;            /* physical pages per layer */
+  int32_t max_blocks;          /* table entries per sequence */
+  int32_t batch;               /* B */
+} sdv_kv;
+
+/* One verify pass over T chunk rows per sequence.
+ *   tokens   [B, T]: rows 0..L_a-1 are the audio chunk, later rows are drafts.
+ *   parent   [T] tree parents shared by all sequences (parent[0] = -1, parent[j] in
+ *            [0, j)), or NULL for a chain (parent[j] = j - 1).  Row j is written to
+ *            slot seq_len[b] + j and takes rotary position seq_len[b] + depth(j); it
+ *            attends to all seq_len[b] cached slots and to the chunk rows that are j
+ *            or its ancestors.
+ *   logit_rows [R] chunk rows whose next-token distributions are produced (for
+ *            greedy acceptance: L_a-1 and every draft row).
+ *   max_ctx  host-side upper bound on every seq_len[b]; sizes the attention grid. */
+typedef struct {
+  int32_t batch, T, L_a, R, max_ctx;
+  const int32_t* tokens;
+  const int32_t* parent;       /* nullable */
+  const int32_t* logit_rows;
+} sdv_verify_in;
+
+/* Outputs of sdv_verify_forward (all device, [B, R] unless noted):
+ *   logits  fp32 [B, R, V] or NULL (the statistics below are produced either way)
+ *   argmax  int32: index of the largest logit, lowest index on ties
+ *   margin  fp32: largest minus second-largest logit (0 on a tie)
+ *   lse     fp32: log(sum_v exp(logit_v))
+ *   hidden  fp32 [B, T, d] or NULL: residual stream after the last layer
+ *   err     int32 [B]: device error bits (OR-ed in; the caller clears it) */
+typedef struct {
+  float* logits;
+  int32_t* argmax;
+  float* margin;
+  float* lse;
+  float* hidden;
+  int32_t* err;
+} sdv_verify_out;
+
+/* Bytes of workspace sdv_verify_forward needs for this model and pass shape. */
+size_t sdv_verify_workspace_size(const sdv_model* m, int32_t batch, int32_t T, int32_t R,
+                                 int32_t max_ctx);
+
+/* The verify forward ("Method steps", step 4).  Writes K/V of the T rows into the
+ * cache pages at slots seq_len[b] + j; does NOT change seq_len (commit with
+ * sdv_kv_rollback).  Requires head_dim 64 or 128, H % Hkv == 0, d, H*dh and F
+ * multiples of 32, 1 <= T <= SDV_MAX_T, 1 <= R <= T. */
+sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_verify_in* in,
+                              sdv_verify_out* out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Greedy acceptance ("Method steps", step 4) for every sequence b.
+ *   Walk from row L_a-1; at each row, the child row whose token equals that row's
+ *   argmax is accepted and the walk continues from it; stop when no child matches.
+ *   On a chain this is n = min({i-1 : y~_i != argmax p_i} U {gamma}).
+ *   argmax   [B, R] from sdv_verify_forward, aligned with logit_rows (every row on a
+ *            walk must be in logit_rows, otherwise the walk stops there).
+ *   n_out    [B] accepted draft rows (0 <= n <= depth of the tree)
+ *   next_out [B] the correction (or bonus) token argmax at the last accepted row
+ *   path_out [B, T] accepted rows in order, -1 padded (nullable)
+ *   base_len [B] nullable; when given (normally kv->seq_len) the commit plan is
+ *            also written: keep_out[b] = base_len[b] + L_a + n, and for i < T
+ *            move_src/move_dst [B, T] = slots to copy so that accepted row i ends at
+ *            slot base + L_a + i (-1 where no copy is needed).
+ *   err      [B] device error bits (duplicate sibling tokens), nullable. */
+sdv_status sdv_accept_greedy(int32_t batch, int32_t T, int32_t L_a, const int32_t* tokens,
+                             const int32_t* parent, int32_t R, const int32_t* logit_rows,
+                             const int32_t* argmax, const int32_t* base_len,
+                             int32_t* n_out, int32_t* next_out, int32_t* path_out,
+                             int32_t* keep_out, int32_t* move_src, int32_t* move_dst,
+                             int32_t* err, void* stream);
+
+/* Speculative-sampling acceptance ("Method steps", step 6; page 3, section 2).
+ *   tgt_logits [B, k+1, V] fp32 target logits (row i scores draft position i, row k
+ *              the bonus position); drf_logits [B, k, V] fp32 draft logits;
+ *   drafts [B, k]; p = softmax(tgt / temperature), q = softmax(drf / temperature).
+ *   For i = 0..k-1 in order: accept drafts[b,i] iff u_accept[b,i] < p(x)/q(x)
+ *   (if q(x) = 0: iff p(x) > 0).  At the first rejection i: token = inverse CDF of
+ *   w = max(0, p_i - q_i) (of p_i if w is empty) at u_sample[b,i], n = i.  If all
+ *   pass: n = k, token = inverse CDF of p_k at u_sample[b,k].  The inverse CDF
+ *   returns the smallest index whose running sum exceeds u * total, with weights
+ *   quantised to 2^-40 so the draw does not depend on summation order.
+ *   u_accept [B, k], u_sample [B, k+1]: fp64 uniforms in [0, 1) (the caller draws them).
+ *   Outputs n_out [B], tok_out [B] (int32). */
+size_t sdv_sample_workspace_size(int32_t batch, int32_t k, int32_t vocab);
+sdv_status sdv_accept_sample(int32_t batch, int32_t k, int32_t vocab, const float* tgt_logits,
+                             const float* drf_logits, const int32_t* drafts,
+                             const double* u_accept, const double* u_sample, float temperature,
+                             int32_t* n_out, int32_t* tok_out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* KV commit / rollback (step 4: roll the cache back to x_{<t}; commit n + 1 tokens).
+ *   keep_len [B]: new committed length per sequence (seq_len[b] := keep_len[b]).
+ *   move_src, move_dst [B, max_move] (both NULL or both given): for i = 0..max_move-1
+ *   in order, when move_src[b,i] >= 0, slot move_src[b,i] of every layer is copied to
+ *   slot move_dst[b,i].  Moves run in ascending i per sequence, so a destination may
+ *   be a later move's source.  Idempotent for in-place (src == dst) entries.
+ *   err [B] nullable: SDV_EBAD_MOVE when a slot or keep_len exceeds the capacity
+ *   (that sequence is then left unchanged). */
+sdv_status sdv_kv_rollback(const sdv_model* m, const sdv_kv* kv, const int32_t* keep_len,
+                           const int32_t* move_src, const int32_t* move_dst, int32_t max_move,
+                           int32_t* err, void* stream);
+
+const char* sdv_last_error(void);
+int32_t sdv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SDV_H */

@@ -1,0 +1,308 @@
+"""Thin ctypes binding of libsdv (argument marshalling only).
+
+Every step of the verify path runs in the HIP kernels of libsdv.so; PyTorch
+provides device memory and the stream.  The library is loaded from this package
+directory; if it is missing, loading raises instead of falling back to anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsdv.so")
+
+SDV_F32, SDV_BF16 = 0, 1
+PAGE = 16
+MAX_T = 128
+
+ERR_BITS = {0x1: "bad token", 0x2: "bad parent/logit row", 0x4: "cache overflow",
+            0x8: "bad rollback move", 0x10: "duplicate sibling token"}
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+
+
+class SdvLayer(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "wg", "wu", "wd")]
+
+
+class SdvModel(ctypes.Structure):
+    _fields_ = [("n_layers", _i32), ("d", _i32), ("n_heads", _i32), ("n_kv_heads", _i32),
+                ("head_dim", _i32), ("ffn", _i32), ("vocab", _i32), ("dtype", _i32),
+                ("eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                ("embed", _vp), ("final_norm", _vp), ("lm_head", _vp),
+                ("layers", ctypes.POINTER(SdvLayer))]
+
+
+class SdvKV(ctypes.Structure):
+    _fields_ = [("k_pages", _vp), ("v_pages", _vp), ("block_table", _vp), ("seq_len", _vp),
+                ("n_blocks", _i32), ("max_blocks", _i32), ("batch", _i32)]
+
+
+class SdvVerifyIn(ctypes.Structure):
+    _fields_ = [("batch", _i32), ("T", _i32), ("L_a", _i32), ("R", _i32), ("max_ctx", _i32),
+                ("tokens", _vp), ("parent", _vp), ("logit_rows", _vp)]
+
+
+class SdvVerifyOut(ctypes.Structure):
+    _fields_ = [("logits", _vp), ("argmax", _vp), ("margin", _vp), ("lse", _vp),
+                ("hidden", _vp), ("err", _vp)]
+
+
+class SdvError(RuntimeError):
+    pass
+
+
+_LIB = None
+
+
+def lib():
+    """Load libsdv.so (once).  Raises if it is not built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise SdvError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.sdv_abi_version.restype = _i32
+        L.sdv_last_error.restype = ctypes.c_char_p
+        L.sdv_verify_workspace_size.restype = ctypes.c_size_t
+        L.sdv_verify_workspace_size.argtypes = [ctypes.POINTER(SdvModel), _i32, _i32, _i32, _i32]
+        L.sdv_verify_forward.restype = ctypes.c_int
+        L.sdv_verify_forward.argtypes = [ctypes.POINTER(SdvModel), ctypes.POINTER(SdvKV),
+                                         ctypes.POINTER(SdvVerifyIn), ctypes.POINTER(SdvVerifyOut),
+                                         _vp, ctypes.c_size_t, _vp]
+        L.sdv_accept_greedy.restype = ctypes.c_int
+        L.sdv_accept_greedy.argtypes = [_i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp,
+                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.sdv_kv_rollback.restype = ctypes.c_int
+        L.sdv_kv_rollback.argtypes = [ctypes.POINTER(SdvModel), ctypes.POINTER(SdvKV), _vp, _vp, _vp,
+                                      _i32, _vp, _vp]
+        L.sdv_sample_workspace_size.restype = ctypes.c_size_t
+        L.sdv_sample_workspace_size.argtypes = [_i32, _i32, _i32]
+        L.sdv_accept_sample.restype = ctypes.c_int
+        L.sdv_accept_sample.argtypes = [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
+                                        _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise SdvError(f"{what} failed ({status}): {lib().sdv_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev_tensor(a: np.ndarray, device) -> torch.Tensor:
+    """numpy fp32 -> float32 tensor; numpy uint16 (bf16 bit patterns) -> bfloat16 tensor."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+class DeviceModel:
+    """Decoder weights resident on the device plus the sdv_model descriptor."""
+
+    def __init__(self, w, device="cuda"):
+        sh = w.shape
+        self.shape = sh
+        self.device = torch.device(device)
+        t = lambda a: _dev_tensor(a, self.device)
+        f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(self.device)
+        self.embed = t(w.embed)
+        self.final_norm = f(w.final_norm)
+        self.lm_head = t(w.lm_head)
+        self.layers = []
+        for lw in w.layers:
+            self.layers.append(dict(attn_norm=f(lw.attn_norm), wq=t(lw.wq), wk=t(lw.wk), wv=t(lw.wv),
+                                    wo=t(lw.wo), ffn_norm=f(lw.ffn_norm), wg=t(lw.wg), wu=t(lw.wu),
+                                    wd=t(lw.wd)))
+        self.codebook = t(w.codebook) if getattr(w, "codebook", None) is not None else None
+        self.stream_emb = f(w.stream_emb) if getattr(w, "stream_emb", None) is not None else None
+        self._build_desc()
+
+    def _build_desc(self):
+        sh = self.shape
+        arr = (SdvLayer * sh.n_layers)()
+        for i, L in enumerate(self.layers):
+            for k, v in L.items():
+                setattr(arr[i], k, v.data_ptr())
+        self._layer_arr = arr
+        self.desc = SdvModel(sh.n_layers, sh.d, sh.n_heads, sh.n_kv_heads, sh.head_dim, sh.ffn, sh.vocab,
+                             SDV_BF16 if sh.dtype == "bf16" else SDV_F32, sh.eps, sh.rope_theta,
+                             self.embed.data_ptr(), self.final_norm.data_ptr(), self.lm_head.data_ptr(),
+                             ctypes.cast(arr, ctypes.POINTER(SdvLayer)))
+
+    @property
+    def weight_bytes(self) -> int:
+        n = self.lm_head.numel() * self.lm_head.element_size()
+        for L in self.layers:
+            for k, v in L.items():
+                n += v.numel() * v.element_size()
+        return n
+
+
+class PagedKV:
+    """Paged cache: k_pages [L][n_blocks][Hkv][16][dh], v_pages [L][n_blocks][Hkv][dh][16],
+    block_table [B, max_blocks], seq_len [B]."""
+
+    def __init__(self, shape, batch: int, capacity: int, device="cuda", perm: Optional[np.ndarray] = None,
+                 n_blocks: Optional[int] = None):
+        self.shape = shape
+        self.device = torch.device(device)
+        self.batch = batch
+        self.max_blocks = (capacity + PAGE - 1) // PAGE
+        self.n_blocks = n_blocks or batch * self.max_blocks
+        dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+        L, Hkv, dh = shape.n_layers, shape.n_kv_heads, shape.head_dim
+        self.k_pages = torch.zeros((L, self.n_blocks, Hkv, PAGE, dh), dtype=dt, device=self.device)
+        self.v_pages = torch.zeros((L, self.n_blocks, Hkv, dh, PAGE), dtype=dt, device=self.device)
+        ids = np.arange(batch * self.max_blocks, dtype=np.int32) if perm is None else np.asarray(perm, np.int32)
+        self.block_table = torch.from_numpy(ids[:batch * self.max_blocks].reshape(batch, self.max_blocks).copy()).to(self.device)
+        self.seq_len = torch.zeros(batch, dtype=torch.int32, device=self.device)
+        self.desc = SdvKV(self.k_pages.data_ptr(), self.v_pages.data_ptr(), self.block_table.data_ptr(),
+                          self.seq_len.data_ptr(), self.n_blocks, self.max_blocks, batch)
+
+    def load(self, kv) -> None:
+        """Write logical cache contents (synth KVCache: k[b][l] [len, Hkv, dh]) into the pages."""
+        sh = self.shape
+        lens = list(kv.lens)
+        bt = self.block_table.cpu().numpy()
+        for b, n in enumerate(lens):
+            nb = (n + PAGE - 1) // PAGE
+            if nb == 0:
+                continue
+            pages = torch.from_numpy(bt[b, :nb].astype(np.int64)).to(self.device)
+            for l in range(sh.n_layers):
+                for src, dst, vt in ((kv.k[b][l], self.k_pages, False), (kv.v[b][l], self.v_pages, True)):
+                    x = _dev_tensor(src, self.device)
+                    pad = torch.zeros((nb * PAGE, sh.n_kv_heads, sh.head_dim), dtype=x.dtype, device=self.device)
+                    pad[:n] = x
+                    pg = pad.view(nb, PAGE, sh.n_kv_heads, sh.head_dim)
+                    pg = pg.permute(0, 2, 3, 1) if vt else pg.permute(0, 2, 1, 3)
+                    dst[l, pages] = pg.contiguous()
+        self.seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+
+    def gather(self, b: int, l: int, lo: int, hi: int):
+        """Logical slots [lo, hi) of sequence b, layer l as (k, v) fp32 [n, Hkv, dh] tensors."""
+        slots = torch.arange(lo, hi, device=self.device)
+        bt = self.block_table[b].long()
+        pg = bt[slots // PAGE]
+        off = slots % PAGE
+        k = self.k_pages[l, pg, :, off, :]           # [n, Hkv, dh]
+        v = self.v_pages[l, pg, :, :, off]           # [n, Hkv, dh]
+        return k.float(), v.float()
+
+
+@dataclass
+class VerifyResult:
+    argmax: torch.Tensor
+    margin: torch.Tensor
+    lse: torch.Tensor
+    err: torch.Tensor
+    logits: Optional[torch.Tensor] = None
+    hidden: Optional[torch.Tensor] = None
+
+
+class Verifier:
+    """Holds the device-side inputs and outputs of verify passes of one shape, so that
+    repeated passes (and graph capture) reuse the same buffers."""
+
+    def __init__(self, model: DeviceModel, kv: PagedKV, T: int, L_a: int, logit_rows: Sequence[int],
+                 parent: Optional[Sequence[int]] = None, max_ctx: Optional[int] = None,
+                 want_logits: bool = True, want_hidden: bool = False):
+        self.model, self.kv = model, kv
+        dev = model.device
+        B = kv.batch
+        self.B, self.T, self.L_a = B, T, L_a
+        self.R = len(logit_rows)
+        self.max_ctx = int(max_ctx if max_ctx is not None else kv.max_blocks * PAGE - T)
+        self.tokens = torch.zeros((B, T), dtype=torch.int32, device=dev)
+        self.logit_rows = torch.tensor(list(logit_rows), dtype=torch.int32, device=dev)
+        self.parent = None if parent is None else torch.tensor(list(parent), dtype=torch.int32, device=dev)
+        V = model.shape.vocab
+        self.logits = torch.empty((B, self.R, V), dtype=torch.float32, device=dev) if want_logits else None
+        self.hidden = torch.empty((B, T, model.shape.d), dtype=torch.float32, device=dev) if want_hidden else None
+        self.argmax = torch.empty((B, self.R), dtype=torch.int32, device=dev)
+        self.margin = torch.empty((B, self.R), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, self.R), dtype=torch.float32, device=dev)
+        self.err = torch.zeros(B, dtype=torch.int32, device=dev)
+        nbytes = lib().sdv_verify_workspace_size(ctypes.byref(model.desc), B, T, self.R, self.max_ctx)
+        if nbytes == 0:
+            raise SdvError("unsupported verify shape: " + lib().sdv_last_error().decode())
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.inp = SdvVerifyIn(B, T, L_a, self.R, self.max_ctx, self.tokens.data_ptr(),
+                               None if self.parent is None else self.parent.data_ptr(),
+                               self.logit_rows.data_ptr())
+        self.out = SdvVerifyOut(_ptr(self.logits), self.argmax.data_ptr(), self.margin.data_ptr(),
+                                self.lse.data_ptr(), _ptr(self.hidden), self.err.data_ptr())
+
+    def set_tokens(self, tokens) -> None:
+        t = torch.as_tensor(np.asarray(tokens, dtype=np.int32).reshape(self.B, self.T))
+        self.tokens.copy_(t)
+
+    def forward(self, stream=None) -> VerifyResult:
+        _check(lib().sdv_verify_forward(ctypes.byref(self.model.desc), ctypes.byref(self.kv.desc),
+                                        ctypes.byref(self.inp), ctypes.byref(self.out),
+                                        ctypes.c_void_p(self.workspace.data_ptr()), self.workspace.numel(),
+                                        _stream(stream)), "sdv_verify_forward")
+        return VerifyResult(self.argmax, self.margin, self.lse, self.err, self.logits, self.hidden)
+
+
+def accept_greedy(B: int, T: int, L_a: int, tokens: torch.Tensor, parent: Optional[torch.Tensor],
+                  logit_rows: torch.Tensor, argmax: torch.Tensor, base_len: Optional[torch.Tensor] = None,
+                  out: Optional[dict] = None, stream=None) -> dict:
+    dev = tokens.device
+    R = logit_rows.numel()
+    if out is None:
+        out = dict(n=torch.empty(B, dtype=torch.int32, device=dev), next=torch.empty(B, dtype=torch.int32, device=dev),
+                   path=torch.empty((B, T), dtype=torch.int32, device=dev),
+                   err=torch.zeros(B, dtype=torch.int32, device=dev))
+        if base_len is not None:
+            out.update(keep=torch.empty(B, dtype=torch.int32, device=dev),
+                       move_src=torch.empty((B, T), dtype=torch.int32, device=dev),
+                       move_dst=torch.empty((B, T), dtype=torch.int32, device=dev))
+    _check(lib().sdv_accept_greedy(B, T, L_a, _ptr(tokens), _ptr(parent), R, _ptr(logit_rows), _ptr(argmax),
+                                   _ptr(base_len), _ptr(out["n"]), _ptr(out["next"]), _ptr(out["path"]),
+                                   _ptr(out.get("keep")), _ptr(out.get("move_src")), _ptr(out.get("move_dst")),
+                                   _ptr(out["err"]), _stream(stream)), "sdv_accept_greedy")
+    return out
+
+
+def kv_rollback(model: DeviceModel, kv: PagedKV, keep_len: torch.Tensor, move_src: Optional[torch.Tensor] = None,
+                move_dst: Optional[torch.Tensor] = None, err: Optional[torch.Tensor] = None, stream=None) -> None:
+    max_move = 0 if move_src is None else move_src.shape[-1]
+    _check(lib().sdv_kv_rollback(ctypes.byref(model.desc), ctypes.byref(kv.desc), _ptr(keep_len), _ptr(move_src),
+                                 _ptr(move_dst), max_move, _ptr(err), _stream(stream)), "sdv_kv_rollback")
+
+
+class Sampler:
+    """Speculative-sampling acceptance with reusable workspace."""
+
+    def __init__(self, B: int, k: int, V: int, device="cuda"):
+        self.B, self.k, self.V = B, k, V
+        nbytes = lib().sdv_sample_workspace_size(B, k, V)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.n = torch.empty(B, dtype=torch.int32, device=device)
+        self.tok = torch.empty(B, dtype=torch.int32, device=device)
+
+    def __call__(self, tgt: torch.Tensor, drf: torch.Tensor, drafts: torch.Tensor, u_acc: torch.Tensor,
+                 u_smp: torch.Tensor, temperature: float = 1.0, stream=None):
+        _check(lib().sdv_accept_sample(self.B, self.k, self.V, _ptr(tgt), _ptr(drf), _ptr(drafts), _ptr(u_acc),
+                                       _ptr(u_smp), float(temperature), _ptr(self.n), _ptr(self.tok),
+                                       _ptr(self.workspace), self.workspace.numel(), _stream(stream)),
+               "sdv_accept_sample")
+        return self.n, self.tok

@@ -1,0 +1,362 @@
+// libsdv host side: argument checks, launch plan, workspace layout and the C ABI.
+//
+// The plan depends only on host-known sizes (model shape, B, T, R, max_ctx), so a
+// sequence of calls with the same sizes issues identical launches; the caller may
+// capture them in a graph.  Nothing here allocates device memory or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "../../include/sdv.h"
+#include "kernels.h"
+
+using namespace sdv;
+
+namespace {
+
+thread_local std::string g_err;
+
+sdv_status fail(sdv_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+sdv_status fail(sdv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// target workgroups per launch: two per compute unit
+constexpr int TARGET_WG = 512;
+
+struct GemmPlan {
+  int NT, S, spp, ncg, MT, row_blocks;
+};
+
+GemmPlan plan_gemm(int M, int N, int K, bool bf) {
+  GemmPlan p;
+  const int KS = bf ? 32 : 16;
+  if (M <= 80) {
+    p.MT = std::max(1, cdiv(M, 16));
+    p.row_blocks = 1;
+  } else {
+    p.MT = 4;
+    p.row_blocks = cdiv(M, 64);
+  }
+  p.NT = 2;
+  p.ncg = cdiv(N, 16 * p.NT);
+  const int steps = K / KS;
+  int S = cdiv(TARGET_WG, (long long)p.ncg * p.row_blocks);
+  S = std::max(1, std::min(S, std::max(1, steps / 4)));
+  S = std::min(S, 32);
+  p.spp = cdiv(steps, S);
+  p.S = cdiv(steps, p.spp);
+  return p;
+}
+
+struct Plan {
+  bool bf;
+  int eb;  // element bytes
+  int M, Mr, G, nq_pad;
+  GemmPlan qkv, o, gu, dn, lm;
+  int split_keys, n_splits;
+  size_t part_floats;
+  size_t off_x, off_a, off_q, off_o, off_h, off_part, off_po, off_pml, off_stats, off_depth, off_anc,
+      off_lmrows, total;
+};
+
+sdv_status check_model(const sdv_model* m) {
+  if (!m) return fail(SDV_ERR_NULL, "model is NULL");
+  if (m->dtype != SDV_F32 && m->dtype != SDV_BF16) return fail(SDV_ERR_SHAPE, "dtype %d", m->dtype);
+  if (m->n_layers < 1 || m->d < 32 || m->n_heads < 1 || m->n_kv_heads < 1 || m->ffn < 32 || m->vocab < 2)
+    return fail(SDV_ERR_SHAPE, "model sizes out of range");
+  if (m->head_dim != 64 && m->head_dim != 128) return fail(SDV_ERR_UNSUPPORTED, "head_dim %d (64 or 128)", m->head_dim);
+  if (m->n_heads % m->n_kv_heads) return fail(SDV_ERR_SHAPE, "n_heads %% n_kv_heads != 0");
+  const int KS = m->dtype == SDV_BF16 ? 32 : 16;
+  if (m->d % 32 || m->ffn % 32 || (m->n_heads * m->head_dim) % KS)
+    return fail(SDV_ERR_UNSUPPORTED, "d and ffn must be multiples of 32");
+  if (m->d > 8192) return fail(SDV_ERR_UNSUPPORTED, "d > 8192");
+  if (!m->embed || !m->final_norm || !m->lm_head || !m->layers) return fail(SDV_ERR_NULL, "model pointer NULL");
+  for (int l = 0; l < m->n_layers; ++l) {
+    const sdv_layer& L = m->layers[l];
+    if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.ffn_norm || !L.wg || !L.wu || !L.wd)
+      return fail(SDV_ERR_NULL, "layer %d has a NULL pointer", l);
+  }
+  return SDV_OK;
+}
+
+Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
+  Plan p;
+  p.bf = m->dtype == SDV_BF16;
+  p.eb = p.bf ? 2 : 4;
+  p.M = B * T;
+  p.Mr = B * R;
+  p.G = m->n_heads / m->n_kv_heads;
+  const int d = m->d, qd = m->n_heads * m->head_dim, kd = m->n_kv_heads * m->head_dim, F = m->ffn;
+  p.qkv = plan_gemm(p.M, qd + 2 * kd, d, p.bf);
+  p.o = plan_gemm(p.M, d, qd, p.bf);
+  p.gu = plan_gemm(p.M, 2 * F, d, p.bf);
+  p.dn = plan_gemm(p.M, d, F, p.bf);
+  p.lm = plan_gemm(p.Mr, m->vocab, d, p.bf);
+  p.lm.S = 1;
+  p.lm.spp = d / (p.bf ? 32 : 16);
+  p.part_floats = std::max({(size_t)p.qkv.S * p.M * (qd + 2 * kd), (size_t)p.o.S * p.M * d,
+                            (size_t)p.gu.S * p.M * 2 * F, (size_t)p.dn.S * p.M * d});
+  // attention: split the keys so that B * Hkv * n_splits fills the GPU
+  const int KT = p.bf ? 32 : 16;
+  const int nkeys = max_ctx + T;
+  int ns = cdiv(TARGET_WG, (long long)B * m->n_kv_heads);
+  ns = std::max(1, std::min(ns, cdiv(nkeys, KT)));
+  p.split_keys = cdiv(cdiv(nkeys, ns), KT) * KT;
+  p.n_splits = cdiv(nkeys, p.split_keys);
+  p.nq_pad = cdiv(T * p.G, 16) * 16;
+
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+  p.off_x = take((size_t)p.M * d * 4);
+  p.off_a = take((size_t)p.M * d * p.eb);
+  p.off_q = take((size_t)p.M * qd * p.eb);
+  p.off_o = take((size_t)p.M * qd * p.eb);
+  p.off_h = take((size_t)p.M * F * p.eb);
+  p.off_part = take(p.part_floats * 4);
+  const size_t nqs = (size_t)B * m->n_kv_heads * p.n_splits * p.nq_pad;
+  p.off_po = take(nqs * m->head_dim * 4);
+  p.off_pml = take(nqs * 2 * 4);
+  p.off_stats = take((size_t)p.Mr * p.lm.ncg * 16);
+  p.off_depth = take((size_t)T * 4);
+  p.off_anc = take((size_t)T * 16);
+  p.off_lmrows = take((size_t)p.Mr * 4);
+  p.total = o;
+  return p;
+}
+
+#define SDV_LAUNCH(expr)                                                                   \
+  do {                                                                                     \
+    hipError_t e_ = (expr);                                                                \
+    if (e_ != hipSuccess) return fail(SDV_ERR_LAUNCH, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+sdv_status run_gemm(const Plan& P, const GemmPlan& g, int epi, const void* A, int lda, const int32_t* a_rows,
+                    int M, const void* W0, const void* W1, const void* W2, int N0, int N1, int N, int K,
+                    float* out, float* logits, float4* stats, hipStream_t s) {
+  GemmArgs a;
+  memset(&a, 0, sizeof a);
+  a.A = A;
+  a.lda = lda;
+  a.a_rows = a_rows;
+  a.M = M;
+  a.W0 = W0;
+  a.W1 = W1 ? W1 : W0;
+  a.W2 = W2 ? W2 : W0;
+  a.N0 = N0;
+  a.N1 = N1;
+  a.N = N;
+  a.K = K;
+  a.steps_per_split = g.spp;
+  a.out = out;
+  a.out_split_stride = (long long)M * N;
+  a.ldo = N;
+  a.logits = logits;
+  a.ldl = N;
+  a.stats = stats;
+  a.n_groups = g.ncg;
+  dim3 grid(g.ncg, epi == EPI_PARTIAL ? g.S : 1, g.row_blocks);
+  SDV_LAUNCH(launch_gemm(P.bf, g.MT, g.NT, epi, grid, a, s));
+  return SDV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sdv_abi_version(void) { return SDV_ABI_VERSION; }
+const char* sdv_last_error(void) { return g_err.c_str(); }
+
+size_t sdv_verify_workspace_size(const sdv_model* m, int32_t batch, int32_t T, int32_t R, int32_t max_ctx) {
+  if (check_model(m) != SDV_OK || batch < 1 || T < 1 || T > SDV_MAX_T || R < 1 || R > T || max_ctx < 0) return 0;
+  return make_plan(m, batch, T, R, max_ctx).total;
+}
+
+sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_verify_in* in, sdv_verify_out* out,
+                              void* ws, size_t ws_bytes, void* stream) {
+  sdv_status st = check_model(m);
+  if (st != SDV_OK) return st;
+  if (!kv || !in || !out) return fail(SDV_ERR_NULL, "kv/in/out is NULL");
+  if (!kv->k_pages || !kv->v_pages || !kv->block_table || !kv->seq_len) return fail(SDV_ERR_NULL, "kv pointer NULL");
+  if (!in->tokens || !in->logit_rows) return fail(SDV_ERR_NULL, "tokens/logit_rows NULL");
+  if (!out->argmax || !out->margin || !out->lse || !out->err) return fail(SDV_ERR_NULL, "output pointer NULL");
+  const int B = in->batch, T = in->T, R = in->R;
+  if (B < 1 || B != kv->batch) return fail(SDV_ERR_SHAPE, "batch %d (kv batch %d)", B, kv->batch);
+  if (T < 1 || T > SDV_MAX_T) return fail(SDV_ERR_SHAPE, "T = %d outside [1, %d]", T, SDV_MAX_T);
+  if (R < 1 || R > T) return fail(SDV_ERR_SHAPE, "R = %d outside [1, T]", R);
+  if (in->L_a < 0 || in->L_a > T) return fail(SDV_ERR_SHAPE, "L_a = %d outside [0, T]", in->L_a);
+  if (in->max_ctx < 0) return fail(SDV_ERR_SHAPE, "max_ctx < 0");
+  if (kv->max_blocks < 1 || kv->n_blocks < 1) return fail(SDV_ERR_SHAPE, "empty cache");
+  if ((long long)in->max_ctx + T > (long long)kv->max_blocks * SDV_PAGE)
+    return fail(SDV_ERR_SHAPE, "max_ctx + T exceeds the cache capacity");
+  const Plan P = make_plan(m, B, T, R, in->max_ctx);
+  if (!ws || ws_bytes < P.total) return fail(SDV_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, P.total);
+
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  float* x = (float*)(w + P.off_x);
+  void* act = w + P.off_a;
+  void* q = w + P.off_q;
+  void* o = w + P.off_o;
+  void* h = w + P.off_h;
+  float* part = (float*)(w + P.off_part);
+  float* po = (float*)(w + P.off_po);
+  float* pml = (float*)(w + P.off_pml);
+  float4* stats = (float4*)(w + P.off_stats);
+  int32_t* depth = (int32_t*)(w + P.off_depth);
+  uint32_t* anc = (uint32_t*)(w + P.off_anc);
+  int32_t* lm_rows = (int32_t*)(w + P.off_lmrows);
+
+  const int d = m->d, H = m->n_heads, Hkv = m->n_kv_heads, dh = m->head_dim, F = m->ffn, V = m->vocab;
+  const int qd = H * dh, kd = Hkv * dh, M = P.M;
+  const size_t layer_elems = (size_t)kv->n_blocks * Hkv * SDV_PAGE * dh;
+
+  {
+    PrologueArgs a{in->parent, in->logit_rows, B, T, R, depth, anc, lm_rows, out->err};
+    SDV_LAUNCH(launch_prologue(a, s));
+  }
+  {
+    EmbedArgs a{in->tokens, m->embed, m->layers[0].attn_norm, x, act, M, T, d, V, m->eps, out->err};
+    SDV_LAUNCH(launch_embed_norm(P.bf, a, s));
+  }
+  for (int l = 0; l < m->n_layers; ++l) {
+    const sdv_layer& L = m->layers[l];
+    void* kp = (char*)kv->k_pages + l * layer_elems * P.eb;
+    void* vp = (char*)kv->v_pages + l * layer_elems * P.eb;
+    // q, k, v projections
+    st = run_gemm(P, P.qkv, EPI_PARTIAL, act, d, nullptr, M, L.wq, L.wk, L.wv, qd, qd + kd, qd + 2 * kd, d, part,
+                  nullptr, nullptr, s);
+    if (st != SDV_OK) return st;
+    {
+      QkvArgs a{part, (long long)M * (qd + 2 * kd), P.qkv.S, q, kp, vp, kv->block_table, kv->max_blocks,
+                kv->n_blocks, kv->seq_len, depth, B, T, H, Hkv, dh, in->max_ctx, m->rope_theta, out->err};
+      SDV_LAUNCH(launch_qkv_epilogue(P.bf, a, s));
+    }
+    {
+      AttnArgs a{q, kp, vp, kv->block_table, kv->max_blocks, kv->n_blocks, kv->seq_len, anc, B, T, H, Hkv,
+                 P.split_keys, P.n_splits, (float)(1.4426950408889634 / sqrt((double)dh)), po, pml, P.nq_pad};
+      SDV_LAUNCH(launch_attention(P.bf, dh, a, s));
+      CombineArgs c{po, pml, o, B, T, H, Hkv, dh, P.n_splits, P.nq_pad};
+      SDV_LAUNCH(launch_combine(P.bf, c, s));
+    }
+    st = run_gemm(P, P.o, EPI_PARTIAL, o, qd, nullptr, M, L.wo, nullptr, nullptr, d, d, d, qd, part, nullptr,
+                  nullptr, s);
+    if (st != SDV_OK) return st;
+    {
+      ResidNormArgs a{x, part, (long long)M * d, P.o.S, L.ffn_norm, act, nullptr, M, d, m->eps};
+      SDV_LAUNCH(launch_resid_norm(P.bf, a, s));
+    }
+    st = run_gemm(P, P.gu, EPI_PARTIAL, act, d, nullptr, M, L.wg, L.wu, nullptr, F, 2 * F, 2 * F, d, part, nullptr,
+                  nullptr, s);
+    if (st != SDV_OK) return st;
+    {
+      SwigluArgs a{part, (long long)M * 2 * F, P.gu.S, h, M, F};
+      SDV_LAUNCH(launch_swiglu(P.bf, a, s));
+    }
+    st = run_gemm(P, P.dn, EPI_PARTIAL, h, F, nullptr, M, L.wd, nullptr, nullptr, d, d, d, F, part, nullptr,
+                  nullptr, s);
+    if (st != SDV_OK) return st;
+    {
+      const bool last = l + 1 == m->n_layers;
+      const float* g = last ? m->final_norm : m->layers[l + 1].attn_norm;
+      ResidNormArgs a{x, part, (long long)M * d, P.dn.S, g, act, last ? out->hidden : nullptr, M, d, m->eps};
+      SDV_LAUNCH(launch_resid_norm(P.bf, a, s));
+    }
+  }
+  st = run_gemm(P, P.lm, EPI_LOGITS, act, d, lm_rows, P.Mr, m->lm_head, nullptr, nullptr, V, V, V, d, nullptr,
+                out->logits, stats, s);
+  if (st != SDV_OK) return st;
+  {
+    RowReduceArgs a{stats, P.Mr, P.lm.ncg, out->argmax, out->margin, out->lse};
+    SDV_LAUNCH(launch_row_reduce(a, s));
+  }
+  return SDV_OK;
+}
+
+sdv_status sdv_accept_greedy(int32_t B, int32_t T, int32_t L_a, const int32_t* tokens, const int32_t* parent,
+                             int32_t R, const int32_t* logit_rows, const int32_t* argmax, const int32_t* base_len,
+                             int32_t* n_out, int32_t* next_out, int32_t* path_out, int32_t* keep_out,
+                             int32_t* move_src, int32_t* move_dst, int32_t* err, void* stream) {
+  if (!tokens || !logit_rows || !argmax || !n_out || !next_out) return fail(SDV_ERR_NULL, "NULL argument");
+  if (B < 1 || T < 1 || T > SDV_MAX_T || R < 1 || R > T) return fail(SDV_ERR_SHAPE, "B/T/R out of range");
+  if (L_a < 1 || L_a > T) return fail(SDV_ERR_SHAPE, "L_a = %d outside [1, T]", L_a);
+  if ((move_src == nullptr) != (move_dst == nullptr)) return fail(SDV_ERR_NULL, "move_src/move_dst: give both or neither");
+  GreedyArgs a{B, T, L_a, R, tokens, parent, logit_rows, argmax, base_len, n_out, next_out, path_out, keep_out,
+               move_src, move_dst, err};
+  SDV_LAUNCH(launch_accept_greedy(a, (hipStream_t)stream));
+  return SDV_OK;
+}
+
+sdv_status sdv_kv_rollback(const sdv_model* m, const sdv_kv* kv, const int32_t* keep_len, const int32_t* move_src,
+                           const int32_t* move_dst, int32_t max_move, int32_t* err, void* stream) {
+  if (!m || !kv || !keep_len) return fail(SDV_ERR_NULL, "NULL argument");
+  if (!kv->k_pages || !kv->v_pages || !kv->block_table || !kv->seq_len) return fail(SDV_ERR_NULL, "kv pointer NULL");
+  if ((move_src == nullptr) != (move_dst == nullptr)) return fail(SDV_ERR_NULL, "move_src/move_dst: give both or neither");
+  if (move_src && max_move < 1) return fail(SDV_ERR_SHAPE, "max_move < 1");
+  if (kv->batch < 1) return fail(SDV_ERR_SHAPE, "batch < 1");
+  RollbackArgs a{kv->k_pages, kv->v_pages, kv->block_table, kv->seq_len, kv->max_blocks, kv->n_blocks, kv->batch,
+                 m->n_layers, m->n_kv_heads, m->head_dim, m->dtype == SDV_BF16 ? 2 : 4, keep_len, move_src,
+                 move_dst, move_src ? max_move : 0, err};
+  SDV_LAUNCH(launch_kv_rollback(a, (hipStream_t)stream));
+  return SDV_OK;
+}
+
+static const int SAMPLE_CHUNK = 4096;
+
+size_t sdv_sample_workspace_size(int32_t B, int32_t k, int32_t V) {
+  if (B < 1 || k < 1 || V < 2) return 0;
+  const size_t rows = (size_t)B * (2 * k + 1);
+  const int nch = cdiv(V, SAMPLE_CHUNK);
+  return align_up(rows * 4, 256) + align_up(rows * 8, 256) + align_up((size_t)B * 4, 256) +
+         align_up((size_t)B * nch * 2 * 8, 256);
+}
+
+sdv_status sdv_accept_sample(int32_t B, int32_t k, int32_t V, const float* tgt, const float* drf,
+                             const int32_t* drafts, const double* u_acc, const double* u_smp, float temperature,
+                             int32_t* n_out, int32_t* tok_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!tgt || !drf || !drafts || !u_acc || !u_smp || !n_out || !tok_out) return fail(SDV_ERR_NULL, "NULL argument");
+  if (B < 1 || k < 1 || V < 2) return fail(SDV_ERR_SHAPE, "B/k/V out of range");
+  if (!(temperature > 0.f)) return fail(SDV_ERR_SHAPE, "temperature must be > 0");
+  const size_t need = sdv_sample_workspace_size(B, k, V);
+  if (!ws || ws_bytes < need) return fail(SDV_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  const size_t rows = (size_t)B * (2 * k + 1);
+  char* w = (char*)ws;
+  SampleArgs a;
+  a.B = B;
+  a.k = k;
+  a.V = V;
+  a.tgt = tgt;
+  a.drf = drf;
+  a.drafts = drafts;
+  a.u_acc = u_acc;
+  a.u_smp = u_smp;
+  a.inv_temp = 1.f / temperature;
+  a.row_m = (float*)w;
+  w += align_up(rows * 4, 256);
+  a.row_s = (double*)w;
+  w += align_up(rows * 8, 256);
+  a.first_rej = (int32_t*)w;
+  w += align_up((size_t)B * 4, 256);
+  a.chunk_sum = (long long*)w;
+  a.chunk = SAMPLE_CHUNK;
+  a.n_chunks = cdiv(V, SAMPLE_CHUNK);
+  a.n_out = n_out;
+  a.tok_out = tok_out;
+  SDV_LAUNCH(launch_accept_sample(a, (hipStream_t)stream));
+  return SDV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,292 @@
+// Chunked causal / tree-masked GQA attention over a paged KV cache, split over keys.
+//
+// A verify pass attends from T chunk rows (audio chunk + drafts + branch rows) to
+// the C cached slots and to the chunk rows that are ancestors-or-self of each row
+// ("Decode Before You Hear", page 1, method step 4 with the runner-up branch of
+// step 2).  The T*G query rows of one kv head (G = H / Hkv) share every K/V tile,
+// so a workgroup owns (sequence, kv head, key split) and all of that head's query
+// tiles; K/V tiles are staged once in LDS and reused by every query tile.
+//
+// Per tile of KT keys (32 for bf16, 16 for fp32) and query tile of 16 rows:
+//   S^T = K Q^T      on MFMA: keys are the A rows, queries the B columns, so each
+//                    lane ends up holding scores of one query for 8 (bf16) or 4
+//                    (fp32) keys;
+//   online softmax   in fp32 (exp2 domain), per lane, with the row max exchanged
+//                    across the 4 lane groups;
+//   O^T += V^T P^T   on MFMA: the scores a lane already holds are exactly its B
+//                    operand, because V is stored transposed inside each page and,
+//                    for bf16, the 32 keys of a tile are assigned to MFMA rows so
+//                    that lane group g holds keys 8g..8g+7 (rows 4g..4g+3 of the two
+//                    S^T tiles map to keys 8g..8g+3 and 8g+4..8g+7).
+// Partials (unnormalised O, running max, running sum) are merged per query row by
+// the combine kernel with log-sum-exp weights.
+#include "common.h"
+#include "kernels.h"
+
+#include <algorithm>
+
+namespace sdv {
+
+template <typename T, int DH, int NQW>
+__global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int VE = Vec16<T>::N;          // elements per 16 B
+  constexpr int KS = 4 * VE;               // contraction length of one mma16 step
+  constexpr int KT = BF ? 32 : 16;         // keys per tile
+  constexpr int KROW = DH + VE;            // padded LDS row of K (elements)
+  constexpr int VROW = 16 + VE;            // padded LDS row of V^T (elements)
+  constexpr int NPG = KT / 16;             // pages per tile
+  constexpr int PE = BF ? 8 : 4;           // scores per lane per tile
+
+  __shared__ __attribute__((aligned(16))) T ldsK[KT * KROW];
+  __shared__ __attribute__((aligned(16))) T ldsV[NPG * DH * VROW];
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z / a.n_qg;
+  const int lane = threadIdx.x & 63, NW = blockDim.x >> 6;
+  // this wave's query tiles: q_base + w + j*NW, q_base = (query group) * NW * NQW
+  const int w = threadIdx.x >> 6;
+  const int q_base = (blockIdx.z % a.n_qg) * NW * NQW;
+  const int r = lane & 15, lg = lane >> 4;
+  const int G = a.H / a.Hkv;
+  const int C = a.seq_len[b];
+  const int nkeys = C + a.T;
+  const int nq = a.T * G;
+  const int NQT = (nq + 15) >> 4;
+  const int k_begin = split * a.split_keys;
+  const int k_end = min(nkeys, k_begin + a.split_keys);
+  const int32_t* bt = a.block_table + (size_t)b * a.max_blocks;
+  const T* kp = (const T*)a.k_pages;
+  const T* vp = (const T*)a.v_pages;
+
+  // queries of this wave: tiles w, w + NW, ...
+  u32x4 qreg[NQW][DH / KS];
+  uint32_t anc[NQW][4];
+  float mrun[NQW], lrun[NQW];
+  f32x4 acc[NQW][DH / 16];
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < NQW; ++j) {
+    const int qi = (q_base + w + j * NW) * 16 + r;
+    const bool ok = qi < nq;
+    const int t = ok ? qi / G : 0;
+    const int h = g * G + (ok ? qi % G : 0);
+    const T* qp = (const T*)a.q + ((size_t)(b * a.T + t) * a.H + h) * DH + lg * VE;
+#pragma unroll
+    for (int ks = 0; ks < DH / KS; ++ks) qreg[j][ks] = ok ? ld16(qp + ks * KS) : zero;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) anc[j][c] = a.anc[t * 4 + c];
+    mrun[j] = -1e30f;
+    lrun[j] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt) acc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int kt0 = k_begin; kt0 < k_end; kt0 += KT) {
+    __syncthreads();
+    // ---- stage K (token-major) and V^T (dh-major) of this tile in LDS; slots at or
+    //      beyond the end of the sequence are zero-filled so no stale value is read
+    for (int c = threadIdx.x; c < KT * DH / VE; c += blockDim.x) {
+      const int key = c / (DH / VE), d0 = (c % (DH / VE)) * VE;
+      const int slot = kt0 + key, pg = slot >> 4;
+      u32x4 v = zero;
+      if (slot < nkeys && pg < a.max_blocks) {
+        const int phys = bt[pg];
+        if (phys >= 0 && phys < a.n_blocks)
+          v = ld16(kp + (((size_t)phys * a.Hkv + g) * 16 + (slot & 15)) * DH + d0);
+      }
+      st16(&ldsK[key * KROW + d0], v);
+    }
+    for (int c = threadIdx.x; c < NPG * DH * (16 / VE); c += blockDim.x) {
+      const int p = c / (DH * (16 / VE)), rem = c % (DH * (16 / VE));
+      const int dd = rem / (16 / VE), o0 = (rem % (16 / VE)) * VE;
+      const int slot0 = kt0 + p * 16 + o0, pg = slot0 >> 4;
+      u32x4 v = zero;
+      if (slot0 < nkeys && pg < a.max_blocks) {
+        const int phys = bt[pg];
+        if (phys >= 0 && phys < a.n_blocks) {
+          v = ld16(vp + (((size_t)phys * a.Hkv + g) * DH + dd) * 16 + o0);
+          if (slot0 + VE > nkeys) {
+            T e[VE];
+            __builtin_memcpy(e, &v, 16);
+#pragma unroll
+            for (int i = 0; i < VE; ++i)
+              if (slot0 + i >= nkeys) e[i] = T(0);
+            __builtin_memcpy(&v, e, 16);
+          }
+        }
+      }
+      st16(&ldsV[(p * DH + dd) * VROW + o0], v);
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int j = 0; j < NQW; ++j) {
+      const int qt = q_base + w + j * NW;
+      if (qt >= NQT) continue;
+      // ---- scores S^T for this tile: sv[e] belongs to key kt0 + PE*lg + e
+      float sv[PE];
+      if constexpr (BF) {
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        const int row0 = 8 * (r >> 2) + (r & 3);
+#pragma unroll
+        for (int ks = 0; ks < DH / KS; ++ks) {
+          const u32x4 k0 = ld16(&ldsK[row0 * KROW + ks * KS + lg * VE]);
+          const u32x4 k1 = ld16(&ldsK[(row0 + 4) * KROW + ks * KS + lg * VE]);
+          s0 = mma16<T>(k0, qreg[j][ks], s0);
+          s1 = mma16<T>(k1, qreg[j][ks], s1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { sv[i] = s0[i]; sv[4 + i] = s1[i]; }
+      } else {
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < DH / KS; ++ks)
+          s0 = mma16<T>(ld16(&ldsK[r * KROW + ks * KS + lg * VE]), qreg[j][ks], s0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[i] = s0[i];
+      }
+      // ---- mask: all cached slots; chunk slots only when an ancestor-or-self row
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < PE; ++e) {
+        const int s = kt0 + PE * lg + e;
+        bool vis = s < nkeys;
+        if (vis && s >= C) {
+          const int jr = s - C;
+          vis = (anc[j][jr >> 5] >> (jr & 31)) & 1u;
+        }
+        sv[e] = vis ? sv[e] * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[e]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(mrun[j], mx);
+      const float alpha = exp2f(mrun[j] - mnew);
+      mrun[j] = mnew;
+      float ps = 0.f, p[PE];
+#pragma unroll
+      for (int e = 0; e < PE; ++e) { p[e] = exp2f(sv[e] - mnew); ps += p[e]; }
+      lrun[j] = lrun[j] * alpha + ps;
+#pragma unroll
+      for (int dt = 0; dt < DH / 16; ++dt) acc[j][dt] *= alpha;
+      // ---- O^T += V^T P^T
+      u32x4 pb;
+      if constexpr (BF) {
+        pb.x = (uint32_t)f2bf(p[0]) | ((uint32_t)f2bf(p[1]) << 16);
+        pb.y = (uint32_t)f2bf(p[2]) | ((uint32_t)f2bf(p[3]) << 16);
+        pb.z = (uint32_t)f2bf(p[4]) | ((uint32_t)f2bf(p[5]) << 16);
+        pb.w = (uint32_t)f2bf(p[6]) | ((uint32_t)f2bf(p[7]) << 16);
+#pragma unroll
+        for (int dt = 0; dt < DH / 16; ++dt) {
+          const u32x4 va = ld16(&ldsV[((lg >> 1) * DH + dt * 16 + r) * VROW + (lg & 1) * 8]);
+          acc[j][dt] = mma16<T>(va, pb, acc[j][dt]);
+        }
+      } else {
+        pb.x = __float_as_uint(p[0]); pb.y = __float_as_uint(p[1]);
+        pb.z = __float_as_uint(p[2]); pb.w = __float_as_uint(p[3]);
+#pragma unroll
+        for (int dt = 0; dt < DH / 16; ++dt) {
+          const u32x4 va = ld16(&ldsV[(dt * 16 + r) * VROW + lg * 4]);
+          acc[j][dt] = mma16<T>(va, pb, acc[j][dt]);
+        }
+      }
+    }
+  }
+
+  // ---- write the split's partial state
+#pragma unroll
+  for (int j = 0; j < NQW; ++j) {
+    const int qt = q_base + w + j * NW;
+    if (qt >= NQT) continue;
+    float l = lrun[j];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int qi = qt * 16 + r;
+    const size_t base = (((size_t)b * a.Hkv + g) * a.n_splits + split) * a.nq_pad + qi;
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a.po[base * DH + dt * 16 + 4 * lg + i] = acc[j][dt][i];
+    if (lg == 0) {
+      a.pml[base * 2] = mrun[j];
+      a.pml[base * 2 + 1] = l;
+    }
+  }
+}
+
+template <typename T, int DH>
+__global__ void attn_combine(CombineArgs a) {
+  const int row = blockIdx.y, h = blockIdx.x;
+  const int b = row / a.T, t = row % a.T;
+  const int G = a.H / a.Hkv, g = h / G, qi = t * G + h % G;
+  const size_t base0 = (((size_t)b * a.Hkv + g) * a.n_splits) * a.nq_pad + qi;
+  float M = -INFINITY;
+  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, a.pml[(base0 + (size_t)s * a.nq_pad) * 2]);
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < a.n_splits; ++s) {
+    const size_t bs = base0 + (size_t)s * a.nq_pad;
+    const float wgt = exp2f(a.pml[bs * 2] - M);
+    den += wgt * a.pml[bs * 2 + 1];
+    num += wgt * a.po[bs * DH + threadIdx.x];
+  }
+  ((T*)a.o)[((size_t)row * a.H + h) * DH + threadIdx.x] = from_f<T>(num / den);
+}
+
+// query tiles per wave that fit without register spills
+template <typename T, int DH> constexpr int attn_cap() {
+  return sizeof(T) == 2 ? (DH == 128 ? 4 : 6) : (DH == 128 ? 3 : 4);
+}
+
+template <typename T, int DH>
+int attn_shape(int NQT, int* nqw_out, int* nw_out) {
+  constexpr int CAP = attn_cap<T, DH>();
+  int nqw = 1;
+  while ((NQT + nqw - 1) / nqw > 8 && nqw < CAP) ++nqw;
+  if (nqw == 5) nqw = 6;
+  const int nw = std::min(8, (NQT + nqw - 1) / nqw);
+  *nqw_out = nqw;
+  *nw_out = nw;
+  return (NQT + nw * nqw - 1) / (nw * nqw);
+}
+
+template <typename T, int DH>
+static hipError_t launch_attn_t(AttnArgs a, hipStream_t s) {
+  const int G = a.H / a.Hkv;
+  const int NQT = (a.T * G + 15) / 16;
+  int nqw, nw;
+  a.n_qg = attn_shape<T, DH>(NQT, &nqw, &nw);
+  dim3 grid(a.n_splits, a.Hkv, a.B * a.n_qg);
+  dim3 block(64 * nw);
+  switch (nqw) {
+    case 1: attn_chunk<T, DH, 1><<<grid, block, 0, s>>>(a); break;
+    case 2: attn_chunk<T, DH, 2><<<grid, block, 0, s>>>(a); break;
+    case 3: attn_chunk<T, DH, 3><<<grid, block, 0, s>>>(a); break;
+    case 4:
+      if constexpr (attn_cap<T, DH>() >= 4) { attn_chunk<T, DH, 4><<<grid, block, 0, s>>>(a); break; }
+      return hipErrorInvalidValue;
+    case 6:
+      if constexpr (attn_cap<T, DH>() >= 6) { attn_chunk<T, DH, 6><<<grid, block, 0, s>>>(a); break; }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(bool is_bf16, int dh, const AttnArgs& a, hipStream_t s) {
+  if (is_bf16) return dh == 64 ? launch_attn_t<bf16, 64>(a, s) : launch_attn_t<bf16, 128>(a, s);
+  return dh == 64 ? launch_attn_t<float, 64>(a, s) : launch_attn_t<float, 128>(a, s);
+}
+
+hipError_t launch_combine(bool is_bf16, const CombineArgs& a, hipStream_t s) {
+  dim3 grid(a.H, a.B * a.T);
+  if (is_bf16) {
+    if (a.dh == 64) attn_combine<bf16, 64><<<grid, 64, 0, s>>>(a);
+    else attn_combine<bf16, 128><<<grid, 128, 0, s>>>(a);
+  } else {
+    if (a.dh == 64) attn_combine<float, 64><<<grid, 64, 0, s>>>(a);
+    else attn_combine<float, 128><<<grid, 128, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sdv

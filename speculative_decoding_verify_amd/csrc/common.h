@@ -1,0 +1,84 @@
+// Device helpers shared by the libsdv kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16;  // raw bf16 bit pattern
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+#define SDV_DEV __device__ __forceinline__
+
+SDV_DEV float bf2f(bf16 u) { return __uint_as_float(((uint32_t)u) << 16); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite)
+SDV_DEV bf16 f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16)(u >> 16);
+}
+
+template <typename T> SDV_DEV float to_f(T v);
+template <> SDV_DEV float to_f<float>(float v) { return v; }
+template <> SDV_DEV float to_f<bf16>(bf16 v) { return bf2f(v); }
+
+template <typename T> SDV_DEV T from_f(float v);
+template <> SDV_DEV float from_f<float>(float v) { return v; }
+template <> SDV_DEV bf16 from_f<bf16>(float v) { return f2bf(v); }
+
+SDV_DEV u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// streamed once: do not keep in the caches
+SDV_DEV u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+SDV_DEV void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// One 16-byte-per-lane MFMA step of C[16x16] += A[16 x k] * B[k x 16].
+// Lane l supplies A row (l % 16) and B column (l % 16) for the k values of lane
+// group l / 16; the same element position in A and B must hold the same k.
+//   bf16: one v_mfma_f32_16x16x32_bf16 (8 k values per lane, k = 32)
+//   fp32: four v_mfma_f32_16x16x4_f32 (element e of each lane per instruction, k = 16)
+// Output: lane l holds C[4 * (l / 16) + i][l % 16] in element i.
+template <typename T> SDV_DEV f32x4 mma16(u32x4 a, u32x4 b, f32x4 c);
+template <> SDV_DEV f32x4 mma16<bf16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+template <> SDV_DEV f32x4 mma16<float>(u32x4 a, u32x4 b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+  return c;
+}
+
+// elements of T held in 16 bytes
+template <typename T> struct Vec16 { static constexpr int N = 16 / sizeof(T); };
+
+SDV_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+SDV_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Sum over a 256-thread block in a fixed order (deterministic).  `red` holds 8 floats.
+SDV_DEV float block_sum_256(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float t = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return t;
+}
+
+// per-sequence error word (device)
+SDV_DEV void set_err(int32_t* err, int b, int bits) {
+  if (err) atomicOr(err + b, bits);
+}

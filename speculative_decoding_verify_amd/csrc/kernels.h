@@ -1,0 +1,172 @@
+// Kernel argument blocks and launchers of libsdv (internal; not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdv {
+
+enum { EPI_PARTIAL = 0, EPI_LOGITS = 1 };
+
+struct GemmArgs {
+  const void* A;            // activations, rows of lda elements
+  int lda;
+  const int32_t* a_rows;    // nullable: output row m reads A row a_rows[m]
+  int M;
+  const void* W0;           // columns n < N0: row n of W0
+  const void* W1;           // columns N0 <= n < N1: row n - N0 of W1
+  const void* W2;           // columns n >= N1: row n - N1 of W2
+  int N0, N1, N, K;
+  int steps_per_split;      // k steps (32 bf16 / 16 fp32 elements) per workgroup split
+  float* out;               // EPI_PARTIAL: out[split * out_split_stride + m * ldo + n]
+  long long out_split_stride;
+  int ldo;
+  float* logits;            // EPI_LOGITS: logits[m * ldl + n] (nullable)
+  int ldl;
+  float4* stats;            // EPI_LOGITS: stats[m * n_groups + column group]
+  int n_groups;
+};
+
+hipError_t launch_gemm(bool is_bf16, int MT, int NT, int epi, dim3 grid, const GemmArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const void* q;            // [B*T, H*dh]
+  const void* k_pages;      // this layer's pages: [n_blocks][Hkv][16][dh]
+  const void* v_pages;      //                      [n_blocks][Hkv][dh][16]
+  const int32_t* block_table;
+  int max_blocks, n_blocks;
+  const int32_t* seq_len;
+  const uint32_t* anc;      // [T][4] ancestor-or-self bits of each chunk row
+  int B, T, H, Hkv;
+  int split_keys, n_splits;
+  float scale_log2;         // log2(e) / sqrt(dh)
+  float* po;                // [B][Hkv][n_splits][nq_pad][dh] unnormalised output
+  float* pml;               // [B][Hkv][n_splits][nq_pad][2] (running max in log2 units, sum)
+  int nq_pad;
+  int n_qg;                 // query-tile groups per (sequence, kv head); grid.z = B * n_qg
+};
+
+hipError_t launch_attention(bool is_bf16, int dh, const AttnArgs& a, hipStream_t s);
+
+struct CombineArgs {
+  const float* po;
+  const float* pml;
+  void* o;                  // [B*T, H*dh]
+  int B, T, H, Hkv, dh, n_splits, nq_pad;
+};
+hipError_t launch_combine(bool is_bf16, const CombineArgs& a, hipStream_t s);
+
+struct PrologueArgs {
+  const int32_t* parent;    // nullable
+  const int32_t* logit_rows;
+  int B, T, R;
+  int32_t* depth;           // [T]
+  uint32_t* anc;            // [T][4]
+  int32_t* lm_rows;         // [B*R] = b*T + logit_rows[r]
+  int32_t* err;             // [B]
+};
+hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
+
+struct EmbedArgs {
+  const int32_t* tokens;    // [B*T]
+  const void* embed;        // [V, d]
+  const float* gain;        // first layer attention-norm gain
+  float* x;                 // [M, d] fp32 residual
+  void* a;                  // [M, d] normalised (storage type)
+  int M, T, d, V;
+  float eps;
+  int32_t* err;
+};
+hipError_t launch_embed_norm(bool is_bf16, const EmbedArgs& a, hipStream_t s);
+
+struct ResidNormArgs {
+  float* x;                 // [M, d] fp32 residual, updated in place
+  const float* part;        // [S][M][d] partial sums to add
+  long long part_stride;
+  int S;
+  const float* gain;
+  void* a;                  // [M, d] normalised output
+  float* hidden;            // nullable [M, d] copy of the updated residual
+  int M, d;
+  float eps;
+};
+hipError_t launch_resid_norm(bool is_bf16, const ResidNormArgs& a, hipStream_t s);
+
+struct QkvArgs {
+  const float* part;        // [S][M][(H+2Hkv)*dh]
+  long long part_stride;
+  int S;
+  void* q;                  // [M, H*dh]
+  void* k_pages;            // this layer
+  void* v_pages;
+  const int32_t* block_table;
+  int max_blocks, n_blocks;
+  const int32_t* seq_len;
+  const int32_t* depth;
+  int B, T, H, Hkv, dh, max_ctx;
+  float rope_theta;
+  int32_t* err;
+};
+hipError_t launch_qkv_epilogue(bool is_bf16, const QkvArgs& a, hipStream_t s);
+
+struct SwigluArgs {
+  const float* part;        // [S][M][2F]: gate columns then up columns
+  long long part_stride;
+  int S;
+  void* h;                  // [M, F]
+  int M, F;
+};
+hipError_t launch_swiglu(bool is_bf16, const SwigluArgs& a, hipStream_t s);
+
+struct RowReduceArgs {
+  const float4* stats;      // [rows][n_groups]
+  int rows, n_groups;
+  int32_t* argmax;
+  float* margin;
+  float* lse;
+};
+hipError_t launch_row_reduce(const RowReduceArgs& a, hipStream_t s);
+
+struct GreedyArgs {
+  int B, T, L_a, R;
+  const int32_t* tokens;
+  const int32_t* parent;
+  const int32_t* logit_rows;
+  const int32_t* argmax;
+  const int32_t* base_len;
+  int32_t *n_out, *next_out, *path_out, *keep_out, *move_src, *move_dst, *err;
+};
+hipError_t launch_accept_greedy(const GreedyArgs& a, hipStream_t s);
+
+struct RollbackArgs {
+  void* k_pages;
+  void* v_pages;
+  const int32_t* block_table;
+  int32_t* seq_len;
+  int max_blocks, n_blocks, B, L, Hkv, dh, elem_bytes;
+  const int32_t* keep_len;
+  const int32_t* move_src;
+  const int32_t* move_dst;
+  int max_move;
+  int32_t* err;
+};
+hipError_t launch_kv_rollback(const RollbackArgs& a, hipStream_t s);
+
+struct SampleArgs {
+  int B, k, V;
+  const float* tgt;         // [B, k+1, V]
+  const float* drf;         // [B, k, V]
+  const int32_t* drafts;    // [B, k]
+  const double* u_acc;      // [B, k]
+  const double* u_smp;      // [B, k+1]
+  float inv_temp;
+  float* row_m;             // [B*(k+1) + B*k] row maximum of the raw logits
+  double* row_s;            // [..] sum_v 2^((z_v - max) * log2(e) / temperature)
+  int32_t* first_rej;       // [B] position of the draw (first rejection, or k)
+  long long* chunk_sum;     // [B][n_chunks][2] quantised weights: draw row, p row
+  int n_chunks, chunk;
+  int32_t* n_out;
+  int32_t* tok_out;
+};
+hipError_t launch_accept_sample(const SampleArgs& a, hipStream_t s);
+
+}  // namespace sdv

@@ -1,0 +1,232 @@
+"""GPU parity of the verify forward, greedy acceptance and rollback (through the C ABI).
+
+Each case runs the HIP path and the CPU oracle on the same seeded inputs and
+compares element by element (tolerances in tests/gpu_helpers.py).  Shapes span
+several MFMA tiles with ragged tails (vocab 3001 / 2053 / 1537, d = 320 / 192,
+T not a multiple of 16, GQA groups of 1, 2 and 3).
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import speculative_decoding_verify_amd as sdv  # noqa: E402
+from oracle import accept as oacc  # noqa: E402
+from oracle import decoder as odec  # noqa: E402
+from synth import (MINI_BF16, MINI_BF16_D128, MINI_F32, make_weights, make_random_kv,  # noqa: E402
+                   uniform_tokens)
+from tests.gpu_helpers import (run_pair, compare_logits, compare_kv, greedy_expectation,  # noqa: E402
+                               mode_of)
+
+
+def _tokens(B, T, V, seed):
+    return np.stack([uniform_tokens(T, V, seed + b, "chunk") for b in range(B)])
+
+
+@pytest.mark.parametrize("shape,lens,L_a,gamma", [
+    (MINI_BF16, (37, 70), 5, 6),
+    (MINI_BF16, (0,), 1, 3),        # empty cache
+    (MINI_BF16, (129,), 9, 0),      # audio only (R = 1)
+    (MINI_F32, (50, 3, 17), 4, 9),
+    (MINI_BF16_D128, (40,), 7, 12),
+])
+def test_verify_parity(shape, lens, L_a, gamma):
+    print(f"case {shape.name} lens={lens} L_a={L_a} gamma={gamma}", flush=True)
+    w = make_weights(shape, seed=101, gain_noise=0.1)
+    T = L_a + gamma
+    kvh = make_random_kv(shape, list(lens), capacity=max(lens) + T, seed=102)
+    toks = _tokens(len(lens), T, shape.vocab, 103)
+    g, o, ver, kv = run_pair(w, kvh, toks, L_a, perm_seed=104)
+    assert np.all(g["err"] == 0)
+    err, flagged, n = compare_logits(shape, g, o)
+    print(f"  logits rel err {err:.2e}; flagged {flagged}/{n}", flush=True)
+    compare_kv(shape, kv, o, list(lens), T)
+    tol = 2e-2 if shape.dtype == "bf16" else 1e-5
+    hd = np.max(np.abs(g["hidden"] - o["hidden"])) / np.max(np.abs(o["hidden"]))
+    assert hd <= tol, hd
+
+
+def test_attention_dominant_hidden():
+    """Scaled q/k/o weights make attention dominate the residual stream, so a wrong
+    attention kernel cannot hide under the FFN's contribution."""
+    shape = MINI_BF16_D128
+    w = make_weights(shape, seed=201, scales={"wq": 8.0, "wk": 8.0, "wo": 20.0, "wd": 0.05})
+    lens = (75, 33)
+    L_a, gamma = 6, 10
+    T = L_a + gamma
+    kvh = make_random_kv(shape, list(lens), capacity=max(lens) + T, seed=202)
+    toks = _tokens(2, T, shape.vocab, 203)
+    g, o, ver, kv = run_pair(w, kvh, toks, L_a, perm_seed=204)
+    hd = np.max(np.abs(g["hidden"] - o["hidden"]), axis=-1) / np.max(np.abs(o["hidden"]), axis=-1)
+    assert hd.max() <= 2e-2, hd.max()
+    compare_logits(shape, g, o)
+
+
+def test_tree_branch_and_greedy_commit():
+    """A runner-up branch forking at the first draft position, verified under a tree mask;
+    the branch carries the true continuation, so acceptance follows it and the commit
+    compacts its rows."""
+    shape = MINI_BF16
+    w = make_weights(shape, seed=301)
+    C, L_a, gamma, nb = 45, 5, 6, 4
+    T = L_a + gamma + nb
+    kvh = make_random_kv(shape, [C], capacity=C + T, seed=302)
+    audio = uniform_tokens(L_a, shape.vocab, 303, "a")
+    ar, _ = odec.greedy_decode(w, odec.Cache(kvh.k, kvh.v), audio, nb + 1, mode_of(shape))
+    main = [(ar[0] + 7) % shape.vocab] + list(uniform_tokens(gamma - 1, shape.vocab, 304, "m"))
+    toks = np.concatenate([audio, main, ar[:nb]])[None, :]
+    parent = [j - 1 for j in range(T)]
+    parent[L_a + gamma] = L_a - 1
+    g, o, ver, kv = run_pair(w, kvh, toks, L_a, parent=parent, perm_seed=305)
+    compare_logits(shape, g, o)
+    compare_kv(shape, kv, o, [C], T)
+    rows = list(range(L_a - 1, T))
+    n, nxt, path, flagged = greedy_expectation(toks[0], parent, L_a, rows, o["logits"][0])
+    acc = sdv.accept_greedy(1, T, L_a, ver.tokens, ver.parent, ver.logit_rows, ver.argmax, base_len=kv.seq_len)
+    torch.cuda.synchronize()
+    if not flagged:
+        assert int(acc["n"][0]) == n and int(acc["next"][0]) == nxt
+        assert acc["path"][0, :n].cpu().tolist() == path
+    assert n == nb and path == list(range(L_a + gamma, T))
+    # commit: rows of the branch move to slots C + L_a + i
+    k_before = [kv.gather(0, l, C + L_a + gamma, C + T)[0].clone() for l in range(shape.n_layers)]
+    sdv.kv_rollback(ver.model, kv, acc["keep"], acc["move_src"], acc["move_dst"], acc["err"])
+    torch.cuda.synchronize()
+    assert int(kv.seq_len[0]) == C + L_a + n
+    assert int(acc["err"][0]) == 0
+    for l in range(shape.n_layers):
+        k_after = kv.gather(0, l, C + L_a, C + L_a + n)[0]
+        assert torch.equal(k_after, k_before[l][:n])
+
+
+@pytest.mark.parametrize("scenario", ["silence", "corrupt3", "random"])
+def test_greedy_scenarios(scenario):
+    """Drafts = greedy decoding under silence.  Audio == silence: full acceptance plus the
+    bonus; draft 3 corrupted: n = 2; random audio: whatever the oracle says."""
+    shape = MINI_BF16
+    w = make_weights(shape, seed=401)
+    C, L_a, gamma = 30, 4, 7
+    T = L_a + gamma
+    kvh = make_random_kv(shape, [C], capacity=C + T, seed=402)
+    sil = np.zeros(L_a, dtype=np.int32)
+    drafts, _ = odec.greedy_decode(w, odec.Cache(kvh.k, kvh.v), sil, gamma + 1, mode_of(shape))
+    d = list(drafts[:gamma])
+    audio = sil if scenario != "random" else uniform_tokens(L_a, shape.vocab, 403, "a")
+    if scenario == "corrupt3":
+        d[2] = (d[2] + 1) % shape.vocab
+    toks = np.concatenate([audio, d])[None, :]
+    g, o, ver, kv = run_pair(w, kvh, toks, L_a, perm_seed=404)
+    compare_logits(shape, g, o)
+    rows = list(range(L_a - 1, T))
+    n, nxt, path, flagged = greedy_expectation(toks[0], None, L_a, rows, o["logits"][0])
+    if scenario == "silence":
+        assert n == gamma and nxt == drafts[gamma]
+    if scenario == "corrupt3":
+        assert n == 2
+    acc = sdv.accept_greedy(1, T, L_a, ver.tokens, None, ver.logit_rows, ver.argmax, base_len=kv.seq_len)
+    torch.cuda.synchronize()
+    if not flagged:
+        assert int(acc["n"][0]) == n and int(acc["next"][0]) == nxt
+    assert int(acc["n"][0]) + 1 >= 1
+
+
+def test_poisoned_dead_slots_do_not_leak():
+    """NaN in every slot beyond the committed length (including the tail of the last
+    page) must not reach any output."""
+    shape = MINI_BF16
+    w = make_weights(shape, seed=501)
+    C, L_a, gamma = 21, 3, 5
+    T = L_a + gamma
+    kvh = make_random_kv(shape, [C], capacity=C + T, seed=502)
+    toks = _tokens(1, T, shape.vocab, 503)
+    model = sdv.DeviceModel(w)
+    kv = sdv.PagedKV(shape, 1, C + T + 40)
+    kv.k_pages.fill_(float("nan"))
+    kv.v_pages.fill_(float("nan"))
+    kv.load(kvh)
+    # load() writes whole pages (zero padded); poison the padded tail again
+    for l in range(shape.n_layers):
+        pg = int(kv.block_table[0, C // 16])
+        kv.k_pages[l, pg, :, C % 16:, :] = float("nan")
+        kv.v_pages[l, pg, :, :, C % 16:] = float("nan")
+    ver = sdv.Verifier(model, kv, T, L_a, list(range(L_a - 1, T)), max_ctx=C + 16)
+    ver.set_tokens(toks)
+    res = ver.forward()
+    torch.cuda.synchronize()
+    assert torch.isfinite(res.logits).all()
+    o = odec.verify_forward(w, odec.Cache(kvh.k, kvh.v), toks, None, list(range(L_a - 1, T)), mode_of(shape))
+    compare_logits(shape, dict(logits=res.logits.cpu().numpy().astype(np.float64), argmax=res.argmax.cpu().numpy(),
+                               margin=res.margin.cpu().numpy(), lse=res.lse.cpu().numpy()), o)
+
+
+def test_paged_placement_is_bit_identical():
+    """Identity and shuffled block tables give bit-identical results."""
+    shape = MINI_BF16
+    w = make_weights(shape, seed=601)
+    lens = (50, 77)
+    T = 9
+    kvh = make_random_kv(shape, list(lens), capacity=max(lens) + T, seed=602)
+    toks = _tokens(2, T, shape.vocab, 603)
+    model = sdv.DeviceModel(w)
+    outs = []
+    for perm_seed in (None, 11, 12):
+        g, _, _, _ = run_pair(w, kvh, toks, 3, perm_seed=perm_seed, model=model)
+        outs.append(g)
+    for g in outs[1:]:
+        assert np.array_equal(g["logits"], outs[0]["logits"])
+        assert np.array_equal(g["hidden"], outs[0]["hidden"])
+
+
+def test_device_errors_are_reported():
+    shape = MINI_BF16
+    w = make_weights(shape, seed=701)
+    C, T = 10, 6
+    kvh = make_random_kv(shape, [C, C], capacity=C + T, seed=702)
+    model = sdv.DeviceModel(w)
+    kv = sdv.PagedKV(shape, 2, C + T + 16)
+    kv.load(kvh)
+    ver = sdv.Verifier(model, kv, T, 2, list(range(1, T)), max_ctx=C)
+    toks = _tokens(2, T, shape.vocab, 703)
+    toks[1, 3] = shape.vocab + 5           # invalid token in sequence 1 only
+    ver.set_tokens(toks)
+    ver.forward()
+    torch.cuda.synchronize()
+    err = ver.err.cpu().numpy()
+    assert err[0] == 0 and (err[1] & 0x1)
+    # host-checkable errors return a status before anything runs
+    with pytest.raises(sdv.SdvError):
+        sdv.Verifier(model, kv, 200, 2, list(range(1, 200)), max_ctx=C)
+    # rollback beyond the capacity is refused on the device, the sequence is untouched
+    keep = torch.tensor([C + 1, 10 ** 6], dtype=torch.int32, device="cuda")
+    e = torch.zeros(2, dtype=torch.int32, device="cuda")
+    sdv.kv_rollback(model, kv, keep, err=e)
+    torch.cuda.synchronize()
+    assert e.cpu().tolist() == [0, 0x8]
+    assert kv.seq_len.cpu().tolist() == [C + 1, C]
+
+
+def test_rollback_idempotent_and_ordered_moves():
+    shape = MINI_F32
+    w = make_weights(shape, seed=801)
+    C = 40
+    kvh = make_random_kv(shape, [C], capacity=C, seed=802)
+    model = sdv.DeviceModel(w)
+    kv = sdv.PagedKV(shape, 1, C + 16)
+    kv.load(kvh)
+    ref = [kv.gather(0, l, 0, C) for l in range(shape.n_layers)]
+    # ordered moves: slot 5 -> 3, then slot 3's new content stays, slot 10 -> 5
+    src = torch.tensor([[5, 10, -1]], dtype=torch.int32, device="cuda")
+    dst = torch.tensor([[3, 5, -1]], dtype=torch.int32, device="cuda")
+    keep = torch.tensor([20], dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        sdv.kv_rollback(model, kv, keep, src if _ == 0 else None, dst if _ == 0 else None)
+    torch.cuda.synchronize()
+    assert int(kv.seq_len[0]) == 20
+    for l in range(shape.n_layers):
+        k, v = kv.gather(0, l, 0, C)
+        assert torch.equal(k[3], ref[l][0][5]) and torch.equal(k[5], ref[l][0][10])
+        assert torch.equal(v[3], ref[l][1][5]) and torch.equal(k[4], ref[l][0][4])

@@ -1,0 +1,340 @@
+"""Benchmark of the single-forward verify step on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  kv_rollback(C)  ->  verify_forward([audio chunk ; drafts])  ->  accept_greedy  ->
+  kv_rollback(C + L_a + n)
+(the speculative-sampling workload times accept_sample alone).  Inputs are resident
+in HBM before timing.  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1.7b-bf16|8b-bf16-tree|toy-f32|sample]
+                  [--graph] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+METRIC = "verified tokens/s per verify pass (chunk+draft) at 1 GPU; % of HBM roofline"
+
+
+def pass_bytes(sh, T, R, C, n_branch_rows=0):
+    """Algorithmic HBM bytes of one verify pass: every weight read once (embedding:
+    the T gathered rows), KV read (C cached rows), KV written (T rows), fp32 logits
+    of the R rows acceptance needs."""
+    eb = sh.elem_bytes
+    w = sh.n_layers * (sh.layer_params() - 2 * sh.d) * eb + sh.vocab * sh.d * eb
+    w += sh.n_layers * 2 * sh.d * 4 + sh.d * 4          # fp32 norm gains
+    w += T * sh.d * eb                                   # gathered embedding rows
+    kv_row = sh.n_layers * 2 * sh.kv_dim * eb
+    return w + C * kv_row + T * kv_row + R * sh.vocab * 4
+
+
+def decoder_gemm_bytes(sh):
+    """Weight bytes streamed by the decoder projection GEMMs (q/k/v, o, gate/up, down) of one pass."""
+    d, F = sh.d, sh.ffn
+    per_layer = (sh.q_dim * d + 2 * sh.kv_dim * d + d * sh.q_dim + 3 * d * F) * sh.elem_bytes
+    return sh.n_layers * per_layer
+
+
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        n = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+        return int(n)
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0))
+
+
+def draft_under_silence(sdv, model, kv, C, L_a, gamma, silence_id=0):
+    """Greedy drafting on the GPU path (untimed setup): feed L_a silence tokens, then
+    decode gamma tokens one at a time; roll the cache back to C afterwards."""
+    import torch
+    ver = sdv.Verifier(model, kv, L_a, L_a, [L_a - 1], max_ctx=C, want_logits=False)
+    ver.set_tokens(np.full((1, L_a), silence_id))
+    res = ver.forward()
+    keep = torch.tensor([C + L_a], dtype=torch.int32, device="cuda")
+    sdv.kv_rollback(model, kv, keep)
+    drafts = [int(res.argmax[0, 0])]
+    step = sdv.Verifier(model, kv, 1, 1, [0], max_ctx=C + L_a + gamma, want_logits=False)
+    for i in range(gamma - 1):
+        step.set_tokens(np.array([[drafts[-1]]]))
+        r = step.forward()
+        keep = torch.tensor([C + L_a + i + 1], dtype=torch.int32, device="cuda")
+        sdv.kv_rollback(model, kv, keep)
+        drafts.append(int(r.argmax[0, 0]))
+    sdv.kv_rollback(model, kv, torch.tensor([C], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    return drafts
+
+
+def bench_verify(args, wl):
+    import torch
+    import speculative_decoding_verify_amd as sdv
+    from synth import make_weights, make_random_kv, uniform_tokens
+
+    sh = wl.shape
+    C = wl.ctx[0]
+    T, L_a, gamma = wl.T, wl.L_a, wl.gamma
+    t0 = time.time()
+    w = make_weights(sh, seed=wl.seed)
+    if wl.kv_init == "prefill":
+        kv_host = None
+    else:
+        kv_host = make_random_kv(sh, [C], capacity=C + T, seed=wl.seed + 1000)
+    model = sdv.DeviceModel(w)
+    kv = sdv.PagedKV(sh, 1, C + T + 64)
+    if kv_host is not None:
+        kv.load(kv_host)
+    else:
+        # prefill the context through the model itself (chunks of 128 rows)
+        ctx = uniform_tokens(C, sh.vocab, wl.seed + 2000, "ctx")
+        done = 0
+        while done < C:
+            n = min(128, C - done)
+            pv = sdv.Verifier(model, kv, n, n, [n - 1], max_ctx=done, want_logits=False)
+            pv.set_tokens(ctx[None, done:done + n])
+            pv.forward()
+            done += n
+            sdv.kv_rollback(model, kv, torch.tensor([done], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    # drafts: greedy under silence on the GPU path; main draft + runner-up branch
+    drafts = draft_under_silence(sdv, model, kv, C, L_a, gamma, wl.silence_id)
+    parent = wl.parent()
+    branch = []
+    if wl.n_branch:
+        # runner-up first token: the second-best token of the first draft position,
+        # continued greedily (untimed setup; uses the GPU path's logits)
+        ver0 = sdv.Verifier(model, kv, L_a, L_a, [L_a - 1], max_ctx=C, want_logits=True)
+        ver0.set_tokens(np.full((1, L_a), wl.silence_id))
+        lg = ver0.forward().logits[0, 0].clone()
+        lg[drafts[0]] = -float("inf")
+        branch = [int(torch.argmax(lg))] + list(uniform_tokens(wl.n_branch - 1, sh.vocab, wl.seed + 3000, "br"))
+        sdv.kv_rollback(model, kv, torch.tensor([C], dtype=torch.int32, device="cuda"))
+    audio = np.full(L_a, wl.silence_id, dtype=np.int32) if args.scenario == "silence" else \
+        uniform_tokens(L_a, sh.vocab, wl.seed + 4000, "audio")
+    tokens = np.concatenate([audio, np.asarray(drafts, np.int32), np.asarray(branch, np.int32)]).astype(np.int32)
+    rows = wl.logit_rows()
+    R = len(rows)
+    ver = sdv.Verifier(model, kv, T, L_a, rows, parent=parent, max_ctx=C, want_logits=True)
+    ver.set_tokens(tokens[None, :])
+    keep_c = torch.tensor([C], dtype=torch.int32, device="cuda")
+    acc_out = None
+
+    def step(stream=None):
+        nonlocal acc_out
+        sdv.kv_rollback(model, kv, keep_c, stream=stream)
+        res = ver.forward(stream)
+        acc_out = sdv.accept_greedy(1, T, L_a, ver.tokens, ver.parent, ver.logit_rows, res.argmax,
+                                    base_len=kv.seq_len, out=acc_out, stream=stream)
+        sdv.kv_rollback(model, kv, acc_out["keep"], acc_out["move_src"], acc_out["move_dst"], acc_out["err"],
+                        stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms = elapsed / args.steps * 1e3
+    n_acc = int(acc_out["n"][0])
+    assert int(acc_out["err"][0]) == 0 and int(ver.err[0]) == 0, "device error during bench"
+
+    # live per-kernel timing of the decoder GEMMs with HIP events recorded by the
+    # library on the launch stream, over K more steps of the same pass
+    n_gemm = 4 * sh.n_layers + 1
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_gemm)]
+    ver.set_profile_events(ev)
+    gemm_ms = []
+    for _ in range(args.steps):
+        step()
+        torch.cuda.synchronize()
+        per = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n_gemm)]
+        gemm_ms.append(per)
+    ver.set_profile_events(None)
+    gemm_ms = np.asarray(gemm_ms)                      # [steps, launches]
+    dec_ms = gemm_ms[:, :4 * sh.n_layers]              # decoder projections (one kernel symbol)
+    avg_launch_ms = float(dec_ms.mean())
+    dec_bytes = decoder_gemm_bytes(sh)
+    achieved = dec_bytes / (dec_ms.sum(axis=1).mean() * 1e-3) / 1e9
+    lm_ms = float(gemm_ms[:, -1].mean())
+    lm_bytes = sh.vocab * sh.d * sh.elem_bytes
+
+    nbytes = pass_bytes(sh, T, R, C)
+    passes_s = 1e3 / ms
+    out = {
+        "metric": METRIC,
+        "value": T * passes_s,
+        "unit": "verified tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if sh.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,0.02) weights, unit-variance synthetic KV, drafts greedy under silence)",
+        "config": {"workload": f"{wl.shape.name} verify: {sh.n_layers} layers d={sh.d} {sh.n_heads}x{sh.head_dim} "
+                               f"q heads / {sh.n_kv_heads} kv heads FFN {sh.ffn} V={sh.vocab}; C={C}; "
+                               f"{L_a} audio + {gamma} drafts" + (f" + {wl.n_branch}-token branch (tree mask)"
+                                                                  if wl.n_branch else ""),
+                   "batch": 1, "T": T, "R": R, "context": C, "scenario": args.scenario,
+                   "graph": bool(args.graph)},
+        "passes_per_s": passes_s,
+        "committed_tokens_per_pass": n_acc + 1,
+        "committed_tokens_per_s": (n_acc + 1) * passes_s,
+        "pass_roofline": {"bound": "hbm", "bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
+                          "peak_GBs": HBM_PEAK_GBS, "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "roofline": {"bound": "hbm", "kernel": "gemm_small_m (decoder q/k/v, o, gate/up, down projections)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "launches_per_pass": 4 * sh.n_layers, "avg_launch_us": avg_launch_ms * 1e3,
+                     "bytes_per_pass": dec_bytes},
+        "lm_head": {"avg_launch_us": lm_ms * 1e3, "GBs": lm_bytes / (lm_ms * 1e-3) / 1e9},
+        "setup_s": setup_s,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_verify(w, kv_host, wl, tokens, parent, rows, T)
+    return out
+
+
+def cpu_baseline_verify(w, kv_host, wl, tokens, parent, rows, T):
+    """The oracle (fp64 NumPy, bf16 rounding mode for bf16 models) timed on the host:
+    one full pass (verify + greedy acceptance + commit plan)."""
+    from oracle import BF16, EXACT
+    from oracle import accept as oacc
+    from oracle import decoder as odec
+    from synth import make_random_kv
+    sh = wl.shape
+    C = wl.ctx[0]
+    if kv_host is None:  # prefilled context: use synthetic KV of the same shape for the timing sample
+        kv_host = make_random_kv(sh, [C], capacity=C + T, seed=wl.seed + 1000)
+    mode = BF16 if sh.dtype == "bf16" else EXACT
+    cache = odec.Cache(kv_host.k, kv_host.v)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        res = odec.verify_forward(w, cache, tokens[None, :], parent, rows, mode)
+        am = [oacc.argmax_lowest(r) for r in res["logits"][0]]
+        n, nxt, path = oacc.accept_greedy(list(tokens), parent, wl.L_a, rows, am)
+        oacc.commit_plan(C, wl.L_a, path)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0 or reps >= 3:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    return {"value": T / dt, "unit": "verified tokens/s", "cores": cpu_threads(), "kind": "oracle",
+            "sample": f"{reps} full verify pass(es) of the same workload, fp64 oracle ({mode} mode), "
+                      f"{dt:.2f} s per pass"}
+
+
+def bench_sample(args):
+    import torch
+    import speculative_decoding_verify_amd as sdv
+    from synth import SAMPLE_FULL, make_sample_inputs
+    wl = SAMPLE_FULL
+    t0 = time.time()
+    si = make_sample_inputs(wl)
+    B, k, V = wl.batch, wl.k, wl.vocab
+    # two resident copies of the inputs, alternated, so consecutive steps do not hit
+    # the 256 MB last-level cache with the previous step's data
+    copies = []
+    for c in range(2):
+        copies.append(dict(tgt=torch.from_numpy(si.target_logits).cuda(), drf=torch.from_numpy(si.draft_logits).cuda(),
+                           drafts=torch.from_numpy(si.drafts).cuda(), ua=torch.from_numpy(si.u_accept).cuda(),
+                           us=torch.from_numpy(si.u_sample).cuda()))
+    smp = sdv.Sampler(B, k, V)
+    setup_s = time.time() - t0
+
+    def step(i):
+        c = copies[i & 1]
+        smp(c["tgt"], c["drf"], c["drafts"], c["ua"], c["us"], 1.0)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t_start) / args.steps * 1e3
+    nbytes = si.target_logits.nbytes + si.draft_logits.nbytes
+    out = {
+        "metric": METRIC, "value": B * k / (ms * 1e-3), "unit": "draft positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"speculative-sampling acceptance: {B} seqs x {k} drafts, V={V}, fp32"},
+        "pass_roofline": {"bound": "hbm", "bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
+                          "peak_GBs": HBM_PEAK_GBS, "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "setup_s": setup_s,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import spec_sampling as ss
+        t0 = time.perf_counter()
+        ss.accept_sample(si.target_logits.astype(np.float64), si.draft_logits.astype(np.float64), si.drafts,
+                         si.u_accept, si.u_sample)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": B * k / dt, "unit": "draft positions/s", "cores": cpu_threads(),
+                               "kind": "oracle", "sample": f"one full batch ({B}x{k}, V={V}), {dt:.2f} s"}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="1.7b-bf16", choices=["1.7b-bf16", "8b-bf16-tree", "toy-f32", "sample"])
+    ap.add_argument("--scenario", default="silence", choices=["silence", "random"])
+    ap.add_argument("--graph", action="store_true", help="replay the step from a captured HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU"}))
+        sys.exit(1)
+    import speculative_decoding_verify_amd as sdv
+    sdv.lib()  # fail loudly if the HIP library is not built
+    from synth.configs import WORKLOADS
+    if args.workload == "sample":
+        out = bench_sample(args)
+    else:
+        out = bench_verify(args, WORKLOADS[args.workload]())
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -136,7 +136,12 @@ typedef struct {
  *   margin  fp32: largest minus second-largest logit (0 on a tie)
  *   lse     fp32: log(sum_v exp(logit_v))
  *   hidden  fp32 [B, T, d] or NULL: residual stream after the last layer
- *   err     int32 [B]: device error bits (OR-ed in; the caller clears it) */
+ *   err     int32 [B]: device error bits (OR-ed in; the caller clears it)
+ *   prof_events  nullable host array of n_prof_events caller-created hipEvent_t
+ *           handles: when given, event 2i is recorded on the stream before and event
+ *           2i+1 after the i-th weight-streaming GEMM launch of the pass (decoder
+ *           projections in order q/k/v, o, gate/up, down per layer, then the LM
+ *           head), for as many launches as there are event pairs. */
 typedef struct {
   float* logits;
   int32_t* argmax;
@@ -144,6 +149,8 @@ typedef struct {
   float* lse;
   float* hidden;
   int32_t* err;
+  void* const* prof_events;
+  int32_t n_prof_events;
 } sdv_verify_out;
 
 /* Bytes of workspace sdv_verify_forward needs for this model and pass shape. */

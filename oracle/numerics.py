@@ -2,12 +2,53 @@
 import numpy as np
 
 
-def bits_to_f64(u: np.ndarray) -> np.ndarray:
-    """bf16 bit patterns (uint16) or fp32 values to fp64 (exact)."""
-    u = np.asarray(u)
+_MEMO = None  # id(array) -> (array, fp64 copy) while memoize_f64() is active
+_CHUNK = 1 << 22
+
+
+def _convert(u: np.ndarray) -> np.ndarray:
     if u.dtype == np.uint16:
         return (u.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
     return u.astype(np.float64)
+
+
+def bits_to_f64(u: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) or fp32 values to fp64 (exact).  Large arrays are
+    converted in chunks on a thread pool; the values are the same either way."""
+    u = np.asarray(u)
+    if _MEMO is not None and id(u) in _MEMO and _MEMO[id(u)][0] is u:
+        return _MEMO[id(u)][1]
+    if u.size <= _CHUNK:
+        out = _convert(u)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        flat = u.reshape(-1)
+        out = np.empty(flat.size, dtype=np.float64)
+
+        def work(i):
+            out[i:i + _CHUNK] = _convert(flat[i:i + _CHUNK])
+
+        with ThreadPoolExecutor(8) as ex:
+            list(ex.map(work, range(0, flat.size, _CHUNK)))
+        out = out.reshape(u.shape)
+    if _MEMO is not None:
+        _MEMO[id(u)] = (u, out)
+    return out
+
+
+class memoize_f64:
+    """Context manager: keep the fp64 copies of converted arrays (weights) so repeated
+    decoder passes over the same model convert each matrix once."""
+
+    def __enter__(self):
+        global _MEMO
+        _MEMO = {}
+        return self
+
+    def __exit__(self, *exc):
+        global _MEMO
+        _MEMO = None
+        return False
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:

@@ -52,7 +52,8 @@ class SdvVerifyIn(ctypes.Structure):
 
 class SdvVerifyOut(ctypes.Structure):
     _fields_ = [("logits", _vp), ("argmax", _vp), ("margin", _vp), ("lse", _vp),
-                ("hidden", _vp), ("err", _vp)]
+                ("hidden", _vp), ("err", _vp), ("prof_events", ctypes.POINTER(_vp)),
+                ("n_prof_events", _i32)]
 
 
 class SdvError(RuntimeError):
@@ -250,6 +251,21 @@ class Verifier:
         self.out = SdvVerifyOut(_ptr(self.logits), self.argmax.data_ptr(), self.margin.data_ptr(),
                                 self.lse.data_ptr(), _ptr(self.hidden), self.err.data_ptr())
 
+    def set_profile_events(self, events) -> None:
+        """events: list of torch.cuda.Event (enable_timing=True), recorded by the library
+        in pairs around its GEMM launches; None disables."""
+        if not events:
+            self._prof = None
+            self.out.prof_events = None
+            self.out.n_prof_events = 0
+            return
+        for e in events:          # torch creates the underlying event on first record
+            e.record()
+        arr = (_vp * len(events))(*[e.cuda_event for e in events])
+        self._prof = (events, arr)
+        self.out.prof_events = ctypes.cast(arr, ctypes.POINTER(_vp))
+        self.out.n_prof_events = len(events)
+
     def set_tokens(self, tokens) -> None:
         t = torch.as_tensor(np.asarray(tokens, dtype=np.int32).reshape(self.B, self.T))
         self.tokens.copy_(t)
@@ -287,6 +303,23 @@ def kv_rollback(model: DeviceModel, kv: PagedKV, keep_len: torch.Tensor, move_sr
     max_move = 0 if move_src is None else move_src.shape[-1]
     _check(lib().sdv_kv_rollback(ctypes.byref(model.desc), ctypes.byref(kv.desc), _ptr(keep_len), _ptr(move_src),
                                  _ptr(move_dst), max_move, _ptr(err), _stream(stream)), "sdv_kv_rollback")
+
+
+def prefill(model: DeviceModel, kv: PagedKV, tokens, chunk: int = MAX_T, stream=None) -> None:
+    """Append `tokens` [B, n] to the cache through verify passes of at most `chunk` rows,
+    committing each chunk (chunked prefill; every sequence starts at the same length)."""
+    tokens = np.asarray(tokens, dtype=np.int32)
+    B, n = tokens.shape
+    start = int(kv.seq_len.max().item())
+    done = 0
+    while done < n:
+        t = min(chunk, n - done)
+        ver = Verifier(model, kv, t, t, [t - 1], max_ctx=start + done, want_logits=False)
+        ver.set_tokens(tokens[:, done:done + t])
+        ver.forward(stream)
+        done += t
+        keep = torch.full((B,), start + done, dtype=torch.int32, device=model.device)
+        kv_rollback(model, kv, keep, stream=stream)
 
 
 class Sampler:

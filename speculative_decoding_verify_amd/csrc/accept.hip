@@ -12,67 +12,59 @@
 namespace sdv {
 
 // ---------------------------------------------------------------------------
-// Greedy tree walk, one thread per sequence.
-__global__ void accept_greedy_kernel(GreedyArgs a) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= a.B) return;
-  const int32_t* tok = a.tokens + (size_t)b * a.T;
+// Greedy tree walk: one block per sequence stages its tokens, the tree and the
+// argmax of every logit row in LDS; one thread walks.
+__global__ __launch_bounds__(128) void accept_greedy_kernel(GreedyArgs a) {
+  __shared__ int32_t tok[128], par[128], am_of_row[128], path[128];
+  const int b = blockIdx.x;
+  for (int j = threadIdx.x; j < a.T; j += blockDim.x) {
+    tok[j] = a.tokens[(size_t)b * a.T + j];
+    par[j] = a.parent ? a.parent[j] : j - 1;
+    am_of_row[j] = -1;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < a.R; i += blockDim.x) {
+    const int row = a.logit_rows[i];
+    if (row >= 0 && row < a.T) am_of_row[row] = a.argmax[(size_t)b * a.R + i];
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
   int node = a.L_a - 1, n = 0, next = -1;
-  int32_t* path = a.path_out ? a.path_out + (size_t)b * a.T : nullptr;
   for (;;) {
-    int r = -1;
-    for (int i = 0; i < a.R; ++i)
-      if (a.logit_rows[i] == node) { r = i; break; }
-    if (r < 0) { next = -1; break; }
-    const int am = a.argmax[(size_t)b * a.R + r];
+    const int am = am_of_row[node];
     next = am;
+    if (am < 0) break;
     int child = -1;
     for (int j = node + 1; j < a.T; ++j) {
-      const int par = a.parent ? a.parent[j] : j - 1;
-      if (par == node && tok[j] == am) {
+      if (par[j] == node && tok[j] == am) {
         if (child >= 0) { set_err(a.err, b, 0x10); break; }
         child = j;
       }
     }
     if (child < 0) break;
-    if (path) path[n] = child;
-    ++n;
+    path[n++] = child;
     node = child;
   }
   a.n_out[b] = n;
   a.next_out[b] = next;
-  if (path)
-    for (int i = n; i < a.T; ++i) path[i] = -1;
+  if (a.path_out)
+    for (int i = 0; i < a.T; ++i) a.path_out[(size_t)b * a.T + i] = i < n ? path[i] : -1;
   if (a.base_len) {
     const int base = a.base_len[b];
     if (a.keep_out) a.keep_out[b] = base + a.L_a + n;
     if (a.move_src && a.move_dst) {
-      // re-walk the accepted rows: row path[i] must end at slot base + L_a + i
-      int nd = a.L_a - 1;
+      // accepted row path[i] must end at slot base + L_a + i
       for (int i = 0; i < a.T; ++i) {
-        int src = -1, dst = -1;
-        if (i < n) {
-          int r = -1;
-          for (int q = 0; q < a.R; ++q)
-            if (a.logit_rows[q] == nd) { r = q; break; }
-          const int am = a.argmax[(size_t)b * a.R + r];
-          int child = -1;
-          for (int j = nd + 1; j < a.T && child < 0; ++j) {
-            const int par = a.parent ? a.parent[j] : j - 1;
-            if (par == nd && tok[j] == am) child = j;
-          }
-          nd = child;
-          if (child != a.L_a + i) { src = base + child; dst = base + a.L_a + i; }
-        }
-        a.move_src[(size_t)b * a.T + i] = src;
-        a.move_dst[(size_t)b * a.T + i] = dst;
+        const bool mv = i < n && path[i] != a.L_a + i;
+        a.move_src[(size_t)b * a.T + i] = mv ? base + path[i] : -1;
+        a.move_dst[(size_t)b * a.T + i] = mv ? base + a.L_a + i : -1;
       }
     }
   }
 }
 
 hipError_t launch_accept_greedy(const GreedyArgs& a, hipStream_t s) {
-  accept_greedy_kernel<<<(a.B + 63) / 64, 64, 0, s>>>(a);
+  accept_greedy_kernel<<<a.B, 128, 0, s>>>(a);
   return hipGetLastError();
 }
 

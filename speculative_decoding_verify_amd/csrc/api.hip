@@ -34,16 +34,24 @@ sdv_status fail(sdv_status st, const char* fmt, ...) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// target workgroups per launch: two per compute unit
-constexpr int TARGET_WG = 512;
+// target workgroups per launch (256 compute units)
+constexpr int TARGET_WG_GEMM = 256;
+constexpr int TARGET_WG_ATTN = 512;
 
 struct GemmPlan {
-  int NT, S, spp, ncg, MT, row_blocks;
+  GemmCfg cfg;
+  int epi, pair_mode, pair_off;
+  int S, spp, ncg, MT, row_blocks;
 };
 
-GemmPlan plan_gemm(int M, int N, int K, bool bf) {
+// N: weight rows (for pair epilogues: all rows of both halves); pairs: rotation or
+// gate/up pairs (0 for plain epilogues)
+GemmPlan plan_gemm(int M, int N, int K, bool bf, int epi, int pair_mode, int pair_off, int pairs) {
   GemmPlan p;
   const int KS = bf ? 32 : 16;
+  p.epi = epi;
+  p.pair_mode = pair_mode;
+  p.pair_off = pair_off;
   if (M <= 80) {
     p.MT = std::max(1, cdiv(M, 16));
     p.row_blocks = 1;
@@ -51,12 +59,19 @@ GemmPlan plan_gemm(int M, int N, int K, bool bf) {
     p.MT = 4;
     p.row_blocks = cdiv(M, 64);
   }
-  p.NT = 2;
-  p.ncg = cdiv(N, 16 * p.NT);
+  // configurations measured best on the decoder shapes: 4 waves splitting K,
+  // NT column tiles per wave
+  if (epi == EPI_SWIGLU || epi == EPI_PARTIAL) p.cfg = GemmCfg{4, 1, 4};
+  else p.cfg = GemmCfg{2, 1, 4};
+  if (epi == EPI_PARTIAL && N <= 2048) p.cfg = GemmCfg{2, 1, 4};
+  const int cols = p.cfg.WN * p.cfg.NT * 16;
+  p.ncg = pair_mode == PAIR_NONE ? cdiv(N, cols) : cdiv(pairs, cols / 2);
   const int steps = K / KS;
-  int S = cdiv(TARGET_WG, (long long)p.ncg * p.row_blocks);
-  S = std::max(1, std::min(S, std::max(1, steps / 4)));
-  S = std::min(S, 32);
+  int S = 1;
+  if (epi == EPI_PARTIAL) {
+    S = cdiv(TARGET_WG_GEMM, (long long)p.ncg * p.row_blocks);
+    S = std::max(1, std::min({S, 16, std::max(1, steps / 4)}));
+  }
   p.spp = cdiv(steps, S);
   p.S = cdiv(steps, p.spp);
   return p;
@@ -70,7 +85,7 @@ struct Plan {
   int split_keys, n_splits;
   size_t part_floats;
   size_t off_x, off_a, off_q, off_o, off_h, off_part, off_po, off_pml, off_stats, off_depth, off_anc,
-      off_lmrows, total;
+      off_lmrows, off_rope, total;
 };
 
 sdv_status check_model(const sdv_model* m) {
@@ -100,24 +115,25 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
   p.M = B * T;
   p.Mr = B * R;
   p.G = m->n_heads / m->n_kv_heads;
-  const int d = m->d, qd = m->n_heads * m->head_dim, kd = m->n_kv_heads * m->head_dim, F = m->ffn;
-  p.qkv = plan_gemm(p.M, qd + 2 * kd, d, p.bf);
-  p.o = plan_gemm(p.M, d, qd, p.bf);
-  p.gu = plan_gemm(p.M, 2 * F, d, p.bf);
-  p.dn = plan_gemm(p.M, d, F, p.bf);
-  p.lm = plan_gemm(p.Mr, m->vocab, d, p.bf);
-  p.lm.S = 1;
-  p.lm.spp = d / (p.bf ? 32 : 16);
-  p.part_floats = std::max({(size_t)p.qkv.S * p.M * (qd + 2 * kd), (size_t)p.o.S * p.M * d,
-                            (size_t)p.gu.S * p.M * 2 * F, (size_t)p.dn.S * p.M * d});
-  // attention: split the keys so that B * Hkv * n_splits fills the GPU
+  const int d = m->d, dh = m->head_dim, H = m->n_heads, Hkv = m->n_kv_heads, F = m->ffn;
+  const int qd = H * dh, kd = Hkv * dh;
+  p.qkv = plan_gemm(p.M, qd + 2 * kd, d, p.bf, EPI_QKV, PAIR_QKV, dh / 2, (H + 2 * Hkv) * dh / 2);
+  p.o = plan_gemm(p.M, d, qd, p.bf, EPI_PARTIAL, PAIR_NONE, 0, 0);
+  p.gu = plan_gemm(p.M, 2 * F, d, p.bf, EPI_SWIGLU, PAIR_SWIGLU, F, F);
+  p.dn = plan_gemm(p.M, d, F, p.bf, EPI_PARTIAL, PAIR_NONE, 0, 0);
+  p.lm = plan_gemm(p.Mr, m->vocab, d, p.bf, EPI_LOGITS, PAIR_NONE, 0, 0);
+  p.part_floats = std::max((size_t)p.o.S * p.M * d, (size_t)p.dn.S * p.M * d);
+  // attention: split the keys so that the grid fills the GPU (the register path
+  // has four waves per workgroup, each streaming its own key tiles)
   const int KT = p.bf ? 32 : 16;
   const int nkeys = max_ctx + T;
-  int ns = cdiv(TARGET_WG, (long long)B * m->n_kv_heads);
-  ns = std::max(1, std::min(ns, cdiv(nkeys, KT)));
+  const int NQT = cdiv(T * p.G, 16);
+  const int target = TARGET_WG_ATTN;
+  int ns = cdiv(target, (long long)B * Hkv);
+  ns = std::max(1, std::min({ns, 32, cdiv(nkeys, KT)}));
   p.split_keys = cdiv(cdiv(nkeys, ns), KT) * KT;
   p.n_splits = cdiv(nkeys, p.split_keys);
-  p.nq_pad = cdiv(T * p.G, 16) * 16;
+  p.nq_pad = NQT * 16;
 
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
@@ -127,13 +143,14 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
   p.off_o = take((size_t)p.M * qd * p.eb);
   p.off_h = take((size_t)p.M * F * p.eb);
   p.off_part = take(p.part_floats * 4);
-  const size_t nqs = (size_t)B * m->n_kv_heads * p.n_splits * p.nq_pad;
-  p.off_po = take(nqs * m->head_dim * 4);
+  const size_t nqs = (size_t)B * Hkv * p.n_splits * p.nq_pad;
+  p.off_po = take(nqs * dh * 4);
   p.off_pml = take(nqs * 2 * 4);
   p.off_stats = take((size_t)p.Mr * p.lm.ncg * 16);
   p.off_depth = take((size_t)T * 4);
   p.off_anc = take((size_t)T * 16);
   p.off_lmrows = take((size_t)p.Mr * 4);
+  p.off_rope = take((size_t)p.M * (dh / 2) * 8);
   p.total = o;
   return p;
 }
@@ -144,9 +161,34 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
     if (e_ != hipSuccess) return fail(SDV_ERR_LAUNCH, "%s: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
 
-sdv_status run_gemm(const Plan& P, const GemmPlan& g, int epi, const void* A, int lda, const int32_t* a_rows,
-                    int M, const void* W0, const void* W1, const void* W2, int N0, int N1, int N, int K,
-                    float* out, float* logits, float4* stats, hipStream_t s) {
+struct ProfEvents {
+  void* const* ev = nullptr;
+  int n_pairs = 0;
+  int next = 0;
+};
+
+// one weight-streaming GEMM launch; `a` carries the operands and epilogue targets
+sdv_status run_gemm(ProfEvents& pe, const Plan& P, const GemmPlan& g, GemmArgs a, hipStream_t s) {
+  a.steps_per_split = g.spp;
+  a.pair_mode = g.pair_mode;
+  a.pair_off = g.pair_off;
+  a.out_split_stride = (long long)a.M * a.N;
+  a.ldo = a.N;
+  a.ldl = a.N;
+  a.n_groups = g.ncg;
+  if (!a.W1) a.W1 = a.W0;
+  if (!a.W2) a.W2 = a.W0;
+  dim3 grid(g.ncg, g.S, g.row_blocks);
+  const bool prof = pe.ev && pe.next < pe.n_pairs;
+  if (prof) SDV_LAUNCH(hipEventRecord((hipEvent_t)pe.ev[2 * pe.next], s));
+  SDV_LAUNCH(launch_gemm(P.bf, g.cfg, g.MT, g.epi, grid, a, s));
+  if (prof) SDV_LAUNCH(hipEventRecord((hipEvent_t)pe.ev[2 * pe.next + 1], s));
+  if (pe.ev) ++pe.next;
+  return SDV_OK;
+}
+
+GemmArgs gemm_args(const void* A, int lda, const int32_t* a_rows, int M, const void* W0, const void* W1,
+                   const void* W2, int N0, int N1, int N, int K) {
   GemmArgs a;
   memset(&a, 0, sizeof a);
   a.A = A;
@@ -154,23 +196,13 @@ sdv_status run_gemm(const Plan& P, const GemmPlan& g, int epi, const void* A, in
   a.a_rows = a_rows;
   a.M = M;
   a.W0 = W0;
-  a.W1 = W1 ? W1 : W0;
-  a.W2 = W2 ? W2 : W0;
+  a.W1 = W1;
+  a.W2 = W2;
   a.N0 = N0;
   a.N1 = N1;
   a.N = N;
   a.K = K;
-  a.steps_per_split = g.spp;
-  a.out = out;
-  a.out_split_stride = (long long)M * N;
-  a.ldo = N;
-  a.logits = logits;
-  a.ldl = N;
-  a.stats = stats;
-  a.n_groups = g.ncg;
-  dim3 grid(g.ncg, epi == EPI_PARTIAL ? g.S : 1, g.row_blocks);
-  SDV_LAUNCH(launch_gemm(P.bf, g.MT, g.NT, epi, grid, a, s));
-  return SDV_OK;
+  return a;
 }
 
 }  // namespace
@@ -224,8 +256,15 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
   const int qd = H * dh, kd = Hkv * dh, M = P.M;
   const size_t layer_elems = (size_t)kv->n_blocks * Hkv * SDV_PAGE * dh;
 
+  ProfEvents pe;
+  if (out->prof_events && out->n_prof_events >= 2) {
+    pe.ev = out->prof_events;
+    pe.n_pairs = out->n_prof_events / 2;
+  }
+  float2* rope = (float2*)(w + P.off_rope);
   {
-    PrologueArgs a{in->parent, in->logit_rows, B, T, R, depth, anc, lm_rows, out->err};
+    PrologueArgs a{in->parent, in->logit_rows, kv->seq_len, B, T, R, depth, anc, lm_rows, rope, dh,
+                   m->rope_theta, out->err};
     SDV_LAUNCH(launch_prologue(a, s));
   }
   {
@@ -236,39 +275,41 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
     const sdv_layer& L = m->layers[l];
     void* kp = (char*)kv->k_pages + l * layer_elems * P.eb;
     void* vp = (char*)kv->v_pages + l * layer_elems * P.eb;
-    // q, k, v projections
-    st = run_gemm(P, P.qkv, EPI_PARTIAL, act, d, nullptr, M, L.wq, L.wk, L.wv, qd, qd + kd, qd + 2 * kd, d, part,
-                  nullptr, nullptr, s);
-    if (st != SDV_OK) return st;
+    // q, k, v projections with rotary embedding and paged K/V append
     {
-      QkvArgs a{part, (long long)M * (qd + 2 * kd), P.qkv.S, q, kp, vp, kv->block_table, kv->max_blocks,
-                kv->n_blocks, kv->seq_len, depth, B, T, H, Hkv, dh, in->max_ctx, m->rope_theta, out->err};
-      SDV_LAUNCH(launch_qkv_epilogue(P.bf, a, s));
+      GemmArgs a = gemm_args(act, d, nullptr, M, L.wq, L.wk, L.wv, qd, qd + kd, qd + 2 * kd, d);
+      a.qkv = QkvEpi{q, kp, vp, kv->block_table, kv->max_blocks, kv->n_blocks, kv->seq_len, rope,
+                     B, T, H, Hkv, in->max_ctx, out->err};
+      if ((st = run_gemm(pe, P, P.qkv, a, s)) != SDV_OK) return st;
     }
     {
       AttnArgs a{q, kp, vp, kv->block_table, kv->max_blocks, kv->n_blocks, kv->seq_len, anc, B, T, H, Hkv,
-                 P.split_keys, P.n_splits, (float)(1.4426950408889634 / sqrt((double)dh)), po, pml, P.nq_pad};
+                 P.split_keys, P.n_splits, (float)(1.4426950408889634 / sqrt((double)dh)), po, pml, P.nq_pad, 1,
+                 in->max_ctx};
       SDV_LAUNCH(launch_attention(P.bf, dh, a, s));
       CombineArgs c{po, pml, o, B, T, H, Hkv, dh, P.n_splits, P.nq_pad};
       SDV_LAUNCH(launch_combine(P.bf, c, s));
     }
-    st = run_gemm(P, P.o, EPI_PARTIAL, o, qd, nullptr, M, L.wo, nullptr, nullptr, d, d, d, qd, part, nullptr,
-                  nullptr, s);
-    if (st != SDV_OK) return st;
+    {
+      GemmArgs a = gemm_args(o, qd, nullptr, M, L.wo, nullptr, nullptr, d, d, d, qd);
+      a.out = part;
+      if ((st = run_gemm(pe, P, P.o, a, s)) != SDV_OK) return st;
+    }
     {
       ResidNormArgs a{x, part, (long long)M * d, P.o.S, L.ffn_norm, act, nullptr, M, d, m->eps};
       SDV_LAUNCH(launch_resid_norm(P.bf, a, s));
     }
-    st = run_gemm(P, P.gu, EPI_PARTIAL, act, d, nullptr, M, L.wg, L.wu, nullptr, F, 2 * F, 2 * F, d, part, nullptr,
-                  nullptr, s);
-    if (st != SDV_OK) return st;
+    // gate/up projections with the SwiGLU epilogue
     {
-      SwigluArgs a{part, (long long)M * 2 * F, P.gu.S, h, M, F};
-      SDV_LAUNCH(launch_swiglu(P.bf, a, s));
+      GemmArgs a = gemm_args(act, d, nullptr, M, L.wg, L.wu, nullptr, F, 2 * F, 2 * F, d);
+      a.out_act = h;
+      if ((st = run_gemm(pe, P, P.gu, a, s)) != SDV_OK) return st;
     }
-    st = run_gemm(P, P.dn, EPI_PARTIAL, h, F, nullptr, M, L.wd, nullptr, nullptr, d, d, d, F, part, nullptr,
-                  nullptr, s);
-    if (st != SDV_OK) return st;
+    {
+      GemmArgs a = gemm_args(h, F, nullptr, M, L.wd, nullptr, nullptr, d, d, d, F);
+      a.out = part;
+      if ((st = run_gemm(pe, P, P.dn, a, s)) != SDV_OK) return st;
+    }
     {
       const bool last = l + 1 == m->n_layers;
       const float* g = last ? m->final_norm : m->layers[l + 1].attn_norm;
@@ -276,9 +317,12 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
       SDV_LAUNCH(launch_resid_norm(P.bf, a, s));
     }
   }
-  st = run_gemm(P, P.lm, EPI_LOGITS, act, d, lm_rows, P.Mr, m->lm_head, nullptr, nullptr, V, V, V, d, nullptr,
-                out->logits, stats, s);
-  if (st != SDV_OK) return st;
+  {
+    GemmArgs a = gemm_args(act, d, lm_rows, P.Mr, m->lm_head, nullptr, nullptr, V, V, V, d);
+    a.logits = out->logits;
+    a.stats = stats;
+    if ((st = run_gemm(pe, P, P.lm, a, s)) != SDV_OK) return st;
+  }
   {
     RowReduceArgs a{stats, P.Mr, P.lm.ncg, out->argmax, out->margin, out->lse};
     SDV_LAUNCH(launch_row_reduce(a, s));

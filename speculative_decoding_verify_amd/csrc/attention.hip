@@ -48,7 +48,7 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
   const int q_base = (blockIdx.z % a.n_qg) * NW * NQW;
   const int r = lane & 15, lg = lane >> 4;
   const int G = a.H / a.Hkv;
-  const int C = a.seq_len[b];
+  const int C = min(max(a.seq_len[b], 0), a.max_ctx);
   const int nkeys = C + a.T;
   const int nq = a.T * G;
   const int NQT = (nq + 15) >> 4;
@@ -214,22 +214,245 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
   }
 }
 
+// Register path for few query tiles per kv head (at most 4): every wave holds all
+// query tiles of the head and streams its own interleaved key tiles straight from
+// the pages into MFMA operands, one tile ahead; the 4 waves of the workgroup merge
+// their states through LDS at the end and write one partial per split.
+template <typename T, int DH, int NQT>
+__global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int VE = Vec16<T>::N;
+  constexpr int KS = 4 * VE;
+  constexpr int KT = BF ? 32 : 16;
+  constexpr int PE = BF ? 8 : 4;
+  constexpr int NKA = (BF ? 2 : 1) * (DH / KS);   // K operand loads per tile
+  constexpr int NVA = DH / 16;                    // V operand loads per tile
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, r = lane & 15, lg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = a.H / a.Hkv;
+  const int C = min(max(a.seq_len[b], 0), a.max_ctx);
+  const int nkeys = C + a.T;
+  const int nq = a.T * G;
+  const int k_begin = split * a.split_keys;
+  const int k_end = min(nkeys, k_begin + a.split_keys);
+  const int ntiles = k_end > k_begin ? (k_end - k_begin + KT - 1) / KT : 0;
+  const int32_t* bt = a.block_table + (size_t)b * a.max_blocks;
+  const T* kp = (const T*)a.k_pages;
+  const T* vp = (const T*)a.v_pages;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+
+  u32x4 qreg[NQT][DH / KS];
+  uint32_t anc[NQT][4];
+  float mrun[NQT], lrun[NQT];
+  f32x4 acc[NQT][DH / 16];
+#pragma unroll
+  for (int j = 0; j < NQT; ++j) {
+    const int qi = j * 16 + r;
+    const bool ok = qi < nq;
+    const int t = ok ? qi / G : 0;
+    const int h = g * G + (ok ? qi % G : 0);
+    const T* qp = (const T*)a.q + ((size_t)(b * a.T + t) * a.H + h) * DH + lg * VE;
+#pragma unroll
+    for (int ks = 0; ks < DH / KS; ++ks) qreg[j][ks] = ok ? ld16(qp + ks * KS) : zero;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) anc[j][c] = a.anc[t * 4 + c];
+    mrun[j] = -1e30f;
+    lrun[j] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt) acc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // load the K and V^T operands of key tile `it` (relative to k_begin); slots at or
+  // beyond the end of the sequence read as zero
+  auto load_tile = [&](int it, u32x4 (&ko)[NKA], u32x4 (&vo)[NVA]) {
+    const int kt0 = k_begin + it * KT;
+    // K rows: bf16 tile has two 16-key halves whose rows map to keys 8*(r/4) + r%4 (+4)
+#pragma unroll
+    for (int hv = 0; hv < (BF ? 2 : 1); ++hv) {
+      const int key = BF ? 8 * (r >> 2) + (r & 3) + 4 * hv : r;
+      const int slot = kt0 + key;
+      const bool ok = it < ntiles && slot < nkeys;
+      int phys = ok ? bt[slot >> 4] : 0;
+      const bool okp = ok && phys >= 0 && phys < a.n_blocks;
+      const T* src = kp + (((size_t)(okp ? phys : 0) * a.Hkv + g) * 16 + (slot & 15)) * DH + lg * VE;
+#pragma unroll
+      for (int ks = 0; ks < DH / KS; ++ks) ko[hv * (DH / KS) + ks] = okp ? ld16(src + ks * KS) : zero;
+    }
+    // V^T: lane holds dh row dt*16 + r for keys PE*lg .. PE*lg + PE - 1
+    const int slot0 = kt0 + PE * lg;
+    const bool okv = it < ntiles && slot0 < nkeys;
+    int physv = okv ? bt[slot0 >> 4] : 0;
+    const bool okpv = okv && physv >= 0 && physv < a.n_blocks;
+    const T* vsrc = vp + (((size_t)(okpv ? physv : 0) * a.Hkv + g) * DH + r) * 16 + (slot0 & 15);
+#pragma unroll
+    for (int dt = 0; dt < NVA; ++dt) {
+      u32x4 v = okpv ? ld16(vsrc + (size_t)dt * 16 * 16) : zero;
+      if (okpv && slot0 + PE > nkeys) {
+        T e[VE];
+        __builtin_memcpy(e, &v, 16);
+#pragma unroll
+        for (int i = 0; i < VE; ++i)
+          if (slot0 + i >= nkeys) e[i] = T(0);
+        __builtin_memcpy(&v, e, 16);
+      }
+      vo[dt] = v;
+    }
+  };
+
+  auto compute_tile = [&](int it, const u32x4 (&ko)[NKA], const u32x4 (&vo)[NVA]) {
+    const int kt0 = k_begin + it * KT;
+#pragma unroll
+    for (int j = 0; j < NQT; ++j) {
+      if (j * 16 >= nq) continue;
+      float sv[PE];
+      if constexpr (BF) {
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < DH / KS; ++ks) {
+          s0 = mma16<T>(ko[ks], qreg[j][ks], s0);
+          s1 = mma16<T>(ko[DH / KS + ks], qreg[j][ks], s1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { sv[i] = s0[i]; sv[4 + i] = s1[i]; }
+      } else {
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < DH / KS; ++ks) s0 = mma16<T>(ko[ks], qreg[j][ks], s0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[i] = s0[i];
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < PE; ++e) {
+        const int s = kt0 + PE * lg + e;
+        bool vis = s < k_end;
+        if (vis && s >= C) {
+          const int jr = s - C;
+          vis = (anc[j][jr >> 5] >> (jr & 31)) & 1u;
+        }
+        sv[e] = vis ? sv[e] * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[e]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(mrun[j], mx);
+      const float alpha = exp2f(mrun[j] - mnew);
+      mrun[j] = mnew;
+      float ps = 0.f, p[PE];
+#pragma unroll
+      for (int e = 0; e < PE; ++e) { p[e] = exp2f(sv[e] - mnew); ps += p[e]; }
+      lrun[j] = lrun[j] * alpha + ps;
+      u32x4 pb;
+      if constexpr (BF) {
+        pb.x = (uint32_t)f2bf(p[0]) | ((uint32_t)f2bf(p[1]) << 16);
+        pb.y = (uint32_t)f2bf(p[2]) | ((uint32_t)f2bf(p[3]) << 16);
+        pb.z = (uint32_t)f2bf(p[4]) | ((uint32_t)f2bf(p[5]) << 16);
+        pb.w = (uint32_t)f2bf(p[6]) | ((uint32_t)f2bf(p[7]) << 16);
+      } else {
+        pb.x = __float_as_uint(p[0]); pb.y = __float_as_uint(p[1]);
+        pb.z = __float_as_uint(p[2]); pb.w = __float_as_uint(p[3]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DH / 16; ++dt) {
+        acc[j][dt] *= alpha;
+        acc[j][dt] = mma16<T>(vo[dt], pb, acc[j][dt]);
+      }
+    }
+  };
+
+  // tiles w, w+4, w+8, ... of the split, one tile ahead
+  u32x4 kA[NKA], vA[NVA], kB[NKA], vB[NVA];
+  load_tile(w, kA, vA);
+  for (int it = w; it < ntiles; it += 8) {
+    load_tile(it + 4, kB, vB);
+    compute_tile(it, kA, vA);
+    if (it + 4 >= ntiles) break;
+    load_tile(it + 8, kA, vA);
+    compute_tile(it + 4, kB, vB);
+  }
+
+  // ---- merge the 4 waves: LDS holds each wave's (m, l) and O^T accumulators
+  __shared__ float sm[4][NQT][64], sl[4][NQT][64];
+  __shared__ float so[4][NQT][DH / 16][4][64];
+#pragma unroll
+  for (int j = 0; j < NQT; ++j) {
+    float l = lrun[j];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    sm[w][j][lane] = mrun[j];
+    sl[w][j][lane] = l;
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) so[w][j][dt][i][lane] = acc[j][dt][i];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < NQT * 64; idx += 256) {
+    const int j = idx / 64, ln = idx % 64;
+    const int qi = j * 16 + (ln & 15);
+    if (qi >= a.nq_pad) continue;
+    float M = sm[0][j][ln];
+#pragma unroll
+    for (int k = 1; k < 4; ++k) M = fmaxf(M, sm[k][j][ln]);
+    float wk[4], L = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { wk[k] = exp2f(sm[k][j][ln] - M); L += wk[k] * sl[k][j][ln]; }
+    const size_t base = (((size_t)b * a.Hkv + g) * a.n_splits + split) * a.nq_pad + qi;
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v += wk[k] * so[k][j][dt][i][ln];
+        a.po[base * DH + dt * 16 + 4 * (ln >> 4) + i] = v;
+      }
+    if ((ln >> 4) == 0) {
+      a.pml[base * 2] = M;
+      a.pml[base * 2 + 1] = L;
+    }
+  }
+}
+
 template <typename T, int DH>
-__global__ void attn_combine(CombineArgs a) {
+__global__ __launch_bounds__(DH) void attn_combine(CombineArgs a) {
+  constexpr int MAXS = 32;
   const int row = blockIdx.y, h = blockIdx.x;
   const int b = row / a.T, t = row % a.T;
   const int G = a.H / a.Hkv, g = h / G, qi = t * G + h % G;
   const size_t base0 = (((size_t)b * a.Hkv + g) * a.n_splits) * a.nq_pad + qi;
+  float m[MAXS], l[MAXS], v[MAXS];
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s) {
+    if (s < a.n_splits) {
+      const size_t bs = base0 + (size_t)s * a.nq_pad;
+      m[s] = a.pml[bs * 2];
+      l[s] = a.pml[bs * 2 + 1];
+      v[s] = a.po[bs * DH + threadIdx.x];
+    }
+  }
   float M = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, a.pml[(base0 + (size_t)s * a.nq_pad) * 2]);
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s)
+    if (s < a.n_splits) M = fmaxf(M, m[s]);
   float num = 0.f, den = 0.f;
-  for (int s = 0; s < a.n_splits; ++s) {
-    const size_t bs = base0 + (size_t)s * a.nq_pad;
-    const float wgt = exp2f(a.pml[bs * 2] - M);
-    den += wgt * a.pml[bs * 2 + 1];
-    num += wgt * a.po[bs * DH + threadIdx.x];
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s) {
+    if (s < a.n_splits) {
+      const float wgt = exp2f(m[s] - M);
+      den += wgt * l[s];
+      num += wgt * v[s];
+    }
   }
   ((T*)a.o)[((size_t)row * a.H + h) * DH + threadIdx.x] = from_f<T>(num / den);
+}
+
+// the register path serves heads with few query tiles (its merge buffers and
+// operands grow with NQT and dh)
+bool attn_uses_reg_path(bool bf, int dh, int NQT) {
+  if (dh == 64) return NQT <= (bf ? 3 : 2);
+  return NQT <= 1;
 }
 
 // query tiles per wave that fit without register spills
@@ -253,6 +476,16 @@ template <typename T, int DH>
 static hipError_t launch_attn_t(AttnArgs a, hipStream_t s) {
   const int G = a.H / a.Hkv;
   const int NQT = (a.T * G + 15) / 16;
+  if (attn_uses_reg_path(sizeof(T) == 2, DH, NQT)) {
+    dim3 grid(a.n_splits, a.Hkv, a.B);
+    a.n_qg = 1;
+    switch (NQT) {
+      case 1: attn_reg<T, DH, 1><<<grid, 256, 0, s>>>(a); break;
+      case 2: attn_reg<T, DH, 2><<<grid, 256, 0, s>>>(a); break;
+      default: attn_reg<T, DH, 3><<<grid, 256, 0, s>>>(a); break;
+    }
+    return hipGetLastError();
+  }
   int nqw, nw;
   a.n_qg = attn_shape<T, DH>(NQT, &nqw, &nw);
   dim3 grid(a.n_splits, a.Hkv, a.B * a.n_qg);
@@ -278,6 +511,7 @@ hipError_t launch_attention(bool is_bf16, int dh, const AttnArgs& a, hipStream_t
 }
 
 hipError_t launch_combine(bool is_bf16, const CombineArgs& a, hipStream_t s) {
+  if (a.n_splits > 32) return hipErrorInvalidValue;
   dim3 grid(a.H, a.B * a.T);
   if (is_bf16) {
     if (a.dh == 64) attn_combine<bf16, 64><<<grid, 64, 0, s>>>(a);

@@ -5,7 +5,21 @@
 
 namespace sdv {
 
-enum { EPI_PARTIAL = 0, EPI_LOGITS = 1 };
+enum { EPI_PARTIAL = 0, EPI_LOGITS = 1, EPI_QKV = 2, EPI_SWIGLU = 3 };
+enum { PAIR_NONE = 0, PAIR_SWIGLU = 1, PAIR_QKV = 2 };
+
+// QKV epilogue: rotary embedding + q write + paged K/V append
+struct QkvEpi {
+  void* q;                  // [M, H*dh]
+  void* k_pages;            // this layer: [n_blocks][Hkv][16][dh]
+  void* v_pages;            //             [n_blocks][Hkv][dh][16]
+  const int32_t* block_table;
+  int max_blocks, n_blocks;
+  const int32_t* seq_len;
+  const float2* rope;       // [B*T][dh/2] (cos, sin) of each chunk row's position
+  int B, T, H, Hkv, max_ctx;
+  int32_t* err;
+};
 
 struct GemmArgs {
   const void* A;            // activations, rows of lda elements
@@ -17,16 +31,26 @@ struct GemmArgs {
   const void* W2;           // columns n >= N1: row n - N1 of W2
   int N0, N1, N, K;
   int steps_per_split;      // k steps (32 bf16 / 16 fp32 elements) per workgroup split
-  float* out;               // EPI_PARTIAL: out[split * out_split_stride + m * ldo + n]
+  int pair_mode;            // column pairing for the SWIGLU / QKV epilogues
+  int pair_off;             // SWIGLU: F (gate row f pairs with up row f); QKV: dh/2
+  float* out;               // PARTIAL: out[split * out_split_stride + m * ldo + n]
   long long out_split_stride;
   int ldo;
-  float* logits;            // EPI_LOGITS: logits[m * ldl + n] (nullable)
+  void* out_act;            // SWIGLU: h [M, F]
+  QkvEpi qkv;               // QKV epilogue arguments
+  float* logits;            // LOGITS: logits[m * ldl + n] (nullable)
   int ldl;
-  float4* stats;            // EPI_LOGITS: stats[m * n_groups + column group]
+  float4* stats;            // LOGITS: stats[m * n_groups + column group]
   int n_groups;
 };
 
-hipError_t launch_gemm(bool is_bf16, int MT, int NT, int epi, dim3 grid, const GemmArgs& a, hipStream_t s);
+// launch configuration: NT column tiles per wave, WN x WK waves per workgroup
+struct GemmCfg {
+  int NT, WN, WK;
+};
+
+hipError_t launch_gemm(bool is_bf16, const GemmCfg& c, int MT, int epi, dim3 grid, const GemmArgs& a,
+                       hipStream_t s);
 
 struct AttnArgs {
   const void* q;            // [B*T, H*dh]
@@ -43,9 +67,11 @@ struct AttnArgs {
   float* pml;               // [B][Hkv][n_splits][nq_pad][2] (running max in log2 units, sum)
   int nq_pad;
   int n_qg;                 // query-tile groups per (sequence, kv head); grid.z = B * n_qg
+  int max_ctx;              // cached lengths are clamped to [0, max_ctx] (max_ctx + T fits the table)
 };
 
 hipError_t launch_attention(bool is_bf16, int dh, const AttnArgs& a, hipStream_t s);
+bool attn_uses_reg_path(bool bf, int dh, int NQT);  // keys per tile: 32 bf16 / 16 fp32 either way
 
 struct CombineArgs {
   const float* po;
@@ -58,10 +84,14 @@ hipError_t launch_combine(bool is_bf16, const CombineArgs& a, hipStream_t s);
 struct PrologueArgs {
   const int32_t* parent;    // nullable
   const int32_t* logit_rows;
+  const int32_t* seq_len;   // [B] cached length: rotary positions are seq_len + depth
   int B, T, R;
   int32_t* depth;           // [T]
   uint32_t* anc;            // [T][4]
   int32_t* lm_rows;         // [B*R] = b*T + logit_rows[r]
+  float2* rope;             // [B*T][dh/2] (cos, sin)
+  int dh;
+  float rope_theta;
   int32_t* err;             // [B]
 };
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
@@ -90,32 +120,6 @@ struct ResidNormArgs {
   float eps;
 };
 hipError_t launch_resid_norm(bool is_bf16, const ResidNormArgs& a, hipStream_t s);
-
-struct QkvArgs {
-  const float* part;        // [S][M][(H+2Hkv)*dh]
-  long long part_stride;
-  int S;
-  void* q;                  // [M, H*dh]
-  void* k_pages;            // this layer
-  void* v_pages;
-  const int32_t* block_table;
-  int max_blocks, n_blocks;
-  const int32_t* seq_len;
-  const int32_t* depth;
-  int B, T, H, Hkv, dh, max_ctx;
-  float rope_theta;
-  int32_t* err;
-};
-hipError_t launch_qkv_epilogue(bool is_bf16, const QkvArgs& a, hipStream_t s);
-
-struct SwigluArgs {
-  const float* part;        // [S][M][2F]: gate columns then up columns
-  long long part_stride;
-  int S;
-  void* h;                  // [M, F]
-  int M, F;
-};
-hipError_t launch_swiglu(bool is_bf16, const SwigluArgs& a, hipStream_t s);
 
 struct RowReduceArgs {
   const float4* stats;      // [rows][n_groups]

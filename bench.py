@@ -232,7 +232,7 @@ def bench_verify(args, wl):
 def cpu_baseline_verify(w, kv_host, wl, tokens, parent, rows, T):
     """The oracle (fp64 NumPy, bf16 rounding mode for bf16 models) timed on the host:
     one full pass (verify + greedy acceptance + commit plan)."""
-    from oracle import BF16, EXACT
+    from oracle import BF16_KV, EXACT
     from oracle import accept as oacc
     from oracle import decoder as odec
     from synth import make_random_kv
@@ -240,7 +240,7 @@ def cpu_baseline_verify(w, kv_host, wl, tokens, parent, rows, T):
     C = wl.ctx[0]
     if kv_host is None:  # prefilled context: use synthetic KV of the same shape for the timing sample
         kv_host = make_random_kv(sh, [C], capacity=C + T, seed=wl.seed + 1000)
-    mode = BF16 if sh.dtype == "bf16" else EXACT
+    mode = BF16_KV if sh.dtype == "bf16" else EXACT
     cache = odec.Cache(kv_host.k, kv_host.v)
     reps = 0
     t0 = time.perf_counter()

@@ -4,14 +4,18 @@ TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the bench's
 CPU-baseline leg may import or run anything in this package; the product path
 never does.  It shares no code with the HIP path.
 
-It is plain NumPy in fp64, deliberately slow and direct.  Two numeric modes:
+It is plain NumPy in fp64, deliberately slow and direct.  Three numeric modes:
 
-  EXACT  every value in fp64, no intermediate rounding: the mathematical
-         definition.  Reference for fp32 models and for all property pins.
-  BF16   fp64 arithmetic that rounds to bf16 (nearest-even) exactly where a
-         bf16 model stores bf16 values (normed activations, q/k/v after RoPE,
-         attention output, SwiGLU output) and to fp32 where it keeps the fp32
-         residual stream.  Reference for bf16 models.
+  EXACT    every value in fp64, no intermediate rounding: the mathematical
+           definition.  Reference for fp32 models and for all property pins.
+  BF16_KV  fp64 arithmetic on bf16 weights; the only rounding is of keys (after
+           RoPE) and values to bf16 when they are written to the cache.
+           Reference for bf16 models, whose kernels store weights and the KV cache
+           in bf16 and carry activations at fp32 precision.
+  BF16     additionally rounds every stored activation to bf16 (normed rows, q,
+           attention output, SwiGLU output) and keeps an fp32 residual: a model
+           that stores all activations in bf16.  Used to measure how far such
+           rounding alone moves the logits.
 
 Modules:
   numerics      bf16 / fp32 rounding, bf16 bit patterns to fp64
@@ -26,3 +30,4 @@ force on tiny inputs, invariants such as verify == token-by-token decoding).
 """
 EXACT = "exact"
 BF16 = "bf16"
+BF16_KV = "bf16-kv"

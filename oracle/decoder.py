@@ -21,7 +21,7 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from . import BF16, EXACT
+from . import BF16, BF16_KV, EXACT
 from .numerics import bits_to_f64, round_bf16, round_f32
 
 
@@ -30,13 +30,15 @@ def _identity(x):
 
 
 class _Rounding:
-    """Where values are rounded: bf16 storage points and the fp32 residual stream."""
+    """Where values are rounded: bf16 activations, the fp32 residual stream, and the
+    bf16 keys/values written to the cache."""
 
     def __init__(self, mode: str):
-        if mode not in (EXACT, BF16):
+        if mode not in (EXACT, BF16, BF16_KV):
             raise ValueError(mode)
         self.act = round_bf16 if mode == BF16 else _identity
         self.res = round_f32 if mode == BF16 else _identity
+        self.kv = round_bf16 if mode in (BF16, BF16_KV) else _identity
 
 
 def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
@@ -185,8 +187,8 @@ def verify_forward(w, cache: Cache, tokens: np.ndarray, parent: Optional[Sequenc
             k = (a @ wk.T).reshape(T, Hkv, dh)
             v = (a @ wv.T).reshape(T, Hkv, dh)
             q = rnd.act(rope(q, pos, sh.rope_theta))
-            k = rnd.act(rope(k, pos, sh.rope_theta))
-            v = rnd.act(v)
+            k = rnd.kv(rope(k, pos, sh.rope_theta))
+            v = rnd.kv(v)
             k_new[b][l], v_new[b][l] = k, v
 
             o = attend(q, cache.k[b][l], cache.v[b][l], k, v, vis)

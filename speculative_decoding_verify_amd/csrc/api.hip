@@ -138,10 +138,11 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
   p.off_x = take((size_t)p.M * d * 4);
-  p.off_a = take((size_t)p.M * d * p.eb);
-  p.off_q = take((size_t)p.M * qd * p.eb);
-  p.off_o = take((size_t)p.M * qd * p.eb);
-  p.off_h = take((size_t)p.M * F * p.eb);
+  // activations are fp32 whatever the storage type of weights and cache
+  p.off_a = take((size_t)p.M * d * 4);
+  p.off_q = take((size_t)p.M * qd * 4);
+  p.off_o = take((size_t)p.M * qd * 4);
+  p.off_h = take((size_t)p.M * F * 4);
   p.off_part = take(p.part_floats * 4);
   const size_t nqs = (size_t)B * Hkv * p.n_splits * p.nq_pad;
   p.off_po = take(nqs * dh * 4);

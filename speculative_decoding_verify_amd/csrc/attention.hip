@@ -1,4 +1,5 @@
 // Chunked causal / tree-masked GQA attention over a paged KV cache, split over keys.
+// Queries and the output are fp32; keys and values are the cache type.
 //
 // A verify pass attends from T chunk rows (audio chunk + drafts + branch rows) to
 // the C cached slots and to the chunk rows that are ancestors-or-self of each row
@@ -26,6 +27,41 @@
 #include <algorithm>
 
 namespace sdv {
+
+// The probabilities feed the P.V contraction as bf16 MFMA operands.  Rounding p
+// itself to bf16 would perturb the attention output by ~2^-9 relative, far above
+// fp32 accumulation noise; instead p = hi + lo with hi = bf16(p), lo = bf16(p - hi)
+// (about 16 significant bits), and P.V takes one MFMA per part.  The normaliser
+// sums the unrounded fp32 p.
+SDV_DEV void split_probs(const float (&p)[8], u32x4& hi, u32x4& lo) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const bf16 hb = f2bf(p[e]);
+    h[e] = hb;
+    l[e] = f2bf(p[e] - bf2f(hb));
+  }
+  hi.x = h[0] | (h[1] << 16); hi.y = h[2] | (h[3] << 16); hi.z = h[4] | (h[5] << 16); hi.w = h[6] | (h[7] << 16);
+  lo.x = l[0] | (l[1] << 16); lo.y = l[2] | (l[3] << 16); lo.z = l[4] | (l[5] << 16); lo.w = l[6] | (l[7] << 16);
+}
+
+// Load the query operand of one lane (fp32 q, row offset `off`): for bf16 caches the 8
+// values of each k step become a hi + lo pair of bf16 operands, for fp32 caches the
+// 4 values are the operand.
+template <bool BF, int DH, int KS, int VE>
+SDV_DEV void load_q(const void* q, size_t off, bool ok, int lg, u32x4 (&out)[DH / KS][BF ? 2 : 1]) {
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const float* qp = (const float*)q + off + lg * VE;
+#pragma unroll
+  for (int ks = 0; ks < DH / KS; ++ks) {
+    if constexpr (BF) {
+      const u32x4 lo4 = ok ? ld16(qp + ks * KS) : zero, hi4 = ok ? ld16(qp + ks * KS + 4) : zero;
+      split_hi_lo(lo4, hi4, out[ks][0], out[ks][1]);
+    } else {
+      out[ks][0] = ok ? ld16(qp + ks * KS) : zero;
+    }
+  }
+}
 
 template <typename T, int DH, int NQW>
 __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
@@ -59,7 +95,8 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
   const T* vp = (const T*)a.v_pages;
 
   // queries of this wave: tiles w, w + NW, ...
-  u32x4 qreg[NQW][DH / KS];
+  constexpr int QP = BF ? 2 : 1;   // q enters bf16 MFMAs as a hi + lo pair
+  u32x4 qreg[NQW][DH / KS][QP];
   uint32_t anc[NQW][4];
   float mrun[NQW], lrun[NQW];
   f32x4 acc[NQW][DH / 16];
@@ -70,9 +107,7 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
     const bool ok = qi < nq;
     const int t = ok ? qi / G : 0;
     const int h = g * G + (ok ? qi % G : 0);
-    const T* qp = (const T*)a.q + ((size_t)(b * a.T + t) * a.H + h) * DH + lg * VE;
-#pragma unroll
-    for (int ks = 0; ks < DH / KS; ++ks) qreg[j][ks] = ok ? ld16(qp + ks * KS) : zero;
+    load_q<BF, DH, KS, VE>(a.q, ((size_t)(b * a.T + t) * a.H + h) * DH, ok, lg, qreg[j]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) anc[j][c] = a.anc[t * 4 + c];
     mrun[j] = -1e30f;
@@ -132,8 +167,11 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
         for (int ks = 0; ks < DH / KS; ++ks) {
           const u32x4 k0 = ld16(&ldsK[row0 * KROW + ks * KS + lg * VE]);
           const u32x4 k1 = ld16(&ldsK[(row0 + 4) * KROW + ks * KS + lg * VE]);
-          s0 = mma16<T>(k0, qreg[j][ks], s0);
-          s1 = mma16<T>(k1, qreg[j][ks], s1);
+#pragma unroll
+          for (int qp = 0; qp < QP; ++qp) {
+            s0 = mma16<T>(k0, qreg[j][ks][qp], s0);
+            s1 = mma16<T>(k1, qreg[j][ks][qp], s1);
+          }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) { sv[i] = s0[i]; sv[4 + i] = s1[i]; }
@@ -141,7 +179,7 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < DH / KS; ++ks)
-          s0 = mma16<T>(ld16(&ldsK[r * KROW + ks * KS + lg * VE]), qreg[j][ks], s0);
+          s0 = mma16<T>(ld16(&ldsK[r * KROW + ks * KS + lg * VE]), qreg[j][ks][0], s0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sv[i] = s0[i];
       }
@@ -169,19 +207,18 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
       lrun[j] = lrun[j] * alpha + ps;
 #pragma unroll
       for (int dt = 0; dt < DH / 16; ++dt) acc[j][dt] *= alpha;
-      // ---- O^T += V^T P^T
-      u32x4 pb;
+      // ---- O^T += V^T P^T (bf16: P as a hi + lo pair, see split_probs)
       if constexpr (BF) {
-        pb.x = (uint32_t)f2bf(p[0]) | ((uint32_t)f2bf(p[1]) << 16);
-        pb.y = (uint32_t)f2bf(p[2]) | ((uint32_t)f2bf(p[3]) << 16);
-        pb.z = (uint32_t)f2bf(p[4]) | ((uint32_t)f2bf(p[5]) << 16);
-        pb.w = (uint32_t)f2bf(p[6]) | ((uint32_t)f2bf(p[7]) << 16);
+        u32x4 phi, plo;
+        split_probs(p, phi, plo);
 #pragma unroll
         for (int dt = 0; dt < DH / 16; ++dt) {
           const u32x4 va = ld16(&ldsV[((lg >> 1) * DH + dt * 16 + r) * VROW + (lg & 1) * 8]);
-          acc[j][dt] = mma16<T>(va, pb, acc[j][dt]);
+          acc[j][dt] = mma16<T>(va, phi, acc[j][dt]);
+          acc[j][dt] = mma16<T>(va, plo, acc[j][dt]);
         }
       } else {
+        u32x4 pb;
         pb.x = __float_as_uint(p[0]); pb.y = __float_as_uint(p[1]);
         pb.z = __float_as_uint(p[2]); pb.w = __float_as_uint(p[3]);
 #pragma unroll
@@ -242,7 +279,8 @@ __global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
   const T* vp = (const T*)a.v_pages;
   const u32x4 zero = {0u, 0u, 0u, 0u};
 
-  u32x4 qreg[NQT][DH / KS];
+  constexpr int QP = BF ? 2 : 1;
+  u32x4 qreg[NQT][DH / KS][QP];
   uint32_t anc[NQT][4];
   float mrun[NQT], lrun[NQT];
   f32x4 acc[NQT][DH / 16];
@@ -252,9 +290,7 @@ __global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
     const bool ok = qi < nq;
     const int t = ok ? qi / G : 0;
     const int h = g * G + (ok ? qi % G : 0);
-    const T* qp = (const T*)a.q + ((size_t)(b * a.T + t) * a.H + h) * DH + lg * VE;
-#pragma unroll
-    for (int ks = 0; ks < DH / KS; ++ks) qreg[j][ks] = ok ? ld16(qp + ks * KS) : zero;
+    load_q<BF, DH, KS, VE>(a.q, ((size_t)(b * a.T + t) * a.H + h) * DH, ok, lg, qreg[j]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) anc[j][c] = a.anc[t * 4 + c];
     mrun[j] = -1e30f;
@@ -310,15 +346,18 @@ __global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < DH / KS; ++ks) {
-          s0 = mma16<T>(ko[ks], qreg[j][ks], s0);
-          s1 = mma16<T>(ko[DH / KS + ks], qreg[j][ks], s1);
+#pragma unroll
+          for (int qp = 0; qp < QP; ++qp) {
+            s0 = mma16<T>(ko[ks], qreg[j][ks][qp], s0);
+            s1 = mma16<T>(ko[DH / KS + ks], qreg[j][ks][qp], s1);
+          }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) { sv[i] = s0[i]; sv[4 + i] = s1[i]; }
       } else {
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < DH / KS; ++ks) s0 = mma16<T>(ko[ks], qreg[j][ks], s0);
+        for (int ks = 0; ks < DH / KS; ++ks) s0 = mma16<T>(ko[ks], qreg[j][ks][0], s0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sv[i] = s0[i];
       }
@@ -343,20 +382,24 @@ __global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < PE; ++e) { p[e] = exp2f(sv[e] - mnew); ps += p[e]; }
       lrun[j] = lrun[j] * alpha + ps;
-      u32x4 pb;
       if constexpr (BF) {
-        pb.x = (uint32_t)f2bf(p[0]) | ((uint32_t)f2bf(p[1]) << 16);
-        pb.y = (uint32_t)f2bf(p[2]) | ((uint32_t)f2bf(p[3]) << 16);
-        pb.z = (uint32_t)f2bf(p[4]) | ((uint32_t)f2bf(p[5]) << 16);
-        pb.w = (uint32_t)f2bf(p[6]) | ((uint32_t)f2bf(p[7]) << 16);
+        u32x4 phi, plo;
+        split_probs(p, phi, plo);
+#pragma unroll
+        for (int dt = 0; dt < DH / 16; ++dt) {
+          acc[j][dt] *= alpha;
+          acc[j][dt] = mma16<T>(vo[dt], phi, acc[j][dt]);
+          acc[j][dt] = mma16<T>(vo[dt], plo, acc[j][dt]);
+        }
       } else {
+        u32x4 pb;
         pb.x = __float_as_uint(p[0]); pb.y = __float_as_uint(p[1]);
         pb.z = __float_as_uint(p[2]); pb.w = __float_as_uint(p[3]);
-      }
 #pragma unroll
-      for (int dt = 0; dt < DH / 16; ++dt) {
-        acc[j][dt] *= alpha;
-        acc[j][dt] = mma16<T>(vo[dt], pb, acc[j][dt]);
+        for (int dt = 0; dt < DH / 16; ++dt) {
+          acc[j][dt] *= alpha;
+          acc[j][dt] = mma16<T>(vo[dt], pb, acc[j][dt]);
+        }
       }
     }
   };
@@ -445,7 +488,7 @@ __global__ __launch_bounds__(DH) void attn_combine(CombineArgs a) {
       num += wgt * v[s];
     }
   }
-  ((T*)a.o)[((size_t)row * a.H + h) * DH + threadIdx.x] = from_f<T>(num / den);
+  ((float*)a.o)[((size_t)row * a.H + h) * DH + threadIdx.x] = num / den;
 }
 
 // the register path serves heads with few query tiles (its merge buffers and

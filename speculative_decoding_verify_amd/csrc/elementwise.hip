@@ -1,6 +1,6 @@
 // Row-wise kernels of the verify forward: prologue (tree bookkeeping and the
 // rotary table), embedding + first norm, residual add + RMSNorm, and the LM-head
-// statistics reduction.
+// statistics reduction.  Activations (residual stream and normalised rows) are fp32.
 //
 // Every split-K reduction sums the partials in split order 0..S-1 so results are
 // deterministic.  Rounding to the storage type happens exactly where a bf16 model
@@ -76,8 +76,8 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // RMSNorm of one fp32 row held in registers (256 threads, PER elements each,
 // element c = threadIdx.x * PER + i).
-template <typename T, int PER>
-SDV_DEV void norm_store(const float (&v)[PER], int d, const float* gain, T* out, float eps, float* red) {
+template <int PER>
+SDV_DEV void norm_store(const float (&v)[PER], int d, const float* gain, float* out, float eps, float* red) {
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) ss += v[i] * v[i];
@@ -86,7 +86,7 @@ SDV_DEV void norm_store(const float (&v)[PER], int d, const float* gain, T* out,
   const int c0 = threadIdx.x * PER;
   if (c0 < d) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) out[c0 + i] = from_f<T>(v[i] * rs * gain[c0 + i]);
+    for (int i = 0; i < PER; ++i) out[c0 + i] = v[i] * rs * gain[c0 + i];
   }
 }
 
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(EmbedArgs a) {
     v[i] = c0 < a.d ? to_f<T>(e[c0 + i]) : 0.f;
     if (c0 < a.d) a.x[(size_t)m * a.d + c0 + i] = v[i];
   }
-  norm_store<T, PER>(v, a.d, a.gain, (T*)a.a + (size_t)m * a.d, a.eps, red);
+  norm_store<PER>(v, a.d, a.gain, (float*)a.a + (size_t)m * a.d, a.eps, red);
 }
 
 // x += sum of the S split partials (in split order), then RMSNorm -> a.  Each
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(ResidNormArgs a) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) v[i] = 0.f;
   }
-  norm_store<T, PER>(v, a.d, a.gain, (T*)a.a + (size_t)m * a.d, a.eps, red);
+  norm_store<PER>(v, a.d, a.gain, (float*)a.a + (size_t)m * a.d, a.eps, red);
 }
 
 // PER columns per thread: the smallest of 4, 8, 12, 16, 24, 32 with 256 * PER >= d and

@@ -1,5 +1,10 @@
 // Weight-streaming GEMM for few rows: out[m, n] = sum_k A[m, k] * W[n, k].
 //
+// A (activations) is fp32.  With bf16 weights each group of 8 activations enters
+// the bf16 MFMA as a hi + lo pair (two MFMAs), so products carry ~16 significant
+// bits of the activation; only the weights are bf16.  With fp32 weights the fp32
+// MFMA is used directly.
+//
 // The decoder projections of a verify pass multiply M = B*T (tens of) activation
 // rows by weight matrices of tens to hundreds of MB, so the kernel is bound by
 // streaming W from HBM once.  Work layout:
@@ -15,9 +20,10 @@
 // Epilogues (all but PARTIAL need the whole K range in one workgroup, S = 1):
 //   PARTIAL  fp32 partial sums of each split;
 //   QKV      rotary embedding on q and k (both halves of every rotation pair sit in
-//            the same workgroup), rounding, q written row-major and k, v appended to
-//            the paged cache (k token-major, v transposed inside the page);
-//   SWIGLU   h = silu(gate) * up (gate and up rows of the same index in one workgroup);
+//            the same workgroup); q written row-major in fp32, k and v rounded to the
+//            cache type and appended to the paged cache (k token-major, v transposed
+//            inside the page);
+//   SWIGLU   h = silu(gate) * up in fp32 (gate and up rows of the same index in one workgroup);
 //   LOGITS   fp32 logits plus per-(row, column group) statistics: largest value, its
 //            index (lowest on ties), second-largest value and sum of exp(v - largest).
 #include "common.h"
@@ -64,15 +70,17 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_rows(GemmArgs a) {
                                : (const T*)a.W2 + (size_t)(n - a.N1) * a.K;
     wrow[ct] = base + lg * VE;
   }
-  const T* arow[MT];
+  const float* arow[MT];
   bool avalid[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = m_base + mt * 16 + r;
     avalid[mt] = m < a.M;
     const int row = avalid[mt] ? (a.a_rows ? a.a_rows[m] : m) : 0;
-    arow[mt] = (const T*)a.A + (size_t)row * a.lda + lg * VE;
+    arow[mt] = (const float*)a.A + (size_t)row * a.lda + lg * VE;
   }
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int AL = BF ? 2 : 1;   // 16-byte activation loads per k step (8 or 4 fp32)
 
   f32x4 acc[MT][NT];
 #pragma unroll
@@ -88,12 +96,14 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_rows(GemmArgs a) {
     for (int ct = 0; ct < NT; ++ct)
       wb[u][ct] = (ws0 + u < ws1) ? ld16_stream(wrow[ct] + (size_t)(ws0 + u) * KS) : zero;
   for (int st = ws0; st < ws1; st += U) {
-    u32x4 ab[U][MT];
+    u32x4 ab[U][MT][AL];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        ab[u][mt] = (avalid[mt] && st + u < ws1) ? ld16(arow[mt] + (size_t)(st + u) * KS) : zero;
+#pragma unroll
+        for (int h = 0; h < AL; ++h)
+          ab[u][mt][h] = (avalid[mt] && st + u < ws1) ? ld16(arow[mt] + (size_t)(st + u) * KS + 4 * h) : zero;
     u32x4 wn_[U][NT];
     const int nx = st + U;
 #pragma unroll
@@ -104,9 +114,20 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_rows(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt) {
+        if constexpr (BF) {
+          u32x4 hi, lo;
+          split_hi_lo(ab[u][mt][0], ab[u][mt][AL - 1], hi, lo);
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) acc[mt][ct] = mma16<T>(ab[u][mt], wb[u][ct], acc[mt][ct]);
+          for (int ct = 0; ct < NT; ++ct) {
+            acc[mt][ct] = mma16<T>(hi, wb[u][ct], acc[mt][ct]);
+            acc[mt][ct] = mma16<T>(lo, wb[u][ct], acc[mt][ct]);
+          }
+        } else {
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct) acc[mt][ct] = mma16<T>(ab[u][mt][0], wb[u][ct], acc[mt][ct]);
+        }
+      }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -164,7 +185,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_rows(GemmArgs a) {
       const float gt = tile[ml][(q * NT + j) * 16 + rr];
       const float up = tile[ml][(q * NT + H + j) * 16 + rr];
       const float sl = gt / (1.f + expf(-gt));
-      ((T*)a.out_act)[(size_t)m * a.pair_off + f] = from_f<T>(sl * up);
+      ((float*)a.out_act)[(size_t)m * a.pair_off + f] = sl * up;
     }
   } else if constexpr (EPI == EPI_QKV) {
     constexpr int H = NT / 2;
@@ -188,9 +209,9 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_rows(GemmArgs a) {
         y2 = x2 * cs.x + x1 * cs.y;
       }
       if (hh < e.H) {
-        T* qo = (T*)e.q + (size_t)m * e.H * dh + hh * dh;
-        qo[i] = from_f<T>(y1);
-        qo[i + half] = from_f<T>(y2);
+        float* qo = (float*)e.q + (size_t)m * e.H * dh + hh * dh;
+        qo[i] = y1;
+        qo[i + half] = y2;
       } else {
         const int C = e.seq_len[b];
         const int slot = C + t;
@@ -279,9 +300,7 @@ template <typename T, int EPI>
 static hipError_t launch_cfg(const GemmCfg& c, int MT, dim3 grid, const GemmArgs& a, hipStream_t s) {
   // (NT, WN, WK) combinations; pair epilogues need an even NT
   if (c.NT == 2 && c.WN == 1 && c.WK == 4) return launch_mt<T, 2, 1, 4, EPI>(MT, grid, a, s);
-  if (c.NT == 2 && c.WN == 1 && c.WK == 8) return launch_mt<T, 2, 1, 8, EPI>(MT, grid, a, s);
   if (c.NT == 4 && c.WN == 1 && c.WK == 4) return launch_mt<T, 4, 1, 4, EPI>(MT, grid, a, s);
-  if (c.NT == 4 && c.WN == 1 && c.WK == 8) return launch_mt<T, 4, 1, 8, EPI>(MT, grid, a, s);
   if (c.NT == 2 && c.WN == 2 && c.WK == 2) return launch_mt<T, 2, 2, 2, EPI>(MT, grid, a, s);
   if (c.NT == 4 && c.WN == 2 && c.WK == 2) return launch_mt<T, 4, 2, 2, EPI>(MT, grid, a, s);
   return hipErrorInvalidValue;

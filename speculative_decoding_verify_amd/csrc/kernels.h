@@ -10,7 +10,7 @@ enum { PAIR_NONE = 0, PAIR_SWIGLU = 1, PAIR_QKV = 2 };
 
 // QKV epilogue: rotary embedding + q write + paged K/V append
 struct QkvEpi {
-  void* q;                  // [M, H*dh]
+  void* q;                  // [M, H*dh] fp32
   void* k_pages;            // this layer: [n_blocks][Hkv][16][dh]
   void* v_pages;            //             [n_blocks][Hkv][dh][16]
   const int32_t* block_table;
@@ -22,7 +22,7 @@ struct QkvEpi {
 };
 
 struct GemmArgs {
-  const void* A;            // activations, rows of lda elements
+  const void* A;            // fp32 activations, rows of lda elements
   int lda;
   const int32_t* a_rows;    // nullable: output row m reads A row a_rows[m]
   int M;
@@ -36,7 +36,7 @@ struct GemmArgs {
   float* out;               // PARTIAL: out[split * out_split_stride + m * ldo + n]
   long long out_split_stride;
   int ldo;
-  void* out_act;            // SWIGLU: h [M, F]
+  void* out_act;            // SWIGLU: h [M, F] fp32
   QkvEpi qkv;               // QKV epilogue arguments
   float* logits;            // LOGITS: logits[m * ldl + n] (nullable)
   int ldl;
@@ -53,7 +53,7 @@ hipError_t launch_gemm(bool is_bf16, const GemmCfg& c, int MT, int epi, dim3 gri
                        hipStream_t s);
 
 struct AttnArgs {
-  const void* q;            // [B*T, H*dh]
+  const void* q;            // [B*T, H*dh] fp32
   const void* k_pages;      // this layer's pages: [n_blocks][Hkv][16][dh]
   const void* v_pages;      //                      [n_blocks][Hkv][dh][16]
   const int32_t* block_table;
@@ -76,7 +76,7 @@ bool attn_uses_reg_path(bool bf, int dh, int NQT);  // keys per tile: 32 bf16 / 
 struct CombineArgs {
   const float* po;
   const float* pml;
-  void* o;                  // [B*T, H*dh]
+  void* o;                  // [B*T, H*dh] fp32
   int B, T, H, Hkv, dh, n_splits, nq_pad;
 };
 hipError_t launch_combine(bool is_bf16, const CombineArgs& a, hipStream_t s);
@@ -101,7 +101,7 @@ struct EmbedArgs {
   const void* embed;        // [V, d]
   const float* gain;        // first layer attention-norm gain
   float* x;                 // [M, d] fp32 residual
-  void* a;                  // [M, d] normalised (storage type)
+  void* a;                  // [M, d] normalised rows, fp32
   int M, T, d, V;
   float eps;
   int32_t* err;
@@ -114,7 +114,7 @@ struct ResidNormArgs {
   long long part_stride;
   int S;
   const float* gain;
-  void* a;                  // [M, d] normalised output
+  void* a;                  // [M, d] normalised rows, fp32
   float* hidden;            // nullable [M, d] copy of the updated residual
   int M, d;
   float eps;

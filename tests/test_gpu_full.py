@@ -22,7 +22,7 @@ if not torch.cuda.is_available():  # pragma: no cover
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import speculative_decoding_verify_amd as sdv  # noqa: E402
-from oracle import EXACT, BF16  # noqa: E402
+from oracle import EXACT, BF16_KV  # noqa: E402
 from oracle import decoder as odec  # noqa: E402
 from oracle.numerics import memoize_f64  # noqa: E402
 from synth import (make_weights, make_random_kv, uniform_tokens, toy_workload, w1p7b_workload,  # noqa: E402
@@ -107,7 +107,7 @@ def test_full_1p7b_random_and_silence():
     with memoize_f64():
         sil = np.zeros(L_a, dtype=np.int32)
         _say("oracle greedy drafting under silence")
-        drafts, _ = odec.greedy_decode(w, cache.copy(), sil, gamma + 1, BF16)
+        drafts, _ = odec.greedy_decode(w, cache.copy(), sil, gamma + 1, BF16_KV)
         for scen in ("random", "silence"):
             if scen == "random":
                 toks = np.concatenate([uniform_tokens(L_a, sh.vocab, 77, "a"), uniform_tokens(gamma, sh.vocab, 78, "d")])
@@ -121,7 +121,7 @@ def test_full_1p7b_random_and_silence():
             g = dict(logits=res.logits.cpu().numpy().astype(np.float64), argmax=res.argmax.cpu().numpy(),
                      margin=res.margin.cpu().numpy(), lse=res.lse.cpu().numpy())
             _say(f"oracle verify pass ({scen})")
-            o = odec.verify_forward(w, cache, toks[None, :], None, rows, BF16)
+            o = odec.verify_forward(w, cache, toks[None, :], None, rows, BF16_KV)
             err, flagged, n = compare_logits(sh, g, o)
             _say(f"1.7b {scen}: rel err {err:.2e}, flagged {flagged}/{n}")
             compare_kv_layer0(sh, kv, o, C, T)
@@ -157,7 +157,7 @@ def test_full_8b_tree():
     g = dict(logits=res.logits.cpu().numpy().astype(np.float64), argmax=res.argmax.cpu().numpy(),
              margin=res.margin.cpu().numpy(), lse=res.lse.cpu().numpy())
     _say("oracle verify pass (8B tree)")
-    o = odec.verify_forward(w, odec.Cache(kvh.k, kvh.v), toks[None, :], parent, rows, BF16)
+    o = odec.verify_forward(w, odec.Cache(kvh.k, kvh.v), toks[None, :], parent, rows, BF16_KV)
     err, flagged, n = compare_logits(sh, g, o)
     _say(f"8b tree: rel err {err:.2e}, flagged {flagged}/{n}")
     compare_kv_layer0(sh, kv, o, C, T)

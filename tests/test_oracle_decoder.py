@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import BF16, EXACT
+from oracle import BF16, BF16_KV, EXACT
 from oracle import accept as acc
 from oracle import decoder as dec
 from oracle.numerics import round_bf16, round_f32, bits_to_f64
@@ -121,7 +121,7 @@ def test_gqa_head_mapping():
 
 # -- verify == decoding ---------------------------------------------------------------
 
-@pytest.mark.parametrize("mode", [EXACT, BF16])
+@pytest.mark.parametrize("mode", [EXACT, BF16, BF16_KV])
 def test_verify_equals_token_by_token(mode):
     shape = SMALL if mode == EXACT else SMALL_BF
     w = _model(shape, 4)
@@ -316,6 +316,13 @@ def test_bf16_mode_rounds_stored_values():
             np.testing.assert_array_equal(arr, round_bf16(arr))
     h = res["hidden"]
     np.testing.assert_array_equal(h, round_f32(h))
+    # the KV-only mode rounds exactly the cache entries
+    kv_only = dec.verify_forward(w, cache, uniform_tokens(5, SMALL_BF.vocab, 62)[None, :], None, range(5), BF16_KV,
+                                 want_attn=True)
+    for l in range(SMALL_BF.n_layers):
+        for arr in (kv_only["k_new"][0][l], kv_only["v_new"][0][l]):
+            np.testing.assert_array_equal(arr, round_bf16(arr))
+    assert not np.array_equal(kv_only["attn"][0][0], round_bf16(kv_only["attn"][0][0]))
     # and the bf16 pass stays close to the exact one on the same (bf16-valued) weights
     ex = dec.verify_forward(w, cache, uniform_tokens(5, SMALL_BF.vocab, 62)[None, :], None, range(5), EXACT)
     assert np.max(np.abs(ex["logits"] - res["logits"])) < 0.05 * np.max(np.abs(ex["logits"]))

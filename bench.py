@@ -217,7 +217,7 @@ def bench_verify(args, wl):
         "committed_tokens_per_s": (n_acc + 1) * passes_s,
         "pass_roofline": {"bound": "hbm", "bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
                           "peak_GBs": HBM_PEAK_GBS, "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "roofline": {"bound": "hbm", "kernel": "gemm_small_m (decoder q/k/v, o, gate/up, down projections)",
+        "roofline": {"bound": "hbm", "kernel": "gemm_rows (decoder q/k/v, o, gate/up, down projections)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None, "launches_per_pass": 4 * sh.n_layers, "avg_launch_us": avg_launch_ms * 1e3,
                      "bytes_per_pass": dec_bytes},

@@ -17,7 +17,9 @@
  *                       norm(max(0, p - q)), bonus token from p when all pass
  *                       (step 6; page 3 section 2);
  *   sdv_kv_rollback     set committed lengths and compact an accepted branch
- *                       ("roll the KV cache back", step 4).
+ *                       ("roll the KV cache back", step 4);
+ *   sdv_pack_weights    one-time rearrangement of row-major weight matrices into
+ *                       the packed tile layout the verify forward streams.
  *
  * Conventions shared by every call
  *   - All data pointers are DEVICE pointers unless a comment says "host".
@@ -34,9 +36,27 @@
  *     set bits in the caller's int32 error word for that sequence; that sequence's
  *     results are then unspecified, other sequences are unaffected, and the kernels
  *     never read or write outside their buffers.
- *   - Matrices are row-major [out_features, in_features] (in_features contiguous).
- *     Storage type: fp32 (SDV_F32) or bf16 (SDV_BF16, raw 16-bit patterns);
- *     norm gains are always fp32.
+ *   - Storage type of weights, embedding and KV pages: fp32 (SDV_F32) or bf16
+ *     (SDV_BF16, raw 16-bit patterns); norm gains are always fp32.  The embedding is
+ *     row-major [V, d]; the projection matrices and the LM head are PACKED (below).
+ *
+ * Packed weights
+ *   A matrix with rows n (output features) and columns k (input features, K of
+ *   them) is stored as 1 KB tiles of 16 rows x KS columns, KS = 32 (bf16) or 16
+ *   (fp32).  Tile (n / 16, k / KS) starts at byte ((n / 16) * (K / KS) + k / KS) * 1024;
+ *   inside it, the 16 bytes holding row n % 16 and columns of k group
+ *   g = (k % KS) / (KS / 4) start at byte (g * 16 + n % 16) * 16.  Rows past the
+ *   sources are zero (the row count is rounded up to a multiple of 16).  Which source
+ *   row becomes packed row n depends on the kind:
+ *     SDV_PACK_PLAIN    row n of the one source;
+ *     SDV_PACK_QKV      sources Wq [H*dh, d], Wk [Hkv*dh, d], Wv [Hkv*dh, d] viewed
+ *                       as one matrix of whole heads; rotation pair p (head p / (dh/2),
+ *                       element i = p % (dh/2), paired with i + dh/2) gives packed row
+ *                       16 * (p / 8) + p % 8 to element i and 16 * (p / 8) + 8 + p % 8
+ *                       to element i + dh/2 (v heads are paired the same way);
+ *     SDV_PACK_GATE_UP  sources Wg [F, d], Wu [F, d]: packed row 16 * (f / 8) + f % 8
+ *                       is gate row f, 16 * (f / 8) + 8 + f % 8 is up row f.
+ *   sdv_pack_weights writes this layout on the device; sdv_packed_bytes gives its size.
  */
 #ifndef SDV_H
 #define SDV_H
@@ -48,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SDV_ABI_VERSION 1
+#define SDV_ABI_VERSION 2
 #define SDV_PAGE 16          /* tokens per KV-cache page */
 #define SDV_MAX_T 128        /* rows per verify pass (chunk + drafts + branches) */
 
@@ -63,6 +83,8 @@ typedef enum {
 
 typedef enum { SDV_F32 = 0, SDV_BF16 = 1 } sdv_dtype;
 
+typedef enum { SDV_PACK_PLAIN = 0, SDV_PACK_QKV = 1, SDV_PACK_GATE_UP = 2 } sdv_pack_kind;
+
 /* device-side error bits written to the per-sequence error word */
 #define SDV_EBAD_TOKEN    0x1   /* a token id outside [0, vocab) (treated as 0) */
 #define SDV_EBAD_PARENT   0x2   /* parent[j] not in [0, j) for j > 0, or parent[0] != -1 */
@@ -70,17 +92,15 @@ typedef enum { SDV_F32 = 0, SDV_BF16 = 1 } sdv_dtype;
 #define SDV_EBAD_MOVE     0x8   /* a rollback move or keep_len outside the capacity */
 #define SDV_EDUP_SIBLING  0x10  /* two children of one tree row carry the same token */
 
-/* One decoder layer: pre-norm attention block and SwiGLU FFN block. */
+/* One decoder layer: pre-norm attention block and SwiGLU FFN block.  Matrices are
+ * packed (see above); the shapes given are those of the row-major sources. */
 typedef struct {
   const float* attn_norm;  /* [d] RMSNorm gain before attention */
-  const void* wq;          /* [H*dh, d] */
-  const void* wk;          /* [Hkv*dh, d] */
-  const void* wv;          /* [Hkv*dh, d] */
-  const void* wo;          /* [d, H*dh] */
+  const void* wqkv;        /* SDV_PACK_QKV of Wq [H*dh, d], Wk, Wv [Hkv*dh, d] */
+  const void* wo;          /* SDV_PACK_PLAIN of Wo [d, H*dh] */
   const float* ffn_norm;   /* [d] RMSNorm gain before the FFN */
-  const void* wg;          /* [F, d] gate projection */
-  const void* wu;          /* [F, d] up projection */
-  const void* wd;          /* [d, F] down projection */
+  const void* wgu;         /* SDV_PACK_GATE_UP of Wg, Wu [F, d] */
+  const void* wd;          /* SDV_PACK_PLAIN of Wd [d, F] */
 } sdv_layer;
 
 /* Decoder: token embedding, n_layers pre-norm blocks, final RMSNorm, untied LM head.
@@ -92,9 +112,9 @@ typedef struct {
   int32_t dtype;             /* sdv_dtype of every matrix, the embedding and the KV pages */
   float eps;                 /* RMSNorm epsilon: x / sqrt(mean(x^2) + eps) * g */
   float rope_theta;
-  const void* embed;         /* [V, d] */
+  const void* embed;         /* [V, d] row-major */
   const float* final_norm;   /* [d] */
-  const void* lm_head;       /* [V, d] */
+  const void* lm_head;       /* SDV_PACK_PLAIN of W_lm [V, d] */
   const sdv_layer* layers;   /* HOST array of n_layers entries (device pointers inside) */
 } sdv_model;
 
@@ -159,8 +179,8 @@ size_t sdv_verify_workspace_size(const sdv_model* m, int32_t batch, int32_t T, i
 
 /* The verify forward ("Method steps", step 4).  Writes K/V of the T rows into the
  * cache pages at slots seq_len[b] + j; does NOT change seq_len (commit with
- * sdv_kv_rollback).  Requires head_dim 64 or 128, H % Hkv == 0, d, H*dh and F
- * multiples of 32, 1 <= T <= SDV_MAX_T, 1 <= R <= T. */
+ * sdv_kv_rollback).  Requires head_dim 64 or 128, H % Hkv == 0, d and F multiples
+ * of 64, d <= 8192, 1 <= T <= SDV_MAX_T, 1 <= R <= T. */
 sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_verify_in* in,
                               sdv_verify_out* out, void* workspace, size_t workspace_bytes,
                               void* stream);
@@ -216,6 +236,21 @@ sdv_status sdv_accept_sample(int32_t batch, int32_t k, int32_t vocab, const floa
 sdv_status sdv_kv_rollback(const sdv_model* m, const sdv_kv* kv, const int32_t* keep_len,
                            const int32_t* move_src, const int32_t* move_dst, int32_t max_move,
                            int32_t* err, void* stream);
+
+/* Packed weights (layout in the header comment).
+ *   sdv_packed_bytes: bytes of the packed form of a matrix with `rows` rows in total
+ *   (all sources together) and K columns; 0 for invalid arguments.
+ *   sdv_pack_weights: reads the row-major device sources (src0 [rows0, K], src1
+ *   [rows1, K], src2 [rows2, K]; unused sources NULL with 0 rows) and writes the packed
+ *   matrix to dst (device, dst_bytes >= sdv_packed_bytes).  K must be a multiple of
+ *   32 (bf16) or 16 (fp32).  SDV_PACK_PLAIN takes src0 only; SDV_PACK_QKV takes q, k,
+ *   v with whole heads of head_dim (64 or 128) rows and equal k and v rows;
+ *   SDV_PACK_GATE_UP takes gate and up with equal rows, a multiple of 8.  Sources and
+ *   destination must not overlap.  Asynchronous on `stream`. */
+size_t sdv_packed_bytes(int32_t dtype, int32_t rows, int32_t K);
+sdv_status sdv_pack_weights(int32_t kind, int32_t dtype, int32_t K, int32_t head_dim, const void* src0,
+                            int32_t rows0, const void* src1, int32_t rows1, const void* src2,
+                            int32_t rows2, void* dst, size_t dst_bytes, void* stream);
 
 const char* sdv_last_error(void);
 int32_t sdv_abi_version(void);

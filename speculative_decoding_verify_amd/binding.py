@@ -28,8 +28,11 @@ _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
 
 
+PACK_PLAIN, PACK_QKV, PACK_GATE_UP = 0, 1, 2
+
+
 class SdvLayer(ctypes.Structure):
-    _fields_ = [(n, _vp) for n in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "wg", "wu", "wd")]
+    _fields_ = [(n, _vp) for n in ("attn_norm", "wqkv", "wo", "ffn_norm", "wgu", "wd")]
 
 
 class SdvModel(ctypes.Structure):
@@ -86,6 +89,11 @@ def lib():
                                       _i32, _vp, _vp]
         L.sdv_sample_workspace_size.restype = ctypes.c_size_t
         L.sdv_sample_workspace_size.argtypes = [_i32, _i32, _i32]
+        L.sdv_packed_bytes.restype = ctypes.c_size_t
+        L.sdv_packed_bytes.argtypes = [_i32, _i32, _i32]
+        L.sdv_pack_weights.restype = ctypes.c_int
+        L.sdv_pack_weights.argtypes = [_i32, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _i32, _vp,
+                                       ctypes.c_size_t, _vp]
         L.sdv_accept_sample.restype = ctypes.c_int
         L.sdv_accept_sample.argtypes = [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
                                         _vp, _vp, _vp, ctypes.c_size_t, _vp]
@@ -114,8 +122,27 @@ def _dev_tensor(a: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
 
 
+def pack_weights(kind: int, sources: Sequence[np.ndarray], head_dim: int = 0, device="cuda") -> torch.Tensor:
+    """Upload row-major matrices (numpy: fp32, or uint16 bf16 bit patterns) and pack
+    them on the device with sdv_pack_weights; returns the packed byte tensor."""
+    dev = torch.device(device)
+    srcs = [_dev_tensor(a, dev) for a in sources]
+    K = int(sources[0].shape[1])
+    dtype = SDV_BF16 if sources[0].dtype == np.uint16 else SDV_F32
+    rows = [int(a.shape[0]) for a in sources] + [0] * (3 - len(sources))
+    ptrs = [ctypes.c_void_p(t.data_ptr()) for t in srcs] + [None] * (3 - len(srcs))
+    nbytes = lib().sdv_packed_bytes(dtype, sum(rows), K)
+    if nbytes == 0:
+        raise SdvError("sdv_packed_bytes rejected the shape")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check(lib().sdv_pack_weights(kind, dtype, K, head_dim, ptrs[0], rows[0], ptrs[1], rows[1], ptrs[2], rows[2],
+                                  ctypes.c_void_p(dst.data_ptr()), nbytes, _stream()), "sdv_pack_weights")
+    torch.cuda.current_stream().synchronize()  # the sources are freed on return
+    return dst
+
+
 class DeviceModel:
-    """Decoder weights resident on the device plus the sdv_model descriptor."""
+    """Decoder weights resident on the device (projections packed) plus the sdv_model descriptor."""
 
     def __init__(self, w, device="cuda"):
         sh = w.shape
@@ -123,14 +150,16 @@ class DeviceModel:
         self.device = torch.device(device)
         t = lambda a: _dev_tensor(a, self.device)
         f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(self.device)
+        pk = lambda kind, srcs, hd=0: pack_weights(kind, srcs, hd, self.device)
         self.embed = t(w.embed)
         self.final_norm = f(w.final_norm)
-        self.lm_head = t(w.lm_head)
+        self.lm_head = pk(PACK_PLAIN, [w.lm_head])
         self.layers = []
         for lw in w.layers:
-            self.layers.append(dict(attn_norm=f(lw.attn_norm), wq=t(lw.wq), wk=t(lw.wk), wv=t(lw.wv),
-                                    wo=t(lw.wo), ffn_norm=f(lw.ffn_norm), wg=t(lw.wg), wu=t(lw.wu),
-                                    wd=t(lw.wd)))
+            self.layers.append(dict(attn_norm=f(lw.attn_norm),
+                                    wqkv=pk(PACK_QKV, [lw.wq, lw.wk, lw.wv], sh.head_dim),
+                                    wo=pk(PACK_PLAIN, [lw.wo]), ffn_norm=f(lw.ffn_norm),
+                                    wgu=pk(PACK_GATE_UP, [lw.wg, lw.wu]), wd=pk(PACK_PLAIN, [lw.wd])))
         self.codebook = t(w.codebook) if getattr(w, "codebook", None) is not None else None
         self.stream_emb = f(w.stream_emb) if getattr(w, "stream_emb", None) is not None else None
         self._build_desc()

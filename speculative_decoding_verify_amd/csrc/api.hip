@@ -40,18 +40,15 @@ constexpr int TARGET_WG_ATTN = 512;
 
 struct GemmPlan {
   GemmCfg cfg;
-  int epi, pair_mode, pair_off;
+  int epi;
   int S, spp, ncg, MT, row_blocks;
 };
 
-// N: weight rows (for pair epilogues: all rows of both halves); pairs: rotation or
-// gate/up pairs (0 for plain epilogues)
-GemmPlan plan_gemm(int M, int N, int K, bool bf, int epi, int pair_mode, int pair_off, int pairs) {
+// N: packed weight rows of the launch (pair epilogues: both members of every pair)
+GemmPlan plan_gemm(int M, int N, int K, bool bf, int epi) {
   GemmPlan p;
   const int KS = bf ? 32 : 16;
   p.epi = epi;
-  p.pair_mode = pair_mode;
-  p.pair_off = pair_off;
   if (M <= 80) {
     p.MT = std::max(1, cdiv(M, 16));
     p.row_blocks = 1;
@@ -59,18 +56,20 @@ GemmPlan plan_gemm(int M, int N, int K, bool bf, int epi, int pair_mode, int pai
     p.MT = 4;
     p.row_blocks = cdiv(M, 64);
   }
-  // configurations measured best on the decoder shapes: 4 waves splitting K,
-  // NT column tiles per wave
-  if (epi == EPI_SWIGLU || epi == EPI_PARTIAL) p.cfg = GemmCfg{4, 1, 4};
-  else p.cfg = GemmCfg{2, 1, 4};
-  if (epi == EPI_PARTIAL && N <= 2048) p.cfg = GemmCfg{2, 1, 4};
-  const int cols = p.cfg.WN * p.cfg.NT * 16;
-  p.ncg = pair_mode == PAIR_NONE ? cdiv(N, cols) : cdiv(pairs, cols / 2);
+  const int ntiles = cdiv(N, 16);
+  // configurations measured on the decoder shapes: few tiles per workgroup and a
+  // deeper register ring where the grid would otherwise be small (q/k/v and o
+  // projections), more tiles per workgroup as the row tiles grow
+  if (epi == EPI_QKV || (epi == EPI_PARTIAL && p.MT < 4 && ntiles <= 128 && K <= 4096)) p.cfg = GemmCfg{2, 4};
+  else if (p.MT >= (epi == EPI_LOGITS ? 3 : 4) && gemm_lds_ok(p.MT, 8)) p.cfg = GemmCfg{8, 2};
+  else p.cfg = GemmCfg{4, 2};
+  p.ncg = cdiv(ntiles, p.cfg.NT);
   const int steps = K / KS;
   int S = 1;
   if (epi == EPI_PARTIAL) {
-    S = cdiv(TARGET_WG_GEMM, (long long)p.ncg * p.row_blocks);
-    S = std::max(1, std::min({S, 16, std::max(1, steps / 4)}));
+    const int target = p.cfg.NT == 2 ? 512 : 256;
+    S = cdiv(target, (long long)p.ncg * p.row_blocks);
+    S = std::max(1, std::min({S, 16, std::max(1, steps / 8)}));
   }
   p.spp = cdiv(steps, S);
   p.S = cdiv(steps, p.spp);
@@ -95,14 +94,12 @@ sdv_status check_model(const sdv_model* m) {
     return fail(SDV_ERR_SHAPE, "model sizes out of range");
   if (m->head_dim != 64 && m->head_dim != 128) return fail(SDV_ERR_UNSUPPORTED, "head_dim %d (64 or 128)", m->head_dim);
   if (m->n_heads % m->n_kv_heads) return fail(SDV_ERR_SHAPE, "n_heads %% n_kv_heads != 0");
-  const int KS = m->dtype == SDV_BF16 ? 32 : 16;
-  if (m->d % 32 || m->ffn % 32 || (m->n_heads * m->head_dim) % KS)
-    return fail(SDV_ERR_UNSUPPORTED, "d and ffn must be multiples of 32");
+  if (m->d % 64 || m->ffn % 64) return fail(SDV_ERR_UNSUPPORTED, "d and ffn must be multiples of 64");
   if (m->d > 8192) return fail(SDV_ERR_UNSUPPORTED, "d > 8192");
   if (!m->embed || !m->final_norm || !m->lm_head || !m->layers) return fail(SDV_ERR_NULL, "model pointer NULL");
   for (int l = 0; l < m->n_layers; ++l) {
     const sdv_layer& L = m->layers[l];
-    if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.ffn_norm || !L.wg || !L.wu || !L.wd)
+    if (!L.attn_norm || !L.wqkv || !L.wo || !L.ffn_norm || !L.wgu || !L.wd)
       return fail(SDV_ERR_NULL, "layer %d has a NULL pointer", l);
   }
   return SDV_OK;
@@ -117,11 +114,11 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
   p.G = m->n_heads / m->n_kv_heads;
   const int d = m->d, dh = m->head_dim, H = m->n_heads, Hkv = m->n_kv_heads, F = m->ffn;
   const int qd = H * dh, kd = Hkv * dh;
-  p.qkv = plan_gemm(p.M, qd + 2 * kd, d, p.bf, EPI_QKV, PAIR_QKV, dh / 2, (H + 2 * Hkv) * dh / 2);
-  p.o = plan_gemm(p.M, d, qd, p.bf, EPI_PARTIAL, PAIR_NONE, 0, 0);
-  p.gu = plan_gemm(p.M, 2 * F, d, p.bf, EPI_SWIGLU, PAIR_SWIGLU, F, F);
-  p.dn = plan_gemm(p.M, d, F, p.bf, EPI_PARTIAL, PAIR_NONE, 0, 0);
-  p.lm = plan_gemm(p.Mr, m->vocab, d, p.bf, EPI_LOGITS, PAIR_NONE, 0, 0);
+  p.qkv = plan_gemm(p.M, qd + 2 * kd, d, p.bf, EPI_QKV);
+  p.o = plan_gemm(p.M, d, qd, p.bf, EPI_PARTIAL);
+  p.gu = plan_gemm(p.M, 2 * F, d, p.bf, EPI_SWIGLU);
+  p.dn = plan_gemm(p.M, d, F, p.bf, EPI_PARTIAL);
+  p.lm = plan_gemm(p.Mr, m->vocab, d, p.bf, EPI_LOGITS);
   p.part_floats = std::max((size_t)p.o.S * p.M * d, (size_t)p.dn.S * p.M * d);
   // attention: split the keys so that the grid fills the GPU (the register path
   // has four waves per workgroup, each streaming its own key tiles)
@@ -138,7 +135,7 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
   p.off_x = take((size_t)p.M * d * 4);
-  // activations are fp32 whatever the storage type of weights and cache
+  // activation rows take 4 bytes per value (bf16 hi/lo pairs or fp32)
   p.off_a = take((size_t)p.M * d * 4);
   p.off_q = take((size_t)p.M * qd * 4);
   p.off_o = take((size_t)p.M * qd * 4);
@@ -171,14 +168,10 @@ struct ProfEvents {
 // one weight-streaming GEMM launch; `a` carries the operands and epilogue targets
 sdv_status run_gemm(ProfEvents& pe, const Plan& P, const GemmPlan& g, GemmArgs a, hipStream_t s) {
   a.steps_per_split = g.spp;
-  a.pair_mode = g.pair_mode;
-  a.pair_off = g.pair_off;
   a.out_split_stride = (long long)a.M * a.N;
   a.ldo = a.N;
   a.ldl = a.N;
   a.n_groups = g.ncg;
-  if (!a.W1) a.W1 = a.W0;
-  if (!a.W2) a.W2 = a.W0;
   dim3 grid(g.ncg, g.S, g.row_blocks);
   const bool prof = pe.ev && pe.next < pe.n_pairs;
   if (prof) SDV_LAUNCH(hipEventRecord((hipEvent_t)pe.ev[2 * pe.next], s));
@@ -188,19 +181,14 @@ sdv_status run_gemm(ProfEvents& pe, const Plan& P, const GemmPlan& g, GemmArgs a
   return SDV_OK;
 }
 
-GemmArgs gemm_args(const void* A, int lda, const int32_t* a_rows, int M, const void* W0, const void* W1,
-                   const void* W2, int N0, int N1, int N, int K) {
+GemmArgs gemm_args(const void* A, int lda, const int32_t* a_rows, int M, const void* W, int N, int K) {
   GemmArgs a;
   memset(&a, 0, sizeof a);
   a.A = A;
   a.lda = lda;
   a.a_rows = a_rows;
   a.M = M;
-  a.W0 = W0;
-  a.W1 = W1;
-  a.W2 = W2;
-  a.N0 = N0;
-  a.N1 = N1;
+  a.W = W;
   a.N = N;
   a.K = K;
   return a;
@@ -278,7 +266,8 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
     void* vp = (char*)kv->v_pages + l * layer_elems * P.eb;
     // q, k, v projections with rotary embedding and paged K/V append
     {
-      GemmArgs a = gemm_args(act, d, nullptr, M, L.wq, L.wk, L.wv, qd, qd + kd, qd + 2 * kd, d);
+      GemmArgs a = gemm_args(act, d, nullptr, M, L.wqkv, qd + 2 * kd, d);
+      a.pair_n = dh / 2;
       a.qkv = QkvEpi{q, kp, vp, kv->block_table, kv->max_blocks, kv->n_blocks, kv->seq_len, rope,
                      B, T, H, Hkv, in->max_ctx, out->err};
       if ((st = run_gemm(pe, P, P.qkv, a, s)) != SDV_OK) return st;
@@ -292,7 +281,7 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
       SDV_LAUNCH(launch_combine(P.bf, c, s));
     }
     {
-      GemmArgs a = gemm_args(o, qd, nullptr, M, L.wo, nullptr, nullptr, d, d, d, qd);
+      GemmArgs a = gemm_args(o, qd, nullptr, M, L.wo, d, qd);
       a.out = part;
       if ((st = run_gemm(pe, P, P.o, a, s)) != SDV_OK) return st;
     }
@@ -302,12 +291,13 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
     }
     // gate/up projections with the SwiGLU epilogue
     {
-      GemmArgs a = gemm_args(act, d, nullptr, M, L.wg, L.wu, nullptr, F, 2 * F, 2 * F, d);
+      GemmArgs a = gemm_args(act, d, nullptr, M, L.wgu, 2 * F, d);
+      a.pair_n = F;
       a.out_act = h;
       if ((st = run_gemm(pe, P, P.gu, a, s)) != SDV_OK) return st;
     }
     {
-      GemmArgs a = gemm_args(h, F, nullptr, M, L.wd, nullptr, nullptr, d, d, d, F);
+      GemmArgs a = gemm_args(h, F, nullptr, M, L.wd, d, F);
       a.out = part;
       if ((st = run_gemm(pe, P, P.dn, a, s)) != SDV_OK) return st;
     }
@@ -319,7 +309,7 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
     }
   }
   {
-    GemmArgs a = gemm_args(act, d, lm_rows, P.Mr, m->lm_head, nullptr, nullptr, V, V, V, d);
+    GemmArgs a = gemm_args(act, d, lm_rows, P.Mr, m->lm_head, V, d);
     a.logits = out->logits;
     a.stats = stats;
     if ((st = run_gemm(pe, P, P.lm, a, s)) != SDV_OK) return st;
@@ -342,6 +332,50 @@ sdv_status sdv_accept_greedy(int32_t B, int32_t T, int32_t L_a, const int32_t* t
   GreedyArgs a{B, T, L_a, R, tokens, parent, logit_rows, argmax, base_len, n_out, next_out, path_out, keep_out,
                move_src, move_dst, err};
   SDV_LAUNCH(launch_accept_greedy(a, (hipStream_t)stream));
+  return SDV_OK;
+}
+
+size_t sdv_packed_bytes(int32_t dtype, int32_t rows, int32_t K) {
+  if ((dtype != SDV_F32 && dtype != SDV_BF16) || rows < 1 || K < 1) return 0;
+  return (size_t)cdiv(rows, 16) * 16 * K * (dtype == SDV_BF16 ? 2 : 4);
+}
+
+sdv_status sdv_pack_weights(int32_t kind, int32_t dtype, int32_t K, int32_t head_dim, const void* src0,
+                            int32_t rows0, const void* src1, int32_t rows1, const void* src2, int32_t rows2,
+                            void* dst, size_t dst_bytes, void* stream) {
+  if (dtype != SDV_F32 && dtype != SDV_BF16) return fail(SDV_ERR_SHAPE, "dtype %d", dtype);
+  const int KS = dtype == SDV_BF16 ? 32 : 16;
+  if (K < KS || K % KS) return fail(SDV_ERR_SHAPE, "K = %d must be a positive multiple of %d", K, KS);
+  if (!dst || !src0) return fail(SDV_ERR_NULL, "dst or src0 is NULL");
+  if (rows0 < 1 || rows1 < 0 || rows2 < 0) return fail(SDV_ERR_SHAPE, "row counts out of range");
+  if ((rows1 > 0 && !src1) || (rows2 > 0 && !src2)) return fail(SDV_ERR_NULL, "a source with rows is NULL");
+  const long long total = (long long)rows0 + rows1 + rows2;
+  PackArgs a;
+  a.kind = kind;
+  a.K = K;
+  a.head_dim = head_dim;
+  a.src[0] = src0;
+  a.src[1] = rows1 ? src1 : nullptr;
+  a.src[2] = rows2 ? src2 : nullptr;
+  a.rows[0] = rows0;
+  a.rows[1] = rows1;
+  a.rows[2] = rows2;
+  if (kind == SDV_PACK_PLAIN) {
+    if (rows1 || rows2) return fail(SDV_ERR_SHAPE, "plain packing takes one source");
+  } else if (kind == SDV_PACK_QKV) {
+    if (head_dim != 64 && head_dim != 128) return fail(SDV_ERR_UNSUPPORTED, "head_dim %d (64 or 128)", head_dim);
+    if (rows0 % head_dim || rows1 % head_dim || rows2 % head_dim || rows1 != rows2 || rows1 < head_dim)
+      return fail(SDV_ERR_SHAPE, "q/k/v rows must be whole heads, k and v alike");
+  } else if (kind == SDV_PACK_GATE_UP) {
+    if (rows0 != rows1 || rows2 || rows0 % 8) return fail(SDV_ERR_SHAPE, "gate and up need equal rows, a multiple of 8");
+  } else {
+    return fail(SDV_ERR_SHAPE, "pack kind %d", kind);
+  }
+  a.n_packed = cdiv(total, 16) * 16;
+  const size_t need = sdv_packed_bytes(dtype, (int32_t)total, K);
+  if (dst_bytes < need) return fail(SDV_ERR_WORKSPACE, "destination %zu < %zu bytes", dst_bytes, need);
+  a.dst = dst;
+  SDV_LAUNCH(launch_pack(dtype == SDV_BF16, a, (hipStream_t)stream));
   return SDV_OK;
 }
 

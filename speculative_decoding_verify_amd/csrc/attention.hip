@@ -488,7 +488,7 @@ __global__ __launch_bounds__(DH) void attn_combine(CombineArgs a) {
       num += wgt * v[s];
     }
   }
-  ((float*)a.o)[((size_t)row * a.H + h) * DH + threadIdx.x] = num / den;
+  act_store1<T>((char*)a.o + (size_t)row * a.H * DH * 4, h * DH + threadIdx.x, num / den);
 }
 
 // the register path serves heads with few query tiles (its merge buffers and

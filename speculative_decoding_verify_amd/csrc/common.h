@@ -69,6 +69,45 @@ SDV_DEV void split_hi_lo(u32x4 a, u32x4 b, u32x4& hi, u32x4& lo) {
   lo.x = l[0] | (l[1] << 16); lo.y = l[2] | (l[3] << 16); lo.z = l[4] | (l[5] << 16); lo.w = l[6] | (l[7] << 16);
 }
 
+// Activation rows: bf16 models store each value as a split pair (k group g of 8
+// values at bytes g*32: 8 bf16 hi parts, then 8 bf16 lo parts), fp32 models store
+// fp32.  act_store1 writes value k of a row, act_store8 values k0..k0+7 (k0 % 8 == 0).
+SDV_DEV void split1(float x, bf16& hi, bf16& lo) {
+  hi = f2bf(x);
+  lo = f2bf(x - bf2f(hi));
+}
+template <typename T> SDV_DEV void act_store1(void* row, int k, float x);
+template <> SDV_DEV void act_store1<float>(void* row, int k, float x) { ((float*)row)[k] = x; }
+template <> SDV_DEV void act_store1<bf16>(void* row, int k, float x) {
+  bf16 hi, lo;
+  split1(x, hi, lo);
+  bf16* g = (bf16*)row + (k >> 3) * 16 + (k & 7);
+  g[0] = hi;
+  g[8] = lo;
+}
+template <typename T> SDV_DEV void act_store8(void* row, int k0, const float (&x)[8]);
+template <> SDV_DEV void act_store8<float>(void* row, int k0, const float (&x)[8]) {
+  float4* p = (float4*)((float*)row + k0);
+  p[0] = make_float4(x[0], x[1], x[2], x[3]);
+  p[1] = make_float4(x[4], x[5], x[6], x[7]);
+}
+template <> SDV_DEV void act_store8<bf16>(void* row, int k0, const float (&x)[8]) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    bf16 hb, lb;
+    split1(x[e], hb, lb);
+    h[e] = hb;
+    l[e] = lb;
+  }
+  u32x4 hi, lo;
+  hi.x = h[0] | (h[1] << 16); hi.y = h[2] | (h[3] << 16); hi.z = h[4] | (h[5] << 16); hi.w = h[6] | (h[7] << 16);
+  lo.x = l[0] | (l[1] << 16); lo.y = l[2] | (l[3] << 16); lo.z = l[4] | (l[5] << 16); lo.w = l[6] | (l[7] << 16);
+  char* g = (char*)row + (k0 >> 3) * 32;
+  st16(g, hi);
+  st16(g + 16, lo);
+}
+
 // elements of T held in 16 bytes
 template <typename T> struct Vec16 { static constexpr int N = 16 / sizeof(T); };
 

@@ -1,11 +1,11 @@
 // Row-wise kernels of the verify forward: prologue (tree bookkeeping and the
 // rotary table), embedding + first norm, residual add + RMSNorm, and the LM-head
-// statistics reduction.  Activations (residual stream and normalised rows) are fp32.
+// statistics reduction.  The residual stream is fp32; normalised rows are written
+// in the activation format of the GEMMs (bf16 hi/lo pairs for bf16 models, fp32
+// otherwise).
 //
 // Every split-K reduction sums the partials in split order 0..S-1 so results are
-// deterministic.  Rounding to the storage type happens exactly where a bf16 model
-// stores values: normalised activations, q/k/v after RoPE, attention output and
-// SwiGLU output; the residual stream stays fp32.
+// deterministic.
 #include "common.h"
 #include "kernels.h"
 
@@ -75,9 +75,10 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // RMSNorm of one fp32 row held in registers (256 threads, PER elements each,
-// element c = threadIdx.x * PER + i).
-template <int PER>
-SDV_DEV void norm_store(const float (&v)[PER], int d, const float* gain, float* out, float eps, float* red) {
+// element c = threadIdx.x * PER + i), stored in the activation format of T.
+template <typename T, int PER>
+SDV_DEV void norm_store(const float (&v)[PER], int d, const float* gain, void* out_row, float eps, float* red) {
+  static_assert(PER % 8 == 0, "whole k groups per thread");
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) ss += v[i] * v[i];
@@ -86,7 +87,12 @@ SDV_DEV void norm_store(const float (&v)[PER], int d, const float* gain, float* 
   const int c0 = threadIdx.x * PER;
   if (c0 < d) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) out[c0 + i] = v[i] * rs * gain[c0 + i];
+    for (int g = 0; g < PER / 8; ++g) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = v[g * 8 + e] * rs * gain[c0 + g * 8 + e];
+      act_store8<T>(out_row, c0 + g * 8, y);
+    }
   }
 }
 
@@ -107,7 +113,7 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(EmbedArgs a) {
     v[i] = c0 < a.d ? to_f<T>(e[c0 + i]) : 0.f;
     if (c0 < a.d) a.x[(size_t)m * a.d + c0 + i] = v[i];
   }
-  norm_store<PER>(v, a.d, a.gain, (float*)a.a + (size_t)m * a.d, a.eps, red);
+  norm_store<T, PER>(v, a.d, a.gain, (char*)a.a + (size_t)m * a.d * 4, a.eps, red);
 }
 
 // x += sum of the S split partials (in split order), then RMSNorm -> a.  Each
@@ -153,11 +159,11 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(ResidNormArgs a) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) v[i] = 0.f;
   }
-  norm_store<PER>(v, a.d, a.gain, (float*)a.a + (size_t)m * a.d, a.eps, red);
+  norm_store<T, PER>(v, a.d, a.gain, (char*)a.a + (size_t)m * a.d * 4, a.eps, red);
 }
 
-// PER columns per thread: the smallest of 4, 8, 12, 16, 24, 32 with 256 * PER >= d and
-// d % PER == 0 (d is a multiple of 32, so PER = 4 always divides it)
+// PER columns per thread: the smallest of 8, 16, 24, 32 with 256 * PER >= d and
+// d % PER == 0 (d is a multiple of 64, so PER = 8 always divides it)
 template <typename T>
 static hipError_t launch_rows(bool resid, int d, int M, const void* args, hipStream_t s) {
 #define SDV_ROWS(P)                                                                     \
@@ -166,7 +172,7 @@ static hipError_t launch_rows(bool resid, int d, int M, const void* args, hipStr
     else embed_norm_kernel<T, P><<<M, 256, 0, s>>>(*(const EmbedArgs*)args);           \
     return hipGetLastError();                                                           \
   }
-  SDV_ROWS(4) SDV_ROWS(8) SDV_ROWS(12) SDV_ROWS(16) SDV_ROWS(24) SDV_ROWS(32)
+  SDV_ROWS(8) SDV_ROWS(16) SDV_ROWS(24) SDV_ROWS(32)
 #undef SDV_ROWS
   return hipErrorInvalidValue;
 }

@@ -1,210 +1,200 @@
 // Weight-streaming GEMM for few rows: out[m, n] = sum_k A[m, k] * W[n, k].
 //
-// A (activations) is fp32.  With bf16 weights each group of 8 activations enters
-// the bf16 MFMA as a hi + lo pair (two MFMAs), so products carry ~16 significant
-// bits of the activation; only the weights are bf16.  With fp32 weights the fp32
-// MFMA is used directly.
-//
-// The decoder projections of a verify pass multiply M = B*T (tens of) activation
-// rows by weight matrices of tens to hundreds of MB, so the kernel is bound by
-// streaming W from HBM once.  Work layout:
-//   * a workgroup has WN x WK waves: the WN waves take different column tiles, the
-//     WK waves split the workgroup's K range (reduced through LDS in a fixed order);
-//   * blockIdx.x: a column group of WN * NT * 16 weight rows; blockIdx.y: a split of
-//     K across workgroups (fp32 partials, summed in split order by the consumer);
-//     blockIdx.z: a block of 16 * MT activation rows;
-//   * each lane streams 16 contiguous bytes of a weight row per k step (four lanes
-//     cover 64 B of one row); the next U steps are in flight while the current U are
-//     multiplied (software pipeline); the activation tile is read through the caches.
+// The decoder projections of a verify pass multiply M = B*T (tens of) activation rows
+// by weight matrices of tens to hundreds of MB, so every launch is bound by reading W
+// from HBM once.  The design serves that stream:
+//   * W is packed once at load time into 1 KB tiles (16 rows x one k step) laid out
+//     in lane order, so each wave load instruction reads one contiguous kilobyte that
+//     is already the B operand of a 16x16 MFMA;
+//   * the activations arrive in the operand format too: bf16 models store each value
+//     as a bf16 hi/lo pair (two MFMAs; the product carries ~16 significant bits of the
+//     activation, only the weights are bf16), fp32 models use the fp32 MFMA;
+//   * the four waves of a workgroup take every fourth k step of the workgroup's range;
+//     each wave keeps D k steps of loads (W tiles and activation pairs) in flight in
+//     registers and consumes the oldest, so HBM sees a steady stream with no
+//     workgroup barrier inside the k loop;
+//   * the waves' partial tiles are summed through LDS in a fixed order, then one of
+//     the epilogues below runs on the finished tile.
+// Grid: x = groups of NT weight tiles (16 * NT packed rows), y = splits of K (fp32
+// partials summed in split order by the consumer), z = blocks of 16 * MT rows.
 //
 // Epilogues (all but PARTIAL need the whole K range in one workgroup, S = 1):
 //   PARTIAL  fp32 partial sums of each split;
-//   QKV      rotary embedding on q and k (both halves of every rotation pair sit in
-//            the same workgroup); q written row-major in fp32, k and v rounded to the
+//   QKV      rotary embedding on q and k: packed rows 0-7 of a tile are the first
+//            members (element i) and rows 8-15 the second members (element i + dh/2)
+//            of 8 rotation pairs; q written row-major in fp32, k and v rounded to the
 //            cache type and appended to the paged cache (k token-major, v transposed
 //            inside the page);
-//   SWIGLU   h = silu(gate) * up in fp32 (gate and up rows of the same index in one workgroup);
+//   SWIGLU   rows 0-7 of a tile are gate rows f, rows 8-15 the up rows of the same f:
+//            h = silu(gate) * up, stored in the activation format;
 //   LOGITS   fp32 logits plus per-(row, column group) statistics: largest value, its
 //            index (lowest on ties), second-largest value and sum of exp(v - largest).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace sdv {
 
-// weight row of local pair/plain column (wave-group q, tile ct, lane row r)
-template <int NT>
-SDV_DEV int map_col(const GemmArgs& a, int q, int ct, int r) {
-  if (a.pair_mode == PAIR_NONE) return (q * NT + ct) * 16 + r;
-  constexpr int H = NT / 2;
-  const int j = ct % H, second = ct >= H;
-  const int p = (q * H + j) * 16 + r;  // pair index
-  if (a.pair_mode == PAIR_SWIGLU) return p + (second ? a.pair_off : 0);
-  // rotation pairs of a head: element i with i + dh/2
-  const int half = a.pair_off;
-  return (p / half) * 2 * half + p % half + (second ? half : 0);
-}
-
-template <typename T, int MT, int NT, int WN, int WK, int U, int EPI>
-__global__ __launch_bounds__(64 * WN * WK) void gemm_rows(GemmArgs a) {
-  constexpr int VE = Vec16<T>::N;   // elements per lane per step (8 bf16 / 4 fp32)
-  constexpr int KS = VE * 4;        // k per step across the 4 lane groups
-  constexpr int NTH = 64 * WN * WK;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wn = wave % WN, wk = wave / WN;
+template <typename T, int MT, int NT, int D, int EPI>
+__global__ __launch_bounds__(256) void gemm_stream(GemmArgs a) {
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int KS = BF ? 32 : 16;   // k values per step (one 1 KB weight tile)
+  constexpr int AB = BF ? 32 : 16;   // activation bytes per lane group per row per step
+  constexpr int TC = 16 * NT;        // packed columns of the workgroup
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, lg = lane >> 4;
   const int cg = blockIdx.x, split = blockIdx.y;
   const int m_base = blockIdx.z * (16 * MT);
 
-  const int total_steps = a.K / KS;
+  const int ksteps = a.K / KS;
   const int s0 = split * a.steps_per_split;
-  const int s1 = min(total_steps, s0 + a.steps_per_split);
-  const int nst = max(0, s1 - s0);
-  const int ws0 = s0 + (nst * wk) / WK, ws1 = s0 + (nst * (wk + 1)) / WK;
+  const int s1 = min(ksteps, s0 + a.steps_per_split);
+  const int nk = max(0, (s1 - s0 - wave + 3) >> 2);  // this wave: steps s0 + wave + 4j
+  const int ntiles = (a.N + 15) >> 4;
 
-  const T* wrow[NT];
+  const char* wp[NT];
 #pragma unroll
-  for (int ct = 0; ct < NT; ++ct) {
-    const int n = min(map_col<NT>(a, cg * WN + wn, ct, r), a.N - 1);
-    const T* base = n < a.N0   ? (const T*)a.W0 + (size_t)n * a.K
-                    : n < a.N1 ? (const T*)a.W1 + (size_t)(n - a.N0) * a.K
-                               : (const T*)a.W2 + (size_t)(n - a.N1) * a.K;
-    wrow[ct] = base + lg * VE;
+  for (int t = 0; t < NT; ++t) {
+    const int tile = min(cg * NT + t, ntiles - 1);
+    wp[t] = (const char*)a.W + ((size_t)tile * ksteps + s0 + wave) * 1024 + lane * 16;
   }
-  const float* arow[MT];
-  bool avalid[MT];
+  const char* ap[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int m = m_base + mt * 16 + r;
-    avalid[mt] = m < a.M;
-    const int row = avalid[mt] ? (a.a_rows ? a.a_rows[m] : m) : 0;
-    arow[mt] = (const float*)a.A + (size_t)row * a.lda + lg * VE;
+    const int m = min(m_base + mt * 16 + r, a.M - 1);
+    const int row = a.a_rows ? a.a_rows[m] : m;
+    ap[mt] = (const char*)a.A + (size_t)row * a.lda * 4 + (size_t)(s0 + wave) * KS * 4 + lg * AB;
   }
-  constexpr bool BF = sizeof(T) == 2;
-  constexpr int AL = BF ? 2 : 1;   // 16-byte activation loads per k step (8 or 4 fp32)
 
+  constexpr int AL = BF ? 2 : 1;
+  u32x4 wb[D][NT], ab[D][MT][AL];
+  auto issue = [&](int j, u32x4 (&w)[NT], u32x4 (&av)[MT][AL]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w[t] = ld16_stream(wp[t] + (size_t)j * 4096);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int h = 0; h < AL; ++h) av[mt][h] = ld16(ap[mt] + (size_t)j * (KS * 16) + 16 * h);
+  };
   f32x4 acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) acc[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  u32x4 wb[U][NT];
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct)
-      wb[u][ct] = (ws0 + u < ws1) ? ld16_stream(wrow[ct] + (size_t)(ws0 + u) * KS) : zero;
-  for (int st = ws0; st < ws1; st += U) {
-    u32x4 ab[U][MT][AL];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int h = 0; h < AL; ++h)
-          ab[u][mt][h] = (avalid[mt] && st + u < ws1) ? ld16(arow[mt] + (size_t)(st + u) * KS + 4 * h) : zero;
-    u32x4 wn_[U][NT];
-    const int nx = st + U;
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int ct = 0; ct < NT; ++ct)
-        wn_[u][ct] = (nx + u < ws1) ? ld16_stream(wrow[ct] + (size_t)(nx + u) * KS) : zero;
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if constexpr (BF) {
-          u32x4 hi, lo;
-          split_hi_lo(ab[u][mt][0], ab[u][mt][AL - 1], hi, lo);
-#pragma unroll
-          for (int ct = 0; ct < NT; ++ct) {
-            acc[mt][ct] = mma16<T>(hi, wb[u][ct], acc[mt][ct]);
-            acc[mt][ct] = mma16<T>(lo, wb[u][ct], acc[mt][ct]);
-          }
-        } else {
-#pragma unroll
-          for (int ct = 0; ct < NT; ++ct) acc[mt][ct] = mma16<T>(ab[u][mt][0], wb[u][ct], acc[mt][ct]);
-        }
-      }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int ct = 0; ct < NT; ++ct) wb[u][ct] = wn_[u][ct];
-  }
-
-  // ---- reduce the WK waves of each column tile through LDS (fixed order) into
-  //      tile[row][local column], local column = (wn * NT + ct) * 16 + r
-  constexpr int NE = MT * NT * 4;
-  constexpr int TC = WN * NT * 16;          // columns of the workgroup
-  __shared__ float tile[16 * MT][TC + 1];
-  if constexpr (WK > 1) {
-    __shared__ float red[WK][WN][NE][64];
+    for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const u32x4 (&w)[NT], const u32x4 (&av)[MT][AL]) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[wk][wn][(mt * NT + ct) * 4 + i][lane] = acc[mt][ct][i];
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < WN * NE * 64; idx += NTH) {
-      const int ln = idx & 63, e = (idx >> 6) % NE, q = (idx >> 6) / NE;
-      float v = 0.f;
+        for (int h = 0; h < AL; ++h) acc[mt][t] = mma16<T>(av[mt][h], w[t], acc[mt][t]);
+  };
+
 #pragma unroll
-      for (int k = 0; k < WK; ++k) v += red[k][q][e][ln];
-      const int i = e & 3, t = e >> 2, ct = t % NT, mt = t / NT;
-      tile[mt * 16 + 4 * (ln >> 4) + i][(q * NT + ct) * 16 + (ln & 15)] = v;
+  for (int u = 0; u < D - 1; ++u)
+    if (u < nk) issue(u, wb[u], ab[u]);
+  // steady state: every prefetch of the group is in range (no branches, so the
+  // compiler keeps D - 1 steps of loads outstanding)
+  int j0 = 0;
+  for (; j0 + 2 * D - 2 < nk; j0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      issue(j0 + u + D - 1, wb[(u + D - 1) % D], ab[(u + D - 1) % D]);
+      compute(wb[u], ab[u]);
     }
-  } else {
+  }
+  // tail: at most 2D - 2 steps remain
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int j = j0 + g * D + u;
+      if (j < nk) {
+        if (j + D - 1 < nk) issue(j + D - 1, wb[(u + D - 1) % D], ab[(u + D - 1) % D]);
+        compute(wb[u], ab[u]);
+      }
+    }
+
+  // ---- sum the four waves in a fixed order, (w0 + w2) + (w1 + w3), into tile[row][col]
+  constexpr int NE = MT * NT * 4;
+  __shared__ float red[2][NE][64];
+  __shared__ float tile[16 * MT][TC + 1];
+  if (wave >= 2) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) tile[mt * 16 + 4 * lg + i][(wn * NT + ct) * 16 + r] = acc[mt][ct][i];
+        for (int v = 0; v < 4; ++v) red[wave - 2][(mt * NT + t) * 4 + v][lane] = acc[mt][t][v];
+  }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[mt][t][v] += red[wave][(mt * NT + t) * 4 + v][lane];
+  }
+  __syncthreads();
+  if (wave == 1) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[0][(mt * NT + t) * 4 + v][lane] = acc[mt][t][v];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          tile[mt * 16 + 4 * lg + v][t * 16 + r] = acc[mt][t][v] + red[0][(mt * NT + t) * 4 + v][lane];
   }
   __syncthreads();
 
   if constexpr (EPI == EPI_PARTIAL) {
     float* out = a.out + (size_t)split * a.out_split_stride;
-    for (int idx = threadIdx.x; idx < 16 * MT * TC; idx += NTH) {
+    for (int idx = threadIdx.x; idx < 16 * MT * TC; idx += 256) {
       const int ml = idx / TC, c = idx % TC;
       const int m = m_base + ml, n = cg * TC + c;
       if (m < a.M && n < a.N) out[(size_t)m * a.ldo + n] = tile[ml][c];
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
-    // local column (q*NT + ct)*16 + r: ct < NT/2 gate, ct >= NT/2 up of the same row
-    constexpr int H = NT / 2;
-    for (int idx = threadIdx.x; idx < 16 * MT * WN * H * 16; idx += NTH) {
-      const int ml = idx / (WN * H * 16), pc = idx % (WN * H * 16);
-      const int q = pc / (H * 16), j = (pc / 16) % H, rr = pc % 16;
+    for (int idx = threadIdx.x; idx < 16 * MT * NT * 8; idx += 256) {
+      const int ml = idx / (NT * 8), pc = idx % (NT * 8);
+      const int t = pc >> 3, i = pc & 7;
       const int m = m_base + ml;
-      const int f = ((cg * WN + q) * H + j) * 16 + rr;
-      if (m >= a.M || f >= a.pair_off) continue;
-      const float gt = tile[ml][(q * NT + j) * 16 + rr];
-      const float up = tile[ml][(q * NT + H + j) * 16 + rr];
+      const int f = (cg * NT + t) * 8 + i;
+      if (m >= a.M || f >= a.pair_n) continue;
+      const float gt = tile[ml][t * 16 + i];
+      const float up = tile[ml][t * 16 + 8 + i];
       const float sl = gt / (1.f + expf(-gt));
-      ((float*)a.out_act)[(size_t)m * a.pair_off + f] = sl * up;
+      act_store1<T>((char*)a.out_act + (size_t)m * a.pair_n * 4, f, sl * up);
     }
   } else if constexpr (EPI == EPI_QKV) {
-    constexpr int H = NT / 2;
     const QkvEpi& e = a.qkv;
-    const int half = a.pair_off;          // dh / 2
+    const int half = a.pair_n;  // dh / 2
     const int dh = 2 * half;
-    for (int idx = threadIdx.x; idx < 16 * MT * WN * H * 16; idx += NTH) {
-      const int ml = idx / (WN * H * 16), pc = idx % (WN * H * 16);
-      const int q = pc / (H * 16), j = (pc / 16) % H, rr = pc % 16;
+    for (int idx = threadIdx.x; idx < 16 * MT * NT * 8; idx += 256) {
+      const int ml = idx / (NT * 8), pc = idx % (NT * 8);
+      const int t = pc >> 3, ii = pc & 7;
       const int m = m_base + ml;
-      const int p = ((cg * WN + q) * H + j) * 16 + rr;   // pair index
-      const int hh = p / half, i = p % half;              // head (q, k, then v heads) and pair
+      const int p = (cg * NT + t) * 8 + ii;  // rotation pair
+      const int hh = p / half, i = p % half;  // head (q, k, then v heads) and element
       if (m >= a.M || hh >= e.H + 2 * e.Hkv) continue;
-      const float x1 = tile[ml][(q * NT + j) * 16 + rr];
-      const float x2 = tile[ml][(q * NT + H + j) * 16 + rr];
-      const int b = m / e.T, t = m % e.T;
+      const float x1 = tile[ml][t * 16 + ii];
+      const float x2 = tile[ml][t * 16 + 8 + ii];
+      const int b = m / e.T, tt = m % e.T;
       float y1 = x1, y2 = x2;
       if (hh < e.H + e.Hkv) {
-        const float2 cs = e.rope[(size_t)(b * e.T + t) * half + i];  // (cos, sin)
+        const float2 cs = e.rope[(size_t)(b * e.T + tt) * half + i];  // (cos, sin)
         y1 = x1 * cs.x - x2 * cs.y;
         y2 = x2 * cs.x + x1 * cs.y;
       }
@@ -214,7 +204,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_rows(GemmArgs a) {
         qo[i + half] = y2;
       } else {
         const int C = e.seq_len[b];
-        const int slot = C + t;
+        const int slot = C + tt;
         if (C < 0 || C > e.max_ctx || slot >= e.max_blocks * 16) {
           if (i == 0) set_err(e.err, b, 0x4);
           continue;
@@ -240,12 +230,12 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_rows(GemmArgs a) {
       }
     }
   } else {  // EPI_LOGITS
-    for (int ml = threadIdx.x; ml < 16 * MT; ml += NTH) {
+    const int nc = min(TC, a.N - cg * TC);
+    for (int ml = threadIdx.x; ml < 16 * MT; ml += 256) {
       const int m = m_base + ml;
       if (m >= a.M) continue;
       float m1 = -INFINITY, m2 = -INFINITY;
       int i1 = 0x7fffffff;
-      const int nc = min(TC, a.N - cg * TC);
       for (int c = 0; c < nc; ++c) {
         const float v = tile[ml][c];
         if (v > m1) { m2 = m1; m1 = v; i1 = cg * TC + c; }
@@ -256,7 +246,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_rows(GemmArgs a) {
       a.stats[(size_t)m * a.n_groups + cg] = make_float4(m1, __int_as_float(i1), m2, se);
     }
     if (a.logits) {
-      for (int idx = threadIdx.x; idx < 16 * MT * TC; idx += NTH) {
+      for (int idx = threadIdx.x; idx < 16 * MT * TC; idx += 256) {
         const int ml = idx / TC, c = idx % TC;
         const int m = m_base + ml, n = cg * TC + c;
         if (m < a.M && n < a.N) a.logits[(size_t)m * a.ldl + n] = tile[ml][c];
@@ -266,43 +256,92 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_rows(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// host-side dispatch: the instantiated (WN, WK, NT, U) configurations
-
-// LDS bytes of a configuration (wave-reduction buffer + output tile)
-constexpr int gemm_lds_bytes(int MT, int NT, int WN, int WK) {
-  return (WK > 1 ? WK * WN * MT * NT * 4 * 64 * 4 : 0) + 16 * MT * (WN * NT * 16 + 1) * 4;
+// Weight packing: packed row n (of n_packed, a multiple of 16) takes source row
+// src_row(n); rows past the sources are zero.  One thread per 16-byte chunk.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
+  constexpr int VE = 16 / sizeof(T);   // values per 16-byte chunk
+  constexpr int KS = 4 * VE;           // k values per tile
+  const int ksteps = a.K / KS;
+  const size_t nchunks = (size_t)a.n_packed * ksteps * 4;
+  for (size_t c = (size_t)blockIdx.x * 256 + threadIdx.x; c < nchunks; c += (size_t)gridDim.x * 256) {
+    // chunk c: tile c / 64, lane c % 64 = (k group, row) inside the tile
+    const size_t tidx = c >> 6;
+    const int ln = (int)(c & 63);
+    const int kg = ln >> 4, rr = ln & 15;
+    const int n = (int)(tidx / ksteps) * 16 + rr;
+    const int ks = (int)(tidx % ksteps);
+    int which = -1, row = 0;
+    if (a.kind == 0) {
+      if (n < a.rows[0]) { which = 0; row = n; }
+    } else {
+      const int t = n >> 4, i = n & 15;
+      const int p = t * 8 + (i & 7);  // pair index
+      const bool second = i >= 8;
+      int vrow;                        // row of the sources viewed as one matrix
+      if (a.kind == 1) {
+        const int half = a.head_dim / 2;
+        vrow = (p / half) * a.head_dim + p % half + (second ? half : 0);
+      } else {
+        vrow = p + (second ? a.rows[0] : 0);
+      }
+      int base = 0;
+      for (int s = 0; s < 3; ++s) {
+        if (vrow >= base && vrow < base + a.rows[s]) { which = s; row = vrow - base; break; }
+        base += a.rows[s];
+      }
+    }
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (which >= 0) v = ld16((const T*)a.src[which] + (size_t)row * a.K + ks * KS + kg * VE);
+    st16((char*)a.dst + c * 16, v);
+  }
 }
-constexpr int LDS_LIMIT = 160 * 1024;
 
-template <typename T, int MT, int NT, int WN, int WK, int EPI>
+hipError_t launch_pack(bool is_bf16, const PackArgs& a, hipStream_t s) {
+  const int eb = is_bf16 ? 2 : 4;
+  const size_t nchunks = (size_t)a.n_packed * a.K * eb / 16;
+  const int blocks = (int)std::min<size_t>(8192, (nchunks + 255) / 256);
+  if (blocks < 1) return hipSuccess;
+  if (is_bf16) pack_kernel<bf16><<<blocks, 256, 0, s>>>(a);
+  else pack_kernel<float><<<blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// host-side dispatch over the instantiated (MT, NT, D) configurations
+
+// LDS bytes of a configuration: two wave-partial buffers + the output tile
+constexpr int gemm_lds_bytes(int MT, int NT) { return 2 * MT * NT * 4 * 64 * 4 + 16 * MT * (16 * NT + 1) * 4; }
+constexpr int LDS_LIMIT = 160 * 1024;
+int gemm_lds_ok(int MT, int NT) { return gemm_lds_bytes(MT, NT) <= LDS_LIMIT; }
+
+template <typename T, int MT, int NT, int D, int EPI>
 static hipError_t launch_one(dim3 grid, const GemmArgs& a, hipStream_t s) {
-  if constexpr (gemm_lds_bytes(MT, NT, WN, WK) <= LDS_LIMIT) {
-    gemm_rows<T, MT, NT, WN, WK, 4, EPI><<<grid, 64 * WN * WK, 0, s>>>(a);
+  if constexpr (gemm_lds_bytes(MT, NT) <= LDS_LIMIT) {
+    gemm_stream<T, MT, NT, D, EPI><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;
   }
 }
 
-template <typename T, int NT, int WN, int WK, int EPI>
+template <typename T, int NT, int D, int EPI>
 static hipError_t launch_mt(int MT, dim3 grid, const GemmArgs& a, hipStream_t s) {
   switch (MT) {
-    case 1: return launch_one<T, 1, NT, WN, WK, EPI>(grid, a, s);
-    case 2: return launch_one<T, 2, NT, WN, WK, EPI>(grid, a, s);
-    case 3: return launch_one<T, 3, NT, WN, WK, EPI>(grid, a, s);
-    case 4: return launch_one<T, 4, NT, WN, WK, EPI>(grid, a, s);
-    case 5: return launch_one<T, 5, NT, WN, WK, EPI>(grid, a, s);
+    case 1: return launch_one<T, 1, NT, D, EPI>(grid, a, s);
+    case 2: return launch_one<T, 2, NT, D, EPI>(grid, a, s);
+    case 3: return launch_one<T, 3, NT, D, EPI>(grid, a, s);
+    case 4: return launch_one<T, 4, NT, D, EPI>(grid, a, s);
+    case 5: return launch_one<T, 5, NT, D, EPI>(grid, a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename T, int EPI>
 static hipError_t launch_cfg(const GemmCfg& c, int MT, dim3 grid, const GemmArgs& a, hipStream_t s) {
-  // (NT, WN, WK) combinations; pair epilogues need an even NT
-  if (c.NT == 2 && c.WN == 1 && c.WK == 4) return launch_mt<T, 2, 1, 4, EPI>(MT, grid, a, s);
-  if (c.NT == 4 && c.WN == 1 && c.WK == 4) return launch_mt<T, 4, 1, 4, EPI>(MT, grid, a, s);
-  if (c.NT == 2 && c.WN == 2 && c.WK == 2) return launch_mt<T, 2, 2, 2, EPI>(MT, grid, a, s);
-  if (c.NT == 4 && c.WN == 2 && c.WK == 2) return launch_mt<T, 4, 2, 2, EPI>(MT, grid, a, s);
+  if (c.NT == 2 && c.D == 4) return launch_mt<T, 2, 4, EPI>(MT, grid, a, s);
+  if (c.NT == 4 && c.D == 2) return launch_mt<T, 4, 2, EPI>(MT, grid, a, s);
+  if (c.NT == 8 && c.D == 2) return launch_mt<T, 8, 2, EPI>(MT, grid, a, s);
   return hipErrorInvalidValue;
 }
 

@@ -6,7 +6,6 @@
 namespace sdv {
 
 enum { EPI_PARTIAL = 0, EPI_LOGITS = 1, EPI_QKV = 2, EPI_SWIGLU = 3 };
-enum { PAIR_NONE = 0, PAIR_SWIGLU = 1, PAIR_QKV = 2 };
 
 // QKV epilogue: rotary embedding + q write + paged K/V append
 struct QkvEpi {
@@ -21,22 +20,32 @@ struct QkvEpi {
   int32_t* err;
 };
 
+// Activation operands of the GEMMs ("A"), one row per chunk row, K values each:
+//   bf16 models: split pairs -- k group g (8 values) of a row occupies 32 bytes at
+//     g * 32: 8 bf16 "hi" parts then 8 bf16 "lo" parts, x = hi + lo + O(2^-16 |x|);
+//   fp32 models: plain fp32.
+// Either way a row takes 4 bytes per k; lda counts k values.
+//
+// Weights are packed in 1 KB tiles of 16 rows x KS k values (KS = 32 bf16 / 16 fp32):
+// tile (n / 16, k / KS) sits at ((n / 16) * (K / KS) + k / KS) * 1024 bytes; inside,
+// the 16-byte chunk of row n % 16 and k group ((k % KS) / (KS / 4)) sits at
+// (k group * 16 + n % 16) * 16, so lane l of a wave reads chunk l.  Pair packings put
+// the two members of 8 pairs into one tile: rows 0-7 the first members, rows 8-15
+// the second members of the same pairs.
 struct GemmArgs {
-  const void* A;            // fp32 activations, rows of lda elements
-  int lda;
+  const void* A;            // activation rows (format above)
+  int lda;                  // row stride in k values
   const int32_t* a_rows;    // nullable: output row m reads A row a_rows[m]
   int M;
-  const void* W0;           // columns n < N0: row n of W0
-  const void* W1;           // columns N0 <= n < N1: row n - N0 of W1
-  const void* W2;           // columns n >= N1: row n - N1 of W2
-  int N0, N1, N, K;
-  int steps_per_split;      // k steps (32 bf16 / 16 fp32 elements) per workgroup split
-  int pair_mode;            // column pairing for the SWIGLU / QKV epilogues
-  int pair_off;             // SWIGLU: F (gate row f pairs with up row f); QKV: dh/2
+  const void* W;            // packed weight tiles
+  int N;                    // output columns (packed rows) that are written
+  int K;
+  int steps_per_split;      // k steps (KS values) per workgroup split
+  int pair_n;               // SWIGLU: F (pairs = h columns); QKV: dh / 2
   float* out;               // PARTIAL: out[split * out_split_stride + m * ldo + n]
   long long out_split_stride;
   int ldo;
-  void* out_act;            // SWIGLU: h [M, F] fp32
+  void* out_act;            // SWIGLU: h [M, F] in the activation format
   QkvEpi qkv;               // QKV epilogue arguments
   float* logits;            // LOGITS: logits[m * ldl + n] (nullable)
   int ldl;
@@ -44,13 +53,25 @@ struct GemmArgs {
   int n_groups;
 };
 
-// launch configuration: NT column tiles per wave, WN x WK waves per workgroup
+// launch configuration: NT weight tiles per workgroup, D k steps in flight per wave
 struct GemmCfg {
-  int NT, WN, WK;
+  int NT, D;
 };
-
+int gemm_lds_ok(int MT, int NT);
 hipError_t launch_gemm(bool is_bf16, const GemmCfg& c, int MT, int epi, dim3 grid, const GemmArgs& a,
                        hipStream_t s);
+
+// weight packing (one-time, at model load): rows of up to three row-major [rows, K]
+// sources, viewed as one matrix, rearranged into tiles; kind 0 plain, 1 q/k/v rotation
+// pairs (head_dim), 2 gate/up pairs
+struct PackArgs {
+  int kind, K, head_dim;
+  const void* src[3];
+  int rows[3];
+  int n_packed;             // packed rows (multiple of 16)
+  void* dst;
+};
+hipError_t launch_pack(bool is_bf16, const PackArgs& a, hipStream_t s);
 
 struct AttnArgs {
   const void* q;            // [B*T, H*dh] fp32
@@ -76,7 +97,7 @@ bool attn_uses_reg_path(bool bf, int dh, int NQT);  // keys per tile: 32 bf16 / 
 struct CombineArgs {
   const float* po;
   const float* pml;
-  void* o;                  // [B*T, H*dh] fp32
+  void* o;                  // [B*T, H*dh] in the activation format
   int B, T, H, Hkv, dh, n_splits, nq_pad;
 };
 hipError_t launch_combine(bool is_bf16, const CombineArgs& a, hipStream_t s);
@@ -101,7 +122,7 @@ struct EmbedArgs {
   const void* embed;        // [V, d]
   const float* gain;        // first layer attention-norm gain
   float* x;                 // [M, d] fp32 residual
-  void* a;                  // [M, d] normalised rows, fp32
+  void* a;                  // [M, d] normalised rows in the activation format
   int M, T, d, V;
   float eps;
   int32_t* err;
@@ -114,7 +135,7 @@ struct ResidNormArgs {
   long long part_stride;
   int S;
   const float* gain;
-  void* a;                  // [M, d] normalised rows, fp32
+  void* a;                  // [M, d] normalised rows in the activation format
   float* hidden;            // nullable [M, d] copy of the updated residual
   int M, d;
   float eps;

@@ -128,6 +128,7 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
   const int target = TARGET_WG_ATTN;
   int ns = cdiv(target, (long long)B * Hkv);
   ns = std::max(1, std::min({ns, 32, cdiv(nkeys, KT)}));
+  ns = std::max(ns, cdiv(nkeys, 255 * KT));  // a split spans at most 511 pages (staged in LDS)
   p.split_keys = cdiv(cdiv(nkeys, ns), KT) * KT;
   p.n_splits = cdiv(nkeys, p.split_keys);
   p.nq_pad = NQT * 16;
@@ -269,13 +270,12 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
       GemmArgs a = gemm_args(act, d, nullptr, M, L.wqkv, qd + 2 * kd, d);
       a.pair_n = dh / 2;
       a.qkv = QkvEpi{q, kp, vp, kv->block_table, kv->max_blocks, kv->n_blocks, kv->seq_len, rope,
-                     B, T, H, Hkv, in->max_ctx, out->err};
+                     B, T, H, Hkv, in->max_ctx, out->err, (float)(1.4426950408889634 / sqrt((double)dh))};
       if ((st = run_gemm(pe, P, P.qkv, a, s)) != SDV_OK) return st;
     }
     {
       AttnArgs a{q, kp, vp, kv->block_table, kv->max_blocks, kv->n_blocks, kv->seq_len, anc, B, T, H, Hkv,
-                 P.split_keys, P.n_splits, (float)(1.4426950408889634 / sqrt((double)dh)), po, pml, P.nq_pad, 1,
-                 in->max_ctx};
+                 P.split_keys, P.n_splits, po, pml, P.nq_pad, 1, in->max_ctx};
       SDV_LAUNCH(launch_attention(P.bf, dh, a, s));
       CombineArgs c{po, pml, o, B, T, H, Hkv, dh, P.n_splits, P.nq_pad};
       SDV_LAUNCH(launch_combine(P.bf, c, s));

@@ -45,22 +45,59 @@ SDV_DEV void split_probs(const float (&p)[8], u32x4& hi, u32x4& lo) {
   lo.x = l[0] | (l[1] << 16); lo.y = l[2] | (l[3] << 16); lo.z = l[4] | (l[5] << 16); lo.w = l[6] | (l[7] << 16);
 }
 
-// Load the query operand of one lane (fp32 q, row offset `off`): for bf16 caches the 8
-// values of each k step become a hi + lo pair of bf16 operands, for fp32 caches the
-// 4 values are the operand.
+// Query operand of one lane.  The q buffer holds the queries pre-scaled by
+// log2(e)/sqrt(dh) in the activation format (4 bytes per value), so for bf16 the 8
+// values of lane group lg in k step ks are one 16-byte hi load and one 16-byte lo
+// load; for fp32 the 4 values are one load.  `off` is the value index of the head's
+// first value (row * H * dh + head * dh).
 template <bool BF, int DH, int KS, int VE>
 SDV_DEV void load_q(const void* q, size_t off, bool ok, int lg, u32x4 (&out)[DH / KS][BF ? 2 : 1]) {
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  const float* qp = (const float*)q + off + lg * VE;
+  const char* base = (const char*)q + off * 4;
 #pragma unroll
   for (int ks = 0; ks < DH / KS; ++ks) {
+    const char* g = base + (size_t)(ks * KS + lg * VE) * 4;
     if constexpr (BF) {
-      const u32x4 lo4 = ok ? ld16(qp + ks * KS) : zero, hi4 = ok ? ld16(qp + ks * KS + 4) : zero;
-      split_hi_lo(lo4, hi4, out[ks][0], out[ks][1]);
+      out[ks][0] = ok ? ld16(g) : zero;
+      out[ks][1] = ok ? ld16(g + 16) : zero;
     } else {
-      out[ks][0] = ok ? ld16(qp + ks * KS) : zero;
+      out[ks][0] = ok ? ld16(g) : zero;
     }
   }
+}
+
+// Physical pages of the split's logical pages [k_begin/16, (k_end-1)/16] staged in LDS
+// once per workgroup (-1 where the table entry is out of range), so key and value
+// loads never wait on a block-table load.  The host keeps split_keys <= 16 * (512 - 1).
+constexpr int ATTN_MAX_PAGES = 512;
+SDV_DEV int stage_pages(const AttnArgs& a, const int32_t* bt, int k_begin, int k_end, int* sPage) {
+  const int pg0 = k_begin >> 4;
+  // at least one entry, so clamped addresses of an empty split stay defined
+  const int npg = k_end > k_begin ? min(((k_end - 1) >> 4) - pg0 + 1, ATTN_MAX_PAGES) : 1;
+  for (int i = threadIdx.x; i < npg; i += blockDim.x) {
+    const int pg = pg0 + i;
+    int phys = pg < a.max_blocks ? bt[pg] : -1;
+    if (phys < 0 || phys >= a.n_blocks) phys = -1;
+    sPage[i] = phys;
+  }
+  __syncthreads();
+  return pg0;
+}
+
+// Probabilities as a bf16 hi/lo operand pair, cheaply: hi = p rounded half-up to 8
+// significant bits, lo = the exact remainder p - hi truncated to bf16, so
+// |p - hi - lo| < 2^-15 |p|.  v_perm gathers the upper halves of two words.
+SDV_DEV void split_probs_fast(const float (&p)[8], u32x4& hi, u32x4& lo) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = (__float_as_uint(p[e]) + 0x8000u) & 0xFFFF0000u;
+    l[e] = __float_as_uint(p[e] - __uint_as_float(h[e]));
+  }
+  hi.x = __builtin_amdgcn_perm(h[1], h[0], 0x07060302u); hi.y = __builtin_amdgcn_perm(h[3], h[2], 0x07060302u);
+  hi.z = __builtin_amdgcn_perm(h[5], h[4], 0x07060302u); hi.w = __builtin_amdgcn_perm(h[7], h[6], 0x07060302u);
+  lo.x = __builtin_amdgcn_perm(l[1], l[0], 0x07060302u); lo.y = __builtin_amdgcn_perm(l[3], l[2], 0x07060302u);
+  lo.z = __builtin_amdgcn_perm(l[5], l[4], 0x07060302u); lo.w = __builtin_amdgcn_perm(l[7], l[6], 0x07060302u);
 }
 
 template <typename T, int DH, int NQW>
@@ -93,6 +130,8 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
   const int32_t* bt = a.block_table + (size_t)b * a.max_blocks;
   const T* kp = (const T*)a.k_pages;
   const T* vp = (const T*)a.v_pages;
+  __shared__ int sPage[ATTN_MAX_PAGES];
+  const int pg0 = stage_pages(a, bt, k_begin, k_end, sPage);
 
   // queries of this wave: tiles w, w + NW, ...
   constexpr int QP = BF ? 2 : 1;   // q enters bf16 MFMAs as a hi + lo pair
@@ -116,43 +155,68 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
     for (int dt = 0; dt < DH / 16; ++dt) acc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int kt0 = k_begin; kt0 < k_end; kt0 += KT) {
-    __syncthreads();
-    // ---- stage K (token-major) and V^T (dh-major) of this tile in LDS; slots at or
-    //      beyond the end of the sequence are zero-filled so no stale value is read
-    for (int c = threadIdx.x; c < KT * DH / VE; c += blockDim.x) {
-      const int key = c / (DH / VE), d0 = (c % (DH / VE)) * VE;
-      const int slot = kt0 + key, pg = slot >> 4;
+  // K (token-major) and V^T (dh-major) of a tile go through LDS; each thread holds
+  // its 16-byte chunks of the next tile in registers while the current one is used.
+  // Slots at or beyond the split end read as zero (values past the sequence end too,
+  // so no stale value is ever read).  The block has at least 4 waves.
+  constexpr int KCH = KT * DH / VE, VCH = NPG * DH * (16 / VE);
+  constexpr int MAXC = (std::max(KCH, VCH) + 255) / 256;
+  u32x4 kst[MAXC], vst[MAXC];
+  auto fetch = [&](int kt0) {
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = threadIdx.x + i * blockDim.x;
       u32x4 v = zero;
-      if (slot < nkeys && pg < a.max_blocks) {
-        const int phys = bt[pg];
-        if (phys >= 0 && phys < a.n_blocks)
-          v = ld16(kp + (((size_t)phys * a.Hkv + g) * 16 + (slot & 15)) * DH + d0);
+      if (c < KCH) {
+        const int key = c / (DH / VE), d0 = (c % (DH / VE)) * VE;
+        const int slot = kt0 + key;
+        const int phys = slot < k_end ? sPage[(slot >> 4) - pg0] : -1;
+        if (phys >= 0) v = ld16(kp + (((size_t)phys * a.Hkv + g) * 16 + (slot & 15)) * DH + d0);
       }
-      st16(&ldsK[key * KROW + d0], v);
-    }
-    for (int c = threadIdx.x; c < NPG * DH * (16 / VE); c += blockDim.x) {
-      const int p = c / (DH * (16 / VE)), rem = c % (DH * (16 / VE));
-      const int dd = rem / (16 / VE), o0 = (rem % (16 / VE)) * VE;
-      const int slot0 = kt0 + p * 16 + o0, pg = slot0 >> 4;
-      u32x4 v = zero;
-      if (slot0 < nkeys && pg < a.max_blocks) {
-        const int phys = bt[pg];
-        if (phys >= 0 && phys < a.n_blocks) {
+      kst[i] = v;
+      v = zero;
+      if (c < VCH) {
+        const int p = c / (DH * (16 / VE)), rem = c % (DH * (16 / VE));
+        const int dd = rem / (16 / VE), o0 = (rem % (16 / VE)) * VE;
+        const int slot0 = kt0 + p * 16 + o0;
+        const int phys = slot0 < k_end ? sPage[(slot0 >> 4) - pg0] : -1;
+        if (phys >= 0) {
           v = ld16(vp + (((size_t)phys * a.Hkv + g) * DH + dd) * 16 + o0);
           if (slot0 + VE > nkeys) {
             T e[VE];
             __builtin_memcpy(e, &v, 16);
 #pragma unroll
-            for (int i = 0; i < VE; ++i)
-              if (slot0 + i >= nkeys) e[i] = T(0);
+            for (int ii = 0; ii < VE; ++ii)
+              if (slot0 + ii >= nkeys) e[ii] = T(0);
             __builtin_memcpy(&v, e, 16);
           }
         }
       }
-      st16(&ldsV[(p * DH + dd) * VROW + o0], v);
+      vst[i] = v;
     }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = threadIdx.x + i * blockDim.x;
+      if (c < KCH) {
+        const int key = c / (DH / VE), d0 = (c % (DH / VE)) * VE;
+        st16(&ldsK[key * KROW + d0], kst[i]);
+      }
+      if (c < VCH) {
+        const int p = c / (DH * (16 / VE)), rem = c % (DH * (16 / VE));
+        const int dd = rem / (16 / VE), o0 = (rem % (16 / VE)) * VE;
+        st16(&ldsV[(p * DH + dd) * VROW + o0], vst[i]);
+      }
+    }
+  };
+
+  if (k_begin < k_end) fetch(k_begin);
+  for (int kt0 = k_begin; kt0 < k_end; kt0 += KT) {
+    __syncthreads();   // every wave is done with the previous tile
+    store();
     __syncthreads();
+    if (kt0 + KT < k_end) fetch(kt0 + KT);
 
 #pragma unroll
     for (int j = 0; j < NQW; ++j) {
@@ -193,7 +257,7 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
           const int jr = s - C;
           vis = (anc[j][jr >> 5] >> (jr & 31)) & 1u;
         }
-        sv[e] = vis ? sv[e] * a.scale_log2 : -INFINITY;
+        sv[e] = vis ? sv[e] : -INFINITY;
         mx = fmaxf(mx, sv[e]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -251,10 +315,13 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
   }
 }
 
-// Register path for few query tiles per kv head (at most 4): every wave holds all
-// query tiles of the head and streams its own interleaved key tiles straight from
-// the pages into MFMA operands, one tile ahead; the 4 waves of the workgroup merge
-// their states through LDS at the end and write one partial per split.
+// Register path for few query tiles per kv head (at most 3): every wave holds all
+// query tiles of the head (pre-scaled by log2(e)/sqrt(dh)) and streams its own
+// interleaved key tiles straight from the pages into MFMA operands, one tile ahead.
+// Per tile the score MFMAs of all query tiles are interleaved; the visibility mask is
+// evaluated only on tiles that reach the chunk rows or the end of the split; the
+// accumulators are rescaled only when some row's running maximum rises.  The 4 waves
+// of the workgroup merge their states through LDS and write one partial per split.
 template <typename T, int DH, int NQT>
 __global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
   constexpr bool BF = sizeof(T) == 2;
@@ -262,7 +329,8 @@ __global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
   constexpr int KS = 4 * VE;
   constexpr int KT = BF ? 32 : 16;
   constexpr int PE = BF ? 8 : 4;
-  constexpr int NKA = (BF ? 2 : 1) * (DH / KS);   // K operand loads per tile
+  constexpr int NH = BF ? 2 : 1;                  // 16-key halves of a tile
+  constexpr int NKA = NH * (DH / KS);             // K operand loads per tile
   constexpr int NVA = DH / 16;                    // V operand loads per tile
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, r = lane & 15, lg = lane >> 4;
@@ -278,6 +346,8 @@ __global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
   const T* kp = (const T*)a.k_pages;
   const T* vp = (const T*)a.v_pages;
   const u32x4 zero = {0u, 0u, 0u, 0u};
+  __shared__ int sPage[ATTN_MAX_PAGES];
+  const int pg0 = stage_pages(a, bt, k_begin, k_end, sPage);
 
   constexpr int QP = BF ? 2 : 1;
   u32x4 qreg[NQT][DH / KS][QP];
@@ -299,95 +369,126 @@ __global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
     for (int dt = 0; dt < DH / 16; ++dt) acc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // load the K and V^T operands of key tile `it` (relative to k_begin); slots at or
-  // beyond the end of the sequence read as zero
+  // K and V^T operands of key tile `it` (relative to k_begin).  Loads are branch-free:
+  // a slot past the split end reads the split's last valid slot instead (its scores
+  // are masked and, past the sequence end, its values zeroed in compute_tile); a
+  // page whose table entry is out of range reads page 0 and is treated the same way.
+  const int last = max(k_end - 1, k_begin);
+  auto page_of = [&](int slot) {
+    const int ph = sPage[(min(slot, last) >> 4) - pg0];
+    return ph < 0 ? 0 : ph;
+  };
   auto load_tile = [&](int it, u32x4 (&ko)[NKA], u32x4 (&vo)[NVA]) {
-    const int kt0 = k_begin + it * KT;
-    // K rows: bf16 tile has two 16-key halves whose rows map to keys 8*(r/4) + r%4 (+4)
+    const int kt0 = k_begin + min(it, max(ntiles - 1, 0)) * KT;
+    // K rows: a bf16 tile has two 16-key halves whose rows map to keys 8*(r/4) + r%4 (+4)
 #pragma unroll
-    for (int hv = 0; hv < (BF ? 2 : 1); ++hv) {
+    for (int hv = 0; hv < NH; ++hv) {
       const int key = BF ? 8 * (r >> 2) + (r & 3) + 4 * hv : r;
-      const int slot = kt0 + key;
-      const bool ok = it < ntiles && slot < nkeys;
-      int phys = ok ? bt[slot >> 4] : 0;
-      const bool okp = ok && phys >= 0 && phys < a.n_blocks;
-      const T* src = kp + (((size_t)(okp ? phys : 0) * a.Hkv + g) * 16 + (slot & 15)) * DH + lg * VE;
+      const int slot = min(kt0 + key, last);
+      const T* src = kp + (((size_t)page_of(slot) * a.Hkv + g) * 16 + (slot & 15)) * DH + lg * VE;
 #pragma unroll
-      for (int ks = 0; ks < DH / KS; ++ks) ko[hv * (DH / KS) + ks] = okp ? ld16(src + ks * KS) : zero;
+      for (int ks = 0; ks < DH / KS; ++ks) ko[hv * (DH / KS) + ks] = ld16(src + ks * KS);
     }
-    // V^T: lane holds dh row dt*16 + r for keys PE*lg .. PE*lg + PE - 1
-    const int slot0 = kt0 + PE * lg;
-    const bool okv = it < ntiles && slot0 < nkeys;
-    int physv = okv ? bt[slot0 >> 4] : 0;
-    const bool okpv = okv && physv >= 0 && physv < a.n_blocks;
-    const T* vsrc = vp + (((size_t)(okpv ? physv : 0) * a.Hkv + g) * DH + r) * 16 + (slot0 & 15);
+    // V^T: lane holds dh row dt*16 + r for keys PE*lg .. PE*lg + PE - 1 (one page)
+    const int slot0 = min(kt0 + PE * lg, last & ~(PE - 1));
+    const T* vsrc = vp + (((size_t)page_of(slot0) * a.Hkv + g) * DH + r) * 16 + (slot0 & 15);
 #pragma unroll
-    for (int dt = 0; dt < NVA; ++dt) {
-      u32x4 v = okpv ? ld16(vsrc + (size_t)dt * 16 * 16) : zero;
-      if (okpv && slot0 + PE > nkeys) {
-        T e[VE];
-        __builtin_memcpy(e, &v, 16);
-#pragma unroll
-        for (int i = 0; i < VE; ++i)
-          if (slot0 + i >= nkeys) e[i] = T(0);
-        __builtin_memcpy(&v, e, 16);
-      }
-      vo[dt] = v;
-    }
+    for (int dt = 0; dt < NVA; ++dt) vo[dt] = ld16(vsrc + (size_t)dt * 16 * 16);
   };
 
-  auto compute_tile = [&](int it, const u32x4 (&ko)[NKA], const u32x4 (&vo)[NVA]) {
+  auto compute_tile = [&](int it, const u32x4 (&ko)[NKA], u32x4 (&vo)[NVA]) {
     const int kt0 = k_begin + it * KT;
+    f32x4 sc[NQT][NH];
+#pragma unroll
+    for (int j = 0; j < NQT; ++j)
+#pragma unroll
+      for (int hv = 0; hv < NH; ++hv) sc[j][hv] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DH / KS; ++ks)
+#pragma unroll
+      for (int qp = 0; qp < QP; ++qp)
+#pragma unroll
+        for (int j = 0; j < NQT; ++j)
+#pragma unroll
+          for (int hv = 0; hv < NH; ++hv) sc[j][hv] = mma16<T>(ko[hv * (DH / KS) + ks], qreg[j][ks][qp], sc[j][hv]);
+    float sv[NQT][PE];
+#pragma unroll
+    for (int j = 0; j < NQT; ++j)
+#pragma unroll
+      for (int hv = 0; hv < NH; ++hv)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[j][4 * hv + i] = sc[j][hv][i];
+    // only tiles that reach the chunk rows (tree / causal mask), the split end or a
+    // page with an out-of-range table entry need a mask (wave-uniform test)
+    bool bad_page = false;
+#pragma unroll
+    for (int pp = 0; pp < KT / 16; ++pp) {
+      const int sl = kt0 + pp * 16;
+      bad_page |= sl <= last && sPage[(sl >> 4) - pg0] < 0;
+    }
+    if (kt0 + KT > C || kt0 + KT > k_end || bad_page) {
+#pragma unroll
+      for (int j = 0; j < NQT; ++j)
+#pragma unroll
+        for (int e = 0; e < PE; ++e) {
+          const int sl = kt0 + PE * lg + e;
+          bool vis = sl < k_end && sPage[(min(sl, last) >> 4) - pg0] >= 0;
+          if (vis && sl >= C) {
+            const int jr = sl - C;
+            vis = (anc[j][jr >> 5] >> (jr & 31)) & 1u;
+          }
+          if (!vis) sv[j][e] = -INFINITY;
+        }
+      // values of keys that are not real cache rows (past the sequence end or on an
+      // invalid page) may hold anything; zero them so 0 * value stays 0
+      const int sl0 = kt0 + PE * lg;
+      const bool pg_ok = sl0 <= last && sPage[(sl0 >> 4) - pg0] >= 0;
+#pragma unroll
+      for (int dt = 0; dt < NVA; ++dt) {
+        T e8[VE];
+        __builtin_memcpy(e8, &vo[dt], 16);
+#pragma unroll
+        for (int i = 0; i < VE; ++i)
+          if (!pg_ok || sl0 + i >= k_end) e8[i] = T(0);
+        __builtin_memcpy((void*)&vo[dt], e8, 16);
+      }
+    }
+    float mnew[NQT];
+    bool rise = false;
 #pragma unroll
     for (int j = 0; j < NQT; ++j) {
-      if (j * 16 >= nq) continue;
-      float sv[PE];
-      if constexpr (BF) {
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      float mx = sv[j][0];
 #pragma unroll
-        for (int ks = 0; ks < DH / KS; ++ks) {
-#pragma unroll
-          for (int qp = 0; qp < QP; ++qp) {
-            s0 = mma16<T>(ko[ks], qreg[j][ks][qp], s0);
-            s1 = mma16<T>(ko[DH / KS + ks], qreg[j][ks][qp], s1);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { sv[i] = s0[i]; sv[4 + i] = s1[i]; }
-      } else {
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < DH / KS; ++ks) s0 = mma16<T>(ko[ks], qreg[j][ks][0], s0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sv[i] = s0[i];
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < PE; ++e) {
-        const int s = kt0 + PE * lg + e;
-        bool vis = s < k_end;
-        if (vis && s >= C) {
-          const int jr = s - C;
-          vis = (anc[j][jr >> 5] >> (jr & 31)) & 1u;
-        }
-        sv[e] = vis ? sv[e] * a.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sv[e]);
-      }
+      for (int e = 1; e < PE; ++e) mx = fmaxf(mx, sv[j][e]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun[j], mx);
-      const float alpha = exp2f(mrun[j] - mnew);
-      mrun[j] = mnew;
-      float ps = 0.f, p[PE];
+      mnew[j] = fmaxf(mrun[j], mx);
+      rise |= mnew[j] > mrun[j];
+    }
+    if (__any(rise)) {
 #pragma unroll
-      for (int e = 0; e < PE; ++e) { p[e] = exp2f(sv[e] - mnew); ps += p[e]; }
-      lrun[j] = lrun[j] * alpha + ps;
+      for (int j = 0; j < NQT; ++j) {
+        const float alpha = __builtin_amdgcn_exp2f(mrun[j] - mnew[j]);
+        mrun[j] = mnew[j];
+        lrun[j] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DH / 16; ++dt) acc[j][dt] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NQT; ++j) {
+      float p[PE], ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < PE; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(sv[j][e] - mrun[j]);
+        ps += p[e];
+      }
+      lrun[j] += ps;
       if constexpr (BF) {
         u32x4 phi, plo;
-        split_probs(p, phi, plo);
+        split_probs_fast(p, phi, plo);
 #pragma unroll
         for (int dt = 0; dt < DH / 16; ++dt) {
-          acc[j][dt] *= alpha;
           acc[j][dt] = mma16<T>(vo[dt], phi, acc[j][dt]);
           acc[j][dt] = mma16<T>(vo[dt], plo, acc[j][dt]);
         }
@@ -396,10 +497,7 @@ __global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
         pb.x = __float_as_uint(p[0]); pb.y = __float_as_uint(p[1]);
         pb.z = __float_as_uint(p[2]); pb.w = __float_as_uint(p[3]);
 #pragma unroll
-        for (int dt = 0; dt < DH / 16; ++dt) {
-          acc[j][dt] *= alpha;
-          acc[j][dt] = mma16<T>(vo[dt], pb, acc[j][dt]);
-        }
+        for (int dt = 0; dt < DH / 16; ++dt) acc[j][dt] = mma16<T>(vo[dt], pb, acc[j][dt]);
       }
     }
   };
@@ -509,7 +607,8 @@ int attn_shape(int NQT, int* nqw_out, int* nw_out) {
   int nqw = 1;
   while ((NQT + nqw - 1) / nqw > 8 && nqw < CAP) ++nqw;
   if (nqw == 5) nqw = 6;
-  const int nw = std::min(8, (NQT + nqw - 1) / nqw);
+  // at least 4 waves: waves without query tiles still help staging K/V
+  const int nw = std::max(4, std::min(8, (NQT + nqw - 1) / nqw));
   *nqw_out = nqw;
   *nw_out = nw;
   return (NQT + nw * nqw - 1) / (nw * nqw);

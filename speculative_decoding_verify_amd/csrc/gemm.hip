@@ -22,7 +22,8 @@
 //   PARTIAL  fp32 partial sums of each split;
 //   QKV      rotary embedding on q and k: packed rows 0-7 of a tile are the first
 //            members (element i) and rows 8-15 the second members (element i + dh/2)
-//            of 8 rotation pairs; q written row-major in fp32, k and v rounded to the
+//            of 8 rotation pairs; q scaled by log2(e)/sqrt(dh) and written in the
+//            activation format, k and v rounded to the
 //            cache type and appended to the paged cache (k token-major, v transposed
 //            inside the page);
 //   SWIGLU   rows 0-7 of a tile are gate rows f, rows 8-15 the up rows of the same f:
@@ -199,9 +200,9 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs a) {
         y2 = x2 * cs.x + x1 * cs.y;
       }
       if (hh < e.H) {
-        float* qo = (float*)e.q + (size_t)m * e.H * dh + hh * dh;
-        qo[i] = y1;
-        qo[i + half] = y2;
+        char* qrow = (char*)e.q + (size_t)m * e.H * dh * 4;
+        act_store1<T>(qrow, hh * dh + i, y1 * e.q_scale);
+        act_store1<T>(qrow, hh * dh + i + half, y2 * e.q_scale);
       } else {
         const int C = e.seq_len[b];
         const int slot = C + tt;

@@ -9,7 +9,7 @@ enum { EPI_PARTIAL = 0, EPI_LOGITS = 1, EPI_QKV = 2, EPI_SWIGLU = 3 };
 
 // QKV epilogue: rotary embedding + q write + paged K/V append
 struct QkvEpi {
-  void* q;                  // [M, H*dh] fp32
+  void* q;                  // [M, H*dh] queries times q_scale, in the activation format
   void* k_pages;            // this layer: [n_blocks][Hkv][16][dh]
   void* v_pages;            //             [n_blocks][Hkv][dh][16]
   const int32_t* block_table;
@@ -18,6 +18,7 @@ struct QkvEpi {
   const float2* rope;       // [B*T][dh/2] (cos, sin) of each chunk row's position
   int B, T, H, Hkv, max_ctx;
   int32_t* err;
+  float q_scale;            // log2(e) / sqrt(dh): attention works in the exp2 domain
 };
 
 // Activation operands of the GEMMs ("A"), one row per chunk row, K values each:
@@ -74,7 +75,7 @@ struct PackArgs {
 hipError_t launch_pack(bool is_bf16, const PackArgs& a, hipStream_t s);
 
 struct AttnArgs {
-  const void* q;            // [B*T, H*dh] fp32
+  const void* q;            // [B*T, H*dh] queries pre-scaled by log2(e)/sqrt(dh), activation format
   const void* k_pages;      // this layer's pages: [n_blocks][Hkv][16][dh]
   const void* v_pages;      //                      [n_blocks][Hkv][dh][16]
   const int32_t* block_table;
@@ -83,7 +84,6 @@ struct AttnArgs {
   const uint32_t* anc;      // [T][4] ancestor-or-self bits of each chunk row
   int B, T, H, Hkv;
   int split_keys, n_splits;
-  float scale_log2;         // log2(e) / sqrt(dh)
   float* po;                // [B][Hkv][n_splits][nq_pad][dh] unnormalised output
   float* pml;               // [B][Hkv][n_splits][nq_pad][2] (running max in log2 units, sum)
   int nq_pad;

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SDV_ABI_VERSION 2
+#define SDV_ABI_VERSION 3
 #define SDV_PAGE 16          /* tokens per KV-cache page */
 #define SDV_MAX_T 128        /* rows per verify pass (chunk + drafts + branches) */
 
@@ -85,12 +85,16 @@ typedef enum { SDV_F32 = 0, SDV_BF16 = 1 } sdv_dtype;
 
 typedef enum { SDV_PACK_PLAIN = 0, SDV_PACK_QKV = 1, SDV_PACK_GATE_UP = 2 } sdv_pack_kind;
 
+/* Which head produces the next-token distributions of a verify pass. */
+typedef enum { SDV_HEAD_LM = 0, SDV_HEAD_CODEBOOK = 1 } sdv_head;
+
 /* device-side error bits written to the per-sequence error word */
 #define SDV_EBAD_TOKEN    0x1   /* a token id outside [0, vocab) (treated as 0) */
 #define SDV_EBAD_PARENT   0x2   /* parent[j] not in [0, j) for j > 0, or parent[0] != -1 */
 #define SDV_EOVERFLOW     0x4   /* seq_len + T exceeds the cache capacity or max_ctx + T */
 #define SDV_EBAD_MOVE     0x8   /* a rollback move or keep_len outside the capacity */
 #define SDV_EDUP_SIBLING  0x10  /* two children of one tree row carry the same token */
+#define SDV_EBAD_PAIR     0x20  /* cfg_partner[b] out of range or not mutual (row uses its own logits) */
 
 /* One decoder layer: pre-norm attention block and SwiGLU FFN block.  Matrices are
  * packed (see above); the shapes given are those of the row-major sources. */
@@ -116,6 +120,16 @@ typedef struct {
   const float* final_norm;   /* [d] */
   const void* lm_head;       /* SDV_PACK_PLAIN of W_lm [V, d] */
   const sdv_layer* layers;   /* HOST array of n_layers entries (device pointers inside) */
+  /* Codebook heads ("An Efficient vLLM-Based Inference Pipeline for Unified Audio
+   * Understanding and Generation", page 2, Figure 1): S audio streams of Vc codes;
+   * stream s scores codes with W_cb (RMSNorm(h; final_norm) + e_s), W_cb shared by all
+   * streams.  Code c of codebook 0 is backbone token codebook_base + c.  Zero / NULL
+   * when the model has no codebook heads. */
+  int32_t n_codebooks;       /* S */
+  int32_t codebook_size;     /* Vc */
+  int32_t codebook_base;     /* backbone id of code 0 of codebook 0 */
+  const void* codebook;      /* SDV_PACK_PLAIN of W_cb [Vc, d] */
+  const float* stream_emb;   /* [S, d] fp32 stream embeddings e_s */
 } sdv_model;
 
 /* Paged KV cache.  Logical slot s of sequence b lives in physical page
@@ -142,21 +156,37 @@ typedef struct {
  *            or its ancestors.
  *   logit_rows [R] chunk rows whose next-token distributions are produced (for
  *            greedy acceptance: L_a-1 and every draft row).
- *   max_ctx  host-side upper bound on every seq_len[b]; sizes the attention grid. */
+ *   max_ctx  host-side upper bound on every seq_len[b]; sizes the attention grid.
+ *   head     SDV_HEAD_LM: logits over the full vocabulary from the LM head;
+ *            SDV_HEAD_CODEBOOK: per-codebook logits from the codebook heads, and the
+ *            statistics and argmax of codebook 0 (as backbone ids) for acceptance.
+ *   cfg_partner [B] device, nullable (codebook head only): classifier-free guidance
+ *            pairs ("paired scheduling", page 2).  For rows b and p = cfg_partner[b]
+ *            with cfg_partner[p] == b, the lower index is the conditional row c, the
+ *            other the unconditional row u, and BOTH rows get the guided logits
+ *            u + cfg_w (c - u) of every codebook, so they accept the same tokens (the
+ *            caller feeds both rows the same tokens).  -1 = no guidance for row b. */
 typedef struct {
   int32_t batch, T, L_a, R, max_ctx;
   const int32_t* tokens;
   const int32_t* parent;       /* nullable */
   const int32_t* logit_rows;
+  int32_t head;                /* sdv_head */
+  const int32_t* cfg_partner;  /* nullable */
+  float cfg_w;
 } sdv_verify_in;
 
 /* Outputs of sdv_verify_forward (all device, [B, R] unless noted):
- *   logits  fp32 [B, R, V] or NULL (the statistics below are produced either way)
- *   argmax  int32: index of the largest logit, lowest index on ties
+ *   logits  fp32 [B, R, V] or NULL (the statistics below are produced either way);
+ *           codebook head: fp32 [B, R, S, Vc] (guided for rows of a pair)
+ *   argmax  int32: index of the largest logit, lowest index on ties; codebook head:
+ *           codebook_base + the argmax code of codebook 0 (margin and lse likewise
+ *           describe codebook 0)
  *   margin  fp32: largest minus second-largest logit (0 on a tie)
  *   lse     fp32: log(sum_v exp(logit_v))
  *   hidden  fp32 [B, T, d] or NULL: residual stream after the last layer
  *   err     int32 [B]: device error bits (OR-ed in; the caller clears it)
+ *   cb_argmax  see the field
  *   prof_events  nullable host array of n_prof_events caller-created hipEvent_t
  *           handles: when given, event 2i is recorded on the stream before and event
  *           2i+1 after the i-th weight-streaming GEMM launch of the pass (decoder
@@ -171,6 +201,7 @@ typedef struct {
   int32_t* err;
   void* const* prof_events;
   int32_t n_prof_events;
+  int32_t* cb_argmax;          /* codebook head: int32 [B, R, S] argmax code per codebook, nullable */
 } sdv_verify_out;
 
 /* Bytes of workspace sdv_verify_forward needs for this model and pass shape. */

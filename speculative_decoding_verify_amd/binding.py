@@ -29,6 +29,7 @@ _i32 = ctypes.c_int32
 
 
 PACK_PLAIN, PACK_QKV, PACK_GATE_UP = 0, 1, 2
+HEAD_LM, HEAD_CODEBOOK = 0, 1
 
 
 class SdvLayer(ctypes.Structure):
@@ -40,7 +41,9 @@ class SdvModel(ctypes.Structure):
                 ("head_dim", _i32), ("ffn", _i32), ("vocab", _i32), ("dtype", _i32),
                 ("eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
                 ("embed", _vp), ("final_norm", _vp), ("lm_head", _vp),
-                ("layers", ctypes.POINTER(SdvLayer))]
+                ("layers", ctypes.POINTER(SdvLayer)),
+                ("n_codebooks", _i32), ("codebook_size", _i32), ("codebook_base", _i32),
+                ("codebook", _vp), ("stream_emb", _vp)]
 
 
 class SdvKV(ctypes.Structure):
@@ -50,13 +53,14 @@ class SdvKV(ctypes.Structure):
 
 class SdvVerifyIn(ctypes.Structure):
     _fields_ = [("batch", _i32), ("T", _i32), ("L_a", _i32), ("R", _i32), ("max_ctx", _i32),
-                ("tokens", _vp), ("parent", _vp), ("logit_rows", _vp)]
+                ("tokens", _vp), ("parent", _vp), ("logit_rows", _vp),
+                ("head", _i32), ("cfg_partner", _vp), ("cfg_w", ctypes.c_float)]
 
 
 class SdvVerifyOut(ctypes.Structure):
     _fields_ = [("logits", _vp), ("argmax", _vp), ("margin", _vp), ("lse", _vp),
                 ("hidden", _vp), ("err", _vp), ("prof_events", ctypes.POINTER(_vp)),
-                ("n_prof_events", _i32)]
+                ("n_prof_events", _i32), ("cb_argmax", _vp)]
 
 
 class SdvError(RuntimeError):
@@ -160,8 +164,11 @@ class DeviceModel:
                                     wqkv=pk(PACK_QKV, [lw.wq, lw.wk, lw.wv], sh.head_dim),
                                     wo=pk(PACK_PLAIN, [lw.wo]), ffn_norm=f(lw.ffn_norm),
                                     wgu=pk(PACK_GATE_UP, [lw.wg, lw.wu]), wd=pk(PACK_PLAIN, [lw.wd])))
-        self.codebook = t(w.codebook) if getattr(w, "codebook", None) is not None else None
-        self.stream_emb = f(w.stream_emb) if getattr(w, "stream_emb", None) is not None else None
+        has_cb = getattr(w, "codebook", None) is not None and sh.n_codebooks > 0
+        self.codebook = pk(PACK_PLAIN, [w.codebook]) if has_cb else None
+        self.stream_emb = f(w.stream_emb) if has_cb else None
+        # codebook 0's codes are the backbone ids after the text part of the vocabulary
+        self.codebook_base = sh.vocab - sh.n_codebooks * sh.codebook_size if has_cb else 0
         self._build_desc()
 
     def _build_desc(self):
@@ -174,7 +181,10 @@ class DeviceModel:
         self.desc = SdvModel(sh.n_layers, sh.d, sh.n_heads, sh.n_kv_heads, sh.head_dim, sh.ffn, sh.vocab,
                              SDV_BF16 if sh.dtype == "bf16" else SDV_F32, sh.eps, sh.rope_theta,
                              self.embed.data_ptr(), self.final_norm.data_ptr(), self.lm_head.data_ptr(),
-                             ctypes.cast(arr, ctypes.POINTER(SdvLayer)))
+                             ctypes.cast(arr, ctypes.POINTER(SdvLayer)),
+                             sh.n_codebooks if self.codebook is not None else 0,
+                             sh.codebook_size if self.codebook is not None else 0, self.codebook_base,
+                             _ptr(self.codebook), _ptr(self.stream_emb))
 
     @property
     def weight_bytes(self) -> int:
@@ -245,6 +255,7 @@ class VerifyResult:
     err: torch.Tensor
     logits: Optional[torch.Tensor] = None
     hidden: Optional[torch.Tensor] = None
+    cb_argmax: Optional[torch.Tensor] = None
 
 
 class Verifier:
@@ -253,7 +264,8 @@ class Verifier:
 
     def __init__(self, model: DeviceModel, kv: PagedKV, T: int, L_a: int, logit_rows: Sequence[int],
                  parent: Optional[Sequence[int]] = None, max_ctx: Optional[int] = None,
-                 want_logits: bool = True, want_hidden: bool = False):
+                 want_logits: bool = True, want_hidden: bool = False, head: int = HEAD_LM,
+                 cfg_partner: Optional[Sequence[int]] = None, cfg_w: float = 1.0):
         self.model, self.kv = model, kv
         dev = model.device
         B = kv.batch
@@ -264,7 +276,14 @@ class Verifier:
         self.logit_rows = torch.tensor(list(logit_rows), dtype=torch.int32, device=dev)
         self.parent = None if parent is None else torch.tensor(list(parent), dtype=torch.int32, device=dev)
         V = model.shape.vocab
-        self.logits = torch.empty((B, self.R, V), dtype=torch.float32, device=dev) if want_logits else None
+        sh = model.shape
+        self.head = head
+        lshape = (B, self.R, V) if head == HEAD_LM else (B, self.R, sh.n_codebooks, sh.codebook_size)
+        self.logits = torch.empty(lshape, dtype=torch.float32, device=dev) if want_logits else None
+        self.cb_argmax = (torch.empty((B, self.R, sh.n_codebooks), dtype=torch.int32, device=dev)
+                          if head == HEAD_CODEBOOK else None)
+        self.cfg_partner = (None if cfg_partner is None
+                            else torch.tensor(list(cfg_partner), dtype=torch.int32, device=dev))
         self.hidden = torch.empty((B, T, model.shape.d), dtype=torch.float32, device=dev) if want_hidden else None
         self.argmax = torch.empty((B, self.R), dtype=torch.int32, device=dev)
         self.margin = torch.empty((B, self.R), dtype=torch.float32, device=dev)
@@ -276,9 +295,10 @@ class Verifier:
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self.inp = SdvVerifyIn(B, T, L_a, self.R, self.max_ctx, self.tokens.data_ptr(),
                                None if self.parent is None else self.parent.data_ptr(),
-                               self.logit_rows.data_ptr())
+                               self.logit_rows.data_ptr(), head, _ptr(self.cfg_partner), float(cfg_w))
         self.out = SdvVerifyOut(_ptr(self.logits), self.argmax.data_ptr(), self.margin.data_ptr(),
-                                self.lse.data_ptr(), _ptr(self.hidden), self.err.data_ptr())
+                                self.lse.data_ptr(), _ptr(self.hidden), self.err.data_ptr(), None, 0,
+                                _ptr(self.cb_argmax))
 
     def set_profile_events(self, events) -> None:
         """events: list of torch.cuda.Event (enable_timing=True), recorded by the library
@@ -304,7 +324,7 @@ class Verifier:
                                         ctypes.byref(self.inp), ctypes.byref(self.out),
                                         ctypes.c_void_p(self.workspace.data_ptr()), self.workspace.numel(),
                                         _stream(stream)), "sdv_verify_forward")
-        return VerifyResult(self.argmax, self.margin, self.lse, self.err, self.logits, self.hidden)
+        return VerifyResult(self.argmax, self.margin, self.lse, self.err, self.logits, self.hidden, self.cb_argmax)
 
 
 def accept_greedy(B: int, T: int, L_a: int, tokens: torch.Tensor, parent: Optional[torch.Tensor],

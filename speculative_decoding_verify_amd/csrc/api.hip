@@ -80,11 +80,12 @@ struct Plan {
   bool bf;
   int eb;  // element bytes
   int M, Mr, G, nq_pad;
-  GemmPlan qkv, o, gu, dn, lm;
+  GemmPlan qkv, o, gu, dn, lm, cb;
+  int S;  // codebook streams (0: the model has no codebook heads)
   int split_keys, n_splits;
   size_t part_floats;
   size_t off_x, off_a, off_q, off_o, off_h, off_part, off_po, off_pml, off_stats, off_depth, off_anc,
-      off_lmrows, off_rope, total;
+      off_lmrows, off_rope, off_cb, total;
 };
 
 sdv_status check_model(const sdv_model* m) {
@@ -97,6 +98,12 @@ sdv_status check_model(const sdv_model* m) {
   if (m->d % 64 || m->ffn % 64) return fail(SDV_ERR_UNSUPPORTED, "d and ffn must be multiples of 64");
   if (m->d > 8192) return fail(SDV_ERR_UNSUPPORTED, "d > 8192");
   if (!m->embed || !m->final_norm || !m->lm_head || !m->layers) return fail(SDV_ERR_NULL, "model pointer NULL");
+  if (m->n_codebooks < 0) return fail(SDV_ERR_SHAPE, "n_codebooks < 0");
+  if (m->n_codebooks > 0) {
+    if (!m->codebook || !m->stream_emb) return fail(SDV_ERR_NULL, "codebook pointers NULL");
+    if (m->codebook_size < 2 || m->codebook_base < 0 || (long long)m->codebook_base + m->codebook_size > m->vocab)
+      return fail(SDV_ERR_SHAPE, "codebook size/base outside the vocabulary");
+  }
   for (int l = 0; l < m->n_layers; ++l) {
     const sdv_layer& L = m->layers[l];
     if (!L.attn_norm || !L.wqkv || !L.wo || !L.ffn_norm || !L.wgu || !L.wd)
@@ -119,6 +126,8 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
   p.gu = plan_gemm(p.M, 2 * F, d, p.bf, EPI_SWIGLU);
   p.dn = plan_gemm(p.M, d, F, p.bf, EPI_PARTIAL);
   p.lm = plan_gemm(p.Mr, m->vocab, d, p.bf, EPI_LOGITS);
+  p.S = m->n_codebooks > 0 ? m->n_codebooks : 0;
+  if (p.S) p.cb = plan_gemm(p.Mr + p.S, m->codebook_size, d, p.bf, EPI_PARTIAL);
   p.part_floats = std::max((size_t)p.o.S * p.M * d, (size_t)p.dn.S * p.M * d);
   // attention: split the keys so that the grid fills the GPU (the register path
   // has four waves per workgroup, each streaming its own key tiles)
@@ -136,8 +145,9 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
   p.off_x = take((size_t)p.M * d * 4);
-  // activation rows take 4 bytes per value (bf16 hi/lo pairs or fp32)
-  p.off_a = take((size_t)p.M * d * 4);
+  // activation rows take 4 bytes per value (bf16 hi/lo pairs or fp32); the codebook
+  // head appends its S stream-embedding rows
+  p.off_a = take((size_t)(p.M + p.S) * d * 4);
   p.off_q = take((size_t)p.M * qd * 4);
   p.off_o = take((size_t)p.M * qd * 4);
   p.off_h = take((size_t)p.M * F * 4);
@@ -148,8 +158,9 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
   p.off_stats = take((size_t)p.Mr * p.lm.ncg * 16);
   p.off_depth = take((size_t)T * 4);
   p.off_anc = take((size_t)T * 16);
-  p.off_lmrows = take((size_t)p.Mr * 4);
+  p.off_lmrows = take((size_t)(p.Mr + p.S) * 4);
   p.off_rope = take((size_t)p.M * (dh / 2) * 8);
+  p.off_cb = p.S ? take((size_t)p.cb.S * (p.Mr + p.S) * m->codebook_size * 4) : o;
   p.total = o;
   return p;
 }
@@ -224,6 +235,9 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
   if (kv->max_blocks < 1 || kv->n_blocks < 1) return fail(SDV_ERR_SHAPE, "empty cache");
   if ((long long)in->max_ctx + T > (long long)kv->max_blocks * SDV_PAGE)
     return fail(SDV_ERR_SHAPE, "max_ctx + T exceeds the cache capacity");
+  if (in->head != SDV_HEAD_LM && in->head != SDV_HEAD_CODEBOOK) return fail(SDV_ERR_SHAPE, "head %d", in->head);
+  if (in->head == SDV_HEAD_CODEBOOK && m->n_codebooks < 1) return fail(SDV_ERR_UNSUPPORTED, "model has no codebook heads");
+  if (in->head == SDV_HEAD_LM && in->cfg_partner) return fail(SDV_ERR_UNSUPPORTED, "guidance pairs need the codebook head");
   const Plan P = make_plan(m, B, T, R, in->max_ctx);
   if (!ws || ws_bytes < P.total) return fail(SDV_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, P.total);
 
@@ -253,13 +267,20 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
   }
   float2* rope = (float2*)(w + P.off_rope);
   {
+    const bool cbh = in->head == SDV_HEAD_CODEBOOK;
     PrologueArgs a{in->parent, in->logit_rows, kv->seq_len, B, T, R, depth, anc, lm_rows, rope, dh,
-                   m->rope_theta, out->err};
+                   m->rope_theta, out->err, cbh ? P.S : 0, M};
     SDV_LAUNCH(launch_prologue(a, s));
   }
   {
     EmbedArgs a{in->tokens, m->embed, m->layers[0].attn_norm, x, act, M, T, d, V, m->eps, out->err};
     SDV_LAUNCH(launch_embed_norm(P.bf, a, s));
+  }
+  if (m->n_codebooks < 0) return fail(SDV_ERR_SHAPE, "n_codebooks < 0");
+  if (m->n_codebooks > 0) {
+    if (!m->codebook || !m->stream_emb) return fail(SDV_ERR_NULL, "codebook pointers NULL");
+    if (m->codebook_size < 2 || m->codebook_base < 0 || (long long)m->codebook_base + m->codebook_size > m->vocab)
+      return fail(SDV_ERR_SHAPE, "codebook size/base outside the vocabulary");
   }
   for (int l = 0; l < m->n_layers; ++l) {
     const sdv_layer& L = m->layers[l];
@@ -308,15 +329,30 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
       SDV_LAUNCH(launch_resid_norm(P.bf, a, s));
     }
   }
-  {
-    GemmArgs a = gemm_args(act, d, lm_rows, P.Mr, m->lm_head, V, d);
-    a.logits = out->logits;
-    a.stats = stats;
-    if ((st = run_gemm(pe, P, P.lm, a, s)) != SDV_OK) return st;
-  }
-  {
-    RowReduceArgs a{stats, P.Mr, P.lm.ncg, out->argmax, out->margin, out->lse};
-    SDV_LAUNCH(launch_row_reduce(a, s));
+  if (in->head == SDV_HEAD_CODEBOOK) {
+    // codebook heads: W_cb on the final-normed logit rows and on the stream
+    // embeddings (rows M..M+S-1 of the activation buffer), then merge + statistics
+    const int S = P.S, Vc = m->codebook_size;
+    float* cbl = (float*)(w + P.off_cb);
+    StreamRowsArgs sr{m->stream_emb, S, d, act, M};
+    SDV_LAUNCH(launch_stream_rows(P.bf, sr, s));
+    GemmArgs a = gemm_args(act, d, lm_rows, P.Mr + S, m->codebook, Vc, d);
+    a.out = cbl;
+    if ((st = run_gemm(pe, P, P.cb, a, s)) != SDV_OK) return st;
+    CbMergeArgs c{cbl, (long long)(P.Mr + S) * Vc, P.cb.S, B, R, S, Vc, in->cfg_partner, in->cfg_w,
+                  m->codebook_base, out->logits, out->cb_argmax, out->argmax, out->margin, out->lse, out->err};
+    SDV_LAUNCH(launch_cb_merge(c, s));
+  } else {
+    {
+      GemmArgs a = gemm_args(act, d, lm_rows, P.Mr, m->lm_head, V, d);
+      a.logits = out->logits;
+      a.stats = stats;
+      if ((st = run_gemm(pe, P, P.lm, a, s)) != SDV_OK) return st;
+    }
+    {
+      RowReduceArgs a{stats, P.Mr, P.lm.ncg, out->argmax, out->margin, out->lse};
+      SDV_LAUNCH(launch_row_reduce(a, s));
+    }
   }
   return SDV_OK;
 }

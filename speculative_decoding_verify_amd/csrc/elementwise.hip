@@ -6,6 +6,8 @@
 //
 // Every split-K reduction sums the partials in split order 0..S-1 so results are
 // deterministic.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -50,6 +52,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
       if (row < 0 || row >= a.T) { set_err(a.err, b, 0x2); row = 0; }
       a.lm_rows[i] = b * a.T + row;
     }
+    for (int i = threadIdx.x; i < a.n_extra; i += blockDim.x) a.lm_rows[a.B * a.R + i] = a.extra_base + i;
     if (bad)
       for (int b = threadIdx.x; b < a.B; b += blockDim.x) set_err(a.err, b, 0x2);
   }
@@ -233,6 +236,92 @@ __global__ __launch_bounds__(256) void row_reduce_kernel(RowReduceArgs a) {
 
 hipError_t launch_row_reduce(const RowReduceArgs& a, hipStream_t s) {
   row_reduce_kernel<<<a.rows, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Codebook heads ("An Efficient vLLM-Based Inference Pipeline for Unified Audio
+// Understanding and Generation", page 2, Figure 1 and the paired-guidance section).
+// Stream s scores codes with W_cb (h_n + e_s), h_n the final-normed hidden row; by
+// linearity that is W_cb h_n + W_cb e_s, so the head GEMM runs on the B*R logit rows
+// plus the S embedding rows, and the merge kernel adds the two.
+
+template <typename T>
+__global__ __launch_bounds__(256) void stream_rows_kernel(StreamRowsArgs a) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.S * a.d; i += gridDim.x * blockDim.x) {
+    const int s = i / a.d, k = i % a.d;
+    act_store1<T>((char*)a.act + (size_t)(a.first_row + s) * a.d * 4, k, a.e[i]);
+  }
+}
+
+hipError_t launch_stream_rows(bool is_bf16, const StreamRowsArgs& a, hipStream_t s) {
+  const int blocks = std::max(1, std::min(64, (a.S * a.d + 255) / 256));
+  if (is_bf16) stream_rows_kernel<bf16><<<blocks, 256, 0, s>>>(a);
+  else stream_rows_kernel<float><<<blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// One workgroup per (b, r, s): logits of codebook s for logit row r of sequence b.
+// Rows of a guidance pair (partners c < u) both get u + w (c - u), evaluated in fp32
+// as written.  Statistics: argmax (lowest index on ties), top-2 margin, log-sum-exp,
+// reduced in a fixed order.
+__global__ __launch_bounds__(256) void cb_merge_kernel(CbMergeArgs a) {
+  const int s = blockIdx.x % a.S;
+  const int br = blockIdx.x / a.S;
+  const int b = br / a.R, r = br % a.R;
+  int p = a.partner ? a.partner[b] : -1;
+  if (p >= 0 && !(p < a.B && p != b && a.partner[p] == b)) {
+    if (threadIdx.x == 0) set_err(a.err, b, 0x20);
+    p = -1;
+  }
+  const int c = p >= 0 ? min(b, p) : b, u = p >= 0 ? max(b, p) : -1;
+  const size_t rc = (size_t)(c * a.R + r) * a.Vc, ru = (size_t)((u < 0 ? 0 : u) * a.R + r) * a.Vc;
+  const size_t re = (size_t)(a.B * a.R + s) * a.Vc;
+  float* lout = a.logits ? a.logits + ((size_t)(b * a.R + r) * a.S + s) * a.Vc : nullptr;
+  Top2 acc = {-INFINITY, -INFINITY, 0.f, 0x7fffffff};
+  for (int v = threadIdx.x; v < a.Vc; v += 256) {
+    float lc = 0.f, lu = 0.f, le = 0.f;
+    for (int k = 0; k < a.n_split; ++k) {
+      const float* pb = a.base + (size_t)k * a.split_stride;
+      lc += pb[rc + v];
+      le += pb[re + v];
+      if (u >= 0) lu += pb[ru + v];
+    }
+    const float cv = lc + le;
+    float x = cv;
+    if (u >= 0) {
+      const float uv = lu + le;
+      x = uv + a.w * (cv - uv);
+    }
+    if (lout) lout[v] = x;
+    acc = top2_merge(acc, Top2{x, -INFINITY, 1.f, v});
+  }
+  __shared__ float sm1[256], sm2[256], sse[256];
+  __shared__ int si1[256];
+  sm1[threadIdx.x] = acc.m1; sm2[threadIdx.x] = acc.m2; sse[threadIdx.x] = acc.se; si1[threadIdx.x] = acc.i1;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) {
+      const int q = threadIdx.x + o;
+      Top2 x{sm1[threadIdx.x], sm2[threadIdx.x], sse[threadIdx.x], si1[threadIdx.x]};
+      Top2 y{sm1[q], sm2[q], sse[q], si1[q]};
+      x = top2_merge(x, y);
+      sm1[threadIdx.x] = x.m1; sm2[threadIdx.x] = x.m2; sse[threadIdx.x] = x.se; si1[threadIdx.x] = x.i1;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    if (a.cb_argmax) a.cb_argmax[(size_t)br * a.S + s] = si1[0];
+    if (s == 0) {
+      a.argmax[br] = a.token_base + si1[0];
+      a.margin[br] = sm1[0] - sm2[0];
+      a.lse[br] = sm1[0] + logf(sse[0]);
+    }
+  }
+}
+
+hipError_t launch_cb_merge(const CbMergeArgs& a, hipStream_t s) {
+  cb_merge_kernel<<<a.B * a.R * a.S, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

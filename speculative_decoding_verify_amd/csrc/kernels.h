@@ -114,6 +114,7 @@ struct PrologueArgs {
   int dh;
   float rope_theta;
   int32_t* err;             // [B]
+  int n_extra, extra_base;  // lm_rows[B*R + i] = extra_base + i for i < n_extra
 };
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
 
@@ -150,6 +151,35 @@ struct RowReduceArgs {
   float* lse;
 };
 hipError_t launch_row_reduce(const RowReduceArgs& a, hipStream_t s);
+
+// Stream embedding rows e_s written as activation rows first_row + s (codebook head).
+struct StreamRowsArgs {
+  const float* e;           // [S, d]
+  int S, d;
+  void* act;                // activation rows (format of the model type)
+  int first_row;
+};
+hipError_t launch_stream_rows(bool is_bf16, const StreamRowsArgs& a, hipStream_t s);
+
+// Codebook logits of the logit rows plus guidance merge and statistics.  `base` holds
+// the head GEMM's split partials: base[split][row][Vc] with rows b*R + r for the logit
+// rows and B*R + s for W_cb e_s.
+struct CbMergeArgs {
+  const float* base;
+  long long split_stride;
+  int n_split;
+  int B, R, S, Vc;
+  const int32_t* partner;   // [B] nullable
+  float w;
+  int token_base;           // backbone id of code 0 of codebook 0
+  float* logits;            // [B, R, S, Vc] nullable
+  int32_t* cb_argmax;       // [B, R, S] nullable
+  int32_t* argmax;          // [B, R] (codebook 0, backbone ids)
+  float* margin;            // [B, R]
+  float* lse;               // [B, R]
+  int32_t* err;             // [B]
+};
+hipError_t launch_cb_merge(const CbMergeArgs& a, hipStream_t s);
 
 struct GreedyArgs {
   int B, T, L_a, R;

@@ -28,23 +28,6 @@
 
 namespace sdv {
 
-// The probabilities feed the P.V contraction as bf16 MFMA operands.  Rounding p
-// itself to bf16 would perturb the attention output by ~2^-9 relative, far above
-// fp32 accumulation noise; instead p = hi + lo with hi = bf16(p), lo = bf16(p - hi)
-// (about 16 significant bits), and P.V takes one MFMA per part.  The normaliser
-// sums the unrounded fp32 p.
-SDV_DEV void split_probs(const float (&p)[8], u32x4& hi, u32x4& lo) {
-  uint32_t h[8], l[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const bf16 hb = f2bf(p[e]);
-    h[e] = hb;
-    l[e] = f2bf(p[e] - bf2f(hb));
-  }
-  hi.x = h[0] | (h[1] << 16); hi.y = h[2] | (h[3] << 16); hi.z = h[4] | (h[5] << 16); hi.w = h[6] | (h[7] << 16);
-  lo.x = l[0] | (l[1] << 16); lo.y = l[2] | (l[3] << 16); lo.z = l[4] | (l[5] << 16); lo.w = l[6] | (l[7] << 16);
-}
-
 // Query operand of one lane.  The q buffer holds the queries pre-scaled by
 // log2(e)/sqrt(dh) in the activation format (4 bytes per value), so for bf16 the 8
 // values of lane group lg in k step ks are one 16-byte hi load and one 16-byte lo
@@ -211,6 +194,10 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
     }
   };
 
+  constexpr int NH = BF ? 2 : 1;                     // 16-key halves of a tile
+  const int krow0 = BF ? 8 * (r >> 2) + (r & 3) : r;  // K row of this lane (half 0)
+  // query tiles of this wave that exist (wave-uniform)
+  const int nj = min(NQW, max(0, (NQT - (q_base + w) + NW - 1) / NW));
   if (k_begin < k_end) fetch(k_begin);
   for (int kt0 = k_begin; kt0 < k_end; kt0 += KT) {
     __syncthreads();   // every wave is done with the previous tile
@@ -218,79 +205,98 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
     __syncthreads();
     if (kt0 + KT < k_end) fetch(kt0 + KT);
 
+    // ---- scores S^T of all this wave's query tiles; each K operand is read from LDS
+    //      once and used by every query tile
+    f32x4 sc[NQW][NH];
+#pragma unroll
+    for (int j = 0; j < NQW; ++j)
+#pragma unroll
+      for (int hv = 0; hv < NH; ++hv) sc[j][hv] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DH / KS; ++ks) {
+      u32x4 kk[NH];
+#pragma unroll
+      for (int hv = 0; hv < NH; ++hv) kk[hv] = ld16(&ldsK[(krow0 + 4 * hv) * KROW + ks * KS + lg * VE]);
+#pragma unroll
+      for (int qp = 0; qp < QP; ++qp)
+#pragma unroll
+        for (int j = 0; j < NQW; ++j)
+          if (j < nj)
+#pragma unroll
+            for (int hv = 0; hv < NH; ++hv) sc[j][hv] = mma16<T>(kk[hv], qreg[j][ks][qp], sc[j][hv]);
+    }
+    float sv[NQW][PE];
+#pragma unroll
+    for (int j = 0; j < NQW; ++j)
+#pragma unroll
+      for (int hv = 0; hv < NH; ++hv)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[j][4 * hv + i] = sc[j][hv][i];
+    // ---- mask only tiles that reach the chunk rows or the split end (wave-uniform)
+    if (kt0 + KT > C || kt0 + KT > k_end) {
+#pragma unroll
+      for (int j = 0; j < NQW; ++j)
+#pragma unroll
+        for (int e = 0; e < PE; ++e) {
+          const int sl = kt0 + PE * lg + e;
+          bool vis = sl < k_end;
+          if (vis && sl >= C) {
+            const int jr = sl - C;
+            vis = (anc[j][jr >> 5] >> (jr & 31)) & 1u;
+          }
+          if (!vis) sv[j][e] = -INFINITY;
+        }
+    }
+    // ---- online softmax; rescale only when some row's maximum rises
+    float mnew[NQW];
+    bool rise = false;
 #pragma unroll
     for (int j = 0; j < NQW; ++j) {
-      const int qt = q_base + w + j * NW;
-      if (qt >= NQT) continue;
-      // ---- scores S^T for this tile: sv[e] belongs to key kt0 + PE*lg + e
-      float sv[PE];
-      if constexpr (BF) {
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-        const int row0 = 8 * (r >> 2) + (r & 3);
+      float mx = sv[j][0];
 #pragma unroll
-        for (int ks = 0; ks < DH / KS; ++ks) {
-          const u32x4 k0 = ld16(&ldsK[row0 * KROW + ks * KS + lg * VE]);
-          const u32x4 k1 = ld16(&ldsK[(row0 + 4) * KROW + ks * KS + lg * VE]);
-#pragma unroll
-          for (int qp = 0; qp < QP; ++qp) {
-            s0 = mma16<T>(k0, qreg[j][ks][qp], s0);
-            s1 = mma16<T>(k1, qreg[j][ks][qp], s1);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { sv[i] = s0[i]; sv[4 + i] = s1[i]; }
-      } else {
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < DH / KS; ++ks)
-          s0 = mma16<T>(ld16(&ldsK[r * KROW + ks * KS + lg * VE]), qreg[j][ks][0], s0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sv[i] = s0[i];
-      }
-      // ---- mask: all cached slots; chunk slots only when an ancestor-or-self row
-      float mx = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < PE; ++e) {
-        const int s = kt0 + PE * lg + e;
-        bool vis = s < nkeys;
-        if (vis && s >= C) {
-          const int jr = s - C;
-          vis = (anc[j][jr >> 5] >> (jr & 31)) & 1u;
-        }
-        sv[e] = vis ? sv[e] : -INFINITY;
-        mx = fmaxf(mx, sv[e]);
-      }
+      for (int e = 1; e < PE; ++e) mx = fmaxf(mx, sv[j][e]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun[j], mx);
-      const float alpha = exp2f(mrun[j] - mnew);
-      mrun[j] = mnew;
-      float ps = 0.f, p[PE];
+      mnew[j] = fmaxf(mrun[j], mx);
+      rise |= mnew[j] > mrun[j];
+    }
+    if (__any(rise)) {
 #pragma unroll
-      for (int e = 0; e < PE; ++e) { p[e] = exp2f(sv[e] - mnew); ps += p[e]; }
-      lrun[j] = lrun[j] * alpha + ps;
+      for (int j = 0; j < NQW; ++j) {
+        const float alpha = __builtin_amdgcn_exp2f(mrun[j] - mnew[j]);
+        mrun[j] = mnew[j];
+        lrun[j] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < DH / 16; ++dt) acc[j][dt] *= alpha;
-      // ---- O^T += V^T P^T (bf16: P as a hi + lo pair, see split_probs)
-      if constexpr (BF) {
-        u32x4 phi, plo;
-        split_probs(p, phi, plo);
-#pragma unroll
-        for (int dt = 0; dt < DH / 16; ++dt) {
-          const u32x4 va = ld16(&ldsV[((lg >> 1) * DH + dt * 16 + r) * VROW + (lg & 1) * 8]);
-          acc[j][dt] = mma16<T>(va, phi, acc[j][dt]);
-          acc[j][dt] = mma16<T>(va, plo, acc[j][dt]);
-        }
-      } else {
-        u32x4 pb;
-        pb.x = __float_as_uint(p[0]); pb.y = __float_as_uint(p[1]);
-        pb.z = __float_as_uint(p[2]); pb.w = __float_as_uint(p[3]);
-#pragma unroll
-        for (int dt = 0; dt < DH / 16; ++dt) {
-          const u32x4 va = ld16(&ldsV[(dt * 16 + r) * VROW + lg * 4]);
-          acc[j][dt] = mma16<T>(va, pb, acc[j][dt]);
-        }
+        for (int dt = 0; dt < DH / 16; ++dt) acc[j][dt] *= alpha;
       }
+    }
+    u32x4 pop[NQW][QP];   // P operand(s) of each query tile
+#pragma unroll
+    for (int j = 0; j < NQW; ++j) {
+      float pj[PE], ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < PE; ++e) {
+        pj[e] = __builtin_amdgcn_exp2f(sv[j][e] - mrun[j]);
+        ps += pj[e];
+      }
+      lrun[j] += ps;
+      if constexpr (BF) {
+        split_probs_fast(pj, pop[j][0], pop[j][QP - 1]);
+      } else {
+        pop[j][0].x = __float_as_uint(pj[0]); pop[j][0].y = __float_as_uint(pj[1]);
+        pop[j][0].z = __float_as_uint(pj[2]); pop[j][0].w = __float_as_uint(pj[3]);
+      }
+    }
+    // ---- O^T += V^T P^T; each V operand is read from LDS once
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt) {
+      const u32x4 va = BF ? ld16(&ldsV[((lg >> 1) * DH + dt * 16 + r) * VROW + (lg & 1) * 8])
+                          : ld16(&ldsV[(dt * 16 + r) * VROW + lg * 4]);
+#pragma unroll
+      for (int j = 0; j < NQW; ++j)
+        if (j < nj)
+#pragma unroll
+          for (int qp = 0; qp < QP; ++qp) acc[j][dt] = mma16<T>(va, pop[j][qp], acc[j][dt]);
     }
   }
 
@@ -598,7 +604,7 @@ bool attn_uses_reg_path(bool bf, int dh, int NQT) {
 
 // query tiles per wave that fit without register spills
 template <typename T, int DH> constexpr int attn_cap() {
-  return sizeof(T) == 2 ? (DH == 128 ? 4 : 6) : (DH == 128 ? 3 : 4);
+  return DH == 128 ? 2 : 3;
 }
 
 template <typename T, int DH>
@@ -606,12 +612,13 @@ int attn_shape(int NQT, int* nqw_out, int* nw_out) {
   constexpr int CAP = attn_cap<T, DH>();
   int nqw = 1;
   while ((NQT + nqw - 1) / nqw > 8 && nqw < CAP) ++nqw;
-  if (nqw == 5) nqw = 6;
-  // at least 4 waves: waves without query tiles still help staging K/V
-  const int nw = std::max(4, std::min(8, (NQT + nqw - 1) / nqw));
+  // query groups of at most 8 waves each, balanced; at least 4 waves per workgroup
+  // (waves without query tiles still help staging K/V)
+  const int n_qg = (NQT + 8 * nqw - 1) / (8 * nqw);
+  const int nw = std::max(4, (NQT + n_qg * nqw - 1) / (n_qg * nqw));
   *nqw_out = nqw;
   *nw_out = nw;
-  return (NQT + nw * nqw - 1) / (nw * nqw);
+  return n_qg;
 }
 
 template <typename T, int DH>
@@ -635,12 +642,11 @@ static hipError_t launch_attn_t(AttnArgs a, hipStream_t s) {
   switch (nqw) {
     case 1: attn_chunk<T, DH, 1><<<grid, block, 0, s>>>(a); break;
     case 2: attn_chunk<T, DH, 2><<<grid, block, 0, s>>>(a); break;
-    case 3: attn_chunk<T, DH, 3><<<grid, block, 0, s>>>(a); break;
+    case 3:
+      if constexpr (attn_cap<T, DH>() >= 3) { attn_chunk<T, DH, 3><<<grid, block, 0, s>>>(a); break; }
+      return hipErrorInvalidValue;
     case 4:
       if constexpr (attn_cap<T, DH>() >= 4) { attn_chunk<T, DH, 4><<<grid, block, 0, s>>>(a); break; }
-      return hipErrorInvalidValue;
-    case 6:
-      if constexpr (attn_cap<T, DH>() >= 6) { attn_chunk<T, DH, 6><<<grid, block, 0, s>>>(a); break; }
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }

@@ -36,7 +36,8 @@ int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 // target workgroups per launch (256 compute units)
 constexpr int TARGET_WG_GEMM = 256;
-constexpr int TARGET_WG_ATTN = 512;
+constexpr int TARGET_WG_ATTN = 256;  // measured: one workgroup per CU beats two rounds
+constexpr long long ATTN_MERGE_MAX_READ = 32768;  // floats of partial output one merging workgroup reads
 
 struct GemmPlan {
   GemmCfg cfg;
@@ -83,9 +84,12 @@ struct Plan {
   GemmPlan qkv, o, gu, dn, lm, cb;
   int S;  // codebook streams (0: the model has no codebook heads)
   int split_keys, n_splits;
+  int n_qg;         // attention query groups per (sequence, kv head)
+  bool attn_fused;  // split partials merged inside the attention kernel
   size_t part_floats;
   size_t off_x, off_a, off_q, off_o, off_h, off_part, off_po, off_pml, off_stats, off_depth, off_anc,
-      off_lmrows, off_rope, off_cb, total;
+      off_lmrows, off_rope, off_cb, off_sem, total;
+  size_t n_sem;     // attention arrival counters: [layer][B][Hkv][n_qg]
 };
 
 sdv_status check_model(const sdv_model* m) {
@@ -134,13 +138,20 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
   const int KT = p.bf ? 32 : 16;
   const int nkeys = max_ctx + T;
   const int NQT = cdiv(T * p.G, 16);
-  const int target = TARGET_WG_ATTN;
-  int ns = cdiv(target, (long long)B * Hkv);
-  ns = std::max(1, std::min({ns, 32, cdiv(nkeys, KT)}));
+  int rows_per_group = 0;
+  p.n_qg = attn_query_groups(p.bf, dh, T, p.G, &rows_per_group);
+  int ns = cdiv(TARGET_WG_ATTN, (long long)B * Hkv * p.n_qg);
+  ns = std::max(1, std::min({ns, ATTN_MAX_SPLITS, cdiv(nkeys, KT)}));
   ns = std::max(ns, cdiv(nkeys, 255 * KT));  // a split spans at most 511 pages (staged in LDS)
   p.split_keys = cdiv(cdiv(nkeys, ns), KT) * KT;
   p.n_splits = cdiv(nkeys, p.split_keys);
   p.nq_pad = NQT * 16;
+  // the last workgroup of a group merges in-kernel while the partials it reads stay
+  // small; larger merges go to the combine kernel, which spreads them over the GPU
+  const long long merge_floats = (long long)p.n_splits * rows_per_group;
+  p.attn_fused = p.n_splits <= ATTN_MAX_SPLITS && merge_floats <= ATTN_MERGE_FLOATS &&
+                 merge_floats * dh <= ATTN_MERGE_MAX_READ;
+  p.n_sem = p.attn_fused ? (size_t)m->n_layers * B * Hkv * p.n_qg : 0;
 
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
@@ -161,6 +172,7 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
   p.off_lmrows = take((size_t)(p.Mr + p.S) * 4);
   p.off_rope = take((size_t)p.M * (dh / 2) * 8);
   p.off_cb = p.S ? take((size_t)p.cb.S * (p.Mr + p.S) * m->codebook_size * 4) : o;
+  p.off_sem = take(p.n_sem * 4);
   p.total = o;
   return p;
 }
@@ -255,6 +267,7 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
   int32_t* depth = (int32_t*)(w + P.off_depth);
   uint32_t* anc = (uint32_t*)(w + P.off_anc);
   int32_t* lm_rows = (int32_t*)(w + P.off_lmrows);
+  uint32_t* sem = (uint32_t*)(w + P.off_sem);
 
   const int d = m->d, H = m->n_heads, Hkv = m->n_kv_heads, dh = m->head_dim, F = m->ffn, V = m->vocab;
   const int qd = H * dh, kd = Hkv * dh, M = P.M;
@@ -269,7 +282,7 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
   {
     const bool cbh = in->head == SDV_HEAD_CODEBOOK;
     PrologueArgs a{in->parent, in->logit_rows, kv->seq_len, B, T, R, depth, anc, lm_rows, rope, dh,
-                   m->rope_theta, out->err, cbh ? P.S : 0, M};
+                   m->rope_theta, out->err, cbh ? P.S : 0, M, sem, (int)P.n_sem};
     SDV_LAUNCH(launch_prologue(a, s));
   }
   {
@@ -296,10 +309,13 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
     }
     {
       AttnArgs a{q, kp, vp, kv->block_table, kv->max_blocks, kv->n_blocks, kv->seq_len, anc, B, T, H, Hkv,
-                 P.split_keys, P.n_splits, po, pml, P.nq_pad, 1, in->max_ctx};
+                 P.split_keys, P.n_splits, po, pml, P.nq_pad, P.n_qg, in->max_ctx,
+                 P.attn_fused ? sem + (size_t)l * B * Hkv * P.n_qg : nullptr, o};
       SDV_LAUNCH(launch_attention(P.bf, dh, a, s));
-      CombineArgs c{po, pml, o, B, T, H, Hkv, dh, P.n_splits, P.nq_pad};
-      SDV_LAUNCH(launch_combine(P.bf, c, s));
+      if (!P.attn_fused) {
+        CombineArgs c{po, pml, o, B, T, H, Hkv, dh, P.n_splits, P.nq_pad};
+        SDV_LAUNCH(launch_combine(P.bf, c, s));
+      }
     }
     {
       GemmArgs a = gemm_args(o, qd, nullptr, M, L.wo, d, qd);

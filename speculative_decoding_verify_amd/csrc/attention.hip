@@ -19,8 +19,10 @@
 //                    for bf16, the 32 keys of a tile are assigned to MFMA rows so
 //                    that lane group g holds keys 8g..8g+7 (rows 4g..4g+3 of the two
 //                    S^T tiles map to keys 8g..8g+3 and 8g+4..8g+7).
-// Partials (unnormalised O, running max, running sum) are merged per query row by
-// the combine kernel with log-sum-exp weights.
+// Partials (unnormalised O, running max, running sum) of the key splits are merged
+// per query row with log-sum-exp weights by the workgroup that finishes last (the
+// hand-off of common.h), or, where a group's merge would not fit its LDS scratch, by
+// the separate combine kernel.
 #include "common.h"
 #include "kernels.h"
 
@@ -83,6 +85,63 @@ SDV_DEV void split_probs_fast(const float (&p)[8], u32x4& hi, u32x4& lo) {
   lo.z = __builtin_amdgcn_perm(l[5], l[4], 0x07060302u); lo.w = __builtin_amdgcn_perm(l[7], l[6], 0x07060302u);
 }
 
+// Merge of the split partial states of query rows [qi0, qi1) of (sequence b, kv head
+// g), run by the last workgroup of the group to finish; splits are taken in order:
+//   M = max_s m_s,  w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s',  o = sum_s w_s o_s.
+// wgt is LDS scratch of n_splits * (qi1 - qi0) floats.
+template <typename T, int DH>
+SDV_DEV void attn_merge(const AttnArgs& a, int b, int g, int qi0, int qi1, float* wgt) {
+  const int nr = qi1 - qi0, ns = a.n_splits, G = a.H / a.Hkv;
+  const size_t grp = ((size_t)b * a.Hkv + g) * ns * a.nq_pad;   // (split 0, row 0) of the group
+  const rsrc_t rml = dev_rsrc(a.pml + grp * 2, (uint32_t)ns * a.nq_pad * 8);
+  const rsrc_t rpo = dev_rsrc(a.po + grp * DH, (uint32_t)ns * a.nq_pad * DH * 4);
+  for (int i = threadIdx.x; i < nr; i += blockDim.x) {
+    float m[ATTN_MAX_SPLITS], l[ATTN_MAX_SPLITS];
+#pragma unroll
+    for (int s = 0; s < ATTN_MAX_SPLITS; ++s) {
+      const u32x2 v = ld_dev8(rml, (uint32_t)((min(s, ns - 1) * a.nq_pad + qi0 + i) * 8));
+      m[s] = __uint_as_float(v.x);
+      l[s] = __uint_as_float(v.y);
+    }
+    float M = m[0];
+#pragma unroll
+    for (int s = 1; s < ATTN_MAX_SPLITS; ++s) M = fmaxf(M, m[s]);
+    float L = 0.f;
+#pragma unroll
+    for (int s = 0; s < ATTN_MAX_SPLITS; ++s) {
+      m[s] = s < ns ? __builtin_amdgcn_exp2f(m[s] - M) : 0.f;
+      L += m[s] * l[s];
+    }
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int s = 0; s < ATTN_MAX_SPLITS; ++s)
+      if (s < ns) wgt[s * nr + i] = m[s] * inv;
+  }
+  __syncthreads();
+  constexpr int NC = DH / 4;   // 16-byte chunks of an output row
+  constexpr int SU = 16;       // splits loaded per round
+  for (int it = threadIdx.x; it < nr * NC; it += blockDim.x) {
+    const int i = it / NC, c = it % NC;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < ns; s0 += SU) {
+      u32x4 v[SU];
+#pragma unroll
+      for (int u = 0; u < SU; ++u)
+        v[u] = ld_dev16(rpo, (uint32_t)(((min(s0 + u, ns - 1) * a.nq_pad + qi0 + i) * DH + 4 * c) * 4));
+#pragma unroll
+      for (int u = 0; u < SU; ++u) {
+        const float wv = s0 + u < ns ? wgt[(s0 + u) * nr + i] : 0.f;
+        acc[0] += wv * __uint_as_float(v[u].x);
+        acc[1] += wv * __uint_as_float(v[u].y);
+        acc[2] += wv * __uint_as_float(v[u].z);
+        acc[3] += wv * __uint_as_float(v[u].w);
+      }
+    }
+    const int qi = qi0 + i, t = qi / G, h = g * G + qi % G;
+    act_store4<T>((char*)a.o + (size_t)(b * a.T + t) * a.H * DH * 4, h * DH + 4 * c, acc);
+  }
+}
+
 template <typename T, int DH, int NQW>
 __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
   constexpr bool BF = sizeof(T) == 2;
@@ -94,8 +153,11 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
   constexpr int NPG = KT / 16;             // pages per tile
   constexpr int PE = BF ? 8 : 4;           // scores per lane per tile
 
-  __shared__ __attribute__((aligned(16))) T ldsK[KT * KROW];
-  __shared__ __attribute__((aligned(16))) T ldsV[NPG * DH * VROW];
+  // K and V^T tiles; after the key loop the same LDS is the merge scratch
+  constexpr int KBYTES = KT * KROW * (int)sizeof(T), VBYTES = NPG * DH * VROW * (int)sizeof(T);
+  __shared__ __attribute__((aligned(16))) char lds_raw[std::max(KBYTES + VBYTES, ATTN_MERGE_FLOATS * 4)];
+  T* const ldsK = (T*)lds_raw;
+  T* const ldsV = (T*)(lds_raw + KBYTES);
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z / a.n_qg;
   const int lane = threadIdx.x & 63, NW = blockDim.x >> 6;
@@ -300,7 +362,12 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
     }
   }
 
-  // ---- write the split's partial state
+  // ---- the split's partial state (or, with a single split, the output rows)
+  const bool fused = a.sem != nullptr;
+  const bool direct = fused && a.n_splits == 1;
+  const size_t grp = ((size_t)b * a.Hkv + g) * a.n_splits * a.nq_pad;
+  const rsrc_t rpo = dev_rsrc(a.po + grp * DH, (uint32_t)a.n_splits * a.nq_pad * DH * 4);
+  const rsrc_t rml = dev_rsrc(a.pml + grp * 2, (uint32_t)a.n_splits * a.nq_pad * 8);
 #pragma unroll
   for (int j = 0; j < NQW; ++j) {
     const int qt = q_base + w + j * NW;
@@ -309,16 +376,30 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     const int qi = qt * 16 + r;
-    const size_t base = (((size_t)b * a.Hkv + g) * a.n_splits + split) * a.nq_pad + qi;
+    const uint32_t pr = (uint32_t)(split * a.nq_pad + qi);
+    if (direct) {
+      if (qi < nq) {
+        const float inv = 1.f / l;
+        char* orow = (char*)a.o + (size_t)(b * a.T + qi / G) * a.H * DH * 4;
+        const int h = g * G + qi % G;
 #pragma unroll
-    for (int dt = 0; dt < DH / 16; ++dt)
+        for (int dt = 0; dt < DH / 16; ++dt) {
+          const float v[4] = {acc[j][dt][0] * inv, acc[j][dt][1] * inv, acc[j][dt][2] * inv, acc[j][dt][3] * inv};
+          act_store4<T>(orow, h * DH + dt * 16 + 4 * lg, v);
+        }
+      }
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a.po[base * DH + dt * 16 + 4 * lg + i] = acc[j][dt][i];
-    if (lg == 0) {
-      a.pml[base * 2] = mrun[j];
-      a.pml[base * 2 + 1] = l;
+      for (int dt = 0; dt < DH / 16; ++dt)
+        st_dev16(rpo, (pr * DH + dt * 16 + 4 * lg) * 4, __builtin_bit_cast(u32x4, acc[j][dt]));
+      if (lg == 0) st_dev8(rml, pr * 8, u32x2{__float_as_uint(mrun[j]), __float_as_uint(l)});
     }
   }
+  if (!fused || direct) return;
+  __shared__ int is_last;
+  const int qg = blockIdx.z % a.n_qg;
+  if (!arrive_last(a.sem + ((size_t)b * a.Hkv + g) * a.n_qg + qg, a.n_splits, &is_last)) return;
+  attn_merge<T, DH>(a, b, g, q_base * 16, min(nq, (q_base + NW * NQW) * 16), (float*)lds_raw);
 }
 
 // Register path for few query tiles per kv head (at most 3): every wave holds all
@@ -535,31 +616,51 @@ __global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
       for (int i = 0; i < 4; ++i) so[w][j][dt][i][lane] = acc[j][dt][i];
   }
   __syncthreads();
+  // the split's partial state (or, with a single split, the output rows)
+  const bool fused = a.sem != nullptr;
+  const bool direct = fused && a.n_splits == 1;
+  const size_t grp = ((size_t)b * a.Hkv + g) * a.n_splits * a.nq_pad;
+  const rsrc_t rpo = dev_rsrc(a.po + grp * DH, (uint32_t)a.n_splits * a.nq_pad * DH * 4);
+  const rsrc_t rml = dev_rsrc(a.pml + grp * 2, (uint32_t)a.n_splits * a.nq_pad * 8);
   for (int idx = threadIdx.x; idx < NQT * 64; idx += 256) {
     const int j = idx / 64, ln = idx % 64;
     const int qi = j * 16 + (ln & 15);
-    if (qi >= a.nq_pad) continue;
     float M = sm[0][j][ln];
 #pragma unroll
     for (int k = 1; k < 4; ++k) M = fmaxf(M, sm[k][j][ln]);
     float wk[4], L = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) { wk[k] = exp2f(sm[k][j][ln] - M); L += wk[k] * sl[k][j][ln]; }
-    const size_t base = (((size_t)b * a.Hkv + g) * a.n_splits + split) * a.nq_pad + qi;
+    const uint32_t pr = (uint32_t)(split * a.nq_pad + qi);
+    const float inv = 1.f / L;
+    char* orow = (char*)a.o + (size_t)(b * a.T + min(qi, nq - 1) / G) * a.H * DH * 4;
+    const int h = g * G + qi % G;
 #pragma unroll
-    for (int dt = 0; dt < DH / 16; ++dt)
+    for (int dt = 0; dt < DH / 16; ++dt) {
+      float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float v = 0.f;
+        v[i] = 0.f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v += wk[k] * so[k][j][dt][i][ln];
-        a.po[base * DH + dt * 16 + 4 * (ln >> 4) + i] = v;
+        for (int k = 0; k < 4; ++k) v[i] += wk[k] * so[k][j][dt][i][ln];
       }
-    if ((ln >> 4) == 0) {
-      a.pml[base * 2] = M;
-      a.pml[base * 2 + 1] = L;
+      const int d0 = dt * 16 + 4 * (ln >> 4);
+      if (direct) {
+        if (qi < nq) {
+          const float vo[4] = {v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv};
+          act_store4<T>(orow, h * DH + d0, vo);
+        }
+      } else {
+        st_dev16(rpo, (pr * DH + d0) * 4,
+                 u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
+      }
     }
+    if (!direct && (ln >> 4) == 0) st_dev8(rml, pr * 8, u32x2{__float_as_uint(M), __float_as_uint(L)});
   }
+  if (!fused || direct) return;
+  __shared__ int is_last;
+  if (!arrive_last(a.sem + (size_t)b * a.Hkv + g, a.n_splits, &is_last)) return;
+  attn_merge<T, DH>(a, b, g, 0, nq, &so[0][0][0][0][0]);
 }
 
 template <typename T, int DH>
@@ -618,6 +719,19 @@ int attn_shape(int NQT, int* nqw_out, int* nw_out) {
   const int nw = std::max(4, (NQT + n_qg * nqw - 1) / (n_qg * nqw));
   *nqw_out = nqw;
   *nw_out = nw;
+  return n_qg;
+}
+
+int attn_query_groups(bool is_bf16, int dh, int T, int G, int* rows_per_group) {
+  const int NQT = (T * G + 15) / 16;
+  if (attn_uses_reg_path(is_bf16, dh, NQT)) {
+    *rows_per_group = T * G;
+    return 1;
+  }
+  int nqw, nw, n_qg;
+  if (is_bf16) n_qg = dh == 64 ? attn_shape<bf16, 64>(NQT, &nqw, &nw) : attn_shape<bf16, 128>(NQT, &nqw, &nw);
+  else n_qg = dh == 64 ? attn_shape<float, 64>(NQT, &nqw, &nw) : attn_shape<float, 128>(NQT, &nqw, &nw);
+  *rows_per_group = std::min(T * G, nw * nqw * 16);
   return n_qg;
 }
 

@@ -7,6 +7,7 @@ typedef uint16_t bf16;  // raw bf16 bit pattern
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 
 #define SDV_DEV __device__ __forceinline__
 
@@ -106,6 +107,57 @@ template <> SDV_DEV void act_store8<bf16>(void* row, int k0, const float (&x)[8]
   char* g = (char*)row + (k0 >> 3) * 32;
   st16(g, hi);
   st16(g + 16, lo);
+}
+
+// act_store4: values k0..k0+3 of a row (k0 % 4 == 0)
+template <typename T> SDV_DEV void act_store4(void* row, int k0, const float (&x)[4]);
+template <> SDV_DEV void act_store4<float>(void* row, int k0, const float (&x)[4]) {
+  *(float4*)((float*)row + k0) = make_float4(x[0], x[1], x[2], x[3]);
+}
+template <> SDV_DEV void act_store4<bf16>(void* row, int k0, const float (&x)[4]) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    bf16 hb, lb;
+    split1(x[e], hb, lb);
+    h[e] = hb;
+    l[e] = lb;
+  }
+  bf16* g = (bf16*)row + (k0 >> 3) * 16 + (k0 & 7);
+  *(uint2*)g = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  *(uint2*)(g + 8) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+}
+
+// ---------------------------------------------------------------------------
+// Hand-off between the workgroups of one kernel (split reductions finished by the
+// workgroup that arrives last).  The producers' parts go through device-scope buffer
+// stores (cache policy sc1: written through the compute unit's and the XCD's caches),
+// and the last workgroup reads them with device-scope loads (sc1: not served from a
+// possibly stale cache of another XCD).  Each producer waits until its stores have
+// completed before it counts itself in, so a workgroup that sees the count complete
+// finds every part in place.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int CPOL_DEVICE = 16;   // sc1
+SDV_DEV rsrc_t dev_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+SDV_DEV void st_dev16(rsrc_t r, uint32_t off, u32x4 v) { __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, CPOL_DEVICE); }
+SDV_DEV void st_dev8(rsrc_t r, uint32_t off, u32x2 v) { __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, CPOL_DEVICE); }
+SDV_DEV u32x4 ld_dev16(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL_DEVICE); }
+SDV_DEV u32x2 ld_dev8(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, CPOL_DEVICE); }
+
+// Every thread's stores are complete, then thread 0 counts the workgroup in on
+// `counter` (zero before the launch).  True in all threads of the workgroup that
+// arrives n-th (last).  `flag` is an int in LDS.
+SDV_DEV bool arrive_last(uint32_t* counter, uint32_t n, int* flag) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *flag = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1;
+  __syncthreads();
+  return *flag != 0;
 }
 
 // elements of T held in 16 bytes

@@ -67,6 +67,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
     sincos(ang, &sn, &cs);
     a.rope[idx] = make_float2((float)cs, (float)sn);
   }
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.n_zero; i += gridDim.x * blockDim.x) a.zero[i] = 0u;
 }
 
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {

@@ -89,7 +89,19 @@ struct AttnArgs {
   int nq_pad;
   int n_qg;                 // query-tile groups per (sequence, kv head); grid.z = B * n_qg
   int max_ctx;              // cached lengths are clamped to [0, max_ctx] (max_ctx + T fits the table)
+  // In-kernel merge: when sem is set, the last workgroup of each (sequence, kv head,
+  // query group) to finish merges the split partials and writes o; sem holds one
+  // arrival counter per (sequence, kv head, query group), zero before the launch.
+  // With sem NULL the partials are left for launch_combine.
+  uint32_t* sem;
+  void* o;                  // [B*T, H*dh] output rows in the activation format
 };
+
+// Query groups per (sequence, kv head) of the attention launch and the query rows a
+// group spans (the merge of one group needs n_splits * rows floats of LDS scratch).
+int attn_query_groups(bool is_bf16, int dh, int T, int G, int* rows_per_group);
+constexpr int ATTN_MERGE_FLOATS = 4096;
+constexpr int ATTN_MAX_SPLITS = 32;
 
 hipError_t launch_attention(bool is_bf16, int dh, const AttnArgs& a, hipStream_t s);
 bool attn_uses_reg_path(bool bf, int dh, int NQT);  // keys per tile: 32 bf16 / 16 fp32 either way
@@ -115,6 +127,8 @@ struct PrologueArgs {
   float rope_theta;
   int32_t* err;             // [B]
   int n_extra, extra_base;  // lm_rows[B*R + i] = extra_base + i for i < n_extra
+  uint32_t* zero;           // n_zero words cleared (the attention arrival counters)
+  int n_zero;
 };
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
 

@@ -39,11 +39,37 @@ def pass_bytes(sh, T, R, C, n_branch_rows=0):
     return w + C * kv_row + T * kv_row + R * sh.vocab * 4
 
 
-def decoder_gemm_bytes(sh):
-    """Weight bytes streamed by the decoder projection GEMMs (q/k/v, o, gate/up, down) of one pass."""
-    d, F = sh.d, sh.ffn
-    per_layer = (sh.q_dim * d + 2 * sh.kv_dim * d + d * sh.q_dim + 3 * d * F) * sh.elem_bytes
-    return sh.n_layers * per_layer
+def gate_up_launch_bytes(sh, M):
+    """Algorithmic HBM bytes of one gate/up projection launch (the pass's dominant
+    kernel): the gate and up weights read once, the M normed rows read (4 bytes per
+    value) and the M SwiGLU rows written (4 bytes per value)."""
+    return 2 * sh.ffn * sh.d * sh.elem_bytes + M * sh.d * 4 + M * sh.ffn * 4
+
+
+# HBM traffic of the gate/up kernel from rocprofv3 counters (FETCH_SIZE, then WRITE_SIZE
+# in separate runs of `bench.py --steps 5 --warmup 2 --no-cpu-baseline`), per dispatch,
+# each scaled by what the same counter reads for a plain 256 MiB device copy
+# (`bench.py --copy-calibration`).  Valid only for the kernel sources they were taken
+# on: the sha256 of the GEMM sources is checked at run time, else traffic is null.
+GATE_UP_TRAFFIC = None
+GEMM_SOURCES = ("speculative_decoding_verify_amd/csrc/gemm.hip", "speculative_decoding_verify_amd/csrc/common.h",
+                "speculative_decoding_verify_amd/csrc/kernels.h")
+
+
+def gemm_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def gate_up_traffic():
+    t = GATE_UP_TRAFFIC
+    if not t or t["sha256"] != gemm_source_sha():
+        return None
+    return (t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"]) * 1024.0
 
 
 def cpu_threads():
@@ -171,8 +197,9 @@ def bench_verify(args, wl):
     n_acc = int(acc_out["n"][0])
     assert int(acc_out["err"][0]) == 0 and int(ver.err[0]) == 0, "device error during bench"
 
-    # live per-kernel timing of the decoder GEMMs with HIP events recorded by the
-    # library on the launch stream, over K more steps of the same pass
+    # live per-launch timing of the GEMMs with HIP events that the library records on
+    # the launch stream around each GEMM launch (per layer: q/k/v, o, gate/up, down;
+    # then the LM head), over K more steps of the same pass
     n_gemm = 4 * sh.n_layers + 1
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_gemm)]
     ver.set_profile_events(ev)
@@ -184,11 +211,13 @@ def bench_verify(args, wl):
         gemm_ms.append(per)
     ver.set_profile_events(None)
     gemm_ms = np.asarray(gemm_ms)                      # [steps, launches]
-    dec_ms = gemm_ms[:, :4 * sh.n_layers]              # decoder projections (one kernel symbol)
-    avg_launch_ms = float(dec_ms.mean())
-    dec_bytes = decoder_gemm_bytes(sh)
-    achieved = dec_bytes / (dec_ms.sum(axis=1).mean() * 1e-3) / 1e9
-    lm_ms = float(gemm_ms[:, -1].mean())
+    per_layer = gemm_ms[:, :4 * sh.n_layers].reshape(args.steps, sh.n_layers, 4)
+    launch_us = {name: float(per_layer[:, :, i].mean()) * 1e3 for i, name in enumerate(("qkv", "o", "gate_up", "down"))}
+    launch_us["lm_head"] = float(gemm_ms[:, -1].mean()) * 1e3
+    gu_us = launch_us["gate_up"]
+    gu_bytes = gate_up_launch_bytes(sh, T)
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    traffic = gate_up_traffic()
     lm_bytes = sh.vocab * sh.d * sh.elem_bytes
 
     nbytes = pass_bytes(sh, T, R, C)
@@ -217,11 +246,12 @@ def bench_verify(args, wl):
         "committed_tokens_per_s": (n_acc + 1) * passes_s,
         "pass_roofline": {"bound": "hbm", "bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
                           "peak_GBs": HBM_PEAK_GBS, "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "roofline": {"bound": "hbm", "kernel": "gemm_rows (decoder q/k/v, o, gate/up, down projections)",
+        "roofline": {"bound": "hbm", "kernel": "gemm_stream, SwiGLU epilogue (gate/up projection)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "launches_per_pass": 4 * sh.n_layers, "avg_launch_us": avg_launch_ms * 1e3,
-                     "bytes_per_pass": dec_bytes},
-        "lm_head": {"avg_launch_us": lm_ms * 1e3, "GBs": lm_bytes / (lm_ms * 1e-3) / 1e9},
+                     "traffic": traffic, "bytes_per_launch": gu_bytes, "avg_launch_us": gu_us,
+                     "launches_per_pass": sh.n_layers},
+        "gemm_launch_us": launch_us,
+        "lm_head": {"avg_launch_us": launch_us["lm_head"], "GBs": lm_bytes / (launch_us["lm_head"] * 1e-6) / 1e9},
         "setup_s": setup_s,
     }
     if not args.no_cpu_baseline:
@@ -309,6 +339,21 @@ def bench_sample(args):
     return out
 
 
+def copy_calibration(nbytes=256 << 20, reps=10):
+    """A plain device-to-device copy of known size: the reference for scaling the
+    FETCH_SIZE / WRITE_SIZE counters of the kernels to bytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    return {"copy_bytes": nbytes, "reps": reps, "us_per_copy": dt * 1e6, "GBs": 2 * nbytes / dt / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -318,6 +363,8 @@ def main():
     ap.add_argument("--scenario", default="silence", choices=["silence", "random"])
     ap.add_argument("--graph", action="store_true", help="replay the step from a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain 256 MiB device-to-device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -326,6 +373,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU"}))
         sys.exit(1)
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration()), flush=True)
+        return
     import speculative_decoding_verify_amd as sdv
     sdv.lib()  # fail loudly if the HIP library is not built
     from synth.configs import WORKLOADS

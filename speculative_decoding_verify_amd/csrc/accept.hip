@@ -13,19 +13,31 @@ namespace sdv {
 
 // ---------------------------------------------------------------------------
 // Greedy tree walk: one block per sequence stages its tokens, the tree and the
-// argmax of every logit row in LDS; one thread walks.
+// argmax of every logit row in LDS; every row checks in parallel whether it is the
+// accepted child of its parent (its token equals the parent's argmax), then one
+// thread walks from the last audio row along the accepted children.
 __global__ __launch_bounds__(128) void accept_greedy_kernel(GreedyArgs a) {
-  __shared__ int32_t tok[128], par[128], am_of_row[128], path[128];
+  __shared__ int32_t tok[128], par[128], am_of_row[128], path[128], child_of[128], n_match[128];
   const int b = blockIdx.x;
   for (int j = threadIdx.x; j < a.T; j += blockDim.x) {
     tok[j] = a.tokens[(size_t)b * a.T + j];
     par[j] = a.parent ? a.parent[j] : j - 1;
     am_of_row[j] = -1;
+    child_of[j] = 0x7fffffff;
+    n_match[j] = 0;
   }
   __syncthreads();
   for (int i = threadIdx.x; i < a.R; i += blockDim.x) {
     const int row = a.logit_rows[i];
     if (row >= 0 && row < a.T) am_of_row[row] = a.argmax[(size_t)b * a.R + i];
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < a.T; j += blockDim.x) {
+    const int p = par[j];
+    if (p >= 0 && p < j && am_of_row[p] >= 0 && tok[j] == am_of_row[p]) {
+      atomicMin(&child_of[p], j);   // siblings with equal tokens: the lowest row, reported below
+      atomicAdd(&n_match[p], 1);
+    }
   }
   __syncthreads();
   if (threadIdx.x != 0) return;
@@ -34,14 +46,9 @@ __global__ __launch_bounds__(128) void accept_greedy_kernel(GreedyArgs a) {
     const int am = am_of_row[node];
     next = am;
     if (am < 0) break;
-    int child = -1;
-    for (int j = node + 1; j < a.T; ++j) {
-      if (par[j] == node && tok[j] == am) {
-        if (child >= 0) { set_err(a.err, b, 0x10); break; }
-        child = j;
-      }
-    }
-    if (child < 0) break;
+    if (n_match[node] > 1) set_err(a.err, b, 0x10);
+    const int child = child_of[node];
+    if (child == 0x7fffffff) break;
     path[n++] = child;
     node = child;
   }
@@ -71,34 +78,48 @@ hipError_t launch_accept_greedy(const GreedyArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // KV commit: block (b, layer) validates the sequence's plan, performs its moves in
 // ascending order (each thread owns fixed element positions, so a slot written by
-// one move and read by a later one is handled in order) and sets seq_len.
+// one move and read by a later one is handled in order) and sets seq_len.  The move
+// lists are staged in LDS, 256 entries at a time, and validated in parallel.
 __global__ __launch_bounds__(256) void kv_rollback_kernel(RollbackArgs a) {
+  constexpr int CH = 256;
+  __shared__ int32_t msrc[CH], mdst[CH];
+  __shared__ int ok;
   const int b = blockIdx.x, l = blockIdx.y;
   const int cap = a.max_blocks * 16;
   const int32_t* bt = a.block_table + (size_t)b * a.max_blocks;
   const int keep = a.keep_len[b];
-  bool ok = keep >= 0 && keep <= cap;
-  if (a.move_src) {
-    for (int i = 0; i < a.max_move && ok; ++i) {
+  if (threadIdx.x == 0) ok = keep >= 0 && keep <= cap;
+  __syncthreads();
+  for (int c0 = 0; c0 < a.max_move; c0 += CH) {
+    const int i = c0 + threadIdx.x;
+    if (i < a.max_move) {
       const int s = a.move_src[(size_t)b * a.max_move + i];
-      if (s < 0) continue;
-      const int d = a.move_dst[(size_t)b * a.max_move + i];
-      ok = s < cap && d >= 0 && d < cap;
-      if (ok) {
-        const int ps = bt[s >> 4], pd = bt[d >> 4];
-        ok = ps >= 0 && ps < a.n_blocks && pd >= 0 && pd < a.n_blocks;
+      if (s >= 0) {
+        const int d = a.move_dst[(size_t)b * a.max_move + i];
+        bool good = s < cap && d >= 0 && d < cap;
+        if (good) {
+          const int ps = bt[s >> 4], pd = bt[d >> 4];
+          good = ps >= 0 && ps < a.n_blocks && pd >= 0 && pd < a.n_blocks;
+        }
+        if (!good) ok = 0;
       }
     }
   }
+  __syncthreads();
   if (!ok) {
     if (l == 0 && threadIdx.x == 0) set_err(a.err, b, 0x8);
     return;
   }
-  if (a.move_src) {
-    const int per = a.Hkv * a.dh;
-    for (int i = 0; i < a.max_move; ++i) {
-      const int s = a.move_src[(size_t)b * a.max_move + i];
-      const int d = a.move_dst[(size_t)b * a.max_move + i];
+  const int per = a.Hkv * a.dh;
+  for (int c0 = 0; c0 < a.max_move; c0 += CH) {
+    const int n = min(CH, a.max_move - c0);
+    if (threadIdx.x < n) {
+      msrc[threadIdx.x] = a.move_src[(size_t)b * a.max_move + c0 + threadIdx.x];
+      mdst[threadIdx.x] = a.move_dst[(size_t)b * a.max_move + c0 + threadIdx.x];
+    }
+    __syncthreads();
+    for (int i = 0; i < n; ++i) {
+      const int s = msrc[i], d = mdst[i];
       if (s < 0 || s == d) continue;
       const size_t ps = (size_t)l * a.n_blocks + bt[s >> 4], pd = (size_t)l * a.n_blocks + bt[d >> 4];
       const int os = s & 15, od = d & 15;
@@ -115,6 +136,7 @@ __global__ __launch_bounds__(256) void kv_rollback_kernel(RollbackArgs a) {
         }
       }
     }
+    __syncthreads();
   }
   if (l == 0 && threadIdx.x == 0) a.seq_len[b] = keep;
 }

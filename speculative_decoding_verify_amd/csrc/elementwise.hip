@@ -20,25 +20,30 @@ namespace sdv {
 // p = seq_len[b] + depth(t), entry i holds (cos, sin) of p * theta^(-2i/dh),
 // evaluated in fp64 and rounded to fp32.
 __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
-  __shared__ int32_t dep[128];
+  __shared__ int32_t par[128], dep[128];
   __shared__ uint32_t anc[128][4];
   __shared__ int bad;
-  if (threadIdx.x == 0) {
-    bad = 0;
-    for (int j = 0; j < a.T; ++j) {
-      int p = a.parent ? a.parent[j] : j - 1;
-      const bool ok = j == 0 ? p == -1 : (p >= 0 && p < j);
-      if (!ok) { bad = 1; p = j - 1; }
-      uint32_t m[4] = {0u, 0u, 0u, 0u};
-      if (p >= 0) {
-        for (int c = 0; c < 4; ++c) m[c] = anc[p][c];
-        dep[j] = dep[p] + 1;
-      } else {
-        dep[j] = 0;
-      }
-      m[j >> 5] |= 1u << (j & 31);
-      for (int c = 0; c < 4; ++c) anc[j][c] = m[c];
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  // parents (an invalid one is reported and replaced by the previous row)
+  for (int j = threadIdx.x; j < a.T; j += blockDim.x) {
+    int p = a.parent ? a.parent[j] : j - 1;
+    const bool ok = j == 0 ? p == -1 : (p >= 0 && p < j);
+    if (!ok) { bad = 1; p = j - 1; }
+    par[j] = p;
+  }
+  __syncthreads();
+  // every row walks up to the root (parents strictly decrease, so the walk ends)
+  for (int j = threadIdx.x; j < a.T; j += blockDim.x) {
+    uint32_t m[4] = {0u, 0u, 0u, 0u};
+    int d = -1;
+    for (int k = j; k >= 0; k = par[k]) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) m[c] |= (k >> 5) == c ? 1u << (k & 31) : 0u;
+      ++d;
     }
+    dep[j] = d;
+    for (int c = 0; c < 4; ++c) anc[j][c] = m[c];
   }
   __syncthreads();
   if (blockIdx.x == 0) {

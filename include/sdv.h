@@ -188,10 +188,11 @@ typedef struct {
  *   err     int32 [B]: device error bits (OR-ed in; the caller clears it)
  *   cb_argmax  see the field
  *   prof_events  nullable host array of n_prof_events caller-created hipEvent_t
- *           handles: when given, event 2i is recorded on the stream before and event
- *           2i+1 after the i-th weight-streaming GEMM launch of the pass (decoder
- *           projections in order q/k/v, o, gate/up, down per layer, then the LM
- *           head), for as many launches as there are event pairs. */
+ *           handles: when given, the i-th weight-streaming GEMM launch of the pass
+ *           (decoder projections in order q/k/v, o, gate/up, down per layer, then the
+ *           LM head) records event 2i when the kernel starts and event 2i+1 when it
+ *           ends (hipExtLaunchKernel), for as many launches as there are event pairs;
+ *           the interval is the kernel's execution time. */
 typedef struct {
   float* logits;
   int32_t* argmax;

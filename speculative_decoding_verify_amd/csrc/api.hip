@@ -198,9 +198,11 @@ sdv_status run_gemm(ProfEvents& pe, const Plan& P, const GemmPlan& g, GemmArgs a
   a.n_groups = g.ncg;
   dim3 grid(g.ncg, g.S, g.row_blocks);
   const bool prof = pe.ev && pe.next < pe.n_pairs;
-  if (prof) SDV_LAUNCH(hipEventRecord((hipEvent_t)pe.ev[2 * pe.next], s));
-  SDV_LAUNCH(launch_gemm(P.bf, g.cfg, g.MT, g.epi, grid, a, s));
-  if (prof) SDV_LAUNCH(hipEventRecord((hipEvent_t)pe.ev[2 * pe.next + 1], s));
+  if (prof)
+    SDV_LAUNCH(launch_gemm(P.bf, g.cfg, g.MT, g.epi, grid, a, s, (hipEvent_t)pe.ev[2 * pe.next],
+                           (hipEvent_t)pe.ev[2 * pe.next + 1]));
+  else
+    SDV_LAUNCH(launch_gemm(P.bf, g.cfg, g.MT, g.epi, grid, a, s));
   if (pe.ev) ++pe.next;
   return SDV_OK;
 }

@@ -69,6 +69,12 @@ SDV_DEV int stage_pages(const AttnArgs& a, const int32_t* bt, int k_begin, int k
   return pg0;
 }
 
+// Word w (0..3) of a row's ancestor mask held in registers, by selects (a per-lane
+// index into a register array would become a loop over the distinct indices).
+SDV_DEV uint32_t anc_word(const uint32_t (&m)[4], int w) {
+  return w == 0 ? m[0] : w == 1 ? m[1] : w == 2 ? m[2] : m[3];
+}
+
 // Probabilities as a bf16 hi/lo operand pair, cheaply: hi = p rounded half-up to 8
 // significant bits, lo = the exact remainder p - hi truncated to bf16, so
 // |p - hi - lo| < 2^-15 |p|.  v_perm gathers the upper halves of two words.
@@ -139,6 +145,65 @@ SDV_DEV void attn_merge(const AttnArgs& a, int b, int g, int qi0, int qi1, float
     }
     const int qi = qi0 + i, t = qi / G, h = g * G + qi % G;
     act_store4<T>((char*)a.o + (size_t)(b * a.T + t) * a.H * DH * 4, h * DH + 4 * c, acc);
+  }
+}
+
+// The same merge for at most 8 splits in one memory round trip per item: a thread's
+// item (row, 16-byte chunk) needs every split's (m, l) and output chunk, all loaded
+// at once, and the next item's loads are issued before the current one is finished.
+template <typename T, int DH>
+SDV_DEV void attn_merge8(const AttnArgs& a, int b, int g, int qi0, int qi1) {
+  constexpr int MS = 8, NC = DH / 4;
+  const int nr = qi1 - qi0, ns = a.n_splits, G = a.H / a.Hkv;
+  const int n_items = nr * NC;
+  const size_t grp = ((size_t)b * a.Hkv + g) * ns * a.nq_pad;
+  const rsrc_t rml = dev_rsrc(a.pml + grp * 2, (uint32_t)ns * a.nq_pad * 8);
+  const rsrc_t rpo = dev_rsrc(a.po + grp * DH, (uint32_t)ns * a.nq_pad * DH * 4);
+  struct Buf {
+    u32x2 ml[MS];
+    u32x4 po[MS];
+  };
+  auto load = [&](int it, Buf& bf) {
+    it = min(it, n_items - 1);
+    const int i = it / NC, c = it % NC;
+#pragma unroll
+    for (int s = 0; s < MS; ++s) {
+      const uint32_t row = (uint32_t)(min(s, ns - 1) * a.nq_pad + qi0 + i);
+      bf.ml[s] = ld_dev8(rml, row * 8);
+      bf.po[s] = ld_dev16(rpo, (row * DH + 4 * c) * 4);
+    }
+  };
+  auto finish = [&](int it, const Buf& bf) {
+    if (it >= n_items) return;
+    const int i = it / NC, c = it % NC;
+    float M = __uint_as_float(bf.ml[0].x);
+#pragma unroll
+    for (int s = 1; s < MS; ++s) M = fmaxf(M, __uint_as_float(bf.ml[s].x));
+    float L = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < MS; ++s) {
+      const float wv = s < ns ? __builtin_amdgcn_exp2f(__uint_as_float(bf.ml[s].x) - M) : 0.f;
+      L += wv * __uint_as_float(bf.ml[s].y);
+      acc[0] += wv * __uint_as_float(bf.po[s].x);
+      acc[1] += wv * __uint_as_float(bf.po[s].y);
+      acc[2] += wv * __uint_as_float(bf.po[s].z);
+      acc[3] += wv * __uint_as_float(bf.po[s].w);
+    }
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] *= inv;
+    const int qi = qi0 + i, t = qi / G, h = g * G + qi % G;
+    act_store4<T>((char*)a.o + (size_t)(b * a.T + t) * a.H * DH * 4, h * DH + 4 * c, acc);
+  };
+  Buf A, B;
+  const int step = blockDim.x;
+  int it = threadIdx.x;
+  load(it, A);
+  for (; it < n_items; it += 2 * step) {
+    load(it + step, B);
+    finish(it, A);
+    if (it + 2 * step < n_items) load(it + 2 * step, A);
+    finish(it + step, B);
   }
 }
 
@@ -297,17 +362,18 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
     // ---- mask only tiles that reach the chunk rows or the split end (wave-uniform)
     if (kt0 + KT > C || kt0 + KT > k_end) {
 #pragma unroll
-      for (int j = 0; j < NQW; ++j)
+      for (int e = 0; e < PE; ++e) {
+        // straight-line visibility: inside the split, and a cached slot or an
+        // ancestor-or-self chunk row
+        const int sl = kt0 + PE * lg + e;
+        const bool live = sl < k_end;
+        const int jr = max(sl - C, 0);
 #pragma unroll
-        for (int e = 0; e < PE; ++e) {
-          const int sl = kt0 + PE * lg + e;
-          bool vis = sl < k_end;
-          if (vis && sl >= C) {
-            const int jr = sl - C;
-            vis = (anc[j][jr >> 5] >> (jr & 31)) & 1u;
-          }
-          if (!vis) sv[j][e] = -INFINITY;
+        for (int j = 0; j < NQW; ++j) {
+          const bool vis = live & ((sl < C) | (((anc_word(anc[j], jr >> 5) >> (jr & 31)) & 1u) != 0u));
+          sv[j][e] = vis ? sv[j][e] : -INFINITY;
         }
+      }
     }
     // ---- online softmax; rescale only when some row's maximum rises
     float mnew[NQW];
@@ -399,18 +465,20 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
   __shared__ int is_last;
   const int qg = blockIdx.z % a.n_qg;
   if (!arrive_last(a.sem + ((size_t)b * a.Hkv + g) * a.n_qg + qg, a.n_splits, &is_last)) return;
-  attn_merge<T, DH>(a, b, g, q_base * 16, min(nq, (q_base + NW * NQW) * 16), (float*)lds_raw);
+  if (a.n_splits <= 8) attn_merge8<T, DH>(a, b, g, q_base * 16, min(nq, (q_base + NW * NQW) * 16));
+  else attn_merge<T, DH>(a, b, g, q_base * 16, min(nq, (q_base + NW * NQW) * 16), (float*)lds_raw);
 }
 
 // Register path for few query tiles per kv head (at most 3): every wave holds all
 // query tiles of the head (pre-scaled by log2(e)/sqrt(dh)) and streams its own
-// interleaved key tiles straight from the pages into MFMA operands, one tile ahead.
+// interleaved key tiles straight from the pages into MFMA operands (two waves per
+// SIMD; the next tile's operands are loaded as soon as the current ones are read).
 // Per tile the score MFMAs of all query tiles are interleaved; the visibility mask is
 // evaluated only on tiles that reach the chunk rows or the end of the split; the
 // accumulators are rescaled only when some row's running maximum rises.  The 4 waves
 // of the workgroup merge their states through LDS and write one partial per split.
 template <typename T, int DH, int NQT>
-__global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_reg(AttnArgs a) {
   constexpr bool BF = sizeof(T) == 2;
   constexpr int VE = Vec16<T>::N;
   constexpr int KS = 4 * VE;
@@ -465,7 +533,7 @@ __global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
     const int ph = sPage[(min(slot, last) >> 4) - pg0];
     return ph < 0 ? 0 : ph;
   };
-  auto load_tile = [&](int it, u32x4 (&ko)[NKA], u32x4 (&vo)[NVA]) {
+  auto load_k = [&](int it, u32x4 (&ko)[NKA]) {
     const int kt0 = k_begin + min(it, max(ntiles - 1, 0)) * KT;
     // K rows: a bf16 tile has two 16-key halves whose rows map to keys 8*(r/4) + r%4 (+4)
 #pragma unroll
@@ -476,6 +544,9 @@ __global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < DH / KS; ++ks) ko[hv * (DH / KS) + ks] = ld16(src + ks * KS);
     }
+  };
+  auto load_v = [&](int it, u32x4 (&vo)[NVA]) {
+    const int kt0 = k_begin + min(it, max(ntiles - 1, 0)) * KT;
     // V^T: lane holds dh row dt*16 + r for keys PE*lg .. PE*lg + PE - 1 (one page)
     const int slot0 = min(kt0 + PE * lg, last & ~(PE - 1));
     const T* vsrc = vp + (((size_t)page_of(slot0) * a.Hkv + g) * DH + r) * 16 + (slot0 & 15);
@@ -483,7 +554,10 @@ __global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
     for (int dt = 0; dt < NVA; ++dt) vo[dt] = ld16(vsrc + (size_t)dt * 16 * 16);
   };
 
-  auto compute_tile = [&](int it, const u32x4 (&ko)[NKA], u32x4 (&vo)[NVA]) {
+  // One register set per wave: the next tile's K is loaded as soon as the score
+  // MFMAs have read the current one, its V after P V (two waves per SIMD cover the
+  // latency).
+  auto compute_tile = [&](int it, u32x4 (&ko)[NKA], u32x4 (&vo)[NVA]) {
     const int kt0 = k_begin + it * KT;
     f32x4 sc[NQT][NH];
 #pragma unroll
@@ -498,6 +572,7 @@ __global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
         for (int j = 0; j < NQT; ++j)
 #pragma unroll
           for (int hv = 0; hv < NH; ++hv) sc[j][hv] = mma16<T>(ko[hv * (DH / KS) + ks], qreg[j][ks][qp], sc[j][hv]);
+    load_k(it + 4, ko);
     float sv[NQT][PE];
 #pragma unroll
     for (int j = 0; j < NQT; ++j)
@@ -515,17 +590,18 @@ __global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
     }
     if (kt0 + KT > C || kt0 + KT > k_end || bad_page) {
 #pragma unroll
-      for (int j = 0; j < NQT; ++j)
+      for (int e = 0; e < PE; ++e) {
+        // straight-line visibility (no short-circuit branches): inside the split, on
+        // a valid page, and a cached slot or an ancestor-or-self chunk row
+        const int sl = kt0 + PE * lg + e;
+        const bool live = (sl < k_end) & (sPage[(min(sl, last) >> 4) - pg0] >= 0);
+        const int jr = max(sl - C, 0);
 #pragma unroll
-        for (int e = 0; e < PE; ++e) {
-          const int sl = kt0 + PE * lg + e;
-          bool vis = sl < k_end && sPage[(min(sl, last) >> 4) - pg0] >= 0;
-          if (vis && sl >= C) {
-            const int jr = sl - C;
-            vis = (anc[j][jr >> 5] >> (jr & 31)) & 1u;
-          }
-          if (!vis) sv[j][e] = -INFINITY;
+        for (int j = 0; j < NQT; ++j) {
+          const bool vis = live & ((sl < C) | (((anc_word(anc[j], jr >> 5) >> (jr & 31)) & 1u) != 0u));
+          sv[j][e] = vis ? sv[j][e] : -INFINITY;
         }
+      }
       // values of keys that are not real cache rows (past the sequence end or on an
       // invalid page) may hold anything; zero them so 0 * value stays 0
       const int sl0 = kt0 + PE * lg;
@@ -535,8 +611,7 @@ __global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
         T e8[VE];
         __builtin_memcpy(e8, &vo[dt], 16);
 #pragma unroll
-        for (int i = 0; i < VE; ++i)
-          if (!pg_ok || sl0 + i >= k_end) e8[i] = T(0);
+        for (int i = 0; i < VE; ++i) e8[i] = (pg_ok & (sl0 + i < k_end)) ? e8[i] : T(0);
         __builtin_memcpy((void*)&vo[dt], e8, 16);
       }
     }
@@ -587,18 +662,14 @@ __global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
         for (int dt = 0; dt < DH / 16; ++dt) acc[j][dt] = mma16<T>(vo[dt], pb, acc[j][dt]);
       }
     }
+    load_v(it + 4, vo);
   };
 
-  // tiles w, w+4, w+8, ... of the split, one tile ahead
-  u32x4 kA[NKA], vA[NVA], kB[NKA], vB[NVA];
-  load_tile(w, kA, vA);
-  for (int it = w; it < ntiles; it += 8) {
-    load_tile(it + 4, kB, vB);
-    compute_tile(it, kA, vA);
-    if (it + 4 >= ntiles) break;
-    load_tile(it + 8, kA, vA);
-    compute_tile(it + 4, kB, vB);
-  }
+  // tiles w, w+4, w+8, ... of the split
+  u32x4 kA[NKA], vA[NVA];
+  load_k(w, kA);
+  load_v(w, vA);
+  for (int it = w; it < ntiles; it += 4) compute_tile(it, kA, vA);
 
   // ---- merge the 4 waves: LDS holds each wave's (m, l) and O^T accumulators
   __shared__ float sm[4][NQT][64], sl[4][NQT][64];
@@ -660,7 +731,8 @@ __global__ __launch_bounds__(256) void attn_reg(AttnArgs a) {
   if (!fused || direct) return;
   __shared__ int is_last;
   if (!arrive_last(a.sem + (size_t)b * a.Hkv + g, a.n_splits, &is_last)) return;
-  attn_merge<T, DH>(a, b, g, 0, nq, &so[0][0][0][0][0]);
+  if (a.n_splits <= 8) attn_merge8<T, DH>(a, b, g, 0, nq);
+  else attn_merge<T, DH>(a, b, g, 0, nq, &so[0][0][0][0][0]);
 }
 
 template <typename T, int DH>
@@ -742,10 +814,14 @@ static hipError_t launch_attn_t(AttnArgs a, hipStream_t s) {
   if (attn_uses_reg_path(sizeof(T) == 2, DH, NQT)) {
     dim3 grid(a.n_splits, a.Hkv, a.B);
     a.n_qg = 1;
-    switch (NQT) {
-      case 1: attn_reg<T, DH, 1><<<grid, 256, 0, s>>>(a); break;
-      case 2: attn_reg<T, DH, 2><<<grid, 256, 0, s>>>(a); break;
-      default: attn_reg<T, DH, 3><<<grid, 256, 0, s>>>(a); break;
+    if constexpr (DH == 128) {
+      attn_reg<T, DH, 1><<<grid, 256, 0, s>>>(a);   // the register path takes one query tile at dh 128
+    } else {
+      switch (NQT) {
+        case 1: attn_reg<T, DH, 1><<<grid, 256, 0, s>>>(a); break;
+        case 2: attn_reg<T, DH, 2><<<grid, 256, 0, s>>>(a); break;
+        default: attn_reg<T, DH, 3><<<grid, 256, 0, s>>>(a); break;
+      }
     }
     return hipGetLastError();
   }

@@ -30,6 +30,8 @@
 //            h = silu(gate) * up, stored in the activation format;
 //   LOGITS   fp32 logits plus per-(row, column group) statistics: largest value, its
 //            index (lowest on ties), second-largest value and sum of exp(v - largest).
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 
 #include "common.h"
@@ -316,10 +318,17 @@ constexpr int gemm_lds_bytes(int MT, int NT) { return 2 * MT * NT * 4 * 64 * 4 +
 constexpr int LDS_LIMIT = 160 * 1024;
 int gemm_lds_ok(int MT, int NT) { return gemm_lds_bytes(MT, NT) <= LDS_LIMIT; }
 
+struct Launch {
+  dim3 grid;
+  hipStream_t s;
+  hipEvent_t ev0, ev1;
+};
+
 template <typename T, int MT, int NT, int D, int EPI>
-static hipError_t launch_one(dim3 grid, const GemmArgs& a, hipStream_t s) {
+static hipError_t launch_one(const Launch& L, const GemmArgs& a) {
   if constexpr (gemm_lds_bytes(MT, NT) <= LDS_LIMIT) {
-    gemm_stream<T, MT, NT, D, EPI><<<grid, 256, 0, s>>>(a);
+    if (L.ev0) hipExtLaunchKernelGGL(gemm_stream<T, MT, NT, D, EPI>, L.grid, dim3(256), 0, L.s, L.ev0, L.ev1, 0, a);
+    else gemm_stream<T, MT, NT, D, EPI><<<L.grid, 256, 0, L.s>>>(a);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;
@@ -327,29 +336,30 @@ static hipError_t launch_one(dim3 grid, const GemmArgs& a, hipStream_t s) {
 }
 
 template <typename T, int NT, int D, int EPI>
-static hipError_t launch_mt(int MT, dim3 grid, const GemmArgs& a, hipStream_t s) {
+static hipError_t launch_mt(int MT, const Launch& L, const GemmArgs& a) {
   switch (MT) {
-    case 1: return launch_one<T, 1, NT, D, EPI>(grid, a, s);
-    case 2: return launch_one<T, 2, NT, D, EPI>(grid, a, s);
-    case 3: return launch_one<T, 3, NT, D, EPI>(grid, a, s);
-    case 4: return launch_one<T, 4, NT, D, EPI>(grid, a, s);
-    case 5: return launch_one<T, 5, NT, D, EPI>(grid, a, s);
+    case 1: return launch_one<T, 1, NT, D, EPI>(L, a);
+    case 2: return launch_one<T, 2, NT, D, EPI>(L, a);
+    case 3: return launch_one<T, 3, NT, D, EPI>(L, a);
+    case 4: return launch_one<T, 4, NT, D, EPI>(L, a);
+    case 5: return launch_one<T, 5, NT, D, EPI>(L, a);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename T, int EPI>
-static hipError_t launch_cfg(const GemmCfg& c, int MT, dim3 grid, const GemmArgs& a, hipStream_t s) {
-  if (c.NT == 2 && c.D == 4) return launch_mt<T, 2, 4, EPI>(MT, grid, a, s);
-  if (c.NT == 4 && c.D == 2) return launch_mt<T, 4, 2, EPI>(MT, grid, a, s);
-  if (c.NT == 8 && c.D == 2) return launch_mt<T, 8, 2, EPI>(MT, grid, a, s);
+static hipError_t launch_cfg(const GemmCfg& c, int MT, const Launch& L, const GemmArgs& a) {
+  if (c.NT == 2 && c.D == 4) return launch_mt<T, 2, 4, EPI>(MT, L, a);
+  if (c.NT == 4 && c.D == 2) return launch_mt<T, 4, 2, EPI>(MT, L, a);
+  if (c.NT == 8 && c.D == 2) return launch_mt<T, 8, 2, EPI>(MT, L, a);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(bool is_bf16, const GemmCfg& c, int MT, int epi, dim3 grid, const GemmArgs& a,
-                       hipStream_t s) {
+                       hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const Launch L{grid, s, ev_start, ev_start ? ev_stop : nullptr};
 #define SDV_EPI(E)                                                                          \
-  if (epi == E) return is_bf16 ? launch_cfg<bf16, E>(c, MT, grid, a, s) : launch_cfg<float, E>(c, MT, grid, a, s);
+  if (epi == E) return is_bf16 ? launch_cfg<bf16, E>(c, MT, L, a) : launch_cfg<float, E>(c, MT, L, a);
   SDV_EPI(EPI_PARTIAL)
   SDV_EPI(EPI_QKV)
   SDV_EPI(EPI_SWIGLU)

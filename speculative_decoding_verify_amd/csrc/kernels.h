@@ -59,8 +59,11 @@ struct GemmCfg {
   int NT, D;
 };
 int gemm_lds_ok(int MT, int NT);
+// With ev_start / ev_stop set, the events are recorded by the dispatch itself at the
+// kernel's start and end (hipExtLaunchKernel), so their interval is the kernel's own
+// execution time.
 hipError_t launch_gemm(bool is_bf16, const GemmCfg& c, int MT, int epi, dim3 grid, const GemmArgs& a,
-                       hipStream_t s);
+                       hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // weight packing (one-time, at model load): rows of up to three row-major [rows, K]
 // sources, viewed as one matrix, rearranged into tiles; kind 0 plain, 1 q/k/v rotation

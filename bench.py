@@ -51,7 +51,9 @@ def gate_up_launch_bytes(sh, M):
 # each scaled by what the same counter reads for a plain 256 MiB device copy
 # (`bench.py --copy-calibration`).  Valid only for the kernel sources they were taken
 # on: the sha256 of the GEMM sources is checked at run time, else traffic is null.
-GATE_UP_TRAFFIC = None
+GATE_UP_TRAFFIC = {"sha256": "b62144e5e26e1b93f57db021de05f86146437d89d383ae4b7d47d54a3964ac60",
+                   "fetch_kib": 34149.0, "fetch_factor": 262144.0 / 131084.0,
+                   "write_kib": 1312.0, "write_factor": 262144.0 / 262144.0}
 GEMM_SOURCES = ("speculative_decoding_verify_amd/csrc/gemm.hip", "speculative_decoding_verify_amd/csrc/common.h",
                 "speculative_decoding_verify_amd/csrc/kernels.h")
 

@@ -1,0 +1,79 @@
+"""The C ABI on the host: libsdv.so loads and exports every function include/sdv.h
+declares, and host-checkable calls behave as the header states (negative status before
+anything is enqueued, a message from sdv_last_error, sizes from pure host arithmetic).
+No call here launches GPU work."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import speculative_decoding_verify_amd as sdv
+from speculative_decoding_verify_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)      # drop comments
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b(sdv_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("sdv_verify_forward", "sdv_accept_greedy", "sdv_accept_sample", "sdv_kv_rollback",
+              "sdv_verify_workspace_size", "sdv_sample_workspace_size", "sdv_pack_weights",
+              "sdv_packed_bytes", "sdv_last_error", "sdv_abi_version"):
+        assert f in names, f
+
+
+def test_library_exports_every_declared_function():
+    L = sdv.lib()
+    names = declared_functions()
+    for f in names:
+        assert hasattr(L, f), f"libsdv.so does not export {f}"
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True)
+    if out.returncode == 0:
+        exported = {ln.split()[-1] for ln in out.stdout.splitlines() if " T " in ln}
+        missing = [f for f in names if f not in exported]
+        assert not missing, missing
+
+
+def test_abi_version_and_packed_sizes():
+    L = sdv.lib()
+    assert L.sdv_abi_version() == 3
+    # rows round up to 16, 2 bytes (bf16) / 4 bytes (fp32) per value
+    assert L.sdv_packed_bytes(1, 6144, 2048) == 6144 * 2048 * 2
+    assert L.sdv_packed_bytes(0, 17, 64) == 32 * 64 * 4
+    assert L.sdv_packed_bytes(1, 0, 64) == 0
+    assert L.sdv_packed_bytes(7, 16, 64) == 0
+
+
+def test_null_arguments_are_rejected_before_launch():
+    L = sdv.lib()
+    st = L.sdv_verify_forward(None, None, None, None, None, 0, None)
+    assert st == -1
+    assert b"NULL" in L.sdv_last_error()
+    st = L.sdv_kv_rollback(None, None, None, None, None, 0, None, None)
+    assert st == -1
+    # both move lists or neither
+    st = L.sdv_accept_greedy(1, 4, 1, ctypes.c_void_p(16), None, 1, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                             None, ctypes.c_void_p(16), ctypes.c_void_p(16), None, None, ctypes.c_void_p(16), None,
+                             None, None)
+    assert st == -1
+    # T above the supported maximum
+    st = L.sdv_accept_greedy(1, 4096, 1, ctypes.c_void_p(16), None, 1, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                             None, ctypes.c_void_p(16), ctypes.c_void_p(16), None, None, None, None, None, None)
+    assert st == -2
+
+
+def test_workspace_sizes_are_host_arithmetic():
+    L = sdv.lib()
+    assert L.sdv_sample_workspace_size(0, 7, 151936) == 0
+    n1 = L.sdv_sample_workspace_size(64, 7, 151936)
+    n2 = L.sdv_sample_workspace_size(128, 7, 151936)
+    assert 0 < n1 < n2

@@ -88,7 +88,7 @@ struct Plan {
   bool attn_fused;  // split partials merged inside the attention kernel
   size_t part_floats;
   size_t off_x, off_a, off_q, off_o, off_h, off_part, off_po, off_pml, off_stats, off_depth, off_anc,
-      off_lmrows, off_rope, off_cb, off_sem, total;
+      off_lmrows, off_rope, off_cb, off_sem, off_kvdst, total;
   size_t n_sem;     // attention arrival counters: [layer][B][Hkv][n_qg]
 };
 
@@ -173,6 +173,7 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
   p.off_rope = take((size_t)p.M * (dh / 2) * 8);
   p.off_cb = p.S ? take((size_t)p.cb.S * (p.Mr + p.S) * m->codebook_size * 4) : o;
   p.off_sem = take(p.n_sem * 4);
+  p.off_kvdst = take((size_t)p.M * 8);
   p.total = o;
   return p;
 }
@@ -270,6 +271,7 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
   uint32_t* anc = (uint32_t*)(w + P.off_anc);
   int32_t* lm_rows = (int32_t*)(w + P.off_lmrows);
   uint32_t* sem = (uint32_t*)(w + P.off_sem);
+  int2* kv_dst = (int2*)(w + P.off_kvdst);
 
   const int d = m->d, H = m->n_heads, Hkv = m->n_kv_heads, dh = m->head_dim, F = m->ffn, V = m->vocab;
   const int qd = H * dh, kd = Hkv * dh, M = P.M;
@@ -284,7 +286,8 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
   {
     const bool cbh = in->head == SDV_HEAD_CODEBOOK;
     PrologueArgs a{in->parent, in->logit_rows, kv->seq_len, B, T, R, depth, anc, lm_rows, rope, dh,
-                   m->rope_theta, out->err, cbh ? P.S : 0, M, sem, (int)P.n_sem};
+                   m->rope_theta, out->err, cbh ? P.S : 0, M, sem, (int)P.n_sem,
+                   kv->block_table, kv->max_blocks, kv->n_blocks, in->max_ctx, kv_dst};
     SDV_LAUNCH(launch_prologue(a, s));
   }
   {
@@ -305,8 +308,7 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
     {
       GemmArgs a = gemm_args(act, d, nullptr, M, L.wqkv, qd + 2 * kd, d);
       a.pair_n = dh / 2;
-      a.qkv = QkvEpi{q, kp, vp, kv->block_table, kv->max_blocks, kv->n_blocks, kv->seq_len, rope,
-                     B, T, H, Hkv, in->max_ctx, out->err, (float)(1.4426950408889634 / sqrt((double)dh))};
+      a.qkv = QkvEpi{q, kp, vp, kv_dst, rope, B, T, H, Hkv, (float)(1.4426950408889634 / sqrt((double)dh))};
       if ((st = run_gemm(pe, P, P.qkv, a, s)) != SDV_OK) return st;
     }
     {

@@ -15,10 +15,11 @@ namespace sdv {
 
 // ---------------------------------------------------------------------------
 // Prologue: tree bookkeeping (depth(j) = depth(parent(j)) + 1 and the
-// ancestor-or-self bits of every chunk row), the LM-head row gather list, and the
-// rotary table of the pass: for chunk row t of sequence b at position
+// ancestor-or-self bits of every chunk row), the LM-head row gather list, the
+// rotary table of the pass (for chunk row t of sequence b at position
 // p = seq_len[b] + depth(t), entry i holds (cos, sin) of p * theta^(-2i/dh),
-// evaluated in fp64 and rounded to fp32.
+// evaluated in fp64 and rounded to fp32) and the cache page and slot every chunk
+// row's K/V goes to (slot seq_len[b] + t).
 __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
   __shared__ int32_t par[128], dep[128];
   __shared__ uint32_t anc[128][4];
@@ -73,6 +74,18 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
     a.rope[idx] = make_float2((float)cs, (float)sn);
   }
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.n_zero; i += gridDim.x * blockDim.x) a.zero[i] = 0u;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.B * a.T; i += gridDim.x * blockDim.x) {
+    const int b = i / a.T, t = i % a.T;
+    const int C = a.seq_len[b];
+    const int slot = C + t;
+    int phys = -1;
+    if (C >= 0 && C <= a.max_ctx && slot < a.max_blocks * 16) phys = a.block_table[(size_t)b * a.max_blocks + (slot >> 4)];
+    if (phys < 0 || phys >= a.n_blocks) {
+      phys = -1;
+      set_err(a.err, b, 0x4);
+    }
+    a.kv_dst[i] = make_int2(phys, slot & 15);
+  }
 }
 
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {

@@ -23,9 +23,9 @@
 //   QKV      rotary embedding on q and k: packed rows 0-7 of a tile are the first
 //            members (element i) and rows 8-15 the second members (element i + dh/2)
 //            of 8 rotation pairs; q scaled by log2(e)/sqrt(dh) and written in the
-//            activation format, k and v rounded to the
-//            cache type and appended to the paged cache (k token-major, v transposed
-//            inside the page);
+//            activation format, k and v rounded to the cache type and appended to
+//            the paged cache (k token-major, v transposed inside the page) at the
+//            page and slot the prologue resolved for the row;
 //   SWIGLU   rows 0-7 of a tile are gate rows f, rows 8-15 the up rows of the same f:
 //            h = silu(gate) * up, stored in the activation format;
 //   LOGITS   fp32 logits plus per-(row, column group) statistics: largest value, its
@@ -94,6 +94,24 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs a) {
 #pragma unroll
         for (int h = 0; h < AL; ++h) acc[mt][t] = mma16<T>(av[mt][h], w[t], acc[mt][t]);
   };
+
+  // q/k/v epilogue inputs of this thread's items (rotary pair and K/V destination),
+  // loaded before the k loop so their latency hides under the weight stream
+  constexpr int QI = EPI == EPI_QKV ? (16 * MT * NT * 8 + 255) / 256 : 1;
+  float2 ep_rope[QI];
+  int2 ep_dst[QI];
+  if constexpr (EPI == EPI_QKV) {
+    const int half = a.pair_n;
+#pragma unroll
+    for (int u = 0; u < QI; ++u) {
+      const int idx = threadIdx.x + 256 * u;
+      const int ml = idx / (NT * 8), pc = idx % (NT * 8);
+      const int m = min(m_base + ml, a.M - 1);
+      const int i = ((cg * NT + (pc >> 3)) * 8 + (pc & 7)) % half;
+      ep_rope[u] = a.qkv.rope[(size_t)m * half + i];   // chunk row m = b * T + t
+      ep_dst[u] = a.qkv.kv_dst[m];
+    }
+  }
 
 #pragma unroll
   for (int u = 0; u < D - 1; ++u)
@@ -185,19 +203,20 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs a) {
     const QkvEpi& e = a.qkv;
     const int half = a.pair_n;  // dh / 2
     const int dh = 2 * half;
-    for (int idx = threadIdx.x; idx < 16 * MT * NT * 8; idx += 256) {
+#pragma unroll
+    for (int u = 0; u < QI; ++u) {
+      const int idx = threadIdx.x + 256 * u;
       const int ml = idx / (NT * 8), pc = idx % (NT * 8);
       const int t = pc >> 3, ii = pc & 7;
       const int m = m_base + ml;
       const int p = (cg * NT + t) * 8 + ii;  // rotation pair
       const int hh = p / half, i = p % half;  // head (q, k, then v heads) and element
-      if (m >= a.M || hh >= e.H + 2 * e.Hkv) continue;
+      if (idx >= 16 * MT * NT * 8 || m >= a.M || hh >= e.H + 2 * e.Hkv) continue;
       const float x1 = tile[ml][t * 16 + ii];
       const float x2 = tile[ml][t * 16 + 8 + ii];
-      const int b = m / e.T, tt = m % e.T;
       float y1 = x1, y2 = x2;
       if (hh < e.H + e.Hkv) {
-        const float2 cs = e.rope[(size_t)(b * e.T + tt) * half + i];  // (cos, sin)
+        const float2 cs = ep_rope[u];  // (cos, sin)
         y1 = x1 * cs.x - x2 * cs.y;
         y2 = x2 * cs.x + x1 * cs.y;
       }
@@ -206,21 +225,12 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs a) {
         act_store1<T>(qrow, hh * dh + i, y1 * e.q_scale);
         act_store1<T>(qrow, hh * dh + i + half, y2 * e.q_scale);
       } else {
-        const int C = e.seq_len[b];
-        const int slot = C + tt;
-        if (C < 0 || C > e.max_ctx || slot >= e.max_blocks * 16) {
-          if (i == 0) set_err(e.err, b, 0x4);
-          continue;
-        }
-        const int phys = e.block_table[(size_t)b * e.max_blocks + (slot >> 4)];
-        if (phys < 0 || phys >= e.n_blocks) {
-          if (i == 0) set_err(e.err, b, 0x4);
-          continue;
-        }
+        const int phys = ep_dst[u].x;   // -1: the prologue reported the row
+        if (phys < 0) continue;
         const bool is_k = hh < e.H + e.Hkv;
         const int g = is_k ? hh - e.H : hh - e.H - e.Hkv;
         const size_t page = (size_t)phys * e.Hkv + g;
-        const int off = slot & 15;
+        const int off = ep_dst[u].y;
         if (is_k) {
           T* kp = (T*)e.k_pages + (page * 16 + off) * dh;
           kp[i] = from_f<T>(y1);

@@ -12,12 +12,9 @@ struct QkvEpi {
   void* q;                  // [M, H*dh] queries times q_scale, in the activation format
   void* k_pages;            // this layer: [n_blocks][Hkv][16][dh]
   void* v_pages;            //             [n_blocks][Hkv][dh][16]
-  const int32_t* block_table;
-  int max_blocks, n_blocks;
-  const int32_t* seq_len;
+  const int2* kv_dst;       // [B*T] (physical page, slot in page) of each chunk row, page -1: none
   const float2* rope;       // [B*T][dh/2] (cos, sin) of each chunk row's position
-  int B, T, H, Hkv, max_ctx;
-  int32_t* err;
+  int B, T, H, Hkv;
   float q_scale;            // log2(e) / sqrt(dh): attention works in the exp2 domain
 };
 
@@ -132,6 +129,11 @@ struct PrologueArgs {
   int n_extra, extra_base;  // lm_rows[B*R + i] = extra_base + i for i < n_extra
   uint32_t* zero;           // n_zero words cleared (the attention arrival counters)
   int n_zero;
+  // destination of each chunk row's K/V: slot seq_len[b] + t through the block table;
+  // a slot outside [0, max_ctx + T) or the table, or an invalid page, sets error 0x4
+  const int32_t* block_table;
+  int max_blocks, n_blocks, max_ctx;
+  int2* kv_dst;             // [B*T] (physical page, slot in page), page -1 when invalid
 };
 hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s);
 

@@ -119,8 +119,11 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _dev_tensor(a: np.ndarray, device) -> torch.Tensor:
-    """numpy fp32 -> float32 tensor; numpy uint16 (bf16 bit patterns) -> bfloat16 tensor."""
+def _dev_tensor(a, device) -> torch.Tensor:
+    """numpy fp32 -> float32 tensor; numpy uint16 (bf16 bit patterns) -> bfloat16 tensor;
+    a torch tensor is moved to `device` as it is."""
+    if isinstance(a, torch.Tensor):
+        return a.to(device)
     if a.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
@@ -200,18 +203,23 @@ class PagedKV:
     block_table [B, max_blocks], seq_len [B]."""
 
     def __init__(self, shape, batch: int, capacity: int, device="cuda", perm: Optional[np.ndarray] = None,
-                 n_blocks: Optional[int] = None):
+                 n_blocks: Optional[int] = None, table: Optional[np.ndarray] = None):
+        """table: optional int32 [batch, max_blocks] block table (-1 = unused entry) over
+        n_blocks physical blocks, for rows of different capacities."""
         self.shape = shape
         self.device = torch.device(device)
         self.batch = batch
-        self.max_blocks = (capacity + PAGE - 1) // PAGE
+        self.max_blocks = (capacity + PAGE - 1) // PAGE if table is None else int(table.shape[1])
         self.n_blocks = n_blocks or batch * self.max_blocks
         dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
         L, Hkv, dh = shape.n_layers, shape.n_kv_heads, shape.head_dim
         self.k_pages = torch.zeros((L, self.n_blocks, Hkv, PAGE, dh), dtype=dt, device=self.device)
         self.v_pages = torch.zeros((L, self.n_blocks, Hkv, dh, PAGE), dtype=dt, device=self.device)
-        ids = np.arange(batch * self.max_blocks, dtype=np.int32) if perm is None else np.asarray(perm, np.int32)
-        self.block_table = torch.from_numpy(ids[:batch * self.max_blocks].reshape(batch, self.max_blocks).copy()).to(self.device)
+        if table is not None:
+            self.block_table = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).to(self.device)
+        else:
+            ids = np.arange(batch * self.max_blocks, dtype=np.int32) if perm is None else np.asarray(perm, np.int32)
+            self.block_table = torch.from_numpy(ids[:batch * self.max_blocks].reshape(batch, self.max_blocks).copy()).to(self.device)
         self.seq_len = torch.zeros(batch, dtype=torch.int32, device=self.device)
         self.desc = SdvKV(self.k_pages.data_ptr(), self.v_pages.data_ptr(), self.block_table.data_ptr(),
                           self.seq_len.data_ptr(), self.n_blocks, self.max_blocks, batch)

@@ -68,7 +68,8 @@ class VerifyWorkload:
     seed: int = 0
     silence_id: int = 0
     page: int = 16                # tokens per KV page
-    kv_init: str = "random"       # "random": synthetic unit-variance KV; "prefill": run tokens through the model
+    kv_init: str = "random"       # "random": synthetic unit-variance KV; "prefill": run tokens through the model;
+                                  # "hashed": the coordinate-hashed unit-variance KV (generated on the device)
     cfg_pairs: bool = False       # rows 2i (conditional) and 2i+1 (unconditional) form CFG pairs
     cfg_w: float = 2.0
 
@@ -135,10 +136,28 @@ def w8b_tree_workload(seed: int = 3) -> VerifyWorkload:
     return VerifyWorkload(SHAPE_8B, batch=1, ctx=(8192,), L_a=25, gamma=32, n_branch=8, seed=seed)
 
 
+def c5_contexts(seed: int = 5, sessions: int = 32, lo: int = 2048, hi: int = 16384):
+    """Cached lengths of the batched multi-codebook workload: one seeded integer in
+    [lo, hi] per session, shared by the session's conditional and unconditional rows."""
+    import numpy as np
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0xC5])))
+    per = g.integers(lo, hi + 1, size=sessions)
+    return tuple(int(c) for c in np.repeat(per, 2))
+
+
+def c5_workload(seed: int = 5) -> VerifyWorkload:
+    """8B-shape backbone with 8 codebook heads of 1024: 32 sessions x (conditional,
+    unconditional) rows, contexts in [2048, 16384], 25 audio + 16 draft codes per
+    session, guidance weight 2; acceptance on codebook 0."""
+    return VerifyWorkload(SHAPE_8B_CB, batch=64, ctx=c5_contexts(seed), L_a=25, gamma=16, seed=seed,
+                          kv_init="hashed", cfg_pairs=True, cfg_w=2.0)
+
+
 WORKLOADS = {
     "toy-f32": toy_workload,
     "1.7b-bf16": w1p7b_workload,
     "8b-bf16-tree": w8b_tree_workload,
+    "c5-codebook": c5_workload,
 }
 
 

@@ -171,6 +171,123 @@ def make_random_kv(shape: ModelShape, lens, capacity: int, seed: int) -> KVCache
     return KVCache(ks, vs, list(lens), capacity)
 
 
+# -- hashed synthetic KV: caches of tens of GB generated where they are used --------
+#
+# Every value is a function of its coordinates only.  The element's linear index
+# (token * n_heads + head) * dh + dim inside its (stream, layer, k/v) block, plus a
+# per-block key, goes through a 32-bit integer hash (two rounds of xorshift-16 and
+# multiply by 0x45d9f3b); the top 24 bits u give (2u + 1 - 2^24) / 2^24 * sqrt(3) in
+# fp32, uniform on (-sqrt 3, sqrt 3), rounded to bf16 (nearest even).  The integer
+# steps stay below 2^63, so NumPy (hashed_kv_np) and torch on the GPU
+# (hashed_kv_torch) produce identical bit patterns: the GPU fills the cache, the host
+# regenerates any slice the oracle needs.
+
+_HASH_MUL = 0x45D9F3B
+_M32_INT = 0xFFFFFFFF
+_S3_F32 = float(np.float32(math.sqrt(3.0)))
+
+
+def _mix32(x: int) -> int:
+    x = ((x >> 16) ^ x) * _HASH_MUL & _M32_INT
+    x = ((x >> 16) ^ x) * _HASH_MUL & _M32_INT
+    return (x >> 16) ^ x
+
+
+def hashed_kv_key(seed: int, stream: int, layer: int, kind: int) -> int:
+    """Key of one (stream, layer, kind) block; kind 0 = keys, 1 = values."""
+    k = _mix32((seed * 0x9E3779B1 + 0x632BE5AB) & _M32_INT)
+    for v in (stream, layer, kind):
+        k = _mix32((k ^ (v * 0x85EBCA6B + 0xC2B2AE35)) & _M32_INT)
+    return k
+
+
+def hashed_kv_np(seed: int, stream: int, layer: int, kind: int, n_tok: int, n_heads: int, dh: int,
+                 tok0: int = 0) -> np.ndarray:
+    """bf16 bit patterns [n_tok, n_heads, dh] of tokens tok0 .. tok0 + n_tok - 1."""
+    key = np.int64(hashed_kv_key(seed, stream, layer, kind))
+    m = np.int64(_M32_INT)
+    mul = np.int64(_HASH_MUL)
+    x = np.arange(tok0 * n_heads * dh, (tok0 + n_tok) * n_heads * dh, dtype=np.int64)
+    x = (x + key) & m
+    x = (((x >> 16) ^ x) * mul) & m
+    x = (((x >> 16) ^ x) * mul) & m
+    x = (x >> 16) ^ x
+    a = (2 * (x >> 8) + 1 - (1 << 24)).astype(np.float32) * np.float32(2.0 ** -24) * np.float32(_S3_F32)
+    return to_bf16_bits(a).reshape(n_tok, n_heads, dh)
+
+
+def hashed_kv_torch(seed: int, stream: int, layer: int, kind: int, n_tok: int, n_heads: int, dh: int,
+                    device, tok0: int = 0):
+    """The same values as hashed_kv_np, generated by torch on `device` (bfloat16)."""
+    import torch
+    key = hashed_kv_key(seed, stream, layer, kind)
+    x = torch.arange(tok0 * n_heads * dh, (tok0 + n_tok) * n_heads * dh, dtype=torch.int64, device=device)
+    x = (x + key) & _M32_INT
+    x = (((x >> 16) ^ x) * _HASH_MUL) & _M32_INT
+    x = (((x >> 16) ^ x) * _HASH_MUL) & _M32_INT
+    x = (x >> 16) ^ x
+    a = (2 * (x >> 8) + 1 - (1 << 24)).to(torch.float32) * (2.0 ** -24) * _S3_F32
+    return a.to(torch.bfloat16).reshape(n_tok, n_heads, dh)
+
+
+class _HashedSide:
+    def __init__(self, owner, kind):
+        self.owner, self.kind = owner, kind
+
+    def __getitem__(self, b):
+        o = self.owner
+        return [o.block(b, l, self.kind) for l in range(o.shape.n_layers)] if o.eager else _HashedRow(o, b, self.kind)
+
+    def __len__(self):
+        return len(self.owner.lens)
+
+
+class _HashedRow:
+    def __init__(self, owner, b, kind):
+        self.owner, self.b, self.kind = owner, b, kind
+
+    def __getitem__(self, l):
+        return self.owner.block(self.b, l, self.kind)
+
+    def __len__(self):
+        return self.owner.shape.n_layers
+
+
+class HashedKV:
+    """Logical cache contents like KVCache (k[b][l], v[b][l] of shape [len_b, Hkv, dh]),
+    generated on access from the hashed recipe: bf16 bit patterns on the host
+    (device=None) or bfloat16 tensors on a torch device.  Stream of row b = streams[b]."""
+
+    def __init__(self, shape: ModelShape, lens, capacity: int, seed: int, streams=None, device=None,
+                 eager: bool = False):
+        self.shape, self.lens, self.capacity, self.seed = shape, list(lens), capacity, seed
+        self.streams = list(range(len(self.lens))) if streams is None else list(streams)
+        self.device, self.eager = device, eager
+        self.k, self.v = _HashedSide(self, 0), _HashedSide(self, 1)
+
+    def block(self, b: int, l: int, kind: int):
+        sh = self.shape
+        n = self.lens[b]
+        if self.device is None:
+            return hashed_kv_np(self.seed, self.streams[b], l, kind, n, sh.n_kv_heads, sh.head_dim)
+        return hashed_kv_torch(self.seed, self.streams[b], l, kind, n, sh.n_kv_heads, sh.head_dim, self.device)
+
+
+def page_table(lens, capacity_extra: int, page: int, seed: int):
+    """Per-row block tables over one shared pool of physical blocks, placed by a seeded
+    permutation: row b owns ceil((lens[b] + capacity_extra) / page) blocks; unused
+    table entries are -1.  Returns (table int32 [B, max_blocks], n_blocks)."""
+    need = [(n + capacity_extra + page - 1) // page for n in lens]
+    n_blocks = int(sum(need))
+    perm = page_permutation(n_blocks, seed)
+    table = np.full((len(lens), max(need)), -1, dtype=np.int32)
+    at = 0
+    for b, nb in enumerate(need):
+        table[b, :nb] = perm[at:at + nb]
+        at += nb
+    return table, n_blocks
+
+
 def page_permutation(n_blocks: int, seed: int) -> np.ndarray:
     """Seeded permutation of physical KV blocks (fragmented placement)."""
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _tensor_key("pages")])))

@@ -98,8 +98,20 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // RMSNorm of one fp32 row held in registers (256 threads, PER elements each,
 // element c = threadIdx.x * PER + i), stored in the activation format of T.
+// The thread's PER gain values, loaded up front (before the block reduction's
+// barrier, which loads cannot cross).
+template <int PER>
+SDV_DEV void load_gain(const float* gain, int d, float (&g)[PER]) {
+  const int c0 = threadIdx.x * PER;
+#pragma unroll
+  for (int q = 0; q < PER / 4; ++q) {
+    const float4 v = c0 < d ? ((const float4*)(gain + c0))[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+    g[4 * q] = v.x; g[4 * q + 1] = v.y; g[4 * q + 2] = v.z; g[4 * q + 3] = v.w;
+  }
+}
+
 template <typename T, int PER>
-SDV_DEV void norm_store(const float (&v)[PER], int d, const float* gain, void* out_row, float eps, float* red) {
+SDV_DEV void norm_store(const float (&v)[PER], int d, const float (&gain)[PER], void* out_row, float eps, float* red) {
   static_assert(PER % 8 == 0, "whole k groups per thread");
   float ss = 0.f;
 #pragma unroll
@@ -112,7 +124,7 @@ SDV_DEV void norm_store(const float (&v)[PER], int d, const float* gain, void* o
     for (int g = 0; g < PER / 8; ++g) {
       float y[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = v[g * 8 + e] * rs * gain[c0 + g * 8 + e];
+      for (int e = 0; e < 8; ++e) y[e] = v[g * 8 + e] * rs * gain[g * 8 + e];
       act_store8<T>(out_row, c0 + g * 8, y);
     }
   }
@@ -129,13 +141,15 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(EmbedArgs a) {
   }
   const T* e = (const T*)a.embed + (size_t)tok * a.d;
   const int c0 = threadIdx.x * PER;
+  float gn[PER];
+  load_gain<PER>(a.gain, a.d, gn);
   float v[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     v[i] = c0 < a.d ? to_f<T>(e[c0 + i]) : 0.f;
     if (c0 < a.d) a.x[(size_t)m * a.d + c0 + i] = v[i];
   }
-  norm_store<T, PER>(v, a.d, a.gain, (char*)a.a + (size_t)m * a.d * 4, a.eps, red);
+  norm_store<T, PER>(v, a.d, gn, (char*)a.a + (size_t)m * a.d * 4, a.eps, red);
 }
 
 // x += sum of the S split partials (in split order), then RMSNorm -> a.  Each
@@ -147,7 +161,11 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(ResidNormArgs a) {
   const int m = blockIdx.x;
   const int c0 = threadIdx.x * PER;
   const bool on = c0 < a.d;
-  float v[PER];
+  float v[PER], gn[PER];
+  load_gain<PER>(a.gain, a.d, gn);
+  float4 x0[PER / 4];
+#pragma unroll
+  for (int q = 0; q < PER / 4; ++q) x0[q] = on ? ((const float4*)(a.x + (size_t)m * a.d + c0))[q] : make_float4(0.f, 0.f, 0.f, 0.f);
   float4 acc4[PER / 4];
 #pragma unroll
   for (int q = 0; q < PER / 4; ++q) acc4[q] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -171,7 +189,7 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(ResidNormArgs a) {
     float4* xp = (float4*)(a.x + (size_t)m * a.d + c0);
 #pragma unroll
     for (int q = 0; q < PER / 4; ++q) {
-      float4 x = xp[q];
+      float4 x = x0[q];
       x.x += acc4[q].x; x.y += acc4[q].y; x.z += acc4[q].z; x.w += acc4[q].w;
       xp[q] = x;
       if (a.hidden) ((float4*)(a.hidden + (size_t)m * a.d + c0))[q] = x;
@@ -181,7 +199,7 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(ResidNormArgs a) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) v[i] = 0.f;
   }
-  norm_store<T, PER>(v, a.d, a.gain, (char*)a.a + (size_t)m * a.d * 4, a.eps, red);
+  norm_store<T, PER>(v, a.d, gn, (char*)a.a + (size_t)m * a.d * 4, a.eps, red);
 }
 
 // PER columns per thread: the smallest of 8, 16, 24, 32 with 256 * PER >= d and

@@ -243,20 +243,39 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs a) {
       }
     }
   } else {  // EPI_LOGITS
+    // 8 threads per row, thread j over columns j, j + 8, ...; the 8 partial states
+    // meet in a fixed xor butterfly, so every thread of the row ends with the same
+    // values: largest (lowest index on ties), second largest (equal to the largest on
+    // a tie), then the sum of exp(v - largest).
     const int nc = min(TC, a.N - cg * TC);
-    for (int ml = threadIdx.x; ml < 16 * MT; ml += 256) {
-      const int m = m_base + ml;
-      if (m >= a.M) continue;
+    const int sub = threadIdx.x & 7;
+    for (int ml0 = 0; ml0 < 16 * MT; ml0 += 32) {
+      const int ml = ml0 + (threadIdx.x >> 3);
+      const bool row_ok = ml < 16 * MT;
       float m1 = -INFINITY, m2 = -INFINITY;
       int i1 = 0x7fffffff;
-      for (int c = 0; c < nc; ++c) {
-        const float v = tile[ml][c];
-        if (v > m1) { m2 = m1; m1 = v; i1 = cg * TC + c; }
-        else if (v > m2) m2 = v;
+      if (row_ok)
+        for (int c = sub; c < nc; c += 8) {
+          const float v = tile[ml][c];
+          if (v > m1) { m2 = m1; m1 = v; i1 = cg * TC + c; }
+          else if (v > m2) m2 = v;
+        }
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        const float om1 = __shfl_xor(m1, o), om2 = __shfl_xor(m2, o);
+        const int oi1 = __shfl_xor(i1, o);
+        const bool other_wins = om1 > m1 || (om1 == m1 && oi1 < i1);
+        const float lose = other_wins ? m1 : om1;   // the losing group's largest
+        m2 = fmaxf(fmaxf(m2, om2), lose);
+        if (other_wins) { m1 = om1; i1 = oi1; }
       }
       float se = 0.f;
-      for (int c = 0; c < nc; ++c) se += __expf(tile[ml][c] - m1);
-      a.stats[(size_t)m * a.n_groups + cg] = make_float4(m1, __int_as_float(i1), m2, se);
+      if (row_ok)
+        for (int c = sub; c < nc; c += 8) se += __expf(tile[ml][c] - m1);
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) se += __shfl_xor(se, o);
+      const int m = m_base + ml;
+      if (row_ok && sub == 0 && m < a.M) a.stats[(size_t)m * a.n_groups + cg] = make_float4(m1, __int_as_float(i1), m2, se);
     }
     if (a.logits) {
       for (int idx = threadIdx.x; idx < 16 * MT * TC; idx += 256) {

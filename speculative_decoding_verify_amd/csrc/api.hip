@@ -50,14 +50,22 @@ GemmPlan plan_gemm(int M, int N, int K, bool bf, int epi) {
   GemmPlan p;
   const int KS = bf ? 32 : 16;
   p.epi = epi;
-  if (M <= 80) {
-    p.MT = std::max(1, cdiv(M, 16));
-    p.row_blocks = 1;
-  } else {
-    p.MT = 4;
-    p.row_blocks = cdiv(M, 64);
-  }
   const int ntiles = cdiv(N, 16);
+  const int steps = K / KS;
+  if (M > 80) {
+    // many rows (batched sessions): the tiled kernel, 128-row blocks, 2 x WN column
+    // tiles per workgroup (WN = 8 when that still gives a full grid)
+    p.MT = 8;
+    p.row_blocks = cdiv(M, 128);
+    const int wn = (long long)cdiv(ntiles, 16) * p.row_blocks >= TARGET_WG_GEMM ? 8 : 4;
+    p.cfg = GemmCfg{wn, 2, true};
+    p.ncg = cdiv(ntiles, 2 * wn);
+    p.spp = steps;
+    p.S = 1;
+    return p;
+  }
+  p.MT = std::max(1, cdiv(M, 16));
+  p.row_blocks = 1;
   // configurations measured on the decoder shapes: few tiles per workgroup and a
   // deeper register ring where the grid would otherwise be small (q/k/v and o
   // projections), more tiles per workgroup as the row tiles grow
@@ -65,7 +73,6 @@ GemmPlan plan_gemm(int M, int N, int K, bool bf, int epi) {
   else if (p.MT >= (epi == EPI_LOGITS ? 3 : 4) && gemm_lds_ok(p.MT, 8)) p.cfg = GemmCfg{8, 2};
   else p.cfg = GemmCfg{4, 2};
   p.ncg = cdiv(ntiles, p.cfg.NT);
-  const int steps = K / KS;
   int S = 1;
   if (epi == EPI_PARTIAL) {
     const int target = p.cfg.NT == 2 ? 512 : 256;
@@ -197,7 +204,7 @@ sdv_status run_gemm(ProfEvents& pe, const Plan& P, const GemmPlan& g, GemmArgs a
   a.ldo = a.N;
   a.ldl = a.N;
   a.n_groups = g.ncg;
-  dim3 grid(g.ncg, g.S, g.row_blocks);
+  const dim3 grid = g.cfg.tiled ? dim3(g.row_blocks, 1, g.ncg) : dim3(g.ncg, g.S, g.row_blocks);
   const bool prof = pe.ev && pe.next < pe.n_pairs;
   if (prof)
     SDV_LAUNCH(launch_gemm(P.bf, g.cfg, g.MT, g.epi, grid, a, s, (hipEvent_t)pe.ev[2 * pe.next],

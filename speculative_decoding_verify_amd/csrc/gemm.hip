@@ -39,6 +39,128 @@
 
 namespace sdv {
 
+// Epilogues on a finished tile (LDS, 16 * MT rows x 16 * NT columns; row m_base + ml,
+// packed column group cg).  The q/k/v epilogue takes each item's rotary pair and K/V
+// destination from qkv_in(item slot u, row m, element i).
+struct QkvItem {
+  float2 rope;
+  int2 dst;
+};
+
+template <typename T, int MT, int NT, int EPI, typename QkvIn>
+SDV_DEV void gemm_epilogue(const GemmArgs& a, float (*tile)[16 * NT + 1], int cg, int split, int m_base,
+                           QkvIn qkv_in) {
+  constexpr int TC = 16 * NT;
+  if constexpr (EPI == EPI_PARTIAL) {
+    float* out = a.out + (size_t)split * a.out_split_stride;
+    for (int idx = threadIdx.x; idx < 16 * MT * TC; idx += 256) {
+      const int ml = idx / TC, c = idx % TC;
+      const int m = m_base + ml, n = cg * TC + c;
+      if (m < a.M && n < a.N) out[(size_t)m * a.ldo + n] = tile[ml][c];
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    for (int idx = threadIdx.x; idx < 16 * MT * NT * 8; idx += 256) {
+      const int ml = idx / (NT * 8), pc = idx % (NT * 8);
+      const int t = pc >> 3, i = pc & 7;
+      const int m = m_base + ml;
+      const int f = (cg * NT + t) * 8 + i;
+      if (m >= a.M || f >= a.pair_n) continue;
+      const float gt = tile[ml][t * 16 + i];
+      const float up = tile[ml][t * 16 + 8 + i];
+      const float sl = gt / (1.f + expf(-gt));
+      act_store1<T>((char*)a.out_act + (size_t)m * a.pair_n * 4, f, sl * up);
+    }
+  } else if constexpr (EPI == EPI_QKV) {
+    const QkvEpi& e = a.qkv;
+    const int half = a.pair_n;  // dh / 2
+    const int dh = 2 * half;
+    constexpr int QI = (16 * MT * NT * 8 + 255) / 256;
+    constexpr int QU = QI <= 8 ? QI : 1;   // unrolled when the items come from registers
+#pragma unroll QU
+    for (int u = 0; u < QI; ++u) {
+      const int idx = threadIdx.x + 256 * u;
+      const int ml = idx / (NT * 8), pc = idx % (NT * 8);
+      const int t = pc >> 3, ii = pc & 7;
+      const int m = m_base + ml;
+      const int p = (cg * NT + t) * 8 + ii;  // rotation pair
+      const int hh = p / half, i = p % half;  // head (q, k, then v heads) and element
+      if (idx >= 16 * MT * NT * 8 || m >= a.M || hh >= e.H + 2 * e.Hkv) continue;
+      const float x1 = tile[ml][t * 16 + ii];
+      const float x2 = tile[ml][t * 16 + 8 + ii];
+      float y1 = x1, y2 = x2;
+      const QkvItem in = qkv_in(u, m, i);
+      if (hh < e.H + e.Hkv) {
+        const float2 cs = in.rope;  // (cos, sin)
+        y1 = x1 * cs.x - x2 * cs.y;
+        y2 = x2 * cs.x + x1 * cs.y;
+      }
+      if (hh < e.H) {
+        char* qrow = (char*)e.q + (size_t)m * e.H * dh * 4;
+        act_store1<T>(qrow, hh * dh + i, y1 * e.q_scale);
+        act_store1<T>(qrow, hh * dh + i + half, y2 * e.q_scale);
+      } else {
+        const int phys = in.dst.x;   // -1: the prologue reported the row
+        if (phys < 0) continue;
+        const bool is_k = hh < e.H + e.Hkv;
+        const int g = is_k ? hh - e.H : hh - e.H - e.Hkv;
+        const size_t page = (size_t)phys * e.Hkv + g;
+        const int off = in.dst.y;
+        if (is_k) {
+          T* kp = (T*)e.k_pages + (page * 16 + off) * dh;
+          kp[i] = from_f<T>(y1);
+          kp[i + half] = from_f<T>(y2);
+        } else {
+          T* vp = (T*)e.v_pages + page * dh * 16;
+          vp[(size_t)i * 16 + off] = from_f<T>(y1);
+          vp[(size_t)(i + half) * 16 + off] = from_f<T>(y2);
+        }
+      }
+    }
+  } else {  // EPI_LOGITS
+    // 8 threads per row, thread j over columns j, j + 8, ...; the 8 partial states
+    // meet in a fixed xor butterfly, so every thread of the row ends with the same
+    // values: largest (lowest index on ties), second largest (equal to the largest on
+    // a tie), then the sum of exp(v - largest).
+    const int nc = min(TC, a.N - cg * TC);
+    const int sub = threadIdx.x & 7;
+    for (int ml0 = 0; ml0 < 16 * MT; ml0 += 32) {
+      const int ml = ml0 + (threadIdx.x >> 3);
+      const bool row_ok = ml < 16 * MT;
+      float m1 = -INFINITY, m2 = -INFINITY;
+      int i1 = 0x7fffffff;
+      if (row_ok)
+        for (int c = sub; c < nc; c += 8) {
+          const float v = tile[ml][c];
+          if (v > m1) { m2 = m1; m1 = v; i1 = cg * TC + c; }
+          else if (v > m2) m2 = v;
+        }
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        const float om1 = __shfl_xor(m1, o), om2 = __shfl_xor(m2, o);
+        const int oi1 = __shfl_xor(i1, o);
+        const bool other_wins = om1 > m1 || (om1 == m1 && oi1 < i1);
+        const float lose = other_wins ? m1 : om1;   // the losing group's largest
+        m2 = fmaxf(fmaxf(m2, om2), lose);
+        if (other_wins) { m1 = om1; i1 = oi1; }
+      }
+      float se = 0.f;
+      if (row_ok)
+        for (int c = sub; c < nc; c += 8) se += __expf(tile[ml][c] - m1);
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) se += __shfl_xor(se, o);
+      const int m = m_base + ml;
+      if (row_ok && sub == 0 && m < a.M) a.stats[(size_t)m * a.n_groups + cg] = make_float4(m1, __int_as_float(i1), m2, se);
+    }
+    if (a.logits) {
+      for (int idx = threadIdx.x; idx < 16 * MT * TC; idx += 256) {
+        const int ml = idx / TC, c = idx % TC;
+        const int m = m_base + ml, n = cg * TC + c;
+        if (m < a.M && n < a.N) a.logits[(size_t)m * a.ldl + n] = tile[ml][c];
+      }
+    }
+  }
+}
+
 template <typename T, int MT, int NT, int D, int EPI>
 __global__ __launch_bounds__(256) void gemm_stream(GemmArgs a) {
   constexpr bool BF = sizeof(T) == 2;
@@ -180,111 +302,109 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs a) {
   }
   __syncthreads();
 
-  if constexpr (EPI == EPI_PARTIAL) {
-    float* out = a.out + (size_t)split * a.out_split_stride;
-    for (int idx = threadIdx.x; idx < 16 * MT * TC; idx += 256) {
-      const int ml = idx / TC, c = idx % TC;
-      const int m = m_base + ml, n = cg * TC + c;
-      if (m < a.M && n < a.N) out[(size_t)m * a.ldo + n] = tile[ml][c];
-    }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    for (int idx = threadIdx.x; idx < 16 * MT * NT * 8; idx += 256) {
-      const int ml = idx / (NT * 8), pc = idx % (NT * 8);
-      const int t = pc >> 3, i = pc & 7;
-      const int m = m_base + ml;
-      const int f = (cg * NT + t) * 8 + i;
-      if (m >= a.M || f >= a.pair_n) continue;
-      const float gt = tile[ml][t * 16 + i];
-      const float up = tile[ml][t * 16 + 8 + i];
-      const float sl = gt / (1.f + expf(-gt));
-      act_store1<T>((char*)a.out_act + (size_t)m * a.pair_n * 4, f, sl * up);
-    }
-  } else if constexpr (EPI == EPI_QKV) {
-    const QkvEpi& e = a.qkv;
-    const int half = a.pair_n;  // dh / 2
-    const int dh = 2 * half;
+  gemm_epilogue<T, MT, NT, EPI>(a, tile, cg, split, m_base, [&](int u, int, int) {
+    if constexpr (EPI == EPI_QKV) return QkvItem{ep_rope[u], ep_dst[u]};
+    else return QkvItem{};
+  });
+}
+
+// ---------------------------------------------------------------------------
+// Tiled GEMM for many rows (M > 80, e.g. a batch of sessions): the weights are no
+// longer the only stream, every packed tile is reused by up to 128 rows.  A
+// workgroup computes a 128 x (32 * WN) output tile; wave (wm, wn) of its 2 x 2 waves
+// owns 64 x (16 * WN) (4 x WN MFMA tiles) and walks the whole K range with D k steps
+// of operands in flight in registers (same ring as gemm_stream).  Grid: x = row
+// blocks (fastest, so the workgroups that share a column group's weights run
+// together and the weights come from HBM once), z = column groups.  The finished
+// tile goes through LDS to the shared epilogues.
+template <typename T, int WN, int D, int EPI>
+__global__ __launch_bounds__(256) void gemm_tiled(GemmArgs a) {
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int KS = BF ? 32 : 16;
+  constexpr int AB = BF ? 32 : 16;   // activation bytes per lane group per row per step
+  constexpr int AL = BF ? 2 : 1;
+  constexpr int WM = 4;              // MFMA row tiles per wave
+  constexpr int MT = 2 * WM, NT = 2 * WN;
+  constexpr int TC = 16 * NT;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 15, lg = lane >> 4;
+  const int m_base = blockIdx.x * (16 * MT);
+  const int cg = blockIdx.z;
+  const int ksteps = a.K / KS;
+  const int ntiles = (a.N + 15) >> 4;
+
+  const char* wp[WN];
 #pragma unroll
-    for (int u = 0; u < QI; ++u) {
-      const int idx = threadIdx.x + 256 * u;
-      const int ml = idx / (NT * 8), pc = idx % (NT * 8);
-      const int t = pc >> 3, ii = pc & 7;
-      const int m = m_base + ml;
-      const int p = (cg * NT + t) * 8 + ii;  // rotation pair
-      const int hh = p / half, i = p % half;  // head (q, k, then v heads) and element
-      if (idx >= 16 * MT * NT * 8 || m >= a.M || hh >= e.H + 2 * e.Hkv) continue;
-      const float x1 = tile[ml][t * 16 + ii];
-      const float x2 = tile[ml][t * 16 + 8 + ii];
-      float y1 = x1, y2 = x2;
-      if (hh < e.H + e.Hkv) {
-        const float2 cs = ep_rope[u];  // (cos, sin)
-        y1 = x1 * cs.x - x2 * cs.y;
-        y2 = x2 * cs.x + x1 * cs.y;
-      }
-      if (hh < e.H) {
-        char* qrow = (char*)e.q + (size_t)m * e.H * dh * 4;
-        act_store1<T>(qrow, hh * dh + i, y1 * e.q_scale);
-        act_store1<T>(qrow, hh * dh + i + half, y2 * e.q_scale);
-      } else {
-        const int phys = ep_dst[u].x;   // -1: the prologue reported the row
-        if (phys < 0) continue;
-        const bool is_k = hh < e.H + e.Hkv;
-        const int g = is_k ? hh - e.H : hh - e.H - e.Hkv;
-        const size_t page = (size_t)phys * e.Hkv + g;
-        const int off = ep_dst[u].y;
-        if (is_k) {
-          T* kp = (T*)e.k_pages + (page * 16 + off) * dh;
-          kp[i] = from_f<T>(y1);
-          kp[i + half] = from_f<T>(y2);
-        } else {
-          T* vp = (T*)e.v_pages + page * dh * 16;
-          vp[(size_t)i * 16 + off] = from_f<T>(y1);
-          vp[(size_t)(i + half) * 16 + off] = from_f<T>(y2);
-        }
-      }
-    }
-  } else {  // EPI_LOGITS
-    // 8 threads per row, thread j over columns j, j + 8, ...; the 8 partial states
-    // meet in a fixed xor butterfly, so every thread of the row ends with the same
-    // values: largest (lowest index on ties), second largest (equal to the largest on
-    // a tie), then the sum of exp(v - largest).
-    const int nc = min(TC, a.N - cg * TC);
-    const int sub = threadIdx.x & 7;
-    for (int ml0 = 0; ml0 < 16 * MT; ml0 += 32) {
-      const int ml = ml0 + (threadIdx.x >> 3);
-      const bool row_ok = ml < 16 * MT;
-      float m1 = -INFINITY, m2 = -INFINITY;
-      int i1 = 0x7fffffff;
-      if (row_ok)
-        for (int c = sub; c < nc; c += 8) {
-          const float v = tile[ml][c];
-          if (v > m1) { m2 = m1; m1 = v; i1 = cg * TC + c; }
-          else if (v > m2) m2 = v;
-        }
+  for (int t = 0; t < WN; ++t) {
+    const int tile = min(cg * NT + wn * WN + t, ntiles - 1);
+    wp[t] = (const char*)a.W + (size_t)tile * ksteps * 1024 + lane * 16;
+  }
+  const char* ap[WM];
 #pragma unroll
-      for (int o = 1; o < 8; o <<= 1) {
-        const float om1 = __shfl_xor(m1, o), om2 = __shfl_xor(m2, o);
-        const int oi1 = __shfl_xor(i1, o);
-        const bool other_wins = om1 > m1 || (om1 == m1 && oi1 < i1);
-        const float lose = other_wins ? m1 : om1;   // the losing group's largest
-        m2 = fmaxf(fmaxf(m2, om2), lose);
-        if (other_wins) { m1 = om1; i1 = oi1; }
-      }
-      float se = 0.f;
-      if (row_ok)
-        for (int c = sub; c < nc; c += 8) se += __expf(tile[ml][c] - m1);
+  for (int mt = 0; mt < WM; ++mt) {
+    const int m = min(m_base + wm * 16 * WM + mt * 16 + r, a.M - 1);
+    const int row = a.a_rows ? a.a_rows[m] : m;
+    ap[mt] = (const char*)a.A + (size_t)row * a.lda * 4 + lg * AB;
+  }
+  u32x4 wb[D][WN], ab[D][WM][AL];
+  auto issue = [&](int j, u32x4 (&w)[WN], u32x4 (&av)[WM][AL]) {
 #pragma unroll
-      for (int o = 1; o < 8; o <<= 1) se += __shfl_xor(se, o);
-      const int m = m_base + ml;
-      if (row_ok && sub == 0 && m < a.M) a.stats[(size_t)m * a.n_groups + cg] = make_float4(m1, __int_as_float(i1), m2, se);
-    }
-    if (a.logits) {
-      for (int idx = threadIdx.x; idx < 16 * MT * TC; idx += 256) {
-        const int ml = idx / TC, c = idx % TC;
-        const int m = m_base + ml, n = cg * TC + c;
-        if (m < a.M && n < a.N) a.logits[(size_t)m * a.ldl + n] = tile[ml][c];
-      }
+    for (int t = 0; t < WN; ++t) w[t] = ld16_stream(wp[t] + (size_t)j * 1024);
+#pragma unroll
+    for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+      for (int h = 0; h < AL; ++h) av[mt][h] = ld16(ap[mt] + (size_t)j * (KS * 4) + 16 * h);
+  };
+  f32x4 acc[WM][WN];
+#pragma unroll
+  for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+    for (int t = 0; t < WN; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const u32x4 (&w)[WN], const u32x4 (&av)[WM][AL]) {
+#pragma unroll
+    for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+      for (int t = 0; t < WN; ++t)
+#pragma unroll
+        for (int h = 0; h < AL; ++h) acc[mt][t] = mma16<T>(av[mt][h], w[t], acc[mt][t]);
+  };
+  const int nk = ksteps;
+#pragma unroll
+  for (int u = 0; u < D - 1; ++u)
+    if (u < nk) issue(u, wb[u], ab[u]);
+  int j0 = 0;
+  for (; j0 + 2 * D - 2 < nk; j0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      issue(j0 + u + D - 1, wb[(u + D - 1) % D], ab[(u + D - 1) % D]);
+      compute(wb[u], ab[u]);
     }
   }
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int j = j0 + g * D + u;
+      if (j < nk) {
+        if (j + D - 1 < nk) issue(j + D - 1, wb[(u + D - 1) % D], ab[(u + D - 1) % D]);
+        compute(wb[u], ab[u]);
+      }
+    }
+
+  __shared__ float tile[16 * MT][TC + 1];
+#pragma unroll
+  for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+    for (int t = 0; t < WN; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) tile[wm * 16 * WM + mt * 16 + 4 * lg + v][wn * 16 * WN + t * 16 + r] = acc[mt][t][v];
+  __syncthreads();
+  gemm_epilogue<T, MT, NT, EPI>(a, tile, cg, 0, m_base, [&](int, int m, int i) {
+    if constexpr (EPI == EPI_QKV) return QkvItem{a.qkv.rope[(size_t)m * a.pair_n + i], a.qkv.kv_dst[m]};
+    else return QkvItem{};
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -355,7 +475,8 @@ struct Launch {
 
 template <typename T, int MT, int NT, int D, int EPI>
 static hipError_t launch_one(const Launch& L, const GemmArgs& a) {
-  if constexpr (gemm_lds_bytes(MT, NT) <= LDS_LIMIT) {
+  // the q/k/v epilogue is planned with two tiles per workgroup only
+  if constexpr (gemm_lds_bytes(MT, NT) <= LDS_LIMIT && (EPI != EPI_QKV || NT == 2)) {
     if (L.ev0) hipExtLaunchKernelGGL(gemm_stream<T, MT, NT, D, EPI>, L.grid, dim3(256), 0, L.s, L.ev0, L.ev1, 0, a);
     else gemm_stream<T, MT, NT, D, EPI><<<L.grid, 256, 0, L.s>>>(a);
     return hipGetLastError();
@@ -376,8 +497,20 @@ static hipError_t launch_mt(int MT, const Launch& L, const GemmArgs& a) {
   }
 }
 
+template <typename T, int WN, int D, int EPI>
+static hipError_t launch_tiled(const Launch& L, const GemmArgs& a) {
+  if (L.ev0) hipExtLaunchKernelGGL(gemm_tiled<T, WN, D, EPI>, L.grid, dim3(256), 0, L.s, L.ev0, L.ev1, 0, a);
+  else gemm_tiled<T, WN, D, EPI><<<L.grid, 256, 0, L.s>>>(a);
+  return hipGetLastError();
+}
+
 template <typename T, int EPI>
 static hipError_t launch_cfg(const GemmCfg& c, int MT, const Launch& L, const GemmArgs& a) {
+  if (c.tiled) {
+    if (c.NT == 4 && c.D == 2) return launch_tiled<T, 4, 2, EPI>(L, a);
+    if (c.NT == 8 && c.D == 2) return launch_tiled<T, 8, 2, EPI>(L, a);
+    return hipErrorInvalidValue;
+  }
   if (c.NT == 2 && c.D == 4) return launch_mt<T, 2, 4, EPI>(MT, L, a);
   if (c.NT == 4 && c.D == 2) return launch_mt<T, 4, 2, EPI>(MT, L, a);
   if (c.NT == 8 && c.D == 2) return launch_mt<T, 8, 2, EPI>(MT, L, a);

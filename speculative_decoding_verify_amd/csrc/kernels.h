@@ -51,9 +51,11 @@ struct GemmArgs {
   int n_groups;
 };
 
-// launch configuration: NT weight tiles per workgroup, D k steps in flight per wave
+// launch configuration: NT weight tiles per workgroup, D k steps in flight per wave;
+// tiled: the many-row kernel (128-row blocks; NT = MFMA column tiles per wave)
 struct GemmCfg {
   int NT, D;
+  bool tiled = false;
 };
 int gemm_lds_ok(int MT, int NT);
 // With ev_start / ev_stop set, the events are recorded by the dispatch itself at the

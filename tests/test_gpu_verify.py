@@ -50,6 +50,29 @@ def test_verify_parity(shape, lens, L_a, gamma):
     assert hd <= tol, hd
 
 
+@pytest.mark.parametrize("shape,lens,L_a,gamma", [
+    (MINI_BF16, (37, 70, 5, 0, 101), 6, 16),            # 110 rows, 85 logit rows: one ragged 128-row block
+    (MINI_F32, (9, 40, 3, 66, 12, 20, 1, 51, 30), 4, 16),  # 180 rows: two row blocks
+    (MINI_BF16_D128, (40, 17, 90, 3, 61, 8), 5, 15),    # 120 rows, 66 logit rows
+])
+def test_verify_parity_many_rows(shape, lens, L_a, gamma):
+    """A batch with more than 80 chunk rows takes the tiled many-row GEMM for every
+    projection (and, above 80 logit rows, for the LM head)."""
+    print(f"case {shape.name} lens={lens} L_a={L_a} gamma={gamma}", flush=True)
+    w = make_weights(shape, seed=111, gain_noise=0.1)
+    T = L_a + gamma
+    kvh = make_random_kv(shape, list(lens), capacity=max(lens) + T, seed=112)
+    toks = _tokens(len(lens), T, shape.vocab, 113)
+    g, o, ver, kv = run_pair(w, kvh, toks, L_a, perm_seed=114)
+    assert np.all(g["err"] == 0)
+    err, flagged, n = compare_logits(shape, g, o)
+    print(f"  logits rel err {err:.2e}; flagged {flagged}/{n}", flush=True)
+    compare_kv(shape, kv, o, list(lens), T)
+    tol = 2e-2 if shape.dtype == "bf16" else 1e-5
+    hd = np.max(np.abs(g["hidden"] - o["hidden"])) / np.max(np.abs(o["hidden"]))
+    assert hd <= tol, hd
+
+
 def test_attention_dominant_hidden():
     """Scaled q/k/o weights make attention dominate the residual stream, so a wrong
     attention kernel cannot hide under the FFN's contribution."""

@@ -783,14 +783,29 @@ template <typename T, int DH> constexpr int attn_cap() {
 template <typename T, int DH>
 int attn_shape(int NQT, int* nqw_out, int* nw_out) {
   constexpr int CAP = attn_cap<T, DH>();
-  int nqw = 1;
-  while ((NQT + nqw - 1) / nqw > 8 && nqw < CAP) ++nqw;
-  // query groups of at most 8 waves each, balanced; at least 4 waves per workgroup
-  // (waves without query tiles still help staging K/V)
-  const int n_qg = (NQT + 8 * nqw - 1) / (8 * nqw);
-  const int nw = std::max(4, (NQT + n_qg * nqw - 1) / (n_qg * nqw));
-  *nqw_out = nqw;
-  *nw_out = nw;
+  // query groups of at most 8 waves x CAP tiles; inside a group, the shape whose
+  // busiest SIMD (wave w runs on SIMD w % 4, and takes tiles w, w + nw, ...) carries
+  // the fewest query tiles per key tile, then the fewest tiles per wave (registers),
+  // then the fewest waves; at least 4 waves (waves without query tiles still stage K/V)
+  const int n_qg = (NQT + 8 * CAP - 1) / (8 * CAP);
+  const int Q = (NQT + n_qg - 1) / n_qg;
+  int best_nw = 8, best_nqw = CAP, best_load = 1 << 30;
+  for (int nqw = 1; nqw <= CAP; ++nqw)
+    for (int nw = 4; nw <= 8; ++nw) {
+      if (nw * nqw < Q) continue;
+      int load[4] = {0, 0, 0, 0};
+      for (int w = 0; w < nw; ++w)
+        for (int j = 0; j < nqw; ++j)
+          if (w + j * nw < Q) ++load[w % 4];
+      const int mx = std::max(std::max(load[0], load[1]), std::max(load[2], load[3]));
+      if (mx < best_load || (mx == best_load && (nqw < best_nqw || (nqw == best_nqw && nw < best_nw)))) {
+        best_load = mx;
+        best_nw = nw;
+        best_nqw = nqw;
+      }
+    }
+  *nqw_out = best_nqw;
+  *nw_out = best_nw;
   return n_qg;
 }
 

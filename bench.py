@@ -51,7 +51,7 @@ def gate_up_launch_bytes(sh, M):
 # each scaled by what the same counter reads for a plain 256 MiB device copy
 # (`bench.py --copy-calibration`).  Valid only for the kernel sources they were taken
 # on: the sha256 of the GEMM sources is checked at run time, else traffic is null.
-GATE_UP_TRAFFIC = {"sha256": "b62144e5e26e1b93f57db021de05f86146437d89d383ae4b7d47d54a3964ac60",
+GATE_UP_TRAFFIC = {"sha256": "ec4afa2dfebb3a3ca9d921d98213df06453ec65b48fd655a001843952e8438d6",
                    "fetch_kib": 34149.0, "fetch_factor": 262144.0 / 131084.0,
                    "write_kib": 1312.0, "write_factor": 262144.0 / 262144.0}
 GEMM_SOURCES = ("speculative_decoding_verify_amd/csrc/gemm.hip", "speculative_decoding_verify_amd/csrc/common.h",
@@ -371,7 +371,7 @@ def bench_c5(args, wl):
         "committed_tokens_per_pass": int((n_acc + 1).sum()) // 2,
         "pass_roofline": {"bound": "hbm", "bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
                           "peak_GBs": HBM_PEAK_GBS, "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "roofline": {"bound": "mfma", "kernel": "gemm_stream, SwiGLU epilogue (gate/up projection), 2624 rows",
+        "roofline": {"bound": "mfma", "kernel": "gemm_tiled, SwiGLU epilogue (gate/up projection), 2624 rows",
                      "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s", "frac": achieved / 2500.0,
                      "traffic": None, "flops_per_launch": gu_flops, "avg_launch_us": launch_us["gate_up"]},
         "gemm_launch_us": launch_us, "setup_s": setup_s,

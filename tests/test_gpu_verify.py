@@ -126,6 +126,36 @@ def test_tree_branch_and_greedy_commit():
         assert torch.equal(k_after, k_before[l][:n])
 
 
+@pytest.mark.parametrize("shape", [MINI_BF16, MINI_F32], ids=lambda s: s.name)
+def test_maximum_chunk_wide_tree(shape):
+    """The largest chunk (T = 128 rows) as a wide tree: 6 audio rows, a main draft of 62
+    and five branches of 12 hanging off different main rows, two batch rows with
+    different cached lengths (one empty).  Every chunk row is a logit row."""
+    w = make_weights(shape, seed=351)
+    L_a, gamma, nbr, blen = 6, 62, 5, 12
+    T = L_a + gamma + nbr * blen
+    assert T == sdv.binding.MAX_T
+    parent = [j - 1 for j in range(T)]
+    for k in range(nbr):
+        first = L_a + gamma + k * blen
+        parent[first] = L_a - 1 + 11 * k      # forks at the last audio row, main rows 11, 22, ...
+    lens = [77, 0]
+    kvh = make_random_kv(shape, lens, capacity=max(lens) + T, seed=352)
+    toks = _tokens(2, T, shape.vocab, 353)
+    g, o, ver, kv = run_pair(w, kvh, toks, L_a, parent=parent, logit_rows=range(T), perm_seed=354)
+    assert np.all(g["err"] == 0)
+    err, flagged, n = compare_logits(shape, g, o)
+    print(f"  T=128 tree: logits rel err {err:.2e}; flagged {flagged}/{n}", flush=True)
+    compare_kv(shape, kv, o, lens, T)
+    acc = sdv.accept_greedy(2, T, L_a, ver.tokens, ver.parent, ver.logit_rows, ver.argmax)
+    torch.cuda.synchronize()
+    rows = list(range(T))
+    for b in range(2):
+        ne, nxt, path, fl = greedy_expectation(toks[b], parent, L_a, rows, o["logits"][b])
+        if not fl:
+            assert int(acc["n"][b]) == ne and int(acc["next"][b]) == nxt
+
+
 @pytest.mark.parametrize("scenario", ["silence", "corrupt3", "random"])
 def test_greedy_scenarios(scenario):
     """Drafts = greedy decoding under silence.  Audio == silence: full acceptance plus the

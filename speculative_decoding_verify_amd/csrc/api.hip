@@ -70,6 +70,8 @@ GemmPlan plan_gemm(int M, int N, int K, bool bf, int epi) {
   // deeper register ring where the grid would otherwise be small (q/k/v and o
   // projections), more tiles per workgroup as the row tiles grow
   if (epi == EPI_QKV || (epi == EPI_PARTIAL && p.MT < 4 && ntiles <= 128 && K <= 4096)) p.cfg = GemmCfg{2, 4};
+  else if (epi == EPI_PARTIAL && K <= 4096) p.cfg = GemmCfg{4, 2};
+  else if (epi == EPI_LOGITS && p.MT <= 2) p.cfg = GemmCfg{4, 4};
   else if (p.MT >= (epi == EPI_LOGITS ? 3 : 4) && gemm_lds_ok(p.MT, 8)) p.cfg = GemmCfg{8, 2};
   else p.cfg = GemmCfg{4, 2};
   p.ncg = cdiv(ntiles, p.cfg.NT);
@@ -94,7 +96,7 @@ struct Plan {
   int n_qg;         // attention query groups per (sequence, kv head)
   bool attn_fused;  // split partials merged inside the attention kernel
   size_t part_floats;
-  size_t off_x, off_a, off_q, off_o, off_h, off_part, off_po, off_pml, off_stats, off_depth, off_anc,
+  size_t off_x, off_a, off_alm, off_q, off_o, off_h, off_part, off_po, off_pml, off_stats, off_depth, off_anc,
       off_lmrows, off_rope, off_cb, off_sem, off_kvdst, total;
   size_t n_sem;     // attention arrival counters: [layer][B][Hkv][n_qg]
 };
@@ -163,12 +165,15 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
   p.off_x = take((size_t)p.M * d * 4);
-  // activation rows take 4 bytes per value (bf16 hi/lo pairs or fp32); the codebook
-  // head appends its S stream-embedding rows
-  p.off_a = take((size_t)(p.M + p.S) * d * 4);
+  // activation operands take 4 bytes per value (bf16 hi/lo pairs or fp32) in whole
+  // 16-row tiles; the head operand holds the B * R logit rows and the codebook
+  // head's S stream-embedding rows
+  const size_t mpad = (size_t)cdiv(p.M, 16) * 16;
+  p.off_a = take(mpad * d * 4);
+  p.off_alm = take((size_t)cdiv(p.Mr + p.S, 16) * 16 * d * 4);
   p.off_q = take((size_t)p.M * qd * 4);
-  p.off_o = take((size_t)p.M * qd * 4);
-  p.off_h = take((size_t)p.M * F * 4);
+  p.off_o = take(mpad * qd * 4);
+  p.off_h = take(mpad * F * 4);
   p.off_part = take(p.part_floats * 4);
   const size_t nqs = (size_t)B * Hkv * p.n_splits * p.nq_pad;
   p.off_po = take(nqs * dh * 4);
@@ -176,7 +181,7 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
   p.off_stats = take((size_t)p.Mr * p.lm.ncg * 16);
   p.off_depth = take((size_t)T * 4);
   p.off_anc = take((size_t)T * 16);
-  p.off_lmrows = take((size_t)(p.Mr + p.S) * 4);
+  p.off_lmrows = take((size_t)p.Mr * 4);
   p.off_rope = take((size_t)p.M * (dh / 2) * 8);
   p.off_cb = p.S ? take((size_t)p.cb.S * (p.Mr + p.S) * m->codebook_size * 4) : o;
   p.off_sem = take(p.n_sem * 4);
@@ -215,12 +220,10 @@ sdv_status run_gemm(ProfEvents& pe, const Plan& P, const GemmPlan& g, GemmArgs a
   return SDV_OK;
 }
 
-GemmArgs gemm_args(const void* A, int lda, const int32_t* a_rows, int M, const void* W, int N, int K) {
+GemmArgs gemm_args(const void* A, int M, const void* W, int N, int K) {
   GemmArgs a;
   memset(&a, 0, sizeof a);
   a.A = A;
-  a.lda = lda;
-  a.a_rows = a_rows;
   a.M = M;
   a.W = W;
   a.N = N;
@@ -267,6 +270,7 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
   char* w = (char*)ws;
   float* x = (float*)(w + P.off_x);
   void* act = w + P.off_a;
+  void* alm = w + P.off_alm;
   void* q = w + P.off_q;
   void* o = w + P.off_o;
   void* h = w + P.off_h;
@@ -291,9 +295,8 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
   }
   float2* rope = (float2*)(w + P.off_rope);
   {
-    const bool cbh = in->head == SDV_HEAD_CODEBOOK;
     PrologueArgs a{in->parent, in->logit_rows, kv->seq_len, B, T, R, depth, anc, lm_rows, rope, dh,
-                   m->rope_theta, out->err, cbh ? P.S : 0, M, sem, (int)P.n_sem,
+                   m->rope_theta, out->err, sem, (int)P.n_sem,
                    kv->block_table, kv->max_blocks, kv->n_blocks, in->max_ctx, kv_dst};
     SDV_LAUNCH(launch_prologue(a, s));
   }
@@ -301,19 +304,13 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
     EmbedArgs a{in->tokens, m->embed, m->layers[0].attn_norm, x, act, M, T, d, V, m->eps, out->err};
     SDV_LAUNCH(launch_embed_norm(P.bf, a, s));
   }
-  if (m->n_codebooks < 0) return fail(SDV_ERR_SHAPE, "n_codebooks < 0");
-  if (m->n_codebooks > 0) {
-    if (!m->codebook || !m->stream_emb) return fail(SDV_ERR_NULL, "codebook pointers NULL");
-    if (m->codebook_size < 2 || m->codebook_base < 0 || (long long)m->codebook_base + m->codebook_size > m->vocab)
-      return fail(SDV_ERR_SHAPE, "codebook size/base outside the vocabulary");
-  }
   for (int l = 0; l < m->n_layers; ++l) {
     const sdv_layer& L = m->layers[l];
     void* kp = (char*)kv->k_pages + l * layer_elems * P.eb;
     void* vp = (char*)kv->v_pages + l * layer_elems * P.eb;
     // q, k, v projections with rotary embedding and paged K/V append
     {
-      GemmArgs a = gemm_args(act, d, nullptr, M, L.wqkv, qd + 2 * kd, d);
+      GemmArgs a = gemm_args(act, M, L.wqkv, qd + 2 * kd, d);
       a.pair_n = dh / 2;
       a.qkv = QkvEpi{q, kp, vp, kv_dst, rope, B, T, H, Hkv, (float)(1.4426950408889634 / sqrt((double)dh))};
       if ((st = run_gemm(pe, P, P.qkv, a, s)) != SDV_OK) return st;
@@ -329,41 +326,46 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
       }
     }
     {
-      GemmArgs a = gemm_args(o, qd, nullptr, M, L.wo, d, qd);
+      GemmArgs a = gemm_args(o, M, L.wo, d, qd);
       a.out = part;
       if ((st = run_gemm(pe, P, P.o, a, s)) != SDV_OK) return st;
     }
     {
-      ResidNormArgs a{x, part, (long long)M * d, P.o.S, L.ffn_norm, act, nullptr, M, d, m->eps};
+      ResidNormArgs a{x, part, (long long)M * d, P.o.S, L.ffn_norm, act, nullptr, M, d, m->eps, nullptr, 0};
       SDV_LAUNCH(launch_resid_norm(P.bf, a, s));
     }
     // gate/up projections with the SwiGLU epilogue
     {
-      GemmArgs a = gemm_args(act, d, nullptr, M, L.wgu, 2 * F, d);
+      GemmArgs a = gemm_args(act, M, L.wgu, 2 * F, d);
       a.pair_n = F;
       a.out_act = h;
       if ((st = run_gemm(pe, P, P.gu, a, s)) != SDV_OK) return st;
     }
     {
-      GemmArgs a = gemm_args(h, F, nullptr, M, L.wd, d, F);
+      GemmArgs a = gemm_args(h, M, L.wd, d, F);
       a.out = part;
       if ((st = run_gemm(pe, P, P.dn, a, s)) != SDV_OK) return st;
     }
-    {
-      const bool last = l + 1 == m->n_layers;
-      const float* g = last ? m->final_norm : m->layers[l + 1].attn_norm;
-      ResidNormArgs a{x, part, (long long)M * d, P.dn.S, g, act, last ? out->hidden : nullptr, M, d, m->eps};
+    if (l + 1 < m->n_layers) {
+      ResidNormArgs a{x, part, (long long)M * d, P.dn.S, m->layers[l + 1].attn_norm, act, nullptr, M, d, m->eps,
+                      nullptr, 0};
+      SDV_LAUNCH(launch_resid_norm(P.bf, a, s));
+    } else {
+      // final norm of the logit rows only, gathered into the head operand (rows
+      // b * R + r), plus the hidden rows when asked for
+      ResidNormArgs a{x, part, (long long)M * d, P.dn.S, m->final_norm, alm, out->hidden, M, d, m->eps,
+                      lm_rows, P.Mr};
       SDV_LAUNCH(launch_resid_norm(P.bf, a, s));
     }
   }
   if (in->head == SDV_HEAD_CODEBOOK) {
     // codebook heads: W_cb on the final-normed logit rows and on the stream
-    // embeddings (rows M..M+S-1 of the activation buffer), then merge + statistics
+    // embeddings (rows Mr..Mr+S-1 of the head operand), then merge + statistics
     const int S = P.S, Vc = m->codebook_size;
     float* cbl = (float*)(w + P.off_cb);
-    StreamRowsArgs sr{m->stream_emb, S, d, act, M};
+    StreamRowsArgs sr{m->stream_emb, S, d, alm, P.Mr};
     SDV_LAUNCH(launch_stream_rows(P.bf, sr, s));
-    GemmArgs a = gemm_args(act, d, lm_rows, P.Mr + S, m->codebook, Vc, d);
+    GemmArgs a = gemm_args(alm, P.Mr + S, m->codebook, Vc, d);
     a.out = cbl;
     if ((st = run_gemm(pe, P, P.cb, a, s)) != SDV_OK) return st;
     CbMergeArgs c{cbl, (long long)(P.Mr + S) * Vc, P.cb.S, B, R, S, Vc, in->cfg_partner, in->cfg_w,
@@ -371,7 +373,7 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
     SDV_LAUNCH(launch_cb_merge(c, s));
   } else {
     {
-      GemmArgs a = gemm_args(act, d, lm_rows, P.Mr, m->lm_head, V, d);
+      GemmArgs a = gemm_args(alm, P.Mr, m->lm_head, V, d);
       a.logits = out->logits;
       a.stats = stats;
       if ((st = run_gemm(pe, P, P.lm, a, s)) != SDV_OK) return st;

@@ -31,7 +31,7 @@
 namespace sdv {
 
 // Query operand of one lane.  The q buffer holds the queries pre-scaled by
-// log2(e)/sqrt(dh) in the activation format (4 bytes per value), so for bf16 the 8
+// log2(e)/sqrt(dh) in the query-row format (4 bytes per value), so for bf16 the 8
 // values of lane group lg in k step ks are one 16-byte hi load and one 16-byte lo
 // load; for fp32 the 4 values are one load.  `off` is the value index of the head's
 // first value (row * H * dh + head * dh).
@@ -144,7 +144,7 @@ SDV_DEV void attn_merge(const AttnArgs& a, int b, int g, int qi0, int qi1, float
       }
     }
     const int qi = qi0 + i, t = qi / G, h = g * G + qi % G;
-    act_store4<T>((char*)a.o + (size_t)(b * a.T + t) * a.H * DH * 4, h * DH + 4 * c, acc);
+    act_store4<T>(a.o, a.H * DH, b * a.T + t, h * DH + 4 * c, acc);
   }
 }
 
@@ -193,7 +193,7 @@ SDV_DEV void attn_merge8(const AttnArgs& a, int b, int g, int qi0, int qi1) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] *= inv;
     const int qi = qi0 + i, t = qi / G, h = g * G + qi % G;
-    act_store4<T>((char*)a.o + (size_t)(b * a.T + t) * a.H * DH * 4, h * DH + 4 * c, acc);
+    act_store4<T>(a.o, a.H * DH, b * a.T + t, h * DH + 4 * c, acc);
   };
   Buf A, B;
   const int step = blockDim.x;
@@ -446,12 +446,12 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
     if (direct) {
       if (qi < nq) {
         const float inv = 1.f / l;
-        char* orow = (char*)a.o + (size_t)(b * a.T + qi / G) * a.H * DH * 4;
+        const int orow = b * a.T + qi / G;
         const int h = g * G + qi % G;
 #pragma unroll
         for (int dt = 0; dt < DH / 16; ++dt) {
           const float v[4] = {acc[j][dt][0] * inv, acc[j][dt][1] * inv, acc[j][dt][2] * inv, acc[j][dt][3] * inv};
-          act_store4<T>(orow, h * DH + dt * 16 + 4 * lg, v);
+          act_store4<T>(a.o, a.H * DH, orow, h * DH + dt * 16 + 4 * lg, v);
         }
       }
     } else {
@@ -704,7 +704,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     for (int k = 0; k < 4; ++k) { wk[k] = exp2f(sm[k][j][ln] - M); L += wk[k] * sl[k][j][ln]; }
     const uint32_t pr = (uint32_t)(split * a.nq_pad + qi);
     const float inv = 1.f / L;
-    char* orow = (char*)a.o + (size_t)(b * a.T + min(qi, nq - 1) / G) * a.H * DH * 4;
+    const int orow = b * a.T + min(qi, nq - 1) / G;
     const int h = g * G + qi % G;
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt) {
@@ -719,7 +719,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       if (direct) {
         if (qi < nq) {
           const float vo[4] = {v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv};
-          act_store4<T>(orow, h * DH + d0, vo);
+          act_store4<T>(a.o, a.H * DH, orow, h * DH + d0, vo);
         }
       } else {
         st_dev16(rpo, (pr * DH + d0) * 4,
@@ -765,7 +765,7 @@ __global__ __launch_bounds__(DH) void attn_combine(CombineArgs a) {
       num += wgt * v[s];
     }
   }
-  act_store1<T>((char*)a.o + (size_t)row * a.H * DH * 4, h * DH + threadIdx.x, num / den);
+  act_store1<T>(a.o, a.H * DH, row, h * DH + threadIdx.x, num / den);
 }
 
 // the register path serves heads with few query tiles (its merge buffers and

@@ -70,62 +70,83 @@ SDV_DEV void split_hi_lo(u32x4 a, u32x4 b, u32x4& hi, u32x4& lo) {
   lo.x = l[0] | (l[1] << 16); lo.y = l[2] | (l[3] << 16); lo.z = l[4] | (l[5] << 16); lo.w = l[6] | (l[7] << 16);
 }
 
-// Activation rows: bf16 models store each value as a split pair (k group g of 8
-// values at bytes g*32: 8 bf16 hi parts, then 8 bf16 lo parts), fp32 models store
-// fp32.  act_store1 writes value k of a row, act_store8 values k0..k0+7 (k0 % 8 == 0).
+// Split pairs: a bf16 model carries each activation value as x = hi + lo + O(2^-16 |x|),
+// two bf16 numbers that enter a bf16 MFMA as two operands.
 SDV_DEV void split1(float x, bf16& hi, bf16& lo) {
   hi = f2bf(x);
   lo = f2bf(x - bf2f(hi));
 }
-template <typename T> SDV_DEV void act_store1(void* row, int k, float x);
-template <> SDV_DEV void act_store1<float>(void* row, int k, float x) { ((float*)row)[k] = x; }
-template <> SDV_DEV void act_store1<bf16>(void* row, int k, float x) {
+SDV_DEV uint32_t pack2(bf16 a, bf16 b) { return (uint32_t)a | ((uint32_t)b << 16); }
+
+// Query rows (read by the attention kernels): one row per chunk row; bf16 models
+// store k group g (8 values) at bytes g * 32 as 8 hi parts then 8 lo parts, fp32
+// models store fp32.
+template <typename T> SDV_DEV void row_store1(void* row, int k, float x);
+template <> SDV_DEV void row_store1<float>(void* row, int k, float x) { ((float*)row)[k] = x; }
+template <> SDV_DEV void row_store1<bf16>(void* row, int k, float x) {
   bf16 hi, lo;
   split1(x, hi, lo);
   bf16* g = (bf16*)row + (k >> 3) * 16 + (k & 7);
   g[0] = hi;
   g[8] = lo;
 }
-template <typename T> SDV_DEV void act_store8(void* row, int k0, const float (&x)[8]);
-template <> SDV_DEV void act_store8<float>(void* row, int k0, const float (&x)[8]) {
-  float4* p = (float4*)((float*)row + k0);
-  p[0] = make_float4(x[0], x[1], x[2], x[3]);
-  p[1] = make_float4(x[4], x[5], x[6], x[7]);
+
+// GEMM activation operands ("A": M rows x K values, 4 bytes per value) are stored
+// in the lane order of the MFMA A operand, so that every wave load of a GEMM reads
+// one contiguous kilobyte.  Rows go 16 to a row tile; row tile rt holds the K / KS
+// k steps (KS = 32 bf16, 16 fp32) one after another, 64 * KS bytes each:
+//   bf16: 1 KB of hi parts, then 1 KB of lo parts; lane l's 16 bytes in each hold
+//         row 16 rt + l % 16, k = 32 s + 8 (l / 16) + 0..7;
+//   fp32: 1 KB; lane l's 16 bytes hold row 16 rt + l % 16, k = 16 s + 4 (l / 16) + 0..3.
+// A buffer of M rows takes 16 * ceil(M / 16) * K * 4 bytes.  Rows past M in the last
+// tile are never written, and the GEMMs never read them.
+template <typename T> SDV_DEV size_t act_pos(int K, int m, int k);
+template <> SDV_DEV size_t act_pos<bf16>(int K, int m, int k) {
+  return ((size_t)(m >> 4) * (K >> 5) + (k >> 5)) * 2048 + (size_t)((((k >> 3) & 3) << 4) | (m & 15)) * 16 +
+         (k & 7) * 2;
 }
-template <> SDV_DEV void act_store8<bf16>(void* row, int k0, const float (&x)[8]) {
-  uint32_t h[8], l[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    bf16 hb, lb;
-    split1(x[e], hb, lb);
-    h[e] = hb;
-    l[e] = lb;
-  }
-  u32x4 hi, lo;
-  hi.x = h[0] | (h[1] << 16); hi.y = h[2] | (h[3] << 16); hi.z = h[4] | (h[5] << 16); hi.w = h[6] | (h[7] << 16);
-  lo.x = l[0] | (l[1] << 16); lo.y = l[2] | (l[3] << 16); lo.z = l[4] | (l[5] << 16); lo.w = l[6] | (l[7] << 16);
-  char* g = (char*)row + (k0 >> 3) * 32;
-  st16(g, hi);
-  st16(g + 16, lo);
+template <> SDV_DEV size_t act_pos<float>(int K, int m, int k) {
+  return ((size_t)(m >> 4) * (K >> 4) + (k >> 4)) * 1024 + (size_t)((((k >> 2) & 3) << 4) | (m & 15)) * 16 +
+         (k & 3) * 4;
 }
 
-// act_store4: values k0..k0+3 of a row (k0 % 4 == 0)
-template <typename T> SDV_DEV void act_store4(void* row, int k0, const float (&x)[4]);
-template <> SDV_DEV void act_store4<float>(void* row, int k0, const float (&x)[4]) {
-  *(float4*)((float*)row + k0) = make_float4(x[0], x[1], x[2], x[3]);
+// act_store1: value k of row m; act_store4: values k0..k0+3 (k0 % 4 == 0);
+// act_store8: values k0..k0+7 (k0 % 8 == 0)
+template <typename T> SDV_DEV void act_store1(void* a, int K, int m, int k, float x);
+template <> SDV_DEV void act_store1<float>(void* a, int K, int m, int k, float x) {
+  *(float*)((char*)a + act_pos<float>(K, m, k)) = x;
 }
-template <> SDV_DEV void act_store4<bf16>(void* row, int k0, const float (&x)[4]) {
-  uint32_t h[4], l[4];
+template <> SDV_DEV void act_store1<bf16>(void* a, int K, int m, int k, float x) {
+  bf16 hi, lo;
+  split1(x, hi, lo);
+  char* p = (char*)a + act_pos<bf16>(K, m, k);
+  *(bf16*)p = hi;
+  *(bf16*)(p + 1024) = lo;
+}
+template <typename T> SDV_DEV void act_store4(void* a, int K, int m, int k0, const float (&x)[4]);
+template <> SDV_DEV void act_store4<float>(void* a, int K, int m, int k0, const float (&x)[4]) {
+  *(float4*)((char*)a + act_pos<float>(K, m, k0)) = make_float4(x[0], x[1], x[2], x[3]);
+}
+template <> SDV_DEV void act_store4<bf16>(void* a, int K, int m, int k0, const float (&x)[4]) {
+  bf16 h[4], l[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    bf16 hb, lb;
-    split1(x[e], hb, lb);
-    h[e] = hb;
-    l[e] = lb;
-  }
-  bf16* g = (bf16*)row + (k0 >> 3) * 16 + (k0 & 7);
-  *(uint2*)g = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-  *(uint2*)(g + 8) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+  for (int e = 0; e < 4; ++e) split1(x[e], h[e], l[e]);
+  char* p = (char*)a + act_pos<bf16>(K, m, k0);
+  *(uint2*)p = make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
+  *(uint2*)(p + 1024) = make_uint2(pack2(l[0], l[1]), pack2(l[2], l[3]));
+}
+template <typename T> SDV_DEV void act_store8(void* a, int K, int m, int k0, const float (&x)[8]);
+template <> SDV_DEV void act_store8<float>(void* a, int K, int m, int k0, const float (&x)[8]) {
+  *(float4*)((char*)a + act_pos<float>(K, m, k0)) = make_float4(x[0], x[1], x[2], x[3]);
+  *(float4*)((char*)a + act_pos<float>(K, m, k0 + 4)) = make_float4(x[4], x[5], x[6], x[7]);
+}
+template <> SDV_DEV void act_store8<bf16>(void* a, int K, int m, int k0, const float (&x)[8]) {
+  bf16 h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) split1(x[e], h[e], l[e]);
+  char* p = (char*)a + act_pos<bf16>(K, m, k0);
+  st16(p, u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])});
+  st16(p + 1024, u32x4{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])});
 }
 
 // ---------------------------------------------------------------------------

@@ -1,8 +1,8 @@
 // Row-wise kernels of the verify forward: prologue (tree bookkeeping and the
 // rotary table), embedding + first norm, residual add + RMSNorm, and the LM-head
 // statistics reduction.  The residual stream is fp32; normalised rows are written
-// in the activation format of the GEMMs (bf16 hi/lo pairs for bf16 models, fp32
-// otherwise).
+// in the activation tile format of the GEMMs (bf16 hi/lo pairs for bf16 models, fp32
+// otherwise; common.h).
 //
 // Every split-K reduction sums the partials in split order 0..S-1 so results are
 // deterministic.
@@ -58,7 +58,6 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
       if (row < 0 || row >= a.T) { set_err(a.err, b, 0x2); row = 0; }
       a.lm_rows[i] = b * a.T + row;
     }
-    for (int i = threadIdx.x; i < a.n_extra; i += blockDim.x) a.lm_rows[a.B * a.R + i] = a.extra_base + i;
     if (bad)
       for (int b = threadIdx.x; b < a.B; b += blockDim.x) set_err(a.err, b, 0x2);
   }
@@ -97,7 +96,7 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // RMSNorm of one fp32 row held in registers (256 threads, PER elements each,
-// element c = threadIdx.x * PER + i), stored in the activation format of T.
+// element c = threadIdx.x * PER + i), stored as row m of an activation operand.
 // The thread's PER gain values, loaded up front (before the block reduction's
 // barrier, which loads cannot cross).
 template <int PER>
@@ -111,7 +110,8 @@ SDV_DEV void load_gain(const float* gain, int d, float (&g)[PER]) {
 }
 
 template <typename T, int PER>
-SDV_DEV void norm_store(const float (&v)[PER], int d, const float (&gain)[PER], void* out_row, float eps, float* red) {
+SDV_DEV void norm_store(const float (&v)[PER], int d, const float (&gain)[PER], void* out, int m, float eps,
+                        float* red) {
   static_assert(PER % 8 == 0, "whole k groups per thread");
   float ss = 0.f;
 #pragma unroll
@@ -125,7 +125,7 @@ SDV_DEV void norm_store(const float (&v)[PER], int d, const float (&gain)[PER], 
       float y[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[e] = v[g * 8 + e] * rs * gain[g * 8 + e];
-      act_store8<T>(out_row, c0 + g * 8, y);
+      act_store8<T>(out, d, m, c0 + g * 8, y);
     }
   }
 }
@@ -149,16 +149,20 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(EmbedArgs a) {
     v[i] = c0 < a.d ? to_f<T>(e[c0 + i]) : 0.f;
     if (c0 < a.d) a.x[(size_t)m * a.d + c0 + i] = v[i];
   }
-  norm_store<T, PER>(v, a.d, gn, (char*)a.a + (size_t)m * a.d * 4, a.eps, red);
+  norm_store<T, PER>(v, a.d, gn, a.a, m, a.eps, red);
 }
 
-// x += sum of the S split partials (in split order), then RMSNorm -> a.  Each
-// thread owns PER consecutive columns; all partial loads are issued before use.
+// x + sum of the S split partials (in split order), then RMSNorm -> a.  Each thread
+// owns PER consecutive columns; all partial loads are issued before use.  Block j:
+// without a.rows, row j (x updated in place); with a.rows, output row j < n_rows
+// normalises source row rows[j], and the blocks after those write hidden rows.
 template <typename T, int PER>
 __global__ __launch_bounds__(256) void resid_norm_kernel(ResidNormArgs a) {
   constexpr int MAXS = 16;
   __shared__ float red[8];
-  const int m = blockIdx.x;
+  const bool gather = a.rows != nullptr;
+  const bool hidden_only = gather && (int)blockIdx.x >= a.n_rows;
+  const int m = !gather ? blockIdx.x : hidden_only ? blockIdx.x - a.n_rows : a.rows[blockIdx.x];
   const int c0 = threadIdx.x * PER;
   const bool on = c0 < a.d;
   float v[PER], gn[PER];
@@ -186,30 +190,30 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(ResidNormArgs a) {
           acc4[q].x += pv[s][q].x; acc4[q].y += pv[s][q].y; acc4[q].z += pv[s][q].z; acc4[q].w += pv[s][q].w;
         }
       }
-    float4* xp = (float4*)(a.x + (size_t)m * a.d + c0);
 #pragma unroll
     for (int q = 0; q < PER / 4; ++q) {
       float4 x = x0[q];
       x.x += acc4[q].x; x.y += acc4[q].y; x.z += acc4[q].z; x.w += acc4[q].w;
-      xp[q] = x;
-      if (a.hidden) ((float4*)(a.hidden + (size_t)m * a.d + c0))[q] = x;
+      if (!gather) ((float4*)(a.x + (size_t)m * a.d + c0))[q] = x;
+      if (hidden_only) ((float4*)(a.hidden + (size_t)m * a.d + c0))[q] = x;
       v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
     }
   } else {
 #pragma unroll
     for (int i = 0; i < PER; ++i) v[i] = 0.f;
   }
-  norm_store<T, PER>(v, a.d, gn, (char*)a.a + (size_t)m * a.d * 4, a.eps, red);
+  if (hidden_only) return;   // uniform over the block
+  norm_store<T, PER>(v, a.d, gn, a.a, blockIdx.x, a.eps, red);
 }
 
 // PER columns per thread: the smallest of 8, 16, 24, 32 with 256 * PER >= d and
 // d % PER == 0 (d is a multiple of 64, so PER = 8 always divides it)
 template <typename T>
-static hipError_t launch_rows(bool resid, int d, int M, const void* args, hipStream_t s) {
-#define SDV_ROWS(P)                                                                     \
-  if (256 * P >= d && d % P == 0) {                                                     \
-    if (resid) resid_norm_kernel<T, P><<<M, 256, 0, s>>>(*(const ResidNormArgs*)args); \
-    else embed_norm_kernel<T, P><<<M, 256, 0, s>>>(*(const EmbedArgs*)args);           \
+static hipError_t launch_rows(bool resid, int d, int blocks, const void* args, hipStream_t s) {
+#define SDV_ROWS(P)                                                                          \
+  if (256 * P >= d && d % P == 0) {                                                          \
+    if (resid) resid_norm_kernel<T, P><<<blocks, 256, 0, s>>>(*(const ResidNormArgs*)args); \
+    else embed_norm_kernel<T, P><<<blocks, 256, 0, s>>>(*(const EmbedArgs*)args);           \
     return hipGetLastError();                                                           \
   }
   SDV_ROWS(8) SDV_ROWS(16) SDV_ROWS(24) SDV_ROWS(32)
@@ -221,8 +225,9 @@ hipError_t launch_embed_norm(bool is_bf16, const EmbedArgs& a, hipStream_t s) {
   return is_bf16 ? launch_rows<bf16>(false, a.d, a.M, &a, s) : launch_rows<float>(false, a.d, a.M, &a, s);
 }
 hipError_t launch_resid_norm(bool is_bf16, const ResidNormArgs& a, hipStream_t s) {
-  if (a.S > 16) return hipErrorInvalidValue;
-  return is_bf16 ? launch_rows<bf16>(true, a.d, a.M, &a, s) : launch_rows<float>(true, a.d, a.M, &a, s);
+  if (a.S > 16 || (a.rows && a.n_rows < 1)) return hipErrorInvalidValue;
+  const int blocks = a.rows ? a.n_rows + (a.hidden ? a.M : 0) : a.M;
+  return is_bf16 ? launch_rows<bf16>(true, a.d, blocks, &a, s) : launch_rows<float>(true, a.d, blocks, &a, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -287,7 +292,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void stream_rows_kernel(StreamRowsArgs a) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.S * a.d; i += gridDim.x * blockDim.x) {
     const int s = i / a.d, k = i % a.d;
-    act_store1<T>((char*)a.act + (size_t)(a.first_row + s) * a.d * 4, k, a.e[i]);
+    act_store1<T>(a.act, a.d, a.first_row + s, k, a.e[i]);
   }
 }
 

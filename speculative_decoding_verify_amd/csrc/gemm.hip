@@ -6,7 +6,8 @@
 //   * W is packed once at load time into 1 KB tiles (16 rows x one k step) laid out
 //     in lane order, so each wave load instruction reads one contiguous kilobyte that
 //     is already the B operand of a 16x16 MFMA;
-//   * the activations arrive in the operand format too: bf16 models store each value
+//   * the activations arrive in the operand format too (the tile format of
+//     common.h, one contiguous kilobyte per wave load): bf16 models store each value
 //     as a bf16 hi/lo pair (two MFMAs; the product carries ~16 significant bits of the
 //     activation, only the weights are bf16), fp32 models use the fp32 MFMA;
 //   * the four waves of a workgroup take every fourth k step of the workgroup's range;
@@ -23,11 +24,11 @@
 //   QKV      rotary embedding on q and k: packed rows 0-7 of a tile are the first
 //            members (element i) and rows 8-15 the second members (element i + dh/2)
 //            of 8 rotation pairs; q scaled by log2(e)/sqrt(dh) and written in the
-//            activation format, k and v rounded to the cache type and appended to
+//            query-row format, k and v rounded to the cache type and appended to
 //            the paged cache (k token-major, v transposed inside the page) at the
 //            page and slot the prologue resolved for the row;
 //   SWIGLU   rows 0-7 of a tile are gate rows f, rows 8-15 the up rows of the same f:
-//            h = silu(gate) * up, stored in the activation format;
+//            h = silu(gate) * up, stored in the activation tile format;
 //   LOGITS   fp32 logits plus per-(row, column group) statistics: largest value, its
 //            index (lowest on ties), second-largest value and sum of exp(v - largest).
 #include <hip/hip_ext.h>
@@ -68,7 +69,7 @@ SDV_DEV void gemm_epilogue(const GemmArgs& a, float (*tile)[16 * NT + 1], int cg
       const float gt = tile[ml][t * 16 + i];
       const float up = tile[ml][t * 16 + 8 + i];
       const float sl = gt / (1.f + expf(-gt));
-      act_store1<T>((char*)a.out_act + (size_t)m * a.pair_n * 4, f, sl * up);
+      act_store1<T>(a.out_act, a.pair_n, m, f, sl * up);
     }
   } else if constexpr (EPI == EPI_QKV) {
     const QkvEpi& e = a.qkv;
@@ -96,8 +97,8 @@ SDV_DEV void gemm_epilogue(const GemmArgs& a, float (*tile)[16 * NT + 1], int cg
       }
       if (hh < e.H) {
         char* qrow = (char*)e.q + (size_t)m * e.H * dh * 4;
-        act_store1<T>(qrow, hh * dh + i, y1 * e.q_scale);
-        act_store1<T>(qrow, hh * dh + i + half, y2 * e.q_scale);
+        row_store1<T>(qrow, hh * dh + i, y1 * e.q_scale);
+        row_store1<T>(qrow, hh * dh + i + half, y2 * e.q_scale);
       } else {
         const int phys = in.dst.x;   // -1: the prologue reported the row
         if (phys < 0) continue;
@@ -165,7 +166,6 @@ template <typename T, int MT, int NT, int D, int EPI>
 __global__ __launch_bounds__(256) void gemm_stream(GemmArgs a) {
   constexpr bool BF = sizeof(T) == 2;
   constexpr int KS = BF ? 32 : 16;   // k values per step (one 1 KB weight tile)
-  constexpr int AB = BF ? 32 : 16;   // activation bytes per lane group per row per step
   constexpr int TC = 16 * NT;        // packed columns of the workgroup
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -185,12 +185,15 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs a) {
     const int tile = min(cg * NT + t, ntiles - 1);
     wp[t] = (const char*)a.W + ((size_t)tile * ksteps + s0 + wave) * 1024 + lane * 16;
   }
+  // activation k steps are 64 * KS bytes apart in a row tile (tile format); lanes of
+  // rows past M read the last row's chunk (same address, no extra traffic)
+  const int row_tiles = (a.M + 15) >> 4;
   const char* ap[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int m = min(m_base + mt * 16 + r, a.M - 1);
-    const int row = a.a_rows ? a.a_rows[m] : m;
-    ap[mt] = (const char*)a.A + (size_t)row * a.lda * 4 + (size_t)(s0 + wave) * KS * 4 + lg * AB;
+    const int rt = min(blockIdx.z * MT + mt, row_tiles - 1);
+    const int rr = min(r, a.M - 1 - rt * 16);
+    ap[mt] = (const char*)a.A + ((size_t)rt * ksteps + s0 + wave) * (64 * KS) + (lg * 16 + rr) * 16;
   }
 
   constexpr int AL = BF ? 2 : 1;
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int h = 0; h < AL; ++h) av[mt][h] = ld16(ap[mt] + (size_t)j * (KS * 16) + 16 * h);
+      for (int h = 0; h < AL; ++h) av[mt][h] = ld16(ap[mt] + (size_t)j * (4 * 64 * KS) + 1024 * h);
   };
   f32x4 acc[MT][NT];
 #pragma unroll
@@ -321,7 +324,6 @@ template <typename T, int WN, int D, int EPI>
 __global__ __launch_bounds__(256) void gemm_tiled(GemmArgs a) {
   constexpr bool BF = sizeof(T) == 2;
   constexpr int KS = BF ? 32 : 16;
-  constexpr int AB = BF ? 32 : 16;   // activation bytes per lane group per row per step
   constexpr int AL = BF ? 2 : 1;
   constexpr int WM = 4;              // MFMA row tiles per wave
   constexpr int MT = 2 * WM, NT = 2 * WN;
@@ -341,12 +343,13 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmArgs a) {
     const int tile = min(cg * NT + wn * WN + t, ntiles - 1);
     wp[t] = (const char*)a.W + (size_t)tile * ksteps * 1024 + lane * 16;
   }
+  const int row_tiles = (a.M + 15) >> 4;
   const char* ap[WM];
 #pragma unroll
   for (int mt = 0; mt < WM; ++mt) {
-    const int m = min(m_base + wm * 16 * WM + mt * 16 + r, a.M - 1);
-    const int row = a.a_rows ? a.a_rows[m] : m;
-    ap[mt] = (const char*)a.A + (size_t)row * a.lda * 4 + lg * AB;
+    const int rt = min(blockIdx.x * MT + wm * WM + mt, row_tiles - 1);
+    const int rr = min(r, a.M - 1 - rt * 16);   // rows past M: the last row's chunk
+    ap[mt] = (const char*)a.A + (size_t)rt * ksteps * (64 * KS) + (lg * 16 + rr) * 16;
   }
   u32x4 wb[D][WN], ab[D][WM][AL];
   auto issue = [&](int j, u32x4 (&w)[WN], u32x4 (&av)[WM][AL]) {
@@ -355,7 +358,7 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < WM; ++mt)
 #pragma unroll
-      for (int h = 0; h < AL; ++h) av[mt][h] = ld16(ap[mt] + (size_t)j * (KS * 4) + 16 * h);
+      for (int h = 0; h < AL; ++h) av[mt][h] = ld16(ap[mt] + (size_t)j * (64 * KS) + 1024 * h);
   };
   f32x4 acc[WM][WN];
 #pragma unroll
@@ -513,6 +516,10 @@ static hipError_t launch_cfg(const GemmCfg& c, int MT, const Launch& L, const Ge
   }
   if (c.NT == 2 && c.D == 4) return launch_mt<T, 2, 4, EPI>(MT, L, a);
   if (c.NT == 4 && c.D == 2) return launch_mt<T, 4, 2, EPI>(MT, L, a);
+  if constexpr (EPI == EPI_LOGITS) {   // LM head on one or two row tiles: deeper ring
+    if (c.NT == 4 && c.D == 4 && MT == 1) return launch_one<T, 1, 4, 4, EPI>(L, a);
+    if (c.NT == 4 && c.D == 4 && MT == 2) return launch_one<T, 2, 4, 4, EPI>(L, a);
+  }
   if (c.NT == 8 && c.D == 2) return launch_mt<T, 8, 2, EPI>(MT, L, a);
   return hipErrorInvalidValue;
 }

@@ -9,7 +9,7 @@ enum { EPI_PARTIAL = 0, EPI_LOGITS = 1, EPI_QKV = 2, EPI_SWIGLU = 3 };
 
 // QKV epilogue: rotary embedding + q write + paged K/V append
 struct QkvEpi {
-  void* q;                  // [M, H*dh] queries times q_scale, in the activation format
+  void* q;                  // [M, H*dh] queries times q_scale, query-row format (common.h)
   void* k_pages;            // this layer: [n_blocks][Hkv][16][dh]
   void* v_pages;            //             [n_blocks][Hkv][dh][16]
   const int2* kv_dst;       // [B*T] (physical page, slot in page) of each chunk row, page -1: none
@@ -18,11 +18,9 @@ struct QkvEpi {
   float q_scale;            // log2(e) / sqrt(dh): attention works in the exp2 domain
 };
 
-// Activation operands of the GEMMs ("A"), one row per chunk row, K values each:
-//   bf16 models: split pairs -- k group g (8 values) of a row occupies 32 bytes at
-//     g * 32: 8 bf16 "hi" parts then 8 bf16 "lo" parts, x = hi + lo + O(2^-16 |x|);
-//   fp32 models: plain fp32.
-// Either way a row takes 4 bytes per k; lda counts k values.
+// Activation operands of the GEMMs ("A", M rows x K values) use the tile format of
+// common.h: bf16 models carry split pairs (x = hi + lo + O(2^-16 |x|)), fp32 models
+// fp32, 16-row tiles in MFMA lane order.
 //
 // Weights are packed in 1 KB tiles of 16 rows x KS k values (KS = 32 bf16 / 16 fp32):
 // tile (n / 16, k / KS) sits at ((n / 16) * (K / KS) + k / KS) * 1024 bytes; inside,
@@ -31,9 +29,7 @@ struct QkvEpi {
 // the two members of 8 pairs into one tile: rows 0-7 the first members, rows 8-15
 // the second members of the same pairs.
 struct GemmArgs {
-  const void* A;            // activation rows (format above)
-  int lda;                  // row stride in k values
-  const int32_t* a_rows;    // nullable: output row m reads A row a_rows[m]
+  const void* A;            // activation operand, M rows x K (tile format)
   int M;
   const void* W;            // packed weight tiles
   int N;                    // output columns (packed rows) that are written
@@ -43,7 +39,7 @@ struct GemmArgs {
   float* out;               // PARTIAL: out[split * out_split_stride + m * ldo + n]
   long long out_split_stride;
   int ldo;
-  void* out_act;            // SWIGLU: h [M, F] in the activation format
+  void* out_act;            // SWIGLU: h [M, F] in the activation tile format
   QkvEpi qkv;               // QKV epilogue arguments
   float* logits;            // LOGITS: logits[m * ldl + n] (nullable)
   int ldl;
@@ -77,7 +73,7 @@ struct PackArgs {
 hipError_t launch_pack(bool is_bf16, const PackArgs& a, hipStream_t s);
 
 struct AttnArgs {
-  const void* q;            // [B*T, H*dh] queries pre-scaled by log2(e)/sqrt(dh), activation format
+  const void* q;            // [B*T, H*dh] queries pre-scaled by log2(e)/sqrt(dh), query-row format
   const void* k_pages;      // this layer's pages: [n_blocks][Hkv][16][dh]
   const void* v_pages;      //                      [n_blocks][Hkv][dh][16]
   const int32_t* block_table;
@@ -96,7 +92,7 @@ struct AttnArgs {
   // arrival counter per (sequence, kv head, query group), zero before the launch.
   // With sem NULL the partials are left for launch_combine.
   uint32_t* sem;
-  void* o;                  // [B*T, H*dh] output rows in the activation format
+  void* o;                  // [B*T, H*dh] output rows, activation tile format
 };
 
 // Query groups per (sequence, kv head) of the attention launch and the query rows a
@@ -111,7 +107,7 @@ bool attn_uses_reg_path(bool bf, int dh, int NQT);  // keys per tile: 32 bf16 / 
 struct CombineArgs {
   const float* po;
   const float* pml;
-  void* o;                  // [B*T, H*dh] in the activation format
+  void* o;                  // [B*T, H*dh] activation tile format
   int B, T, H, Hkv, dh, n_splits, nq_pad;
 };
 hipError_t launch_combine(bool is_bf16, const CombineArgs& a, hipStream_t s);
@@ -128,7 +124,6 @@ struct PrologueArgs {
   int dh;
   float rope_theta;
   int32_t* err;             // [B]
-  int n_extra, extra_base;  // lm_rows[B*R + i] = extra_base + i for i < n_extra
   uint32_t* zero;           // n_zero words cleared (the attention arrival counters)
   int n_zero;
   // destination of each chunk row's K/V: slot seq_len[b] + t through the block table;
@@ -144,23 +139,29 @@ struct EmbedArgs {
   const void* embed;        // [V, d]
   const float* gain;        // first layer attention-norm gain
   float* x;                 // [M, d] fp32 residual
-  void* a;                  // [M, d] normalised rows in the activation format
+  void* a;                  // [M, d] normalised rows, activation tile format
   int M, T, d, V;
   float eps;
   int32_t* err;
 };
 hipError_t launch_embed_norm(bool is_bf16, const EmbedArgs& a, hipStream_t s);
 
+// Residual add + RMSNorm.  Without `rows`: x[m] += sum of the partials, and row m of
+// `a` gets the normalised row, for m < M.  With `rows` (after the last layer): x is
+// left as it is; output row j < n_rows of `a` gets the normalised row rows[j] (the
+// LM-head operand), and with `hidden` set, hidden[m] = x[m] + partials for m < M.
 struct ResidNormArgs {
-  float* x;                 // [M, d] fp32 residual, updated in place
+  float* x;                 // [M, d] fp32 residual
   const float* part;        // [S][M][d] partial sums to add
   long long part_stride;
   int S;
   const float* gain;
-  void* a;                  // [M, d] normalised rows in the activation format
-  float* hidden;            // nullable [M, d] copy of the updated residual
+  void* a;                  // normalised rows, activation tile format
+  float* hidden;            // nullable [M, d] updated residual (with `rows` only)
   int M, d;
   float eps;
+  const int32_t* rows;      // nullable [n_rows] source rows of the output rows
+  int n_rows;
 };
 hipError_t launch_resid_norm(bool is_bf16, const ResidNormArgs& a, hipStream_t s);
 
@@ -177,7 +178,7 @@ hipError_t launch_row_reduce(const RowReduceArgs& a, hipStream_t s);
 struct StreamRowsArgs {
   const float* e;           // [S, d]
   int S, d;
-  void* act;                // activation rows (format of the model type)
+  void* act;                // activation operand (tile format of the model type)
   int first_row;
 };
 hipError_t launch_stream_rows(bool is_bf16, const StreamRowsArgs& a, hipStream_t s);

@@ -51,14 +51,15 @@ SDV_DEV void load_q(const void* q, size_t off, bool ok, int lg, u32x4 (&out)[DH 
   }
 }
 
-// Physical pages of the split's logical pages [k_begin/16, (k_end-1)/16] staged in LDS
-// once per workgroup (-1 where the table entry is out of range), so key and value
-// loads never wait on a block-table load.  The host keeps split_keys <= 16 * (512 - 1).
+// Physical pages of every logical page the split can reach, [k_begin/16, (k_begin +
+// split_keys)/16), staged in LDS once per workgroup (-1 where the table entry is out of
+// range), so key and value loads never wait on a block-table load.  The range does
+// not depend on the sequence length, so the table loads need not wait for it.  The
+// host keeps split_keys a multiple of 16 and at most 16 * (512 - 1).
 constexpr int ATTN_MAX_PAGES = 512;
-SDV_DEV int stage_pages(const AttnArgs& a, const int32_t* bt, int k_begin, int k_end, int* sPage) {
+SDV_DEV int stage_pages(const AttnArgs& a, const int32_t* bt, int k_begin, int* sPage) {
   const int pg0 = k_begin >> 4;
-  // at least one entry, so clamped addresses of an empty split stay defined
-  const int npg = k_end > k_begin ? min(((k_end - 1) >> 4) - pg0 + 1, ATTN_MAX_PAGES) : 1;
+  const int npg = min(a.split_keys >> 4, ATTN_MAX_PAGES);
   for (int i = threadIdx.x; i < npg; i += blockDim.x) {
     const int pg = pg0 + i;
     int phys = pg < a.max_blocks ? bt[pg] : -1;
@@ -240,10 +241,8 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
   const int32_t* bt = a.block_table + (size_t)b * a.max_blocks;
   const T* kp = (const T*)a.k_pages;
   const T* vp = (const T*)a.v_pages;
-  __shared__ int sPage[ATTN_MAX_PAGES];
-  const int pg0 = stage_pages(a, bt, k_begin, k_end, sPage);
-
-  // queries of this wave: tiles w, w + NW, ...
+  // queries of this wave: tiles w, w + NW, ... (loaded before the page table is
+  // staged, so both round trips overlap)
   constexpr int QP = BF ? 2 : 1;   // q enters bf16 MFMAs as a hi + lo pair
   u32x4 qreg[NQW][DH / KS][QP];
   uint32_t anc[NQW][4];
@@ -264,6 +263,8 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt) acc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  __shared__ int sPage[ATTN_MAX_PAGES];
+  const int pg0 = stage_pages(a, bt, k_begin, sPage);
 
   // K (token-major) and V^T (dh-major) of a tile go through LDS; each thread holds
   // its 16-byte chunks of the next tile in registers while the current one is used.
@@ -501,9 +502,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const T* kp = (const T*)a.k_pages;
   const T* vp = (const T*)a.v_pages;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  __shared__ int sPage[ATTN_MAX_PAGES];
-  const int pg0 = stage_pages(a, bt, k_begin, k_end, sPage);
-
+  // the queries are loaded before the page table is staged, so both round trips overlap
   constexpr int QP = BF ? 2 : 1;
   u32x4 qreg[NQT][DH / KS][QP];
   uint32_t anc[NQT][4];
@@ -523,6 +522,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt) acc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  __shared__ int sPage[ATTN_MAX_PAGES];
+  const int pg0 = stage_pages(a, bt, k_begin, sPage);
 
   // K and V^T operands of key tile `it` (relative to k_begin).  Loads are branch-free:
   // a slot past the split end reads the split's last valid slot instead (its scores

@@ -228,7 +228,7 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z / a.n_qg;
   const int lane = threadIdx.x & 63, NW = blockDim.x >> 6;
   // this wave's query tiles: q_base + w + j*NW, q_base = (query group) * NW * NQW
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int q_base = (blockIdx.z % a.n_qg) * NW * NQW;
   const int r = lane & 15, lg = lane >> 4;
   const int G = a.H / a.Hkv;
@@ -326,6 +326,10 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
   const int krow0 = BF ? 8 * (r >> 2) + (r & 3) : r;  // K row of this lane (half 0)
   // query tiles of this wave that exist (wave-uniform)
   const int nj = min(NQW, max(0, (NQT - (q_base + w) + NW - 1) / NW));
+  // The query loads are complete before the key loop: the loop's waits then cover
+  // only the tile prefetch (otherwise the first score MFMAs of every tile would wait
+  // on the in-order load counter until the next tile's loads had landed).
+  vmem_wait_all();
   if (k_begin < k_end) fetch(k_begin);
   for (int kt0 = k_begin; kt0 < k_end; kt0 += KT) {
     __syncthreads();   // every wave is done with the previous tile
@@ -736,37 +740,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   else attn_merge<T, DH>(a, b, g, 0, nq, &so[0][0][0][0][0]);
 }
 
+// Split merge as its own kernel (many splits or large merges): item (row, head) of
+// the chunk takes DH / 4 threads, each owning 4 consecutive output values; a thread
+// loads every split's (m, l) pair and 16-byte output chunk in one round, then sums
+// the splits in order.
 template <typename T, int DH>
-__global__ __launch_bounds__(DH) void attn_combine(CombineArgs a) {
+__global__ __launch_bounds__(256) void attn_combine(CombineArgs a) {
   constexpr int MAXS = 32;
-  const int row = blockIdx.y, h = blockIdx.x;
+  constexpr int TPI = DH / 4;   // threads per item
+  const int item = blockIdx.x * (256 / TPI) + threadIdx.x / TPI;
+  const int c4 = threadIdx.x % TPI;
+  if (item >= a.B * a.T * a.H) return;
+  const int row = item / a.H, h = item % a.H;
   const int b = row / a.T, t = row % a.T;
   const int G = a.H / a.Hkv, g = h / G, qi = t * G + h % G;
   const size_t base0 = (((size_t)b * a.Hkv + g) * a.n_splits) * a.nq_pad + qi;
-  float m[MAXS], l[MAXS], v[MAXS];
+  float2 ml[MAXS];
+  float4 v[MAXS];
 #pragma unroll
   for (int s = 0; s < MAXS; ++s) {
     if (s < a.n_splits) {
       const size_t bs = base0 + (size_t)s * a.nq_pad;
-      m[s] = a.pml[bs * 2];
-      l[s] = a.pml[bs * 2 + 1];
-      v[s] = a.po[bs * DH + threadIdx.x];
+      ml[s] = *(const float2*)(a.pml + bs * 2);
+      v[s] = *(const float4*)(a.po + bs * DH + 4 * c4);
     }
   }
   float M = -INFINITY;
 #pragma unroll
   for (int s = 0; s < MAXS; ++s)
-    if (s < a.n_splits) M = fmaxf(M, m[s]);
-  float num = 0.f, den = 0.f;
+    if (s < a.n_splits) M = fmaxf(M, ml[s].x);
+  float den = 0.f, num[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < MAXS; ++s) {
     if (s < a.n_splits) {
-      const float wgt = exp2f(m[s] - M);
-      den += wgt * l[s];
-      num += wgt * v[s];
+      const float wgt = exp2f(ml[s].x - M);
+      den += wgt * ml[s].y;
+      num[0] += wgt * v[s].x;
+      num[1] += wgt * v[s].y;
+      num[2] += wgt * v[s].z;
+      num[3] += wgt * v[s].w;
     }
   }
-  act_store1<T>(a.o, a.H * DH, row, h * DH + threadIdx.x, num / den);
+  const float out[4] = {num[0] / den, num[1] / den, num[2] / den, num[3] / den};
+  act_store4<T>(a.o, a.H * DH, row, h * DH + 4 * c4, out);
 }
 
 // the register path serves heads with few query tiles (its merge buffers and
@@ -866,13 +882,14 @@ hipError_t launch_attention(bool is_bf16, int dh, const AttnArgs& a, hipStream_t
 
 hipError_t launch_combine(bool is_bf16, const CombineArgs& a, hipStream_t s) {
   if (a.n_splits > 32) return hipErrorInvalidValue;
-  dim3 grid(a.H, a.B * a.T);
+  const int items = a.B * a.T * a.H;
+  const int grid = (items + 256 / (a.dh / 4) - 1) / (256 / (a.dh / 4));
   if (is_bf16) {
-    if (a.dh == 64) attn_combine<bf16, 64><<<grid, 64, 0, s>>>(a);
-    else attn_combine<bf16, 128><<<grid, 128, 0, s>>>(a);
+    if (a.dh == 64) attn_combine<bf16, 64><<<grid, 256, 0, s>>>(a);
+    else attn_combine<bf16, 128><<<grid, 256, 0, s>>>(a);
   } else {
-    if (a.dh == 64) attn_combine<float, 64><<<grid, 64, 0, s>>>(a);
-    else attn_combine<float, 128><<<grid, 128, 0, s>>>(a);
+    if (a.dh == 64) attn_combine<float, 64><<<grid, 256, 0, s>>>(a);
+    else attn_combine<float, 128><<<grid, 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }

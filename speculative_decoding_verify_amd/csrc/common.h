@@ -167,6 +167,10 @@ SDV_DEV void st_dev8(rsrc_t r, uint32_t off, u32x2 v) { __builtin_amdgcn_raw_buf
 SDV_DEV u32x4 ld_dev16(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL_DEVICE); }
 SDV_DEV u32x2 ld_dev8(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, CPOL_DEVICE); }
 
+// Wait until every vector memory load and store of the wave has completed (the
+// vector-memory counter at zero; export and LDS counters left alone).
+SDV_DEV void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Every thread's stores are complete, then thread 0 counts the workgroup in on
 // `counter` (zero before the launch).  True in all threads of the workgroup that
 // arrives n-th (last).  `flag` is an int in LDS.

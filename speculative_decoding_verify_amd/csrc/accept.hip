@@ -15,9 +15,11 @@ namespace sdv {
 // Greedy tree walk: one block per sequence stages its tokens, the tree and the
 // argmax of every logit row in LDS; every row checks in parallel whether it is the
 // accepted child of its parent (its token equals the parent's argmax), then one
-// thread walks from the last audio row along the accepted children.
+// thread walks from the last audio row along the accepted children, and all threads
+// write the path and the commit moves.
 __global__ __launch_bounds__(128) void accept_greedy_kernel(GreedyArgs a) {
   __shared__ int32_t tok[128], par[128], am_of_row[128], path[128], child_of[128], n_match[128];
+  __shared__ int32_t s_n, s_base;
   const int b = blockIdx.x;
   for (int j = threadIdx.x; j < a.T; j += blockDim.x) {
     tok[j] = a.tokens[(size_t)b * a.T + j];
@@ -26,6 +28,7 @@ __global__ __launch_bounds__(128) void accept_greedy_kernel(GreedyArgs a) {
     child_of[j] = 0x7fffffff;
     n_match[j] = 0;
   }
+  if (threadIdx.x == 0) s_base = a.base_len ? a.base_len[b] : 0;
   __syncthreads();
   for (int i = threadIdx.x; i < a.R; i += blockDim.x) {
     const int row = a.logit_rows[i];
@@ -40,32 +43,32 @@ __global__ __launch_bounds__(128) void accept_greedy_kernel(GreedyArgs a) {
     }
   }
   __syncthreads();
-  if (threadIdx.x != 0) return;
-  int node = a.L_a - 1, n = 0, next = -1;
-  for (;;) {
-    const int am = am_of_row[node];
-    next = am;
-    if (am < 0) break;
-    if (n_match[node] > 1) set_err(a.err, b, 0x10);
-    const int child = child_of[node];
-    if (child == 0x7fffffff) break;
-    path[n++] = child;
-    node = child;
+  if (threadIdx.x == 0) {
+    int node = a.L_a - 1, n = 0, next = -1;
+    for (;;) {
+      const int am = am_of_row[node];
+      next = am;
+      if (am < 0) break;
+      if (n_match[node] > 1) set_err(a.err, b, 0x10);
+      const int child = child_of[node];
+      if (child == 0x7fffffff) break;
+      path[n++] = child;
+      node = child;
+    }
+    s_n = n;
+    a.n_out[b] = n;
+    a.next_out[b] = next;
+    if (a.base_len && a.keep_out) a.keep_out[b] = s_base + a.L_a + n;
   }
-  a.n_out[b] = n;
-  a.next_out[b] = next;
-  if (a.path_out)
-    for (int i = 0; i < a.T; ++i) a.path_out[(size_t)b * a.T + i] = i < n ? path[i] : -1;
-  if (a.base_len) {
-    const int base = a.base_len[b];
-    if (a.keep_out) a.keep_out[b] = base + a.L_a + n;
-    if (a.move_src && a.move_dst) {
+  __syncthreads();
+  const int n = s_n, base = s_base;
+  for (int i = threadIdx.x; i < a.T; i += blockDim.x) {
+    if (a.path_out) a.path_out[(size_t)b * a.T + i] = i < n ? path[i] : -1;
+    if (a.base_len && a.move_src && a.move_dst) {
       // accepted row path[i] must end at slot base + L_a + i
-      for (int i = 0; i < a.T; ++i) {
-        const bool mv = i < n && path[i] != a.L_a + i;
-        a.move_src[(size_t)b * a.T + i] = mv ? base + path[i] : -1;
-        a.move_dst[(size_t)b * a.T + i] = mv ? base + a.L_a + i : -1;
-      }
+      const bool mv = i < n && path[i] != a.L_a + i;
+      a.move_src[(size_t)b * a.T + i] = mv ? base + path[i] : -1;
+      a.move_dst[(size_t)b * a.T + i] = mv ? base + a.L_a + i : -1;
     }
   }
 }

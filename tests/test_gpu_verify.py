@@ -73,6 +73,35 @@ def test_verify_parity_many_rows(shape, lens, L_a, gamma):
     assert hd <= tol, hd
 
 
+@pytest.mark.parametrize("shape", [MINI_BF16, MINI_F32], ids=lambda s: s.name)
+@pytest.mark.parametrize("B,L_a,gamma", [
+    (1, 4, 12),    # 16 chunk rows: one whole row tile, 13 logit rows
+    (1, 5, 12),    # 17 rows: a one-row tail tile; 13 logit rows
+    (2, 4, 12),    # 32 rows, 26 logit rows (two tiles, a ten-row tail)
+    (5, 4, 12),    # 80 rows, the most the few-row GEMM takes; 65 logit rows (one-row tail)
+    (3, 4, 23),    # 81 rows: the first batch on the tiled GEMM; 72 logit rows
+    (4, 4, 23),    # 108 rows, 96 logit rows: the LM head on the tiled GEMM too
+])
+def test_row_tile_boundaries(shape, B, L_a, gamma):
+    """Activation operands are stored in whole 16-row tiles whose padding rows are
+    never written: chunk-row and logit-row counts at and around the tile, few-row and
+    many-row boundaries all match the oracle."""
+    T = L_a + gamma
+    lens = [23 + 17 * b for b in range(B)]
+    print(f"case {shape.name} B={B} T={T} rows={B * T} logit rows={B * (gamma + 1)}", flush=True)
+    w = make_weights(shape, seed=121, gain_noise=0.1)
+    kvh = make_random_kv(shape, lens, capacity=max(lens) + T, seed=122)
+    toks = _tokens(B, T, shape.vocab, 123)
+    g, o, ver, kv = run_pair(w, kvh, toks, L_a, perm_seed=124)
+    assert np.all(g["err"] == 0)
+    err, flagged, n = compare_logits(shape, g, o)
+    print(f"  logits rel err {err:.2e}; flagged {flagged}/{n}", flush=True)
+    compare_kv(shape, kv, o, lens, T)
+    tol = 2e-2 if shape.dtype == "bf16" else 1e-5
+    hd = np.max(np.abs(g["hidden"] - o["hidden"])) / np.max(np.abs(o["hidden"]))
+    assert hd <= tol, hd
+
+
 def test_attention_dominant_hidden():
     """Scaled q/k/o weights make attention dominate the residual stream, so a wrong
     attention kernel cannot hide under the FFN's contribution."""

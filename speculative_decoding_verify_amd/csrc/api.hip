@@ -58,7 +58,7 @@ GemmPlan plan_gemm(int M, int N, int K, bool bf, int epi) {
     p.MT = 8;
     p.row_blocks = cdiv(M, 128);
     const int wn = (long long)cdiv(ntiles, 16) * p.row_blocks >= TARGET_WG_GEMM ? 8 : 4;
-    p.cfg = GemmCfg{wn, 2, true};
+    p.cfg = GemmCfg{wn, 3, true};   // 3 k steps in the LDS ring
     p.ncg = cdiv(ntiles, 2 * wn);
     p.spp = steps;
     p.S = 1;

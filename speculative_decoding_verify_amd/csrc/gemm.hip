@@ -315,12 +315,35 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs a) {
 // Tiled GEMM for many rows (M > 80, e.g. a batch of sessions): the weights are no
 // longer the only stream, every packed tile is reused by up to 128 rows.  A
 // workgroup computes a 128 x (32 * WN) output tile; wave (wm, wn) of its 2 x 2 waves
-// owns 64 x (16 * WN) (4 x WN MFMA tiles) and walks the whole K range with D k steps
-// of operands in flight in registers (same ring as gemm_stream).  Grid: x = row
-// blocks (fastest, so the workgroups that share a column group's weights run
-// together and the weights come from HBM once), z = column groups.  The finished
-// tile goes through LDS to the shared epilogues.
-template <typename T, int WN, int D, int EPI>
+// owns 64 x (16 * WN) (4 x WN MFMA tiles).  Each k step's operands, 2 * WN weight
+// tiles and 8 row tiles of activations (all of them 1 KB blocks in MFMA lane order),
+// are copied once per workgroup from global memory into an LDS ring of R steps by
+// LDS DMA (global_load_lds, no registers held while in flight), and every wave
+// reads the blocks it multiplies from LDS, so each byte crosses the L2 -> CU path
+// once per workgroup instead of once per wave that uses it.  Grid: x = row blocks
+// (fastest, so the workgroups that share a column group's weights run together and
+// the weights come from HBM once), z = column groups.  The finished tile goes
+// through LDS (the ring's memory) to the shared epilogues.
+SDV_DEV void lds_dma16(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#endif
+}
+// wait until at most N vector memory operations of the wave are outstanding
+template <int N> SDV_DEV void vmem_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <typename T, int WN, int R>
+constexpr int tiled_lds_bytes() {
+  constexpr int AL = sizeof(T) == 2 ? 2 : 1;
+  constexpr int ring = R * (2 * WN + 8 * AL) * 1024;
+  constexpr int tile = 128 * (32 * WN + 1) * 4;
+  return ring > tile ? ring : tile;
+}
+
+template <typename T, int WN, int R, int EPI>
 __global__ __launch_bounds__(256) void gemm_tiled(GemmArgs a) {
   constexpr bool BF = sizeof(T) == 2;
   constexpr int KS = BF ? 32 : 16;
@@ -328,6 +351,11 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmArgs a) {
   constexpr int WM = 4;              // MFMA row tiles per wave
   constexpr int MT = 2 * WM, NT = 2 * WN;
   constexpr int TC = 16 * NT;
+  constexpr int NL = NT + MT * AL;   // 1 KB blocks per k step: weight tiles, then row tiles
+  constexpr int SB = NL * 1024;      // bytes of one ring slot
+  static_assert(NL % 4 == 0, "blocks per step split evenly over the 4 waves");
+  constexpr int NPW = NL / 4;        // blocks each wave copies per step
+  __shared__ __attribute__((aligned(1024))) char smem[tiled_lds_bytes<T, WN, R>()];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -336,67 +364,72 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmArgs a) {
   const int cg = blockIdx.z;
   const int ksteps = a.K / KS;
   const int ntiles = (a.N + 15) >> 4;
-
-  const char* wp[WN];
-#pragma unroll
-  for (int t = 0; t < WN; ++t) {
-    const int tile = min(cg * NT + wn * WN + t, ntiles - 1);
-    wp[t] = (const char*)a.W + (size_t)tile * ksteps * 1024 + lane * 16;
-  }
   const int row_tiles = (a.M + 15) >> 4;
-  const char* ap[WM];
+
+  // this wave's blocks of every step: block c = wave + 4 i; global address of this
+  // lane's 16 bytes at step 0 and the step stride
+  const char* gp[NPW];
+  int gstride[NPW];
 #pragma unroll
-  for (int mt = 0; mt < WM; ++mt) {
-    const int rt = min(blockIdx.x * MT + wm * WM + mt, row_tiles - 1);
-    const int rr = min(r, a.M - 1 - rt * 16);   // rows past M: the last row's chunk
-    ap[mt] = (const char*)a.A + (size_t)rt * ksteps * (64 * KS) + (lg * 16 + rr) * 16;
+  for (int i = 0; i < NPW; ++i) {
+    const int c = wave + 4 * i;
+    if (c < NT) {
+      const int tile = min(cg * NT + c, ntiles - 1);
+      gp[i] = (const char*)a.W + (size_t)tile * ksteps * 1024 + lane * 16;
+      gstride[i] = 1024;
+    } else {
+      const int q = c - NT, mt8 = q / AL, h = q % AL;
+      const int rt = min(blockIdx.x * MT + mt8, row_tiles - 1);
+      const int rr = min(r, a.M - 1 - rt * 16);   // rows past M: the last row's chunk
+      gp[i] = (const char*)a.A + (size_t)rt * ksteps * (64 * KS) + h * 1024 + (lg * 16 + rr) * 16;
+      gstride[i] = 64 * KS;
+    }
   }
-  u32x4 wb[D][WN], ab[D][WM][AL];
-  auto issue = [&](int j, u32x4 (&w)[WN], u32x4 (&av)[WM][AL]) {
+  auto copy_step = [&](int s, int slot) {
+    char* dst = smem + slot * SB;
 #pragma unroll
-    for (int t = 0; t < WN; ++t) w[t] = ld16_stream(wp[t] + (size_t)j * 1024);
-#pragma unroll
-    for (int mt = 0; mt < WM; ++mt)
-#pragma unroll
-      for (int h = 0; h < AL; ++h) av[mt][h] = ld16(ap[mt] + (size_t)j * (64 * KS) + 1024 * h);
+    for (int i = 0; i < NPW; ++i) lds_dma16(gp[i] + (size_t)s * gstride[i], dst + (wave + 4 * i) * 1024);
   };
+
   f32x4 acc[WM][WN];
 #pragma unroll
   for (int mt = 0; mt < WM; ++mt)
 #pragma unroll
     for (int t = 0; t < WN; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const u32x4 (&w)[WN], const u32x4 (&av)[WM][AL]) {
+
+  const int nk = ksteps;
+#pragma unroll
+  for (int u = 0; u < R - 1; ++u)
+    if (u < nk) copy_step(u, u);
+  for (int j = 0; j < nk; ++j) {
+    // this wave's copies of step j have landed (later steps may still be in flight);
+    // after the barrier every wave's have, and every wave is done with step j - 1
+    if (j + R - 2 < nk) vmem_wait<(R - 2) * NPW>();
+    else vmem_wait<0>();
+    // a bare barrier: __syncthreads() would also wait for the copies still in flight.
+    // The compiler fences keep every LDS access on its side of it.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (j + R - 1 < nk) copy_step(j + R - 1, (j + R - 1) % R);
+    const char* slot = smem + (j % R) * SB + lane * 16;
+    u32x4 av[WM][AL];
 #pragma unroll
     for (int mt = 0; mt < WM; ++mt)
 #pragma unroll
-      for (int t = 0; t < WN; ++t)
+      for (int h = 0; h < AL; ++h) av[mt][h] = *(const u32x4*)(slot + (NT + (wm * WM + mt) * AL + h) * 1024);
 #pragma unroll
-        for (int h = 0; h < AL; ++h) acc[mt][t] = mma16<T>(av[mt][h], w[t], acc[mt][t]);
-  };
-  const int nk = ksteps;
+    for (int t = 0; t < WN; ++t) {
+      const u32x4 w = *(const u32x4*)(slot + (wn * WN + t) * 1024);
 #pragma unroll
-  for (int u = 0; u < D - 1; ++u)
-    if (u < nk) issue(u, wb[u], ab[u]);
-  int j0 = 0;
-  for (; j0 + 2 * D - 2 < nk; j0 += D) {
+      for (int mt = 0; mt < WM; ++mt)
 #pragma unroll
-    for (int u = 0; u < D; ++u) {
-      issue(j0 + u + D - 1, wb[(u + D - 1) % D], ab[(u + D - 1) % D]);
-      compute(wb[u], ab[u]);
+        for (int h = 0; h < AL; ++h) acc[mt][t] = mma16<T>(av[mt][h], w, acc[mt][t]);
     }
   }
-#pragma unroll
-  for (int g = 0; g < 2; ++g)
-#pragma unroll
-    for (int u = 0; u < D; ++u) {
-      const int j = j0 + g * D + u;
-      if (j < nk) {
-        if (j + D - 1 < nk) issue(j + D - 1, wb[(u + D - 1) % D], ab[(u + D - 1) % D]);
-        compute(wb[u], ab[u]);
-      }
-    }
 
-  __shared__ float tile[16 * MT][TC + 1];
+  __syncthreads();   // the ring's memory becomes the output tile
+  float (*tile)[TC + 1] = reinterpret_cast<float (*)[TC + 1]>(smem);
 #pragma unroll
   for (int mt = 0; mt < WM; ++mt)
 #pragma unroll
@@ -500,18 +533,19 @@ static hipError_t launch_mt(int MT, const Launch& L, const GemmArgs& a) {
   }
 }
 
-template <typename T, int WN, int D, int EPI>
+template <typename T, int WN, int R, int EPI>
 static hipError_t launch_tiled(const Launch& L, const GemmArgs& a) {
-  if (L.ev0) hipExtLaunchKernelGGL(gemm_tiled<T, WN, D, EPI>, L.grid, dim3(256), 0, L.s, L.ev0, L.ev1, 0, a);
-  else gemm_tiled<T, WN, D, EPI><<<L.grid, 256, 0, L.s>>>(a);
+  static_assert(tiled_lds_bytes<T, WN, R>() <= LDS_LIMIT, "tiled GEMM LDS");
+  if (L.ev0) hipExtLaunchKernelGGL(gemm_tiled<T, WN, R, EPI>, L.grid, dim3(256), 0, L.s, L.ev0, L.ev1, 0, a);
+  else gemm_tiled<T, WN, R, EPI><<<L.grid, 256, 0, L.s>>>(a);
   return hipGetLastError();
 }
 
 template <typename T, int EPI>
 static hipError_t launch_cfg(const GemmCfg& c, int MT, const Launch& L, const GemmArgs& a) {
   if (c.tiled) {
-    if (c.NT == 4 && c.D == 2) return launch_tiled<T, 4, 2, EPI>(L, a);
-    if (c.NT == 8 && c.D == 2) return launch_tiled<T, 8, 2, EPI>(L, a);
+    if (c.NT == 4 && c.D == 3) return launch_tiled<T, 4, 3, EPI>(L, a);
+    if (c.NT == 8 && c.D == 3) return launch_tiled<T, 8, 3, EPI>(L, a);
     return hipErrorInvalidValue;
   }
   if (c.NT == 2 && c.D == 4) return launch_mt<T, 2, 4, EPI>(MT, L, a);

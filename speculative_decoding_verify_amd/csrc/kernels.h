@@ -48,7 +48,8 @@ struct GemmArgs {
 };
 
 // launch configuration: NT weight tiles per workgroup, D k steps in flight per wave;
-// tiled: the many-row kernel (128-row blocks; NT = MFMA column tiles per wave)
+// tiled: the many-row kernel (128-row blocks; NT = MFMA column tiles per wave, D = k
+// steps in its LDS ring)
 struct GemmCfg {
   int NT, D;
   bool tiled = false;

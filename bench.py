@@ -49,11 +49,11 @@ def gate_up_launch_bytes(sh, M):
 # HBM traffic of the gate/up kernel from rocprofv3 counters (FETCH_SIZE, then WRITE_SIZE
 # in separate runs of `bench.py --steps 5 --warmup 2 --no-cpu-baseline`), per dispatch,
 # each scaled by what the same counter reads for a plain 256 MiB device copy
-# (`bench.py --copy-calibration`).  Valid only for the kernel sources they were taken
-# on: the sha256 of the GEMM sources is checked at run time, else traffic is null.
-GATE_UP_TRAFFIC = {"sha256": "ec4afa2dfebb3a3ca9d921d98213df06453ec65b48fd655a001843952e8438d6",
-                   "fetch_kib": 34149.0, "fetch_factor": 262144.0 / 131084.0,
-                   "write_kib": 1312.0, "write_factor": 262144.0 / 262144.0}
+# (`bench.py --copy-calibration`).  Valid only for the workload and the kernel sources
+# they were taken on: both are checked at run time, else traffic is null.
+GATE_UP_TRAFFIC = {"workload": "1.7b-bf16", "sha256": "c6755a9464969bb08a3d22d066f32097f7fa672484b632ad2b0261532eb9a014",
+                   "fetch_kib": 34375.0, "fetch_factor": 262144.0 / 131084.0,
+                   "write_kib": 1344.0, "write_factor": 262144.0 / 262144.0}
 GEMM_SOURCES = ("speculative_decoding_verify_amd/csrc/gemm.hip", "speculative_decoding_verify_amd/csrc/common.h",
                 "speculative_decoding_verify_amd/csrc/kernels.h")
 
@@ -67,9 +67,9 @@ def gemm_source_sha():
     return h.hexdigest()
 
 
-def gate_up_traffic():
+def gate_up_traffic(workload):
     t = GATE_UP_TRAFFIC
-    if not t or t["sha256"] != gemm_source_sha():
+    if not t or t["workload"] != workload or t["sha256"] != gemm_source_sha():
         return None
     return (t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"]) * 1024.0
 
@@ -219,7 +219,7 @@ def bench_verify(args, wl):
     gu_us = launch_us["gate_up"]
     gu_bytes = gate_up_launch_bytes(sh, T)
     achieved = gu_bytes / (gu_us * 1e-6) / 1e9
-    traffic = gate_up_traffic()
+    traffic = gate_up_traffic(args.workload)
     lm_bytes = sh.vocab * sh.d * sh.elem_bytes
 
     nbytes = pass_bytes(sh, T, R, C)

@@ -113,9 +113,14 @@ MINI_BF16_D128 = ModelShape("mini-bf16-dh128", n_layers=2, d=512, n_heads=4, n_k
                             head_dim=128, ffn=640, vocab=2053, dtype="bf16")
 MINI_F32 = ModelShape("mini-f32", n_layers=2, d=192, n_heads=3, n_kv_heads=1, head_dim=64,
                       ffn=448, vocab=1537, dtype="f32")
+# the 1.7B model width on a small vocabulary (parity at d = 2048 in seconds)
+MINI_BF16_D2048 = ModelShape("mini-bf16-d2048", n_layers=3, d=2048, n_heads=16, n_kv_heads=4, head_dim=128,
+                             ffn=4096, vocab=1009, dtype="bf16")
+MINI_F32_D2048 = ModelShape("mini-f32-d2048", n_layers=3, d=2048, n_heads=16, n_kv_heads=4, head_dim=128,
+                            ffn=4096, vocab=1009, dtype="f32")
 
 SHAPES = {s.name: s for s in (TOY_F32, SHAPE_1P7B, SHAPE_8B, SHAPE_8B_CB,
-                              MINI_BF16, MINI_BF16_D128, MINI_F32)}
+                              MINI_BF16, MINI_BF16_D128, MINI_F32, MINI_BF16_D2048, MINI_F32_D2048)}
 
 
 # -- the verify workloads --------------------------------------------------------

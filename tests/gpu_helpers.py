@@ -88,9 +88,11 @@ def compare_logits(sh, g, o):
 
 def compare_kv(sh, kv, o, lens, T):
     """Keys/values written for the chunk rows vs the oracle's.  Layer 0 sees identical
-    inputs on both sides, so its bf16 K/V agree to one bf16 ulp (fp32: 1e-5 relative);
-    deeper layers see a residual stream that already carries rounding differences and
-    are held to the logits' per-row relative tolerance."""
+    inputs on both sides, so its bf16 K/V agree to one bf16 ulp (fp32: every element
+    within 1e-5 of the tensor's largest magnitude -- fp32 accumulation over K terms
+    leaves an absolute error that grows with K, so small elements are not held to a
+    fixed absolute floor); deeper layers see a residual stream that already carries
+    rounding differences and are held to the logits' per-row relative tolerance."""
     tol = logit_tol(sh)
     for b in range(len(lens)):
         for l in range(sh.n_layers):
@@ -101,7 +103,7 @@ def compare_kv(sh, kv, o, lens, T):
                     assert bad.mean() < 1e-3 and not np.any(np.abs(gt - ot) > np.abs(ot) * 2.0 ** -6 + 1e-5), \
                         f"K/V mismatch b={b} l={l}: {bad.sum()} elements beyond 1 ulp"
                 elif l == 0:
-                    np.testing.assert_allclose(gt, ot, rtol=1e-5, atol=1e-6)
+                    np.testing.assert_allclose(gt, ot, rtol=1e-5, atol=1e-5 * np.max(np.abs(ot)))
                 else:
                     rel = np.max(np.abs(gt - ot)) / np.max(np.abs(ot))
                     assert rel <= tol, f"K/V mismatch b={b} l={l}: rel {rel:.2e}"

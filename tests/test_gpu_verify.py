@@ -17,8 +17,8 @@ if not torch.cuda.is_available():  # pragma: no cover
 import speculative_decoding_verify_amd as sdv  # noqa: E402
 from oracle import accept as oacc  # noqa: E402
 from oracle import decoder as odec  # noqa: E402
-from synth import (MINI_BF16, MINI_BF16_D128, MINI_F32, make_weights, make_random_kv,  # noqa: E402
-                   uniform_tokens)
+from synth import (MINI_BF16, MINI_BF16_D128, MINI_BF16_D2048, MINI_F32, MINI_F32_D2048,  # noqa: E402
+                   make_weights, make_random_kv, uniform_tokens)
 from tests.gpu_helpers import (run_pair, compare_logits, compare_kv, greedy_expectation,  # noqa: E402
                                mode_of)
 
@@ -97,6 +97,30 @@ def test_row_tile_boundaries(shape, B, L_a, gamma):
     err, flagged, n = compare_logits(shape, g, o)
     print(f"  logits rel err {err:.2e}; flagged {flagged}/{n}", flush=True)
     compare_kv(shape, kv, o, lens, T)
+    tol = 2e-2 if shape.dtype == "bf16" else 1e-5
+    hd = np.max(np.abs(g["hidden"] - o["hidden"])) / np.max(np.abs(o["hidden"]))
+    assert hd <= tol, hd
+
+
+@pytest.mark.parametrize("shape", [MINI_BF16_D2048, MINI_F32_D2048], ids=lambda s: s.name)
+@pytest.mark.parametrize("lens,L_a,gamma", [
+    ((37, 70), 5, 16),     # 42 rows
+    ((12,), 1, 0),         # a single row
+])
+def test_parity_d2048(shape, lens, L_a, gamma):
+    """The 1.7B model width (d = 2048, 256 threads x 8 columns in the norms, K = 2048
+    and 4096 in the projections) on a small vocabulary: logits, hidden rows and the
+    written K/V match the oracle."""
+    print(f"case {shape.name} lens={lens} L_a={L_a} gamma={gamma}", flush=True)
+    w = make_weights(shape, seed=131, gain_noise=0.1)
+    T = L_a + gamma
+    kvh = make_random_kv(shape, list(lens), capacity=max(lens) + T, seed=132)
+    toks = _tokens(len(lens), T, shape.vocab, 133)
+    g, o, ver, kv = run_pair(w, kvh, toks, L_a, perm_seed=134)
+    assert np.all(g["err"] == 0), g["err"]
+    err, flagged, n = compare_logits(shape, g, o)
+    print(f"  logits rel err {err:.2e}; flagged {flagged}/{n}", flush=True)
+    compare_kv(shape, kv, o, list(lens), T)
     tol = 2e-2 if shape.dtype == "bf16" else 1e-5
     hd = np.max(np.abs(g["hidden"] - o["hidden"])) / np.max(np.abs(o["hidden"]))
     assert hd <= tol, hd

@@ -148,7 +148,7 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
   const int nkeys = max_ctx + T;
   const int NQT = cdiv(T * p.G, 16);
   int rows_per_group = 0;
-  p.n_qg = attn_query_groups(p.bf, dh, T, p.G, &rows_per_group);
+  p.n_qg = attn_query_groups(p.bf, dh, T, p.G, B * Hkv, &rows_per_group);
   int ns = cdiv(TARGET_WG_ATTN, (long long)B * Hkv * p.n_qg);
   ns = std::max(1, std::min({ns, ATTN_MAX_SPLITS, cdiv(nkeys, KT)}));
   ns = std::max(ns, cdiv(nkeys, 255 * KT));  // a split spans at most 511 pages (staged in LDS)

@@ -798,13 +798,16 @@ template <typename T, int DH> constexpr int attn_cap() {
 }
 
 template <typename T, int DH>
-int attn_shape(int NQT, int* nqw_out, int* nw_out) {
+int attn_shape(int NQT, int heads, int* nqw_out, int* nw_out) {
   constexpr int CAP = attn_cap<T, DH>();
-  // query groups of at most 8 waves x CAP tiles; inside a group, the shape whose
+  // query groups of at most 8 waves x CAP tiles -- of at most 4 tiles (one per SIMD)
+  // when the (sequence, kv head) pairs alone fill the GPU (heads >= 256: no key splits
+  // are needed, and a shorter busiest SIMD beats reading the keys and values once per
+  // group; measured on the batched 64-row pass); inside a group, the shape whose
   // busiest SIMD (wave w runs on SIMD w % 4, and takes tiles w, w + nw, ...) carries
   // the fewest query tiles per key tile, then the fewest tiles per wave (registers),
   // then the fewest waves; at least 4 waves (waves without query tiles still stage K/V)
-  const int n_qg = (NQT + 8 * CAP - 1) / (8 * CAP);
+  const int n_qg = std::max((NQT + 8 * CAP - 1) / (8 * CAP), heads >= 256 ? (NQT + 3) / 4 : 1);
   const int Q = (NQT + n_qg - 1) / n_qg;
   int best_nw = 8, best_nqw = CAP, best_load = 1 << 30;
   for (int nqw = 1; nqw <= CAP; ++nqw)
@@ -826,15 +829,17 @@ int attn_shape(int NQT, int* nqw_out, int* nw_out) {
   return n_qg;
 }
 
-int attn_query_groups(bool is_bf16, int dh, int T, int G, int* rows_per_group) {
+int attn_query_groups(bool is_bf16, int dh, int T, int G, int heads, int* rows_per_group) {
   const int NQT = (T * G + 15) / 16;
   if (attn_uses_reg_path(is_bf16, dh, NQT)) {
     *rows_per_group = T * G;
     return 1;
   }
   int nqw, nw, n_qg;
-  if (is_bf16) n_qg = dh == 64 ? attn_shape<bf16, 64>(NQT, &nqw, &nw) : attn_shape<bf16, 128>(NQT, &nqw, &nw);
-  else n_qg = dh == 64 ? attn_shape<float, 64>(NQT, &nqw, &nw) : attn_shape<float, 128>(NQT, &nqw, &nw);
+  if (is_bf16)
+    n_qg = dh == 64 ? attn_shape<bf16, 64>(NQT, heads, &nqw, &nw) : attn_shape<bf16, 128>(NQT, heads, &nqw, &nw);
+  else
+    n_qg = dh == 64 ? attn_shape<float, 64>(NQT, heads, &nqw, &nw) : attn_shape<float, 128>(NQT, heads, &nqw, &nw);
   *rows_per_group = std::min(T * G, nw * nqw * 16);
   return n_qg;
 }
@@ -858,7 +863,7 @@ static hipError_t launch_attn_t(AttnArgs a, hipStream_t s) {
     return hipGetLastError();
   }
   int nqw, nw;
-  a.n_qg = attn_shape<T, DH>(NQT, &nqw, &nw);
+  a.n_qg = attn_shape<T, DH>(NQT, a.B * a.Hkv, &nqw, &nw);
   dim3 grid(a.n_splits, a.Hkv, a.B * a.n_qg);
   dim3 block(64 * nw);
   switch (nqw) {

@@ -98,7 +98,7 @@ struct AttnArgs {
 
 // Query groups per (sequence, kv head) of the attention launch and the query rows a
 // group spans (the merge of one group needs n_splits * rows floats of LDS scratch).
-int attn_query_groups(bool is_bf16, int dh, int T, int G, int* rows_per_group);
+int attn_query_groups(bool is_bf16, int dh, int T, int G, int heads, int* rows_per_group);
 constexpr int ATTN_MERGE_FLOATS = 4096;
 constexpr int ATTN_MAX_SPLITS = 32;
 

@@ -126,6 +126,26 @@ def test_parity_d2048(shape, lens, L_a, gamma):
     assert hd <= tol, hd
 
 
+def test_many_sequences_fine_query_groups():
+    """128 sequences x 2 kv heads fill the GPU with (sequence, head) pairs alone, so the
+    chunk attention splits each head's 5 query tiles into groups of at most 4 and takes
+    no key splits; logits and K/V match the oracle."""
+    shape = MINI_BF16_D128
+    B, L_a, gamma = 128, 8, 32
+    T = L_a + gamma
+    rng = np.random.default_rng(141)
+    lens = [int(x) for x in rng.integers(3, 60, size=B)]
+    print(f"case {shape.name} B={B} T={T} heads={B * shape.n_kv_heads}", flush=True)
+    w = make_weights(shape, seed=142, gain_noise=0.1)
+    kvh = make_random_kv(shape, lens, capacity=max(lens) + T, seed=143)
+    toks = _tokens(B, T, shape.vocab, 144)
+    g, o, ver, kv = run_pair(w, kvh, toks, L_a, perm_seed=145)
+    assert np.all(g["err"] == 0)
+    err, flagged, n = compare_logits(shape, g, o)
+    print(f"  logits rel err {err:.2e}; flagged {flagged}/{n}", flush=True)
+    compare_kv(shape, kv, o, lens, T)
+
+
 def test_attention_dominant_hidden():
     """Scaled q/k/o weights make attention dominate the residual stream, so a wrong
     attention kernel cannot hide under the FFN's contribution."""

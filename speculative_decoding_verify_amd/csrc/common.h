@@ -54,22 +54,6 @@ template <> SDV_DEV f32x4 mma16<float>(u32x4 a, u32x4 b, f32x4 c) {
   return c;
 }
 
-// Split 8 fp32 values (two 16-byte halves) into bf16 hi and lo parts,
-// x = hi + lo + O(2^-16 |x|): an activation enters a bf16 MFMA as two operands.
-SDV_DEV void split_hi_lo(u32x4 a, u32x4 b, u32x4& hi, u32x4& lo) {
-  const float x[8] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), __uint_as_float(a.w),
-                      __uint_as_float(b.x), __uint_as_float(b.y), __uint_as_float(b.z), __uint_as_float(b.w)};
-  uint32_t h[8], l[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const bf16 hb = f2bf(x[e]);
-    h[e] = hb;
-    l[e] = f2bf(x[e] - bf2f(hb));
-  }
-  hi.x = h[0] | (h[1] << 16); hi.y = h[2] | (h[3] << 16); hi.z = h[4] | (h[5] << 16); hi.w = h[6] | (h[7] << 16);
-  lo.x = l[0] | (l[1] << 16); lo.y = l[2] | (l[3] << 16); lo.z = l[4] | (l[5] << 16); lo.w = l[6] | (l[7] << 16);
-}
-
 // Split pairs: a bf16 model carries each activation value as x = hi + lo + O(2^-16 |x|),
 // two bf16 numbers that enter a bf16 MFMA as two operands.
 SDV_DEV void split1(float x, bf16& hi, bf16& lo) {
@@ -188,11 +172,6 @@ SDV_DEV bool arrive_last(uint32_t* counter, uint32_t n, int* flag) {
 // elements of T held in 16 bytes
 template <typename T> struct Vec16 { static constexpr int N = 16 / sizeof(T); };
 
-SDV_DEV float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
 SDV_DEV float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);

@@ -51,7 +51,7 @@ def gate_up_launch_bytes(sh, M):
 # each scaled by what the same counter reads for a plain 256 MiB device copy
 # (`bench.py --copy-calibration`).  Valid only for the workload and the kernel sources
 # they were taken on: both are checked at run time, else traffic is null.
-GATE_UP_TRAFFIC = {"workload": "1.7b-bf16", "sha256": "c6755a9464969bb08a3d22d066f32097f7fa672484b632ad2b0261532eb9a014",
+GATE_UP_TRAFFIC = {"workload": "1.7b-bf16", "sha256": "5b209530e9d26fa41f3b8d91226a0a25cb2a0b97fd293b8835c03e53e2ad44c8",
                    "fetch_kib": 34375.0, "fetch_factor": 262144.0 / 131084.0,
                    "write_kib": 1344.0, "write_factor": 262144.0 / 262144.0}
 GEMM_SOURCES = ("speculative_decoding_verify_amd/csrc/gemm.hip", "speculative_decoding_verify_amd/csrc/common.h",

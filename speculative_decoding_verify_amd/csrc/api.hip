@@ -60,8 +60,20 @@ GemmPlan plan_gemm(int M, int N, int K, bool bf, int epi) {
     const int wn = (long long)cdiv(ntiles, 16) * p.row_blocks >= TARGET_WG_GEMM ? 8 : 4;
     p.cfg = GemmCfg{wn, 3, true};   // 3 k steps in the LDS ring
     p.ncg = cdiv(ntiles, 2 * wn);
-    p.spp = steps;
-    p.S = 1;
+    // split-partials launches split K so that the grid's last round of workgroups is
+    // as full as possible (at least 16 k steps per split, at most 4 splits)
+    int S = 1;
+    if (epi == EPI_PARTIAL) {
+      const long long wg1 = (long long)p.ncg * p.row_blocks;
+      double best = 0.0;
+      for (int sp = 1; sp <= 4 && steps / sp >= 16; ++sp) {
+        const long long n = wg1 * sp;
+        const double eff = (double)n / (double)(cdiv(n, TARGET_WG_GEMM) * TARGET_WG_GEMM);
+        if (eff > best + 1e-9) { best = eff; S = sp; }
+      }
+    }
+    p.spp = cdiv(steps, S);
+    p.S = cdiv(steps, p.spp);
     return p;
   }
   p.MT = std::max(1, cdiv(M, 16));
@@ -209,7 +221,7 @@ sdv_status run_gemm(ProfEvents& pe, const Plan& P, const GemmPlan& g, GemmArgs a
   a.ldo = a.N;
   a.ldl = a.N;
   a.n_groups = g.ncg;
-  const dim3 grid = g.cfg.tiled ? dim3(g.row_blocks, 1, g.ncg) : dim3(g.ncg, g.S, g.row_blocks);
+  const dim3 grid = g.cfg.tiled ? dim3(g.row_blocks, g.S, g.ncg) : dim3(g.ncg, g.S, g.row_blocks);
   const bool prof = pe.ev && pe.next < pe.n_pairs;
   if (prof)
     SDV_LAUNCH(launch_gemm(P.bf, g.cfg, g.MT, g.epi, grid, a, s, (hipEvent_t)pe.ev[2 * pe.next],

@@ -322,8 +322,9 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs a) {
 // reads the blocks it multiplies from LDS, so each byte crosses the L2 -> CU path
 // once per workgroup instead of once per wave that uses it.  Grid: x = row blocks
 // (fastest, so the workgroups that share a column group's weights run together and
-// the weights come from HBM once), z = column groups.  The finished tile goes
-// through LDS (the ring's memory) to the shared epilogues.
+// the weights come from HBM once), y = splits of K (split-partials epilogue only), z =
+// column groups.  The finished tile goes through LDS (the ring's memory) to the shared
+// epilogues.
 SDV_DEV void lds_dma16(const void* g, void* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
@@ -363,6 +364,10 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmArgs a) {
   const int m_base = blockIdx.x * (16 * MT);
   const int cg = blockIdx.z;
   const int ksteps = a.K / KS;
+  // this workgroup's k steps [s0, s0 + nk): split blockIdx.y of the K range (fp32
+  // partials summed by the consumer; the other epilogues take the whole range)
+  const int s0 = blockIdx.y * a.steps_per_split;
+  const int nk = max(0, min(ksteps, s0 + a.steps_per_split) - s0);
   const int ntiles = (a.N + 15) >> 4;
   const int row_tiles = (a.M + 15) >> 4;
 
@@ -375,13 +380,13 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmArgs a) {
     const int c = wave + 4 * i;
     if (c < NT) {
       const int tile = min(cg * NT + c, ntiles - 1);
-      gp[i] = (const char*)a.W + (size_t)tile * ksteps * 1024 + lane * 16;
+      gp[i] = (const char*)a.W + ((size_t)tile * ksteps + s0) * 1024 + lane * 16;
       gstride[i] = 1024;
     } else {
       const int q = c - NT, mt8 = q / AL, h = q % AL;
       const int rt = min(blockIdx.x * MT + mt8, row_tiles - 1);
       const int rr = min(r, a.M - 1 - rt * 16);   // rows past M: the last row's chunk
-      gp[i] = (const char*)a.A + (size_t)rt * ksteps * (64 * KS) + h * 1024 + (lg * 16 + rr) * 16;
+      gp[i] = (const char*)a.A + ((size_t)rt * ksteps + s0) * (64 * KS) + h * 1024 + (lg * 16 + rr) * 16;
       gstride[i] = 64 * KS;
     }
   }
@@ -397,7 +402,6 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < WN; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = ksteps;
 #pragma unroll
   for (int u = 0; u < R - 1; ++u)
     if (u < nk) copy_step(u, u);
@@ -437,7 +441,7 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) tile[wm * 16 * WM + mt * 16 + 4 * lg + v][wn * 16 * WN + t * 16 + r] = acc[mt][t][v];
   __syncthreads();
-  gemm_epilogue<T, MT, NT, EPI>(a, tile, cg, 0, m_base, [&](int, int m, int i) {
+  gemm_epilogue<T, MT, NT, EPI>(a, tile, cg, blockIdx.y, m_base, [&](int, int m, int i) {
     if constexpr (EPI == EPI_QKV) return QkvItem{a.qkv.rope[(size_t)m * a.pair_n + i], a.qkv.kv_dst[m]};
     else return QkvItem{};
   });

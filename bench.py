@@ -51,7 +51,7 @@ def gate_up_launch_bytes(sh, M):
 # each scaled by what the same counter reads for a plain 256 MiB device copy
 # (`bench.py --copy-calibration`).  Valid only for the workload and the kernel sources
 # they were taken on: both are checked at run time, else traffic is null.
-GATE_UP_TRAFFIC = {"workload": "1.7b-bf16", "sha256": "5b209530e9d26fa41f3b8d91226a0a25cb2a0b97fd293b8835c03e53e2ad44c8",
+GATE_UP_TRAFFIC = {"workload": "1.7b-bf16", "sha256": "3fd1756377fb26717f44c72c32e48649ecad72433495398cd8bf9162b1b586fe",
                    "fetch_kib": 34375.0, "fetch_factor": 262144.0 / 131084.0,
                    "write_kib": 1344.0, "write_factor": 262144.0 / 262144.0}
 GEMM_SOURCES = ("speculative_decoding_verify_amd/csrc/gemm.hip", "speculative_decoding_verify_amd/csrc/common.h",

@@ -58,20 +58,38 @@ GEMM_SOURCES = ("speculative_decoding_verify_amd/csrc/gemm.hip", "speculative_de
                 "speculative_decoding_verify_amd/csrc/kernels.h")
 
 
-def gemm_source_sha():
+# the same for the row-statistics launch of the speculative-sampling acceptance
+# (64 x 7 drafts, V = 151936)
+ROW_STATS_TRAFFIC = {"workload": "sample", "sha256": "fbfca9f7a64e4cc888b3ebe1372631ccdd6ee92218f7685a8541ddb198a3834f",
+                     "fetch_kib": 284937.3, "fetch_factor": 262144.0 / 131084.0,
+                     "write_kib": 60.0, "write_factor": 262144.0 / 262144.0}
+SAMPLE_SOURCES = ("speculative_decoding_verify_amd/csrc/accept.hip", "speculative_decoding_verify_amd/csrc/common.h",
+                  "speculative_decoding_verify_amd/csrc/kernels.h")
+
+
+def source_sha(files):
     import hashlib
     h = hashlib.sha256()
-    for f in GEMM_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def gate_up_traffic(workload):
-    t = GATE_UP_TRAFFIC
-    if not t or t["workload"] != workload or t["sha256"] != gemm_source_sha():
+def gemm_source_sha():
+    return source_sha(GEMM_SOURCES)
+
+
+def counter_traffic(t, workload, files):
+    """HBM bytes per launch from stored counter readings, or None once the kernel's
+    sources differ from those the counters were taken on."""
+    if not t or t["workload"] != workload or t["sha256"] != source_sha(files):
         return None
     return (t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"]) * 1024.0
+
+
+def gate_up_traffic(workload):
+    return counter_traffic(GATE_UP_TRAFFIC, workload, GEMM_SOURCES)
 
 
 def cpu_threads():
@@ -409,23 +427,47 @@ def bench_sample(args):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t_start) / args.steps * 1e3
     nbytes = si.target_logits.nbytes + si.draft_logits.nbytes
+
+    # live duration of the row-statistics launch (it reads every logit once), from two
+    # HIP events the library records on the launch stream, over K more steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    stats_ms = []
+    for i in range(args.steps):
+        c = copies[i & 1]
+        smp(c["tgt"], c["drf"], c["drafts"], c["ua"], c["us"], 1.0, prof_events=ev)
+        torch.cuda.synchronize()
+        stats_ms.append(ev[0].elapsed_time(ev[1]))
+    stats_us = float(np.mean(stats_ms)) * 1e3
+    rows = B * (2 * k + 1)
+    stats_bytes = nbytes + rows * (4 + 8)           # logits in; row maximum (fp32) and sum (fp64) out
+    achieved = stats_bytes / (stats_us * 1e-6) / 1e9
     out = {
         "metric": METRIC, "value": B * k / (ms * 1e-3), "unit": "draft positions/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"speculative-sampling acceptance: {B} seqs x {k} drafts, V={V}, fp32"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": counter_traffic(ROW_STATS_TRAFFIC, "sample", SAMPLE_SOURCES),
+                     "kernel": "spec_row_stats_kernel (maximum and exponential sum of every logit row)",
+                     "bytes_per_launch": stats_bytes, "avg_launch_us": stats_us},
         "pass_roofline": {"bound": "hbm", "bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
                           "peak_GBs": HBM_PEAK_GBS, "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "setup_s": setup_s,
     }
     if not args.no_cpu_baseline:
         from oracle import spec_sampling as ss
-        t0 = time.perf_counter()
-        ss.accept_sample(si.target_logits.astype(np.float64), si.draft_logits.astype(np.float64), si.drafts,
-                         si.u_accept, si.u_sample)
-        dt = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": B * k / dt, "unit": "draft positions/s", "cores": cpu_threads(),
-                               "kind": "oracle", "sample": f"one full batch ({B}x{k}, V={V}), {dt:.2f} s"}
+        tgt64, drf64 = si.target_logits.astype(np.float64), si.draft_logits.astype(np.float64)
+        # repeat the full batch until about 10 s of CPU work have been timed
+        reps, dt = 0, 0.0
+        while dt < 10.0 and reps < 100:
+            t0 = time.perf_counter()
+            ss.accept_sample(tgt64, drf64, si.drafts, si.u_accept, si.u_sample)
+            dt += time.perf_counter() - t0
+            reps += 1
+        out["cpu_baseline"] = {"value": reps * B * k / dt, "unit": "draft positions/s", "cores": cpu_threads(),
+                               "kind": "oracle",
+                               "sample": f"{reps} full batches ({B}x{k}, V={V}) in {dt:.1f} s"}
     return out
 
 

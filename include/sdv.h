@@ -249,13 +249,18 @@ sdv_status sdv_accept_greedy(int32_t batch, int32_t T, int32_t L_a, const int32_
  *   returns the smallest index whose running sum exceeds u * total, with weights
  *   quantised to 2^-40 so the draw does not depend on summation order.
  *   u_accept [B, k], u_sample [B, k+1]: fp64 uniforms in [0, 1) (the caller draws them).
- *   Outputs n_out [B], tok_out [B] (int32). */
+ *   Logits of -inf (masked vocabulary entries) have probability 0; every row needs at
+ *   least one finite logit.
+ *   Outputs n_out [B], tok_out [B] (int32).
+ *   prof_events: nullable host array of 2 caller-created hipEvent_t handles; when
+ *   given, the launch that reads every logit row (maximum and exponential sum per
+ *   row) records event 0 when it starts and event 1 when it ends. */
 size_t sdv_sample_workspace_size(int32_t batch, int32_t k, int32_t vocab);
 sdv_status sdv_accept_sample(int32_t batch, int32_t k, int32_t vocab, const float* tgt_logits,
                              const float* drf_logits, const int32_t* drafts,
                              const double* u_accept, const double* u_sample, float temperature,
                              int32_t* n_out, int32_t* tok_out, void* workspace,
-                             size_t workspace_bytes, void* stream);
+                             size_t workspace_bytes, void* const* prof_events, void* stream);
 
 /* KV commit / rollback (step 4: roll the cache back to x_{<t}; commit n + 1 tokens).
  *   keep_len [B]: new committed length per sequence (seq_len[b] := keep_len[b]).

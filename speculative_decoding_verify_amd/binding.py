@@ -100,7 +100,7 @@ def lib():
                                        ctypes.c_size_t, _vp]
         L.sdv_accept_sample.restype = ctypes.c_int
         L.sdv_accept_sample.argtypes = [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
-                                        _vp, _vp, _vp, ctypes.c_size_t, _vp]
+                                        _vp, _vp, _vp, ctypes.c_size_t, ctypes.POINTER(_vp), _vp]
         _LIB = L
     return _LIB
 
@@ -390,9 +390,20 @@ class Sampler:
         self.tok = torch.empty(B, dtype=torch.int32, device=device)
 
     def __call__(self, tgt: torch.Tensor, drf: torch.Tensor, drafts: torch.Tensor, u_acc: torch.Tensor,
-                 u_smp: torch.Tensor, temperature: float = 1.0, stream=None):
+                 u_smp: torch.Tensor, temperature: float = 1.0, stream=None, prof_events=None):
+        """prof_events: None or two torch.cuda.Event (enable_timing=True) that the
+        library records around its row-statistics launch."""
+        ev = None
+        if prof_events is not None:
+            if len(prof_events) != 2:
+                raise ValueError("prof_events takes exactly two events")
+            for e in prof_events:     # torch creates the underlying event on first record
+                e.record()
+            ev = (_vp * 2)(*[e.cuda_event for e in prof_events])
         _check(lib().sdv_accept_sample(self.B, self.k, self.V, _ptr(tgt), _ptr(drf), _ptr(drafts), _ptr(u_acc),
                                        _ptr(u_smp), float(temperature), _ptr(self.n), _ptr(self.tok),
-                                       _ptr(self.workspace), self.workspace.numel(), _stream(stream)),
+                                       _ptr(self.workspace), self.workspace.numel(),
+                                       None if ev is None else ctypes.cast(ev, ctypes.POINTER(_vp)),
+                                       _stream(stream)),
                "sdv_accept_sample")
         return self.n, self.tok

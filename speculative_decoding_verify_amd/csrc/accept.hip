@@ -6,6 +6,8 @@
 // Speculative sampling follows "speculative-decoding-omni" (page 3), section 2:
 // accept x with probability min(1, p(x)/q(x)), on the first rejection draw from
 // norm(max(0, p - q)), otherwise a bonus draw from p.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -166,6 +168,15 @@ SDV_DEV void ms_merge(float& m, double& s, float m2, double s2, float c) {
   else s += s2 * (double)exp2f((m2 - m) * c);
 }
 
+// Masked vocabulary entries (logit -inf) have probability 0.  While a thread has
+// seen nothing but -inf its maximum is -inf and its sum 0; the exponent then takes
+// 0 in place of the maximum so that the -inf terms add 0 instead of NaN.
+SDV_DEV float safe_max(float m) { return m == -INFINITY ? 0.f : m; }
+
+// one workgroup per logit row; each thread issues SR 16-byte loads before any
+// arithmetic, so a wave keeps SR KB of the row in flight
+static constexpr int SR = 8;
+
 __global__ __launch_bounds__(256) void spec_row_stats_kernel(SampleArgs a) {
   const int row = blockIdx.x;
   const int nt = a.B * (a.k + 1);
@@ -173,19 +184,36 @@ __global__ __launch_bounds__(256) void spec_row_stats_kernel(SampleArgs a) {
   const float c = LOG2E * a.inv_temp;
   float m = -INFINITY;
   double s = 0.0;
-  // online max / sum; 16-byte loads when the row is aligned
+  // online max / sum over 16-byte loads when the row is aligned
   const bool vec = ((reinterpret_cast<uintptr_t>(z) & 15) == 0);
   const int nv = vec ? a.V / 4 : 0;
-  for (int i = threadIdx.x; i < nv; i += 256) {
-    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(z) + i);
+  const f32x4* zv = reinterpret_cast<const f32x4*>(z);
+  int i = threadIdx.x;
+  for (; i + (SR - 1) * 256 < nv; i += SR * 256) {
+    f32x4 v[SR];
+#pragma unroll
+    for (int u = 0; u < SR; ++u) v[u] = __builtin_nontemporal_load(zv + i + u * 256);
+    float vm = m;
+#pragma unroll
+    for (int u = 0; u < SR; ++u) vm = fmaxf(vm, fmaxf(fmaxf(v[u].x, v[u].y), fmaxf(v[u].z, v[u].w)));
+    if (vm > m) { s = s * (double)exp2f((m - vm) * c); m = vm; }
+    const float me = safe_max(m);
+#pragma unroll
+    for (int u = 0; u < SR; ++u)
+      s += (double)(exp2f((v[u].x - me) * c) + exp2f((v[u].y - me) * c) + exp2f((v[u].z - me) * c) +
+                    exp2f((v[u].w - me) * c));
+  }
+  for (; i < nv; i += 256) {
+    const f32x4 v = __builtin_nontemporal_load(zv + i);
     const float vm = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
     if (vm > m) { s = s * (double)exp2f((m - vm) * c); m = vm; }
-    s += (double)(exp2f((v.x - m) * c) + exp2f((v.y - m) * c) + exp2f((v.z - m) * c) + exp2f((v.w - m) * c));
+    const float me = safe_max(m);
+    s += (double)(exp2f((v.x - me) * c) + exp2f((v.y - me) * c) + exp2f((v.z - me) * c) + exp2f((v.w - me) * c));
   }
-  for (int i = nv * 4 + threadIdx.x; i < a.V; i += 256) {
-    const float v = z[i];
+  for (int j = nv * 4 + threadIdx.x; j < a.V; j += 256) {
+    const float v = z[j];
     if (v > m) { s = s * (double)exp2f((m - v) * c); m = v; }
-    s += (double)exp2f((v - m) * c);
+    s += (double)exp2f((v - safe_max(m)) * c);
   }
   // block merge in a fixed pattern
   __shared__ float sm[256];
@@ -214,128 +242,276 @@ SDV_DEV double prob_at(float zx, float m, double s, float inv_temp) {
   return exp2((double)(zx - m) * (1.4426950408889634 * (double)inv_temp)) / s;
 }
 
-__global__ void spec_decide_kernel(SampleArgs a) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= a.B) return;
+// Position of sequence b's draw: the first draft position whose test fails, or k
+// when every draft passes.  Called by the 64 lanes of one wave: lane i of each
+// group of 64 positions evaluates position base + i, the ballot keeps the lowest
+// failing position.  A draft outside q's support (q(x) = 0) passes iff p(x) > 0.
+SDV_DEV int draw_position(const SampleArgs& a, int b) {
   const int nt = a.B * (a.k + 1);
-  int pos = a.k;
-  for (int i = 0; i < a.k; ++i) {
-    int x = a.drafts[(size_t)b * a.k + i];
-    x = min(max(x, 0), a.V - 1);
-    const int rt = b * (a.k + 1) + i, rd = nt + b * a.k + i;
-    const double px = prob_at(a.tgt[(size_t)rt * a.V + x], a.row_m[rt], a.row_s[rt], a.inv_temp);
-    const double qx = prob_at(a.drf[(size_t)(rd - nt) * a.V + x], a.row_m[rd], a.row_s[rd], a.inv_temp);
-    const bool acc = qx > 0.0 ? a.u_acc[(size_t)b * a.k + i] < px / qx : px > 0.0;
-    if (!acc) { pos = i; break; }
+  const int lane = threadIdx.x & 63;
+  for (int base = 0; base < a.k; base += 64) {
+    const int i = base + lane;
+    bool rej = false;
+    if (i < a.k) {
+      int x = a.drafts[(size_t)b * a.k + i];
+      x = min(max(x, 0), a.V - 1);
+      const int rt = b * (a.k + 1) + i, rd = nt + b * a.k + i;
+      const double px = prob_at(a.tgt[(size_t)rt * a.V + x], a.row_m[rt], a.row_s[rt], a.inv_temp);
+      const double qx = prob_at(a.drf[(size_t)(rd - nt) * a.V + x], a.row_m[rd], a.row_s[rd], a.inv_temp);
+      const bool acc = qx > 0.0 ? a.u_acc[(size_t)b * a.k + i] < px / qx : px > 0.0;
+      rej = !acc;
+    }
+    const unsigned long long mask = __ballot(rej);
+    if (mask) return base + __ffsll(mask) - 1;
   }
-  a.first_rej[b] = pos;
-  a.n_out[b] = pos;
+  return a.k;
 }
 
-// quantised weight of index v for the draw of sequence b: max(0, p - q) at a
-// rejection (which = 0) or p (which = 1, also the bonus row)
-SDV_DEV long long qweight(const SampleArgs& a, int b, int pos, int v, int which) {
+// The two rows a draw at position `pos` reads: p_pos, and q_pos at a rejection
+// (pos < k); each with its maximum and 1/sum.
+struct DrawRows {
+  const float* zp;
+  const float* zq;  // nullptr for the bonus draw (pos == k)
+  float pm, qm, pinv, qinv, c;
+};
+
+SDV_DEV DrawRows draw_rows(const SampleArgs& a, int b, int pos) {
   const int nt = a.B * (a.k + 1);
-  const float c = LOG2E * a.inv_temp;
   const int rt = b * (a.k + 1) + pos;
-  const float p = exp2f((a.tgt[(size_t)rt * a.V + v] - a.row_m[rt]) * c) * (float)(1.0 / a.row_s[rt]);
-  float w = p;
-  if (which == 0 && pos < a.k) {
+  DrawRows r;
+  r.c = LOG2E * a.inv_temp;
+  r.zp = a.tgt + (size_t)rt * a.V;
+  r.pm = a.row_m[rt];
+  r.pinv = (float)(1.0 / a.row_s[rt]);
+  r.zq = nullptr;
+  r.qm = 0.f;
+  r.qinv = 0.f;
+  if (pos < a.k) {
     const int rd = nt + b * a.k + pos;
-    const float q = exp2f((a.drf[(size_t)(rd - nt) * a.V + v] - a.row_m[rd]) * c) * (float)(1.0 / a.row_s[rd]);
+    r.zq = a.drf + (size_t)(rd - nt) * a.V;
+    r.qm = a.row_m[rd];
+    r.qinv = (float)(1.0 / a.row_s[rd]);
+  }
+  return r;
+}
+
+// floor(w * 2^40) for w in [0, 1]: the quantised weight
+SDV_DEV long long quantise(float w) { return (long long)((double)w * 1099511627776.0); }
+
+// Quantised weights of one vocabulary entry from its two logits: w0 = max(0, p - q)
+// at a rejection (p at the bonus position), w1 = p.  Contraction is off so that the
+// sum pass and the search pass compute bit-identical weights.
+SDV_DEV void pair_weights(const DrawRows& r, bool has_q, float zp, float zq, long long& w0, long long& w1) {
+#pragma clang fp contract(off)
+  const float p = exp2f((zp - r.pm) * r.c) * r.pinv;
+  float w = p;
+  if (has_q) {
+    const float q = exp2f((zq - r.qm) * r.c) * r.qinv;
     w = fmaxf(0.f, p - q);
   }
-  return (long long)((double)w * 1099511627776.0);  // floor(w * 2^40), w >= 0
+  w0 = quantise(w);
+  w1 = quantise(p);
 }
 
+// One workgroup per (chunk of the vocabulary, sequence): wave 0 takes the accept /
+// reject decision of the sequence (the chunk-0 workgroup writes it out), then every
+// thread sums the quantised weights of its share of the chunk for both draws.
 __global__ __launch_bounds__(256) void spec_chunk_sum_kernel(SampleArgs a) {
   const int b = blockIdx.y, ch = blockIdx.x;
-  const int pos = a.first_rej[b];
+  __shared__ int pos_s;
+  if (threadIdx.x < 64) {
+    const int pos = draw_position(a, b);
+    if (threadIdx.x == 0) {
+      pos_s = pos;
+      if (ch == 0) {
+        a.first_rej[b] = pos;
+        a.n_out[b] = pos;
+      }
+    }
+  }
+  __syncthreads();
+  const int pos = pos_s;
+  const DrawRows r = draw_rows(a, b, pos);
+  const bool has_q = r.zq != nullptr;
+  const float* zq = has_q ? r.zq : r.zp;
   const int v0 = ch * a.chunk, v1 = min(a.V, v0 + a.chunk);
   long long s0 = 0, s1 = 0;
-  for (int v = v0 + threadIdx.x; v < v1; v += 256) {
-    s0 += qweight(a, b, pos, v, 0);
-    s1 += qweight(a, b, pos, v, 1);
+  const bool vec = ((reinterpret_cast<uintptr_t>(r.zp + v0) | reinterpret_cast<uintptr_t>(zq + v0)) & 15) == 0;
+  const int n4 = vec ? (v1 - v0) >> 2 : 0;
+  const f32x4* p4 = reinterpret_cast<const f32x4*>(r.zp + v0);
+  const f32x4* q4 = reinterpret_cast<const f32x4*>(zq + v0);
+  for (int j0 = threadIdx.x; j0 < n4; j0 += 4 * 256) {
+    f32x4 x[4], y[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = min(j0 + u * 256, n4 - 1);
+      x[u] = p4[j];
+      y[u] = q4[j];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (j0 + u * 256 < n4) {
+        long long w0, w1;
+        pair_weights(r, has_q, x[u].x, y[u].x, w0, w1); s0 += w0; s1 += w1;
+        pair_weights(r, has_q, x[u].y, y[u].y, w0, w1); s0 += w0; s1 += w1;
+        pair_weights(r, has_q, x[u].z, y[u].z, w0, w1); s0 += w0; s1 += w1;
+        pair_weights(r, has_q, x[u].w, y[u].w, w0, w1); s0 += w0; s1 += w1;
+      }
+    }
   }
-  __shared__ long long r0[256], r1[256];
-  r0[threadIdx.x] = s0;
-  r1[threadIdx.x] = s1;
+  for (int v = v0 + n4 * 4 + threadIdx.x; v < v1; v += 256) {
+    long long w0, w1;
+    pair_weights(r, has_q, r.zp[v], zq[v], w0, w1);
+    s0 += w0;
+    s1 += w1;
+  }
+  // integer sums: exact in any order
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    s0 += __shfl_xor(s0, o, 64);
+    s1 += __shfl_xor(s1, o, 64);
+  }
+  __shared__ long long r0[4], r1[4];
+  if ((threadIdx.x & 63) == 0) {
+    r0[threadIdx.x >> 6] = s0;
+    r1[threadIdx.x >> 6] = s1;
+  }
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) { r0[threadIdx.x] += r0[threadIdx.x + o]; r1[threadIdx.x] += r1[threadIdx.x + o]; }
-    __syncthreads();
-  }
   if (threadIdx.x == 0) {
-    a.chunk_sum[((size_t)b * a.n_chunks + ch) * 2] = r0[0];
-    a.chunk_sum[((size_t)b * a.n_chunks + ch) * 2 + 1] = r1[0];
+    a.chunk_sum[((size_t)b * a.n_chunks + ch) * 2] = r0[0] + r0[1] + r0[2] + r0[3];
+    a.chunk_sum[((size_t)b * a.n_chunks + ch) * 2 + 1] = r1[0] + r1[1] + r1[2] + r1[3];
   }
 }
 
-// inverse CDF: smallest v with (running sum of weights up to v) > floor(u * total)
+// Inclusive prefix sum of one value per thread over the 256 threads: a shuffle scan
+// inside each wave, then the totals of the lower waves (through `wtot`, 4 entries
+// that no other call uses).  Also returns the block total.
+SDV_DEV long long block_scan(long long v, long long* wtot, long long& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const long long t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  if (lane == 63) wtot[w] = v;
+  __syncthreads();
+  long long below = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const long long t = wtot[i];
+    below += i < w ? t : 0;
+    total += t;
+  }
+  return v + below;
+}
+
+// Inverse CDF of sequence b's draw: the smallest index v whose running sum of
+// quantised weights exceeds floor(u * total).  The draw takes the residual weights;
+// when they are all zero (p == q on this position) it takes p.  Threads own
+// contiguous runs, first of chunks (their sums from the previous kernel), then of
+// the selected chunk's entries (weights staged in LDS by coalesced loads); a prefix
+// scan finds the run that holds the crossing and its thread walks it.
 __global__ __launch_bounds__(256) void spec_find_kernel(SampleArgs a) {
+  constexpr int PER = SAMPLE_CHUNK / 256;
+  static_assert((PER & (PER - 1)) == 0, "entries per thread must be a power of two");
   const int b = blockIdx.x;
+  __shared__ long long wts[SAMPLE_CHUNK];
+  __shared__ long long wtot[3][4];
+  __shared__ int sel_s;
+  __shared__ long long rem_s;
   const int pos = a.first_rej[b];
-  __shared__ long long pre[257];
-  __shared__ int sel_chunk, which_s;
-  __shared__ long long target_s;
+  const long long* cs = a.chunk_sum + (size_t)b * a.n_chunks * 2;
+  const int cper = (a.n_chunks + 255) / 256;
+  const int c0 = min(a.n_chunks, (int)threadIdx.x * cper), c1 = min(a.n_chunks, c0 + cper);
+  long long t0 = 0, t1 = 0;
+  for (int c = c0; c < c1; ++c) {
+    t0 += cs[2 * c];
+    t1 += cs[2 * c + 1];
+  }
+  long long S0, S1;
+  const long long inc0 = block_scan(t0, wtot[0], S0);
+  const long long inc1 = block_scan(t1, wtot[1], S1);
+  const int which = S0 > 0 ? 0 : 1;
+  const long long S = which == 0 ? S0 : S1;
+  const double u = a.u_smp[(size_t)b * (a.k + 1) + pos];
+  long long target = (long long)(u * (double)S);
+  if (target >= S) target = S - 1;
+  if (target < 0) target = 0;
+  // the chunk holding the crossing (the last chunk when the total is zero)
   if (threadIdx.x == 0) {
-    int which = 0;
-    long long S = 0;
-    for (int c = 0; c < a.n_chunks; ++c) S += a.chunk_sum[((size_t)b * a.n_chunks + c) * 2];
-    if (S <= 0) {  // empty residual (p == q): draw from p
-      which = 1;
-      S = 0;
-      for (int c = 0; c < a.n_chunks; ++c) S += a.chunk_sum[((size_t)b * a.n_chunks + c) * 2 + 1];
-    }
-    const double u = a.u_smp[(size_t)b * (a.k + 1) + pos];
-    long long target = (long long)(u * (double)S);
-    if (target >= S) target = S - 1;
-    if (target < 0) target = 0;
-    long long run = 0;
-    int c = 0;
-    for (; c < a.n_chunks; ++c) {
-      const long long cs = a.chunk_sum[((size_t)b * a.n_chunks + c) * 2 + which];
-      if (run + cs > target) break;
-      run += cs;
-    }
-    if (c >= a.n_chunks) c = a.n_chunks - 1;
-    sel_chunk = c;
-    which_s = which;
-    target_s = target - run;
+    sel_s = a.n_chunks - 1;
+    rem_s = 0;
   }
   __syncthreads();
-  const int c = sel_chunk, which = which_s;
-  const long long target = target_s;
-  const int v0 = c * a.chunk, v1 = min(a.V, v0 + a.chunk);
-  // each thread owns a contiguous run of the chunk
-  const int per = (a.chunk + 255) / 256;
-  const int my0 = v0 + threadIdx.x * per, my1 = min(v1, my0 + per);
-  long long mine = 0;
-  for (int v = my0; v < my1; ++v) mine += qweight(a, b, pos, v, which);
-  pre[threadIdx.x + 1] = mine;
-  if (threadIdx.x == 0) pre[0] = 0;
-  __syncthreads();
-  if (threadIdx.x == 0)
-    for (int i = 1; i <= 256; ++i) pre[i] += pre[i - 1];
-  __syncthreads();
-  // the thread whose run contains the crossing finds the index
-  if (pre[threadIdx.x] <= target && pre[threadIdx.x + 1] > target) {
-    long long run = pre[threadIdx.x];
-    int tok = my1 - 1;
-    for (int v = my0; v < my1; ++v) {
-      run += qweight(a, b, pos, v, which);
-      if (run > target) { tok = v; break; }
+  {
+    const long long inc = which == 0 ? inc0 : inc1;
+    long long run = inc - (which == 0 ? t0 : t1);
+    if (run <= target && inc > target) {
+      for (int c = c0; c < c1; ++c) {
+        const long long w = cs[2 * c + which];
+        if (run + w > target) {
+          sel_s = c;
+          rem_s = target - run;
+          break;
+        }
+        run += w;
+      }
     }
-    a.tok_out[b] = tok;
   }
-  // no crossing inside the chunk can only come from an empty chunk selection
-  if (threadIdx.x == 0 && pre[256] <= target) a.tok_out[b] = v1 - 1;
+  __syncthreads();
+  const int c = sel_s;
+  const long long rem = rem_s;
+  const int v0 = c * SAMPLE_CHUNK, n = min(a.V - v0, SAMPLE_CHUNK);
+  const DrawRows r = draw_rows(a, b, pos);
+  const bool has_q = r.zq != nullptr;
+  const float* zp = r.zp + v0;
+  const float* zq = (has_q ? r.zq : r.zp) + v0;
+  // stage the chosen weights of the chunk: entry j = threadIdx.x + 256 u
+  {
+    float xp[PER], xq[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int j = min((int)threadIdx.x + 256 * u, n - 1);
+      xp[u] = zp[j];
+      xq[u] = zq[j];
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int j = threadIdx.x + 256 * u;
+      long long w0, w1;
+      pair_weights(r, has_q, xp[u], xq[u], w0, w1);
+      wts[j] = j < n ? (which == 0 ? w0 : w1) : 0;
+    }
+  }
+  __syncthreads();
+  // thread t owns entries t*PER .. t*PER + PER - 1
+  const long long* mw = wts + threadIdx.x * PER;
+  long long mine = 0;  // summed in a lane-rotated order (fewer LDS bank conflicts; exact)
+#pragma unroll
+  for (int i = 0; i < PER; ++i) mine += mw[(i + threadIdx.x) & (PER - 1)];
+  long long total;
+  const long long inc = block_scan(mine, wtot[2], total);
+  long long run = inc - mine;
+  if (run <= rem && inc > rem) {
+    int j = PER - 1;
+    for (int i = 0; i < PER; ++i) {
+      run += mw[i];
+      if (run > rem) {
+        j = i;
+        break;
+      }
+    }
+    a.tok_out[b] = v0 + threadIdx.x * PER + j;
+  }
+  // no crossing inside the chunk: only when the total weight is zero (invalid rows)
+  if (threadIdx.x == 0 && total <= rem) a.tok_out[b] = v0 + n - 1;
 }
 
-hipError_t launch_accept_sample(const SampleArgs& a, hipStream_t s) {
+hipError_t launch_accept_sample(const SampleArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int rows = a.B * (2 * a.k + 1);
-  spec_row_stats_kernel<<<rows, 256, 0, s>>>(a);
-  spec_decide_kernel<<<(a.B + 63) / 64, 64, 0, s>>>(a);
+  if (ev0) hipExtLaunchKernelGGL(spec_row_stats_kernel, dim3(rows), dim3(256), 0, s, ev0, ev1, 0, a);
+  else spec_row_stats_kernel<<<rows, 256, 0, s>>>(a);
   spec_chunk_sum_kernel<<<dim3(a.n_chunks, a.B), 256, 0, s>>>(a);
   spec_find_kernel<<<a.B, 256, 0, s>>>(a);
   return hipGetLastError();

@@ -470,7 +470,6 @@ sdv_status sdv_kv_rollback(const sdv_model* m, const sdv_kv* kv, const int32_t* 
   return SDV_OK;
 }
 
-static const int SAMPLE_CHUNK = 4096;
 
 size_t sdv_sample_workspace_size(int32_t B, int32_t k, int32_t V) {
   if (B < 1 || k < 1 || V < 2) return 0;
@@ -482,7 +481,8 @@ size_t sdv_sample_workspace_size(int32_t B, int32_t k, int32_t V) {
 
 sdv_status sdv_accept_sample(int32_t B, int32_t k, int32_t V, const float* tgt, const float* drf,
                              const int32_t* drafts, const double* u_acc, const double* u_smp, float temperature,
-                             int32_t* n_out, int32_t* tok_out, void* ws, size_t ws_bytes, void* stream) {
+                             int32_t* n_out, int32_t* tok_out, void* ws, size_t ws_bytes, void* const* prof_events,
+                             void* stream) {
   if (!tgt || !drf || !drafts || !u_acc || !u_smp || !n_out || !tok_out) return fail(SDV_ERR_NULL, "NULL argument");
   if (B < 1 || k < 1 || V < 2) return fail(SDV_ERR_SHAPE, "B/k/V out of range");
   if (!(temperature > 0.f)) return fail(SDV_ERR_SHAPE, "temperature must be > 0");
@@ -511,7 +511,8 @@ sdv_status sdv_accept_sample(int32_t B, int32_t k, int32_t V, const float* tgt, 
   a.n_chunks = cdiv(V, SAMPLE_CHUNK);
   a.n_out = n_out;
   a.tok_out = tok_out;
-  SDV_LAUNCH(launch_accept_sample(a, (hipStream_t)stream));
+  SDV_LAUNCH(launch_accept_sample(a, (hipStream_t)stream, prof_events ? (hipEvent_t)prof_events[0] : nullptr,
+                                  prof_events ? (hipEvent_t)prof_events[1] : nullptr));
   return SDV_OK;
 }
 

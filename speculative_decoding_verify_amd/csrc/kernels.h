@@ -229,6 +229,9 @@ struct RollbackArgs {
 };
 hipError_t launch_kv_rollback(const RollbackArgs& a, hipStream_t s);
 
+// vocabulary entries per chunk of the sampling draw (one workgroup sums a chunk)
+constexpr int SAMPLE_CHUNK = 4096;
+
 struct SampleArgs {
   int B, k, V;
   const float* tgt;         // [B, k+1, V]
@@ -241,10 +244,11 @@ struct SampleArgs {
   double* row_s;            // [..] sum_v 2^((z_v - max) * log2(e) / temperature)
   int32_t* first_rej;       // [B] position of the draw (first rejection, or k)
   long long* chunk_sum;     // [B][n_chunks][2] quantised weights: draw row, p row
-  int n_chunks, chunk;
+  int n_chunks, chunk;      // chunk == SAMPLE_CHUNK
   int32_t* n_out;
   int32_t* tok_out;
 };
-hipError_t launch_accept_sample(const SampleArgs& a, hipStream_t s);
+// ev0 / ev1 (nullable): recorded at the start and end of the row-statistics launch
+hipError_t launch_accept_sample(const SampleArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 
 }  // namespace sdv

@@ -73,3 +73,41 @@ def test_sampling_parity_full_size():
     si = make_sample_inputs(SAMPLE_FULL)
     flagged = _check(si)
     print(f"flagged {flagged} / {SAMPLE_FULL.batch}", flush=True)
+
+
+def test_sampling_masked_logits():
+    """Logits of -inf have probability 0.  Some rows are masked over their first 12000
+    entries, longer than any thread's first group of loads, so threads start on -inf;
+    some drafts sit on entries masked in q only (accepted iff p can produce them) or in
+    both (always rejected)."""
+    w = SampleWorkload(batch=12, k=4, vocab=20011, seed=970)
+    si = make_sample_inputs(w)
+    rng = np.random.default_rng(971)
+    ninf = np.float32(-np.inf)
+    for arr in (si.target_logits, si.draft_logits):
+        mask = rng.random(arr.shape) < 0.3
+        arr[mask] = ninf
+        arr[:, 1, :12000] = ninf
+    # keep at least the rows' largest entries finite so every row has support
+    si.target_logits[:, :, 12000] = 3.0
+    si.draft_logits[:, :, 12001] = 3.0
+    for b in range(0, 12, 3):
+        x = int(si.drafts[b, 0])
+        si.draft_logits[b, 0, x] = ninf          # q(x) = 0
+        if b % 2 == 0:
+            si.target_logits[b, 0, x] = ninf     # and p(x) = 0
+    with np.errstate(invalid="ignore"):
+        _check(si)
+    n, tok = _run(si)
+    on, otok, _ = ss.accept_sample(si.target_logits.astype(np.float64), si.draft_logits.astype(np.float64),
+                                   si.drafts, si.u_accept, si.u_sample)
+    rows = np.arange(12)
+    tgt_at = si.target_logits[rows, n, tok]
+    assert np.all(np.isfinite(tgt_at))   # an emitted token is never masked in p
+
+
+def test_sampling_more_chunks_than_threads():
+    """V = 1,100,003: 269 chunks of 4096 entries, more than the 256 threads of the
+    draw's workgroup (several chunks per thread), and a ragged last chunk."""
+    w = SampleWorkload(batch=3, k=2, vocab=1_100_003, seed=980)
+    _check(make_sample_inputs(w))

@@ -196,3 +196,29 @@ def test_inverse_cdf_is_smallest_index_over_threshold():
     assert ss.inverse_cdf(w, 0.26)[0] == 3
     assert ss.inverse_cdf(w, 0.76)[0] == 4
     assert ss.inverse_cdf(w, 0.999999)[0] == 4
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_masked_vocabulary_entries(seed):
+    """Logits of -inf (masked entries) have probability 0: the emitted token still has
+    distribution p (section 2's losslessness, now with zeros in p and q), so a token
+    masked in p is never emitted, and a draft outside q's support is accepted exactly
+    when p can produce it."""
+    rng = np.random.default_rng(40 + seed)
+    V = 5 + seed % 2
+    p = rng.dirichlet(np.ones(V))
+    q = rng.dirichlet(np.ones(V))
+    p[rng.choice(V, 2, replace=False)] = 0.0
+    q[rng.choice(V, 2, replace=False)] = 0.0
+    p /= p.sum()
+    q /= q.sum()
+    with np.errstate(divide="ignore"):
+        dist, acc = _enumerate_first_token(p, q, n_acc=2048, n_smp=1024)
+        assert np.all(dist[p == 0.0] == 0.0)
+        assert acc == pytest.approx(1.0 - ss.total_variation(p, q), abs=2.0 / 2048)
+        np.testing.assert_allclose(dist, p, atol=3.0 / 1024)
+        tgt, drf = np.log(np.stack([p, p])), np.log(q)[None, :]
+    for x in np.nonzero(q == 0.0)[0]:
+        n, tok, _ = ss.accept_one_sequence(tgt, drf, [int(x)], [0.999], [0.5, 0.5])
+        assert n == (1 if p[x] > 0.0 else 0)
+        assert p[tok] > 0.0

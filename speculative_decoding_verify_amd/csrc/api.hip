@@ -84,6 +84,19 @@ GemmPlan plan_gemm(int M, int N, int K, bool bf, int epi) {
   if (epi == EPI_QKV || (epi == EPI_PARTIAL && p.MT < 4 && ntiles <= 128 && K <= 4096)) p.cfg = GemmCfg{2, 4};
   else if (epi == EPI_PARTIAL && K <= 4096) p.cfg = GemmCfg{4, 2};
   else if (epi == EPI_LOGITS && p.MT <= 2) p.cfg = GemmCfg{4, 4};
+  else if (epi == EPI_LOGITS && p.MT == 3) p.cfg = GemmCfg{6, 2};  // 2 waves per SIMD fit (8 tiles: 1)
+  else if (epi == EPI_SWIGLU && p.MT >= 4) {
+    // at 4-5 row tiles the activation re-reads (one copy per workgroup) cost as much as
+    // the weights, so wide workgroups pay; take the width whose grid fills its last
+    // round of workgroups best, the widest on ties (8B shape: 6 tiles = 256 workgroups)
+    p.cfg = GemmCfg{4, 2};
+    double best = -1.0;
+    for (int nt : {8, 6, 4}) {
+      const long long n = cdiv(ntiles, nt);
+      const double eff = (double)n / (double)(cdiv(n, TARGET_WG_GEMM) * TARGET_WG_GEMM);
+      if (eff > best + 1e-9 && gemm_lds_ok(p.MT, nt)) { best = eff; p.cfg = GemmCfg{nt, 2}; }
+    }
+  }
   else if (p.MT >= (epi == EPI_LOGITS ? 3 : 4) && gemm_lds_ok(p.MT, 8)) p.cfg = GemmCfg{8, 2};
   else p.cfg = GemmCfg{4, 2};
   p.ncg = cdiv(ntiles, p.cfg.NT);

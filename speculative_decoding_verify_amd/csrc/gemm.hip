@@ -559,6 +559,8 @@ static hipError_t launch_cfg(const GemmCfg& c, int MT, const Launch& L, const Ge
     if (c.NT == 4 && c.D == 4 && MT == 2) return launch_one<T, 2, 4, 4, EPI>(L, a);
   }
   if (c.NT == 8 && c.D == 2) return launch_mt<T, 8, 2, EPI>(MT, L, a);
+  if constexpr (EPI == EPI_SWIGLU || EPI == EPI_LOGITS)   // six tiles: gate/up and LM head only
+    if (c.NT == 6 && c.D == 2) return launch_mt<T, 6, 2, EPI>(MT, L, a);
   return hipErrorInvalidValue;
 }
 

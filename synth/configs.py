@@ -119,8 +119,15 @@ MINI_BF16_D2048 = ModelShape("mini-bf16-d2048", n_layers=3, d=2048, n_heads=16, 
 MINI_F32_D2048 = ModelShape("mini-f32-d2048", n_layers=3, d=2048, n_heads=16, n_kv_heads=4, head_dim=128,
                             ffn=4096, vocab=1009, dtype="f32")
 
+# the 8B FFN width on a narrow model: 2 x 12288 gate/up rows = 1536 packed tiles
+MINI_BF16_FFN12K = ModelShape("mini-bf16-ffn12288", n_layers=2, d=256, n_heads=4, n_kv_heads=2, head_dim=64,
+                              ffn=12288, vocab=2003, dtype="bf16")
+MINI_F32_FFN12K = ModelShape("mini-f32-ffn12288", n_layers=2, d=256, n_heads=4, n_kv_heads=2, head_dim=64,
+                             ffn=12288, vocab=2003, dtype="f32")
+
 SHAPES = {s.name: s for s in (TOY_F32, SHAPE_1P7B, SHAPE_8B, SHAPE_8B_CB,
-                              MINI_BF16, MINI_BF16_D128, MINI_F32, MINI_BF16_D2048, MINI_F32_D2048)}
+                              MINI_BF16, MINI_BF16_D128, MINI_F32, MINI_BF16_D2048, MINI_F32_D2048,
+                              MINI_BF16_FFN12K, MINI_F32_FFN12K)}
 
 
 # -- the verify workloads --------------------------------------------------------

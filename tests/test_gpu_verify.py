@@ -18,7 +18,7 @@ import speculative_decoding_verify_amd as sdv  # noqa: E402
 from oracle import accept as oacc  # noqa: E402
 from oracle import decoder as odec  # noqa: E402
 from synth import (MINI_BF16, MINI_BF16_D128, MINI_BF16_D2048, MINI_F32, MINI_F32_D2048,  # noqa: E402
-                   make_weights, make_random_kv, uniform_tokens)
+                   MINI_BF16_FFN12K, MINI_F32_FFN12K, make_weights, make_random_kv, uniform_tokens)
 from tests.gpu_helpers import (run_pair, compare_logits, compare_kv, greedy_expectation,  # noqa: E402
                                mode_of)
 
@@ -118,6 +118,29 @@ def test_parity_d2048(shape, lens, L_a, gamma):
     kvh = make_random_kv(shape, list(lens), capacity=max(lens) + T, seed=132)
     toks = _tokens(len(lens), T, shape.vocab, 133)
     g, o, ver, kv = run_pair(w, kvh, toks, L_a, perm_seed=134)
+    assert np.all(g["err"] == 0), g["err"]
+    err, flagged, n = compare_logits(shape, g, o)
+    print(f"  logits rel err {err:.2e}; flagged {flagged}/{n}", flush=True)
+    compare_kv(shape, kv, o, list(lens), T)
+    tol = 2e-2 if shape.dtype == "bf16" else 1e-5
+    hd = np.max(np.abs(g["hidden"] - o["hidden"])) / np.max(np.abs(o["hidden"]))
+    assert hd <= tol, hd
+
+
+@pytest.mark.parametrize("shape", [MINI_BF16_FFN12K, MINI_F32_FFN12K], ids=lambda s: s.name)
+@pytest.mark.parametrize("lens,L_a,gamma", [
+    ((50,), 25, 40),       # 65 rows (5 row tiles, a one-row tail), 41 logit rows
+    ((20, 33), 5, 25),     # 60 rows (4 row tiles), 52 logit rows
+])
+def test_wide_ffn_six_tile_gate_up(shape, lens, L_a, gamma):
+    """1536 gate/up tiles at 4-5 row tiles: the gate/up launch takes six tiles per
+    workgroup (256 workgroups); 33-48 logit rows put the LM head on six tiles too."""
+    print(f"case {shape.name} lens={lens} L_a={L_a} gamma={gamma}", flush=True)
+    w = make_weights(shape, seed=141, gain_noise=0.1)
+    T = L_a + gamma
+    kvh = make_random_kv(shape, list(lens), capacity=max(lens) + T, seed=142)
+    toks = _tokens(len(lens), T, shape.vocab, 143)
+    g, o, ver, kv = run_pair(w, kvh, toks, L_a, perm_seed=144)
     assert np.all(g["err"] == 0), g["err"]
     err, flagged, n = compare_logits(shape, g, o)
     print(f"  logits rel err {err:.2e}; flagged {flagged}/{n}", flush=True)

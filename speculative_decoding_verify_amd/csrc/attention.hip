@@ -79,6 +79,28 @@ SDV_DEV uint32_t anc_word(const uint32_t (&m)[4], int w) {
 // Probabilities as a bf16 hi/lo operand pair, cheaply: hi = p rounded half-up to 8
 // significant bits, lo = the exact remainder p - hi truncated to bf16, so
 // |p - hi - lo| < 2^-15 |p|.  v_perm gathers the upper halves of two words.
+// Reductions over the lane pairs (l, l ^ 16) and (l, l ^ 32) with gfx950's lane-swap
+// instructions: after v_permlane16_swap / v_permlane32_swap of a value with itself,
+// the two results at every lane are the values of the lower and the upper lane of its
+// pair, so both lanes of a pair compute the same result from the same two operands.
+// Plain VALU, where a shuffle would take a round trip through the LDS crossbar.
+SDV_DEV float pair16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+SDV_DEV float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+SDV_DEV float pair16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+SDV_DEV float pair32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 SDV_DEV void split_probs_fast(const float (&p)[8], u32x4& hi, u32x4& lo) {
   uint32_t h[8], l[8];
 #pragma unroll
@@ -388,8 +410,7 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
       float mx = sv[j][0];
 #pragma unroll
       for (int e = 1; e < PE; ++e) mx = fmaxf(mx, sv[j][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = pair32_max(pair16_max(mx));
       mnew[j] = fmaxf(mrun[j], mx);
       rise |= mnew[j] > mrun[j];
     }
@@ -444,8 +465,7 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
     const int qt = q_base + w + j * NW;
     if (qt >= NQT) continue;
     float l = lrun[j];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = pair32_sum(pair16_sum(l));
     const int qi = qt * 16 + r;
     const uint32_t pr = (uint32_t)(split * a.nq_pad + qi);
     if (direct) {
@@ -627,8 +647,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       float mx = sv[j][0];
 #pragma unroll
       for (int e = 1; e < PE; ++e) mx = fmaxf(mx, sv[j][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = pair32_max(pair16_max(mx));
       mnew[j] = fmaxf(mrun[j], mx);
       rise |= mnew[j] > mrun[j];
     }
@@ -682,8 +701,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
   for (int j = 0; j < NQT; ++j) {
     float l = lrun[j];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = pair32_sum(pair16_sum(l));
     sm[w][j][lane] = mrun[j];
     sl[w][j][lane] = l;
 #pragma unroll

@@ -361,12 +361,26 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 15, lg = lane >> 4;
-  const int m_base = blockIdx.x * (16 * MT);
-  const int cg = blockIdx.z;
+  // workgroup -> (row block rb, K split sp, column group cg).  Workgroups are dealt to
+  // the 8 XCDs round-robin by linear id; when the grid divides by 8, XCD x takes the
+  // x-th eighth of the items (row blocks fastest, then splits, then column groups), so
+  // the row blocks that share a column group's weight tiles share one L2.
+  int rb = blockIdx.x, sp = blockIdx.y, cg = blockIdx.z;
+  {
+    const int RB = gridDim.x, SP = gridDim.y, n = RB * SP * gridDim.z;
+    const int L = blockIdx.x + RB * (blockIdx.y + SP * blockIdx.z);
+    if ((n & 7) == 0) {
+      const int I = (L & 7) * (n >> 3) + (L >> 3);
+      rb = I % RB;
+      sp = (I / RB) % SP;
+      cg = I / (RB * SP);
+    }
+  }
+  const int m_base = rb * (16 * MT);
   const int ksteps = a.K / KS;
-  // this workgroup's k steps [s0, s0 + nk): split blockIdx.y of the K range (fp32
-  // partials summed by the consumer; the other epilogues take the whole range)
-  const int s0 = blockIdx.y * a.steps_per_split;
+  // this workgroup's k steps [s0, s0 + nk): split sp of the K range (fp32 partials
+  // summed by the consumer; the other epilogues take the whole range)
+  const int s0 = sp * a.steps_per_split;
   const int nk = max(0, min(ksteps, s0 + a.steps_per_split) - s0);
   const int ntiles = (a.N + 15) >> 4;
   const int row_tiles = (a.M + 15) >> 4;
@@ -384,7 +398,7 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmArgs a) {
       gstride[i] = 1024;
     } else {
       const int q = c - NT, mt8 = q / AL, h = q % AL;
-      const int rt = min(blockIdx.x * MT + mt8, row_tiles - 1);
+      const int rt = min(rb * MT + mt8, row_tiles - 1);
       const int rr = min(r, a.M - 1 - rt * 16);   // rows past M: the last row's chunk
       gp[i] = (const char*)a.A + ((size_t)rt * ksteps + s0) * (64 * KS) + h * 1024 + (lg * 16 + rr) * 16;
       gstride[i] = 64 * KS;
@@ -441,7 +455,7 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) tile[wm * 16 * WM + mt * 16 + 4 * lg + v][wn * 16 * WN + t * 16 + r] = acc[mt][t][v];
   __syncthreads();
-  gemm_epilogue<T, MT, NT, EPI>(a, tile, cg, blockIdx.y, m_base, [&](int, int m, int i) {
+  gemm_epilogue<T, MT, NT, EPI>(a, tile, cg, sp, m_base, [&](int, int m, int i) {
     if constexpr (EPI == EPI_QKV) return QkvItem{a.qkv.rope[(size_t)m * a.pair_n + i], a.qkv.kv_dst[m]};
     else return QkvItem{};
   });

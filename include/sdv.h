@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SDV_ABI_VERSION 3
+#define SDV_ABI_VERSION 4   /* 4: sdv_accept_sample takes prof_events */
 #define SDV_PAGE 16          /* tokens per KV-cache page */
 #define SDV_MAX_T 128        /* rows per verify pass (chunk + drafts + branches) */
 

@@ -68,6 +68,7 @@ class SdvError(RuntimeError):
 
 
 _LIB = None
+ABI_VERSION = 4   # SDV_ABI_VERSION of include/sdv.h that these signatures follow
 
 
 def lib():
@@ -78,6 +79,9 @@ def lib():
             raise SdvError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
         L = ctypes.CDLL(LIB_PATH)
         L.sdv_abi_version.restype = _i32
+        if L.sdv_abi_version() != ABI_VERSION:
+            raise SdvError(f"{LIB_PATH} has ABI version {L.sdv_abi_version()}, this binding needs "
+                           f"{ABI_VERSION}; rebuild with __graft_entry__.build()")
         L.sdv_last_error.restype = ctypes.c_char_p
         L.sdv_verify_workspace_size.restype = ctypes.c_size_t
         L.sdv_verify_workspace_size.argtypes = [ctypes.POINTER(SdvModel), _i32, _i32, _i32, _i32]

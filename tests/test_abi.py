@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_packed_sizes():
     L = sdv.lib()
-    assert L.sdv_abi_version() == 3
+    assert L.sdv_abi_version() == 4
     # rows round up to 16, 2 bytes (bf16) / 4 bytes (fp32) per value
     assert L.sdv_packed_bytes(1, 6144, 2048) == 6144 * 2048 * 2
     assert L.sdv_packed_bytes(0, 17, 64) == 32 * 64 * 4

@@ -111,3 +111,15 @@ def test_sampling_more_chunks_than_threads():
     draw's workgroup (several chunks per thread), and a ragged last chunk."""
     w = SampleWorkload(batch=3, k=2, vocab=1_100_003, seed=980)
     _check(make_sample_inputs(w))
+
+
+def test_sampling_more_drafts_than_a_wave():
+    """k = 70 draft positions: the decision ballots positions in groups of 64.  The
+    first 66 draft rows equal the target rows (p = q: always accepted), so the first
+    rejection, if any, falls in the second group."""
+    w = SampleWorkload(batch=4, k=70, vocab=3001, seed=990)
+    si = make_sample_inputs(w)
+    si.draft_logits[:, :66] = si.target_logits[:, :66]
+    n, _ = _run(si)
+    assert np.all(n >= 66)
+    _check(si)

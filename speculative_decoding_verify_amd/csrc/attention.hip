@@ -76,9 +76,6 @@ SDV_DEV uint32_t anc_word(const uint32_t (&m)[4], int w) {
   return w == 0 ? m[0] : w == 1 ? m[1] : w == 2 ? m[2] : m[3];
 }
 
-// Probabilities as a bf16 hi/lo operand pair, cheaply: hi = p rounded half-up to 8
-// significant bits, lo = the exact remainder p - hi truncated to bf16, so
-// |p - hi - lo| < 2^-15 |p|.  v_perm gathers the upper halves of two words.
 // Reductions over the lane pairs (l, l ^ 16) and (l, l ^ 32) with gfx950's lane-swap
 // instructions: after v_permlane16_swap / v_permlane32_swap of a value with itself,
 // the two results at every lane are the values of the lower and the upper lane of its
@@ -101,6 +98,9 @@ SDV_DEV float pair32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Probabilities as a bf16 hi/lo operand pair, cheaply: hi = p rounded half-up to 8
+// significant bits, lo = the exact remainder p - hi truncated to bf16, so
+// |p - hi - lo| < 2^-15 |p|.  v_perm gathers the upper halves of two words.
 SDV_DEV void split_probs_fast(const float (&p)[8], u32x4& hi, u32x4& lo) {
   uint32_t h[8], l[8];
 #pragma unroll

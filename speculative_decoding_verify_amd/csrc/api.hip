@@ -58,7 +58,10 @@ GemmPlan plan_gemm(int M, int N, int K, bool bf, int epi) {
     p.MT = 8;
     p.row_blocks = cdiv(M, 128);
     const int wn = (long long)cdiv(ntiles, 16) * p.row_blocks >= TARGET_WG_GEMM ? 8 : 4;
-    p.cfg = GemmCfg{wn, 3, true};   // 3 k steps in the LDS ring
+    // LDS ring of 3 k steps at WN = 4; at WN = 8 a ring of 2 steps and an epilogue on
+    // 64-row halves keep the workgroup at 64 KB, two per CU (the batched 2624-row pass:
+    // gate/up 997 -> 809 us, o 214 -> 160, down 507 -> 415, q/k/v 300 -> 248)
+    p.cfg = GemmCfg{wn, wn == 8 ? 2 : 3, true};
     p.ncg = cdiv(ntiles, 2 * wn);
     // split-partials launches split K so that the grid's last round of workgroups is
     // as full as possible (at least 16 k steps per split, at most 4 splits)

@@ -340,7 +340,9 @@ template <typename T, int WN, int R>
 constexpr int tiled_lds_bytes() {
   constexpr int AL = sizeof(T) == 2 ? 2 : 1;
   constexpr int ring = R * (2 * WN + 8 * AL) * 1024;
-  constexpr int tile = 128 * (32 * WN + 1) * 4;
+  // with a two-step ring the epilogue runs on 64-row halves of the output block, so
+  // that two workgroups fit in a CU's LDS
+  constexpr int tile = (R == 2 ? 64 : 128) * (32 * WN + 1) * 4;
   return ring > tile ? ring : tile;
 }
 
@@ -460,6 +462,27 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmArgs a) {
 
   __syncthreads();   // the ring's memory becomes the output tile
   float (*tile)[TC + 1] = reinterpret_cast<float (*)[TC + 1]>(smem);
+  if constexpr (R == 2) {
+    // half h: the two waves of rows 64h .. 64h + 63 store them, then all threads run the
+    // epilogue on them
+    for (int hf = 0; hf < 2; ++hf) {
+      if (wm == hf) {
+#pragma unroll
+        for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+          for (int t = 0; t < WN; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) tile[mt * 16 + 4 * lg + v][wn * 16 * WN + t * 16 + r] = acc[mt][t][v];
+      }
+      __syncthreads();
+      gemm_epilogue<T, MT / 2, NT, EPI>(a, tile, cg, sp, m_base + hf * 16 * WM, [&](int, int m, int i) {
+        if constexpr (EPI == EPI_QKV) return QkvItem{a.qkv.rope[(size_t)m * a.pair_n + i], a.qkv.kv_dst[m]};
+        else return QkvItem{};
+      });
+      __syncthreads();
+    }
+    return;
+  }
 #pragma unroll
   for (int mt = 0; mt < WM; ++mt)
 #pragma unroll
@@ -575,7 +598,7 @@ template <typename T, int EPI>
 static hipError_t launch_cfg(const GemmCfg& c, int MT, const Launch& L, const GemmArgs& a) {
   if (c.tiled) {
     if (c.NT == 4 && c.D == 3) return launch_tiled<T, 4, 3, EPI>(L, a);
-    if (c.NT == 8 && c.D == 3) return launch_tiled<T, 8, 3, EPI>(L, a);
+    if (c.NT == 8 && c.D == 2) return launch_tiled<T, 8, 2, EPI>(L, a);
     return hipErrorInvalidValue;
   }
   if (c.NT == 2 && c.D == 4) return launch_mt<T, 2, 4, EPI>(MT, L, a);

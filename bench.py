@@ -51,8 +51,8 @@ def gate_up_launch_bytes(sh, M):
 # each scaled by what the same counter reads for a plain 256 MiB device copy
 # (`bench.py --copy-calibration`).  Valid only for the workload and the kernel sources
 # they were taken on: both are checked at run time, else traffic is null.
-GATE_UP_TRAFFIC = {"workload": "1.7b-bf16", "sha256": "40389b2d613cb2b18976d595a59364c13faed62265a448345c1dae7b6998fdd2",
-                   "fetch_kib": 34375.0, "fetch_factor": 262144.0 / 131084.0,
+GATE_UP_TRAFFIC = {"workload": "1.7b-bf16", "sha256": "1f2e20b165ea0707cce46f9d32e44eb39ca284dd8af7f3b6fb72fb9ac882fa1e",
+                   "fetch_kib": 34365.5, "fetch_factor": 262144.0 / 131084.0,
                    "write_kib": 1344.0, "write_factor": 262144.0 / 262144.0}
 GEMM_SOURCES = ("speculative_decoding_verify_amd/csrc/gemm.hip", "speculative_decoding_verify_amd/csrc/common.h",
                 "speculative_decoding_verify_amd/csrc/kernels.h")

@@ -125,9 +125,16 @@ MINI_BF16_FFN12K = ModelShape("mini-bf16-ffn12288", n_layers=2, d=256, n_heads=4
 MINI_F32_FFN12K = ModelShape("mini-f32-ffn12288", n_layers=2, d=256, n_heads=4, n_kv_heads=2, head_dim=64,
                              ffn=12288, vocab=2003, dtype="f32")
 
+# a vocabulary of 70,001 (4376 packed LM-head tiles): with more than 80 logit rows the LM
+# head takes the tiled kernel at 8 tile columns per wave
+MINI_BF16_V70K = ModelShape("mini-bf16-v70001", n_layers=1, d=256, n_heads=4, n_kv_heads=2, head_dim=64,
+                            ffn=512, vocab=70001, dtype="bf16")
+MINI_F32_V70K = ModelShape("mini-f32-v70001", n_layers=1, d=256, n_heads=4, n_kv_heads=2, head_dim=64,
+                           ffn=512, vocab=70001, dtype="f32")
+
 SHAPES = {s.name: s for s in (TOY_F32, SHAPE_1P7B, SHAPE_8B, SHAPE_8B_CB,
                               MINI_BF16, MINI_BF16_D128, MINI_F32, MINI_BF16_D2048, MINI_F32_D2048,
-                              MINI_BF16_FFN12K, MINI_F32_FFN12K)}
+                              MINI_BF16_FFN12K, MINI_F32_FFN12K, MINI_BF16_V70K, MINI_F32_V70K)}
 
 
 # -- the verify workloads --------------------------------------------------------

@@ -18,7 +18,8 @@ import speculative_decoding_verify_amd as sdv  # noqa: E402
 from oracle import accept as oacc  # noqa: E402
 from oracle import decoder as odec  # noqa: E402
 from synth import (MINI_BF16, MINI_BF16_D128, MINI_BF16_D2048, MINI_F32, MINI_F32_D2048,  # noqa: E402
-                   MINI_BF16_FFN12K, MINI_F32_FFN12K, make_weights, make_random_kv, uniform_tokens)
+                   MINI_BF16_FFN12K, MINI_F32_FFN12K, MINI_BF16_V70K, MINI_F32_V70K, make_weights,
+                   make_random_kv, uniform_tokens)
 from tests.gpu_helpers import (run_pair, compare_logits, compare_kv, greedy_expectation,  # noqa: E402
                                mode_of)
 
@@ -148,6 +149,25 @@ def test_wide_ffn_six_tile_gate_up(shape, lens, L_a, gamma):
     tol = 2e-2 if shape.dtype == "bf16" else 1e-5
     hd = np.max(np.abs(g["hidden"] - o["hidden"])) / np.max(np.abs(o["hidden"]))
     assert hd <= tol, hd
+
+
+@pytest.mark.parametrize("shape", [MINI_BF16_V70K, MINI_F32_V70K], ids=lambda s: s.name)
+def test_large_vocab_tiled_lm_head(shape):
+    """90 logit rows over a vocabulary of 70,001: the LM head runs on the tiled kernel at
+    8 tile columns per wave, whose epilogue (logits and row statistics) works on 64-row
+    halves of the 128-row block."""
+    lens, L_a, gamma = (21, 40, 7), 4, 29
+    print(f"case {shape.name} lens={lens} L_a={L_a} gamma={gamma}", flush=True)
+    w = make_weights(shape, seed=151, gain_noise=0.1)
+    T = L_a + gamma
+    kvh = make_random_kv(shape, list(lens), capacity=max(lens) + T, seed=152)
+    toks = _tokens(len(lens), T, shape.vocab, 153)
+    g, o, ver, kv = run_pair(w, kvh, toks, L_a, perm_seed=154)
+    assert np.all(g["err"] == 0), g["err"]
+    err, flagged, n = compare_logits(shape, g, o)
+    print(f"  logits rel err {err:.2e}; flagged {flagged}/{n}", flush=True)
+    assert n == len(lens) * (gamma + 1)
+    compare_kv(shape, kv, o, list(lens), T)
 
 
 def test_many_sequences_fine_query_groups():

@@ -8,6 +8,7 @@ attention; a verify pass equals recomputation without a cache; a tree branch
 equals a linear chunk of its own path; rounding equals torch's bf16 cast.
 """
 import itertools
+import math
 
 import numpy as np
 import pytest
@@ -326,3 +327,46 @@ def test_bf16_mode_rounds_stored_values():
     # and the bf16 pass stays close to the exact one on the same (bf16-valued) weights
     ex = dec.verify_forward(w, cache, uniform_tokens(5, SMALL_BF.vocab, 62)[None, :], None, range(5), EXACT)
     assert np.max(np.abs(ex["logits"] - res["logits"])) < 0.05 * np.max(np.abs(ex["logits"]))
+
+
+# -- the activation and the attention scale --------------------------------------------
+
+def test_silu_closed_forms():
+    """silu(x) = x * sigmoid(x).  Because sigmoid(x) + sigmoid(-x) = 1, silu(x) - silu(-x)
+    equals x exactly; silu(x) / x tends to 1 for large x and silu(x) to 0 for very
+    negative x (a swapped sign would give the opposite limits); its minimum sits at
+    x = -(1 + W(1/e)) with value -W(1/e), W the Lambert W function (scipy)."""
+    from scipy.optimize import minimize_scalar
+    from scipy.special import lambertw
+    x = np.linspace(-12.0, 12.0, 97)
+    np.testing.assert_allclose(dec.silu(x) - dec.silu(-x), x, rtol=0, atol=1e-14)
+    assert dec.silu(np.array(0.0)) == 0.0
+    np.testing.assert_allclose(dec.silu(np.array([40.0, 60.0])) / np.array([40.0, 60.0]), 1.0, rtol=1e-15)
+    assert abs(float(dec.silu(np.array(-60.0)))) < 1e-20
+    w = float(lambertw(np.exp(-1.0)).real)
+    r = minimize_scalar(lambda t: float(dec.silu(np.array(t))), bracket=(-3.0, -1.0, 0.0), tol=1e-12)
+    assert abs(r.x + 1.0 + w) < 1e-6 and abs(r.fun + w) < 1e-12
+
+
+@pytest.mark.parametrize("dh", [8, 64, 128])
+def test_attention_scale_is_inverse_sqrt_head_dim(dh):
+    """One query against two cached keys with dot products a and b: the two attention
+    weights are softmax([a, b] / sqrt(dh)), so with values e_0 and e_1 the output is
+    (sigmoid((a - b) / sqrt(dh)), sigmoid((b - a) / sqrt(dh))).  A scale of 1/dh or none
+    at all gives other weights at every head dimension tested."""
+    a, b = 6.0, -2.0
+    q = np.zeros((1, 1, dh))
+    q[0, 0, 0] = 1.0
+    Kc = np.zeros((2, 1, dh))
+    Kc[0, 0, 0] = a
+    Kc[1, 0, 0] = b
+    Kc[1, 0, 1] = 3.0            # orthogonal to q: does not change q . k
+    Vc = np.zeros((2, 1, dh))
+    Vc[0, 0, 0] = 1.0
+    Vc[1, 0, 1] = 1.0
+    empty = np.zeros((1, 1, dh))
+    o = dec.attend(q, Kc, Vc, empty, empty, np.zeros((1, 1), bool))[0]
+    w0 = 1.0 / (1.0 + math.exp(-(a - b) / math.sqrt(dh)))
+    np.testing.assert_allclose(o[:2], [w0, 1.0 - w0], rtol=0, atol=1e-15)
+    for wrong in (1.0 / dh, 1.0):
+        assert abs(o[0] - 1.0 / (1.0 + math.exp(-(a - b) * wrong))) > 1e-3

@@ -222,3 +222,68 @@ def test_masked_vocabulary_entries(seed):
         n, tok, _ = ss.accept_one_sequence(tgt, drf, [int(x)], [0.999], [0.5, 0.5])
         assert n == (1 if p[x] > 0.0 else 0)
         assert p[tok] > 0.0
+
+
+# -- temperature ------------------------------------------------------------------------
+
+def test_temperature_to_infinity_gives_uniform_distributions():
+    """p = softmax(z / T): as T grows both distributions become uniform over V, so every
+    ratio p(x)/q(x) is 1 and every draft is accepted (u < 1); the bonus draw of a uniform
+    distribution over V at u is floor(u V).  A temperature that multiplied the logits
+    instead would make p and q one-hot and reject."""
+    rng = np.random.default_rng(7)
+    V, k = 11, 4
+    tgt = rng.standard_normal((k + 1, V)) * 3.0
+    drf = rng.standard_normal((k, V)) * 3.0
+    drafts = rng.integers(0, V, size=k)
+    u_acc = np.full(k, 1.0 - 1e-9)
+    for us in (0.0, 0.3, 0.95):
+        n, tok, _ = ss.accept_one_sequence(tgt, drf, drafts, u_acc, [0.5] * k + [us], temperature=1e12)
+        assert n == k and tok == int(us * V)
+
+
+def test_temperature_two_on_two_tokens():
+    """V = 2, T = 2: p(0) = sigmoid((z0 - z1) / 2), and likewise q.  The acceptance of draft
+    0 switches exactly where u crosses p(0)/q(0)."""
+    zp, zq = np.array([0.2, 0.9]), np.array([2.2, 0.1])
+    p0 = 1.0 / (1.0 + math.exp(-(zp[0] - zp[1]) / 2.0))
+    q0 = 1.0 / (1.0 + math.exp(-(zq[0] - zq[1]) / 2.0))
+    ratio = p0 / q0
+    assert ratio < 1.0
+    tgt, drf = np.stack([zp, zp]), zq[None, :]
+    for u, want in ((ratio - 1e-9, 1), (ratio + 1e-9, 0)):
+        n, _, _ = ss.accept_one_sequence(tgt, drf, [0], [u], [0.5, 0.5], temperature=2.0)
+        assert n == want
+    # at T = 1 the same u decides differently (the ratio moves)
+    r1 = (1.0 / (1.0 + math.exp(-(zp[0] - zp[1])))) / (1.0 / (1.0 + math.exp(-(zq[0] - zq[1]))))
+    assert abs(r1 - ratio) > 1e-3
+
+
+def test_temperature_to_zero_is_greedy_acceptance():
+    """As T -> 0 the target is one-hot at its argmax: a draft equal to the argmax is
+    accepted (p(x)/q(x) >= 1 with q one-hot too), any other draft is rejected and the
+    replacement is the argmax (the residual max(0, p - q) is one-hot there)."""
+    rng = np.random.default_rng(3)
+    V, k = 9, 3
+    tgt = rng.standard_normal((k + 1, V))
+    am = tgt.argmax(axis=1)
+    drf = tgt[:k].copy()
+    drafts = am[:k].copy()
+    drafts[2] = (am[2] + 1) % V
+    drf[2, drafts[2]] = tgt[2].max() + 1.0   # q prefers the wrong token
+    n, tok, _ = ss.accept_one_sequence(tgt, drf, drafts, [0.5] * k, [0.5] * (k + 1), temperature=1e-6)
+    assert n == 2 and tok == am[2]
+
+
+def test_philox_known_answer_vectors():
+    """Philox4x32-10 against the known-answer vectors published with the Random123
+    library (Salmon et al., SC'11): zero counter and key, all-ones, and the pi-digit
+    counter and key."""
+    from synth.gen import philox4x32_10
+    cases = [([0, 0, 0, 0], [0, 0], [0x6627e8d5, 0xe169c58d, 0xbc57ac4c, 0x9b00dbd8]),
+             ([0xffffffff] * 4, [0xffffffff] * 2, [0x408f276d, 0x41c83b0e, 0xa20bc7c6, 0x6d5451fd]),
+             ([0x243f6a88, 0x85a308d3, 0x13198a2e, 0x03707344], [0xa4093822, 0x299f31d0],
+              [0xd16cfe09, 0x94fdcceb, 0x5001e420, 0x24126ea1])]
+    for ctr, key, want in cases:
+        got = philox4x32_10(np.array(ctr, dtype=np.uint32), np.array(key, dtype=np.uint32))
+        assert [int(x) for x in got] == want

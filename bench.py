@@ -409,14 +409,13 @@ def bench_sample(args):
     copies = []
     for c in range(2):
         copies.append(dict(tgt=torch.from_numpy(si.target_logits).cuda(), drf=torch.from_numpy(si.draft_logits).cuda(),
-                           drafts=torch.from_numpy(si.drafts).cuda(), ua=torch.from_numpy(si.u_accept).cuda(),
-                           us=torch.from_numpy(si.u_sample).cuda()))
+                           drafts=torch.from_numpy(si.drafts).cuda()))
     smp = sdv.Sampler(B, k, V)
     setup_s = time.time() - t0
 
     def step(i):
         c = copies[i & 1]
-        smp(c["tgt"], c["drf"], c["drafts"], c["ua"], c["us"], 1.0)
+        smp(c["tgt"], c["drf"], c["drafts"], si.seed)
 
     for i in range(args.warmup):
         step(i)
@@ -434,7 +433,7 @@ def bench_sample(args):
     stats_ms = []
     for i in range(args.steps):
         c = copies[i & 1]
-        smp(c["tgt"], c["drf"], c["drafts"], c["ua"], c["us"], 1.0, prof_events=ev)
+        smp(c["tgt"], c["drf"], c["drafts"], si.seed, prof_events=ev)
         torch.cuda.synchronize()
         stats_ms.append(ev[0].elapsed_time(ev[1]))
     stats_us = float(np.mean(stats_ms)) * 1e3

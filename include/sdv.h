@@ -68,9 +68,10 @@
 extern "C" {
 #endif
 
-#define SDV_ABI_VERSION 4   /* 4: sdv_accept_sample takes prof_events */
+#define SDV_ABI_VERSION 5   /* 5: sdv_accept_sample draws Philox uniforms itself and reports flags */
 #define SDV_PAGE 16          /* tokens per KV-cache page */
 #define SDV_MAX_T 128        /* rows per verify pass (chunk + drafts + branches) */
+#define SDV_SAMPLE_MAX_K 1024  /* draft positions per sequence of sdv_accept_sample */
 
 typedef enum {
   SDV_OK = 0,
@@ -242,25 +243,45 @@ sdv_status sdv_accept_greedy(int32_t batch, int32_t T, int32_t L_a, const int32_
  *   tgt_logits [B, k+1, V] fp32 target logits (row i scores draft position i, row k
  *              the bonus position); drf_logits [B, k, V] fp32 draft logits;
  *   drafts [B, k]; p = softmax(tgt / temperature), q = softmax(drf / temperature).
- *   For i = 0..k-1 in order: accept drafts[b,i] iff u_accept[b,i] < p(x)/q(x)
- *   (if q(x) = 0: iff p(x) > 0).  At the first rejection i: token = inverse CDF of
- *   w = max(0, p_i - q_i) (of p_i if w is empty) at u_sample[b,i], n = i.  If all
- *   pass: n = k, token = inverse CDF of p_k at u_sample[b,k].  The inverse CDF
- *   returns the smallest index whose running sum exceeds u * total, with weights
- *   quantised to 2^-40 so the draw does not depend on summation order.
- *   u_accept [B, k], u_sample [B, k+1]: fp64 uniforms in [0, 1) (the caller draws them).
+ *   Random numbers: Philox4x32-10 (Salmon et al., SC'11) under the 64-bit key `seed`
+ *   (low word first), counter (s, i, 0, stream) with s = seq_ids[b] (seq_ids NULL:
+ *   s = b) and i the 0-based position; U0(s, i) = r0 * 2^-32 from stream 0,
+ *   U1(s, i) = (r1 * 2^21 + (r2 >> 11)) * 2^-53 from stream 1 (sdv_philox_uniforms
+ *   writes the same numbers).
+ *   For i = 0..k-1 in order: accept drafts[b,i] iff U0(s, i) < p(x)/q(x) (if q(x) = 0:
+ *   iff p(x) > 0).  At the first rejection i: token = inverse CDF of w = max(0, p_i - q_i)
+ *   (of p_i if w is empty) at U1(s, i), n = i.  If all pass: n = k, token = inverse CDF
+ *   of p_k at U1(s, k).  The inverse CDF returns the smallest index whose running sum
+ *   exceeds u * total, with weights quantised to 2^-40 so the draw does not depend on
+ *   summation order.
  *   Logits of -inf (masked vocabulary entries) have probability 0; every row needs at
  *   least one finite logit.
- *   Outputs n_out [B], tok_out [B] (int32).
+ *   Outputs n_out [B], tok_out [B] (int32); flags_out [B] (nullable) per sequence:
+ *     SDV_SAMPLE_NEAR_ACCEPT  an acceptance test up to the draw position had
+ *                             |U0 - p(x)/q(x)| < 1e-6 (another rounding could decide
+ *                             it the other way);
+ *     SDV_SAMPLE_NEAR_DRAW    the draw's target u * total lies within 1e-6 (probability
+ *                             units) of a partial sum;
+ *     SDV_SAMPLE_BAD_DRAFT    a draft id outside [0, V): n_out and tok_out are -1.
+ *   k <= SDV_SAMPLE_MAX_K; temperature finite and > 0.
  *   prof_events: nullable host array of 2 caller-created hipEvent_t handles; when
  *   given, the launch that reads every logit row (maximum and exponential sum per
  *   row) records event 0 when it starts and event 1 when it ends. */
+#define SDV_SAMPLE_NEAR_ACCEPT 0x1
+#define SDV_SAMPLE_NEAR_DRAW   0x2
+#define SDV_SAMPLE_BAD_DRAFT   0x100
 size_t sdv_sample_workspace_size(int32_t batch, int32_t k, int32_t vocab);
 sdv_status sdv_accept_sample(int32_t batch, int32_t k, int32_t vocab, const float* tgt_logits,
-                             const float* drf_logits, const int32_t* drafts,
-                             const double* u_accept, const double* u_sample, float temperature,
-                             int32_t* n_out, int32_t* tok_out, void* workspace,
-                             size_t workspace_bytes, void* const* prof_events, void* stream);
+                             const float* drf_logits, const int32_t* drafts, float temperature,
+                             uint64_t seed, const int32_t* seq_ids, int32_t* n_out, int32_t* tok_out,
+                             uint32_t* flags_out, void* workspace, size_t workspace_bytes,
+                             void* const* prof_events, void* stream);
+
+/* The Philox4x32-10 uniforms sdv_accept_sample uses, written out: for b < B and
+ * pos < n_pos, u0_out[b, pos] = U0(s, pos) and u1_out[b, pos] = U1(s, pos) (both
+ * [B, n_pos] fp64, either nullable), s = seq_ids[b] or b. */
+sdv_status sdv_philox_uniforms(uint64_t seed, const int32_t* seq_ids, int32_t batch, int32_t n_pos,
+                               double* u0_out, double* u1_out, void* stream);
 
 /* KV commit / rollback (step 4: roll the cache back to x_{<t}; commit n + 1 tokens).
  *   keep_len [B]: new committed length per sequence (seq_len[b] := keep_len[b]).

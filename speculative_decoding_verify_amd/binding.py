@@ -68,7 +68,7 @@ class SdvError(RuntimeError):
 
 
 _LIB = None
-ABI_VERSION = 4   # SDV_ABI_VERSION of include/sdv.h that these signatures follow
+ABI_VERSION = 5   # SDV_ABI_VERSION of include/sdv.h that these signatures follow
 
 
 def lib():
@@ -103,8 +103,10 @@ def lib():
         L.sdv_pack_weights.argtypes = [_i32, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _i32, _vp,
                                        ctypes.c_size_t, _vp]
         L.sdv_accept_sample.restype = ctypes.c_int
-        L.sdv_accept_sample.argtypes = [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
-                                        _vp, _vp, _vp, ctypes.c_size_t, ctypes.POINTER(_vp), _vp]
+        L.sdv_accept_sample.argtypes = [_i32, _i32, _i32, _vp, _vp, _vp, ctypes.c_float, ctypes.c_uint64, _vp,
+                                        _vp, _vp, _vp, _vp, ctypes.c_size_t, ctypes.POINTER(_vp), _vp]
+        L.sdv_philox_uniforms.restype = ctypes.c_int
+        L.sdv_philox_uniforms.argtypes = [ctypes.c_uint64, _vp, _i32, _i32, _vp, _vp, _vp]
         _LIB = L
     return _LIB
 
@@ -383,20 +385,28 @@ def prefill(model: DeviceModel, kv: PagedKV, tokens, chunk: int = MAX_T, stream=
         kv_rollback(model, kv, keep, stream=stream)
 
 
+SAMPLE_NEAR_ACCEPT, SAMPLE_NEAR_DRAW, SAMPLE_BAD_DRAFT = 0x1, 0x2, 0x100
+
+
 class Sampler:
-    """Speculative-sampling acceptance with reusable workspace."""
+    """Speculative-sampling acceptance with reusable workspace and outputs."""
 
     def __init__(self, B: int, k: int, V: int, device="cuda"):
         self.B, self.k, self.V = B, k, V
         nbytes = lib().sdv_sample_workspace_size(B, k, V)
+        if nbytes == 0:
+            raise SdvError(f"unsupported sampling shape B={B} k={k} V={V}")
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.n = torch.empty(B, dtype=torch.int32, device=device)
         self.tok = torch.empty(B, dtype=torch.int32, device=device)
+        self.flags = torch.empty(B, dtype=torch.int32, device=device)   # uint32 bits
 
-    def __call__(self, tgt: torch.Tensor, drf: torch.Tensor, drafts: torch.Tensor, u_acc: torch.Tensor,
-                 u_smp: torch.Tensor, temperature: float = 1.0, stream=None, prof_events=None):
-        """prof_events: None or two torch.cuda.Event (enable_timing=True) that the
-        library records around its row-statistics launch."""
+    def __call__(self, tgt: torch.Tensor, drf: torch.Tensor, drafts: torch.Tensor, seed: int,
+                 seq_ids: Optional[torch.Tensor] = None, temperature: float = 1.0, stream=None,
+                 prof_events=None):
+        """Returns (n, tok, flags) device tensors.  prof_events: None or two
+        torch.cuda.Event (enable_timing=True) that the library records around its
+        row-statistics launch."""
         ev = None
         if prof_events is not None:
             if len(prof_events) != 2:
@@ -404,10 +414,21 @@ class Sampler:
             for e in prof_events:     # torch creates the underlying event on first record
                 e.record()
             ev = (_vp * 2)(*[e.cuda_event for e in prof_events])
-        _check(lib().sdv_accept_sample(self.B, self.k, self.V, _ptr(tgt), _ptr(drf), _ptr(drafts), _ptr(u_acc),
-                                       _ptr(u_smp), float(temperature), _ptr(self.n), _ptr(self.tok),
+        _check(lib().sdv_accept_sample(self.B, self.k, self.V, _ptr(tgt), _ptr(drf), _ptr(drafts),
+                                       float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(seq_ids),
+                                       _ptr(self.n), _ptr(self.tok), _ptr(self.flags),
                                        _ptr(self.workspace), self.workspace.numel(),
                                        None if ev is None else ctypes.cast(ev, ctypes.POINTER(_vp)),
                                        _stream(stream)),
                "sdv_accept_sample")
-        return self.n, self.tok
+        return self.n, self.tok, self.flags
+
+
+def philox_uniforms(seed: int, B: int, n_pos: int, seq_ids: Optional[torch.Tensor] = None, device="cuda",
+                    stream=None):
+    """(u0, u1) fp64 [B, n_pos] device tensors from sdv_philox_uniforms."""
+    u0 = torch.empty((B, n_pos), dtype=torch.float64, device=device)
+    u1 = torch.empty((B, n_pos), dtype=torch.float64, device=device)
+    _check(lib().sdv_philox_uniforms(int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(seq_ids), B, n_pos, _ptr(u0), _ptr(u1),
+                                     _stream(stream)), "sdv_philox_uniforms")
+    return u0, u1

@@ -242,29 +242,91 @@ SDV_DEV double prob_at(float zx, float m, double s, float inv_temp) {
   return exp2((double)(zx - m) * (1.4426950408889634 * (double)inv_temp)) / s;
 }
 
-// Position of sequence b's draw: the first draft position whose test fails, or k
-// when every draft passes.  Called by the 64 lanes of one wave: lane i of each
-// group of 64 positions evaluates position base + i, the ballot keeps the lowest
-// failing position.  A draft outside q's support (q(x) = 0) passes iff p(x) > 0.
-SDV_DEV int draw_position(const SampleArgs& a, int b) {
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
+// 1, 2, 3", SC'11): ten rounds of two 32x32 -> 64-bit products on the even counter
+// words, the high halves xor-ed into the odd words together with the round key, and
+// a Weyl increment of the key between rounds.
+SDV_DEV uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// The two uniforms of (seq, pos) under key `seed`: counter (seq, pos, 0, stream).
+// U0 = r0 * 2^-32 from stream 0 decides acceptance; U1 = (r1 * 2^21 + (r2 >> 11)) *
+// 2^-53 from stream 1 drives the draw.
+SDV_DEV double philox_u0(unsigned long long seed, uint32_t seq, uint32_t pos) {
+  const uint4 r = philox4x32_10(make_uint4(seq, pos, 0u, 0u), (uint32_t)seed, (uint32_t)(seed >> 32));
+  return (double)r.x * 0x1p-32;
+}
+SDV_DEV double philox_u1(unsigned long long seed, uint32_t seq, uint32_t pos) {
+  const uint4 r = philox4x32_10(make_uint4(seq, pos, 0u, 1u), (uint32_t)seed, (uint32_t)(seed >> 32));
+  return (double)(((unsigned long long)r.y << 21) + (r.z >> 11)) * 0x1p-53;
+}
+
+SDV_DEV uint32_t seq_of(const SampleArgs& a, int b) { return a.seq_ids ? (uint32_t)a.seq_ids[b] : (uint32_t)b; }
+
+// Decision of sequence b: the position of its draw (the first draft position whose
+// test fails, or k when every draft passes), whether a decision up to that position
+// lies within FLAG_TOL of its threshold, and whether a draft id is outside [0, V).
+// Called by the 64 lanes of one wave: lane i of each group of 64 positions evaluates
+// position base + i, and the ballot keeps the lowest failing position.  A draft
+// outside q's support (q(x) = 0) passes iff p(x) > 0.
+struct Decision {
+  int pos;
+  bool near, bad;
+};
+
+static constexpr double FLAG_TOL = 1e-6;
+
+SDV_DEV Decision decide(const SampleArgs& a, int b) {
   const int nt = a.B * (a.k + 1);
   const int lane = threadIdx.x & 63;
+  const uint32_t seq = seq_of(a, b);
+  bool bad = false;
   for (int base = 0; base < a.k; base += 64) {
     const int i = base + lane;
-    bool rej = false;
+    const int x = i < a.k ? a.drafts[(size_t)b * a.k + i] : 0;
+    bad |= __ballot(x < 0 || x >= a.V) != 0;
+  }
+  Decision d{a.k, false, bad};
+  if (bad) return d;
+  for (int base = 0; base < a.k; base += 64) {
+    const int i = base + lane;
+    bool rej = false, near = false;
     if (i < a.k) {
-      int x = a.drafts[(size_t)b * a.k + i];
-      x = min(max(x, 0), a.V - 1);
+      const int x = a.drafts[(size_t)b * a.k + i];
       const int rt = b * (a.k + 1) + i, rd = nt + b * a.k + i;
       const double px = prob_at(a.tgt[(size_t)rt * a.V + x], a.row_m[rt], a.row_s[rt], a.inv_temp);
       const double qx = prob_at(a.drf[(size_t)(rd - nt) * a.V + x], a.row_m[rd], a.row_s[rd], a.inv_temp);
-      const bool acc = qx > 0.0 ? a.u_acc[(size_t)b * a.k + i] < px / qx : px > 0.0;
+      const double u = philox_u0(a.seed, seq, (uint32_t)i);
+      bool acc;
+      if (qx > 0.0) {
+        const double ratio = px / qx;
+        acc = u < ratio;
+        near = fabs(u - ratio) < FLAG_TOL;
+      } else {
+        acc = px > 0.0;
+      }
       rej = !acc;
     }
-    const unsigned long long mask = __ballot(rej);
-    if (mask) return base + __ffsll(mask) - 1;
+    const unsigned long long mask = __ballot(rej), nmask = __ballot(near);
+    if (mask) {
+      const int first = __ffsll(mask) - 1;
+      const unsigned long long upto = first == 63 ? ~0ull : ((2ull << first) - 1);
+      d.pos = base + first;
+      d.near |= (nmask & upto) != 0;
+      return d;
+    }
+    d.near |= nmask != 0;
   }
-  return a.k;
+  return d;
 }
 
 // The two rows a draw at position `pos` reads: p_pos, and q_pos at a rejection
@@ -315,21 +377,31 @@ SDV_DEV void pair_weights(const DrawRows& r, bool has_q, float zp, float zq, lon
 
 // One workgroup per (chunk of the vocabulary, sequence): wave 0 takes the accept /
 // reject decision of the sequence (the chunk-0 workgroup writes it out), then every
-// thread sums the quantised weights of its share of the chunk for both draws.
+// thread sums the quantised weights of its share of the chunk for both draws.  A
+// sequence with an invalid draft id sums nothing.
 __global__ __launch_bounds__(256) void spec_chunk_sum_kernel(SampleArgs a) {
   const int b = blockIdx.y, ch = blockIdx.x;
-  __shared__ int pos_s;
+  __shared__ int pos_s, bad_s;
   if (threadIdx.x < 64) {
-    const int pos = draw_position(a, b);
+    const Decision d = decide(a, b);
     if (threadIdx.x == 0) {
-      pos_s = pos;
+      pos_s = d.pos;
+      bad_s = d.bad;
       if (ch == 0) {
-        a.first_rej[b] = pos;
-        a.n_out[b] = pos;
+        a.first_rej[b] = d.bad ? -1 : d.pos;
+        a.seq_flags[b] = (d.near ? SAMPLE_FLAG_NEAR_ACCEPT : 0u) | (d.bad ? SAMPLE_FLAG_BAD_DRAFT : 0u);
+        a.n_out[b] = d.bad ? -1 : d.pos;
       }
     }
   }
   __syncthreads();
+  if (bad_s) {
+    if (threadIdx.x == 0) {
+      a.chunk_sum[((size_t)b * a.n_chunks + ch) * 2] = 0;
+      a.chunk_sum[((size_t)b * a.n_chunks + ch) * 2 + 1] = 0;
+    }
+    return;
+  }
   const int pos = pos_s;
   const DrawRows r = draw_rows(a, b, pos);
   const bool has_q = r.zq != nullptr;
@@ -421,6 +493,13 @@ __global__ __launch_bounds__(256) void spec_find_kernel(SampleArgs a) {
   __shared__ int sel_s;
   __shared__ long long rem_s;
   const int pos = a.first_rej[b];
+  if (pos < 0) {  // invalid draft id: no draw
+    if (threadIdx.x == 0) {
+      a.tok_out[b] = -1;
+      if (a.flags_out) a.flags_out[b] = a.seq_flags[b];
+    }
+    return;
+  }
   const long long* cs = a.chunk_sum + (size_t)b * a.n_chunks * 2;
   const int cper = (a.n_chunks + 255) / 256;
   const int c0 = min(a.n_chunks, (int)threadIdx.x * cper), c1 = min(a.n_chunks, c0 + cper);
@@ -434,7 +513,7 @@ __global__ __launch_bounds__(256) void spec_find_kernel(SampleArgs a) {
   const long long inc1 = block_scan(t1, wtot[1], S1);
   const int which = S0 > 0 ? 0 : 1;
   const long long S = which == 0 ? S0 : S1;
-  const double u = a.u_smp[(size_t)b * (a.k + 1) + pos];
+  const double u = philox_u1(a.seed, seq_of(a, b), (uint32_t)pos);
   long long target = (long long)(u * (double)S);
   if (target >= S) target = S - 1;
   if (target < 0) target = 0;
@@ -493,19 +572,47 @@ __global__ __launch_bounds__(256) void spec_find_kernel(SampleArgs a) {
   long long total;
   const long long inc = block_scan(mine, wtot[2], total);
   long long run = inc - mine;
+  // a draw whose target lies within FLAG_TOL (in probability units, 2^40 per unit) of a
+  // partial sum is flagged: the partial sums are monotone, so the nearest ones are the
+  // two around the crossing entry
+  constexpr long long TOL_Q = (long long)(FLAG_TOL * 1099511627776.0);
   if (run <= rem && inc > rem) {
     int j = PER - 1;
+    long long before = run, after = inc;
     for (int i = 0; i < PER; ++i) {
-      run += mw[i];
-      if (run > rem) {
+      if (run + mw[i] > rem) {
         j = i;
+        before = run;
+        after = run + mw[i];
         break;
       }
+      run += mw[i];
     }
     a.tok_out[b] = v0 + threadIdx.x * PER + j;
+    const bool near = rem - before < TOL_Q || after - rem < TOL_Q;
+    if (a.flags_out) a.flags_out[b] = a.seq_flags[b] | (near ? SAMPLE_FLAG_NEAR_DRAW : 0u);
   }
   // no crossing inside the chunk: only when the total weight is zero (invalid rows)
-  if (threadIdx.x == 0 && total <= rem) a.tok_out[b] = v0 + n - 1;
+  if (threadIdx.x == 0 && total <= rem) {
+    a.tok_out[b] = v0 + n - 1;
+    if (a.flags_out) a.flags_out[b] = a.seq_flags[b] | SAMPLE_FLAG_NEAR_DRAW;
+  }
+}
+
+// The uniforms themselves, for callers that draw elsewhere and for tests.
+__global__ __launch_bounds__(256) void philox_uniforms_kernel(PhiloxArgs a) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)a.B * a.n_pos) return;
+  const int b = (int)(i / a.n_pos), pos = (int)(i % a.n_pos);
+  const uint32_t seq = a.seq_ids ? (uint32_t)a.seq_ids[b] : (uint32_t)b;
+  if (a.u0) a.u0[i] = philox_u0(a.seed, seq, (uint32_t)pos);
+  if (a.u1) a.u1[i] = philox_u1(a.seed, seq, (uint32_t)pos);
+}
+
+hipError_t launch_philox_uniforms(const PhiloxArgs& a, hipStream_t s) {
+  const long long n = (long long)a.B * a.n_pos;
+  philox_uniforms_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_accept_sample(const SampleArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {

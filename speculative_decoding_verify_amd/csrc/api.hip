@@ -16,6 +16,7 @@
 
 using namespace sdv;
 
+
 namespace {
 
 thread_local std::string g_err;
@@ -259,6 +260,9 @@ GemmArgs gemm_args(const void* A, int M, const void* W, int N, int K) {
   return a;
 }
 
+sdv_status verify_forward_impl(const sdv_model* m, const sdv_kv* kv, const sdv_verify_in* in, sdv_verify_out* out,
+                               void* ws, size_t ws_bytes, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -273,6 +277,15 @@ size_t sdv_verify_workspace_size(const sdv_model* m, int32_t batch, int32_t T, i
 
 sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_verify_in* in, sdv_verify_out* out,
                               void* ws, size_t ws_bytes, void* stream) {
+  return verify_forward_impl(m, kv, in, out, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+sdv_status verify_forward_impl(const sdv_model* m, const sdv_kv* kv, const sdv_verify_in* in, sdv_verify_out* out,
+                               void* ws, size_t ws_bytes, void* stream) {
   sdv_status st = check_model(m);
   if (st != SDV_OK) return st;
   if (!kv || !in || !out) return fail(SDV_ERR_NULL, "kv/in/out is NULL");
@@ -414,6 +427,10 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
   return SDV_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
 sdv_status sdv_accept_greedy(int32_t B, int32_t T, int32_t L_a, const int32_t* tokens, const int32_t* parent,
                              int32_t R, const int32_t* logit_rows, const int32_t* argmax, const int32_t* base_len,
                              int32_t* n_out, int32_t* next_out, int32_t* path_out, int32_t* keep_out,
@@ -488,20 +505,21 @@ sdv_status sdv_kv_rollback(const sdv_model* m, const sdv_kv* kv, const int32_t* 
 
 
 size_t sdv_sample_workspace_size(int32_t B, int32_t k, int32_t V) {
-  if (B < 1 || k < 1 || V < 2) return 0;
+  if (B < 1 || k < 1 || k > SDV_SAMPLE_MAX_K || V < 2) return 0;
   const size_t rows = (size_t)B * (2 * k + 1);
   const int nch = cdiv(V, SAMPLE_CHUNK);
-  return align_up(rows * 4, 256) + align_up(rows * 8, 256) + align_up((size_t)B * 4, 256) +
+  return align_up(rows * 4, 256) + align_up(rows * 8, 256) + 2 * align_up((size_t)B * 4, 256) +
          align_up((size_t)B * nch * 2 * 8, 256);
 }
 
 sdv_status sdv_accept_sample(int32_t B, int32_t k, int32_t V, const float* tgt, const float* drf,
-                             const int32_t* drafts, const double* u_acc, const double* u_smp, float temperature,
-                             int32_t* n_out, int32_t* tok_out, void* ws, size_t ws_bytes, void* const* prof_events,
-                             void* stream) {
-  if (!tgt || !drf || !drafts || !u_acc || !u_smp || !n_out || !tok_out) return fail(SDV_ERR_NULL, "NULL argument");
+                             const int32_t* drafts, float temperature, uint64_t seed, const int32_t* seq_ids,
+                             int32_t* n_out, int32_t* tok_out, uint32_t* flags_out, void* ws, size_t ws_bytes,
+                             void* const* prof_events, void* stream) {
+  if (!tgt || !drf || !drafts || !n_out || !tok_out) return fail(SDV_ERR_NULL, "NULL argument");
   if (B < 1 || k < 1 || V < 2) return fail(SDV_ERR_SHAPE, "B/k/V out of range");
-  if (!(temperature > 0.f)) return fail(SDV_ERR_SHAPE, "temperature must be > 0");
+  if (k > SDV_SAMPLE_MAX_K) return fail(SDV_ERR_SHAPE, "k = %d > %d", k, SDV_SAMPLE_MAX_K);
+  if (!(temperature > 0.f) || !isfinite(temperature)) return fail(SDV_ERR_SHAPE, "temperature must be finite and > 0");
   const size_t need = sdv_sample_workspace_size(B, k, V);
   if (!ws || ws_bytes < need) return fail(SDV_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   const size_t rows = (size_t)B * (2 * k + 1);
@@ -513,8 +531,8 @@ sdv_status sdv_accept_sample(int32_t B, int32_t k, int32_t V, const float* tgt, 
   a.tgt = tgt;
   a.drf = drf;
   a.drafts = drafts;
-  a.u_acc = u_acc;
-  a.u_smp = u_smp;
+  a.seed = seed;
+  a.seq_ids = seq_ids;
   a.inv_temp = 1.f / temperature;
   a.row_m = (float*)w;
   w += align_up(rows * 4, 256);
@@ -522,13 +540,25 @@ sdv_status sdv_accept_sample(int32_t B, int32_t k, int32_t V, const float* tgt, 
   w += align_up(rows * 8, 256);
   a.first_rej = (int32_t*)w;
   w += align_up((size_t)B * 4, 256);
+  a.seq_flags = (uint32_t*)w;
+  w += align_up((size_t)B * 4, 256);
   a.chunk_sum = (long long*)w;
   a.chunk = SAMPLE_CHUNK;
   a.n_chunks = cdiv(V, SAMPLE_CHUNK);
   a.n_out = n_out;
   a.tok_out = tok_out;
+  a.flags_out = flags_out;
   SDV_LAUNCH(launch_accept_sample(a, (hipStream_t)stream, prof_events ? (hipEvent_t)prof_events[0] : nullptr,
                                   prof_events ? (hipEvent_t)prof_events[1] : nullptr));
+  return SDV_OK;
+}
+
+sdv_status sdv_philox_uniforms(uint64_t seed, const int32_t* seq_ids, int32_t B, int32_t n_pos, double* u0_out,
+                               double* u1_out, void* stream) {
+  if (!u0_out && !u1_out) return fail(SDV_ERR_NULL, "both outputs are NULL");
+  if (B < 1 || n_pos < 1) return fail(SDV_ERR_SHAPE, "B/n_pos out of range");
+  PhiloxArgs a{seed, seq_ids, B, n_pos, u0_out, u1_out};
+  SDV_LAUNCH(launch_philox_uniforms(a, (hipStream_t)stream));
   return SDV_OK;
 }
 

@@ -237,18 +237,33 @@ struct SampleArgs {
   const float* tgt;         // [B, k+1, V]
   const float* drf;         // [B, k, V]
   const int32_t* drafts;    // [B, k]
-  const double* u_acc;      // [B, k]
-  const double* u_smp;      // [B, k+1]
+  unsigned long long seed;  // Philox key
+  const int32_t* seq_ids;   // [B] nullable: Philox counter word 0 of sequence b (NULL: b)
   float inv_temp;
   float* row_m;             // [B*(k+1) + B*k] row maximum of the raw logits
   double* row_s;            // [..] sum_v 2^((z_v - max) * log2(e) / temperature)
-  int32_t* first_rej;       // [B] position of the draw (first rejection, or k)
+  int32_t* first_rej;       // [B] position of the draw (first rejection, or k); -1: invalid draft
+  uint32_t* seq_flags;      // [B] decision flags (SAMPLE_FLAG_*) handed to the draw
   long long* chunk_sum;     // [B][n_chunks][2] quantised weights: draw row, p row
   int n_chunks, chunk;      // chunk == SAMPLE_CHUNK
   int32_t* n_out;
   int32_t* tok_out;
+  uint32_t* flags_out;      // [B] nullable
 };
+// values of the per-sequence flag word (the ABI's SDV_SAMPLE_* bits)
+constexpr uint32_t SAMPLE_FLAG_NEAR_ACCEPT = 0x1, SAMPLE_FLAG_NEAR_DRAW = 0x2, SAMPLE_FLAG_BAD_DRAFT = 0x100;
 // ev0 / ev1 (nullable): recorded at the start and end of the row-statistics launch
 hipError_t launch_accept_sample(const SampleArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+
+// Philox4x32-10 uniforms of counters (seq, pos, 0, stream): u0 from stream 0, u1 from
+// stream 1, [B, n_pos] each (nullable)
+struct PhiloxArgs {
+  unsigned long long seed;
+  const int32_t* seq_ids;   // [B] nullable (NULL: b)
+  int B, n_pos;
+  double* u0;
+  double* u1;
+};
+hipError_t launch_philox_uniforms(const PhiloxArgs& a, hipStream_t s);
 
 }  // namespace sdv

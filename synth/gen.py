@@ -374,6 +374,7 @@ class SampleInputs:
     u_accept: np.ndarray        # fp64 [B, k]
     u_sample: np.ndarray        # fp64 [B, k+1]
     temperature: float = 1.0
+    seed: int = 0               # Philox key of u_accept / u_sample (sequence b uses counter word b)
 
 
 def make_sample_inputs(w: SampleWorkload, batch: Optional[int] = None, vocab: Optional[int] = None,
@@ -405,4 +406,4 @@ def make_sample_inputs(w: SampleWorkload, batch: Optional[int] = None, vocab: Op
         list(ex.map(one, range(B)))
     u0, _ = philox_uniforms(w.seed, np.arange(B)[:, None], np.arange(k)[None, :], stream=0)
     _, u1 = philox_uniforms(w.seed, np.arange(B)[:, None], np.arange(k + 1)[None, :], stream=1)
-    return SampleInputs(tl, dl, drafts, u0, u1)
+    return SampleInputs(tl, dl, drafts, u0, u1, seed=w.seed)

@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ("sdv_verify_forward", "sdv_accept_greedy", "sdv_accept_sample", "sdv_kv_rollback",
               "sdv_verify_workspace_size", "sdv_sample_workspace_size", "sdv_pack_weights",
-              "sdv_packed_bytes", "sdv_last_error", "sdv_abi_version"):
+              "sdv_packed_bytes", "sdv_last_error", "sdv_abi_version", "sdv_philox_uniforms"):
         assert f in names, f
 
 
@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_packed_sizes():
     L = sdv.lib()
-    assert L.sdv_abi_version() == 4
+    assert L.sdv_abi_version() == 5
     # rows round up to 16, 2 bytes (bf16) / 4 bytes (fp32) per value
     assert L.sdv_packed_bytes(1, 6144, 2048) == 6144 * 2048 * 2
     assert L.sdv_packed_bytes(0, 17, 64) == 32 * 64 * 4
@@ -77,3 +77,20 @@ def test_workspace_sizes_are_host_arithmetic():
     n1 = L.sdv_sample_workspace_size(64, 7, 151936)
     n2 = L.sdv_sample_workspace_size(128, 7, 151936)
     assert 0 < n1 < n2
+
+
+def test_sampling_arguments_are_checked_on_the_host():
+    L = sdv.lib()
+    p = ctypes.c_void_p(256)
+    ws = L.sdv_sample_workspace_size(4, 3, 100)
+    assert L.sdv_sample_workspace_size(4, 1025, 100) == 0           # k above the maximum
+    # NULL logits, bad temperature, workspace too small: rejected before any launch
+    assert L.sdv_accept_sample(4, 3, 100, None, p, p, ctypes.c_float(1.0), 7, None, p, p, None, p, ws, None,
+                               None) == -1
+    for t in (0.0, -1.0, float("inf"), float("nan")):
+        assert L.sdv_accept_sample(4, 3, 100, p, p, p, ctypes.c_float(t), 7, None, p, p, None, p, ws, None,
+                                   None) == -2
+    assert L.sdv_accept_sample(4, 3, 100, p, p, p, ctypes.c_float(1.0), 7, None, p, p, None, p, ws - 1, None,
+                               None) == -4
+    assert L.sdv_philox_uniforms(1, None, 4, 3, None, None, None) == -1
+    assert L.sdv_philox_uniforms(1, None, 0, 3, p, None, None) == -2

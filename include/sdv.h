@@ -218,6 +218,19 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
                               sdv_verify_out* out, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* The verify forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and effects as sdv_verify_forward; the
+ * workspace is a static device array of SDV_NOALLOC_MAX_WORKSPACE bytes inside the
+ * library (one per GPU, held until the process ends).  A pass whose
+ * sdv_verify_workspace_size exceeds that returns SDV_ERR_WORKSPACE before anything is
+ * enqueued.  Calls on one GPU share the array: calls that overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.  Allocates and
+ * frees nothing. */
+#define SDV_NOALLOC_MAX_WORKSPACE (64u << 20)
+sdv_status sdv_verify_forward_noalloc(const sdv_model* m, const sdv_kv* kv, const sdv_verify_in* in,
+                                      sdv_verify_out* out, void* stream);
+
 /* Greedy acceptance ("Method steps", step 4) for every sequence b.
  *   Walk from row L_a-1; at each row, the child row whose token equals that row's
  *   argmax is accepted and the walk continues from it; stop when no child matches.

@@ -89,6 +89,9 @@ def lib():
         L.sdv_verify_forward.argtypes = [ctypes.POINTER(SdvModel), ctypes.POINTER(SdvKV),
                                          ctypes.POINTER(SdvVerifyIn), ctypes.POINTER(SdvVerifyOut),
                                          _vp, ctypes.c_size_t, _vp]
+        L.sdv_verify_forward_noalloc.restype = ctypes.c_int
+        L.sdv_verify_forward_noalloc.argtypes = [ctypes.POINTER(SdvModel), ctypes.POINTER(SdvKV),
+                                                 ctypes.POINTER(SdvVerifyIn), ctypes.POINTER(SdvVerifyOut), _vp]
         L.sdv_accept_greedy.restype = ctypes.c_int
         L.sdv_accept_greedy.argtypes = [_i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp,
                                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -333,11 +336,18 @@ class Verifier:
         t = torch.as_tensor(np.asarray(tokens, dtype=np.int32).reshape(self.B, self.T))
         self.tokens.copy_(t)
 
-    def forward(self, stream=None) -> VerifyResult:
-        _check(lib().sdv_verify_forward(ctypes.byref(self.model.desc), ctypes.byref(self.kv.desc),
-                                        ctypes.byref(self.inp), ctypes.byref(self.out),
-                                        ctypes.c_void_p(self.workspace.data_ptr()), self.workspace.numel(),
-                                        _stream(stream)), "sdv_verify_forward")
+    def forward(self, stream=None, noalloc: bool = False) -> VerifyResult:
+        """noalloc: call sdv_verify_forward_noalloc (the library's static scratch) instead
+        of passing this Verifier's workspace."""
+        if noalloc:
+            _check(lib().sdv_verify_forward_noalloc(ctypes.byref(self.model.desc), ctypes.byref(self.kv.desc),
+                                                    ctypes.byref(self.inp), ctypes.byref(self.out), _stream(stream)),
+                   "sdv_verify_forward_noalloc")
+        else:
+            _check(lib().sdv_verify_forward(ctypes.byref(self.model.desc), ctypes.byref(self.kv.desc),
+                                            ctypes.byref(self.inp), ctypes.byref(self.out),
+                                            ctypes.c_void_p(self.workspace.data_ptr()), self.workspace.numel(),
+                                            _stream(stream)), "sdv_verify_forward")
         return VerifyResult(self.argmax, self.margin, self.lse, self.err, self.logits, self.hidden, self.cb_argmax)
 
 

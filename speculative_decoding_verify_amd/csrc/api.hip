@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "../../include/sdv.h"
@@ -16,6 +17,12 @@
 
 using namespace sdv;
 
+// Scratch memory of sdv_verify_forward_noalloc: one array per GPU, allocated when the
+// code object loads and held until the process ends.  Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the symbol): it
+// takes each GPU's device address from hipGetSymbolAddress (current_scratch below).
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)SDV_NOALLOC_MAX_WORKSPACE;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -260,8 +267,32 @@ GemmArgs gemm_args(const void* A, int M, const void* W, int N, int K) {
   return a;
 }
 
+// The device address of each GPU's copy of `scratch`, looked up once per device.
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// device address of the current device's scratch array (looked up on the first call
+// on that device, with that device current)
+sdv_status current_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SDV_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(SDV_ERR_UNSUPPORTED, "device ordinal %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SDV_ERR_LAUNCH, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SDV_OK;
+}
+
 sdv_status verify_forward_impl(const sdv_model* m, const sdv_kv* kv, const sdv_verify_in* in, sdv_verify_out* out,
-                               void* ws, size_t ws_bytes, void* stream);
+                               void* ws, size_t ws_bytes, void* stream, bool use_scratch);
 
 }  // namespace
 
@@ -277,7 +308,12 @@ size_t sdv_verify_workspace_size(const sdv_model* m, int32_t batch, int32_t T, i
 
 sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_verify_in* in, sdv_verify_out* out,
                               void* ws, size_t ws_bytes, void* stream) {
-  return verify_forward_impl(m, kv, in, out, ws, ws_bytes, stream);
+  return verify_forward_impl(m, kv, in, out, ws, ws_bytes, stream, false);
+}
+
+sdv_status sdv_verify_forward_noalloc(const sdv_model* m, const sdv_kv* kv, const sdv_verify_in* in,
+                                      sdv_verify_out* out, void* stream) {
+  return verify_forward_impl(m, kv, in, out, nullptr, 0, stream, true);
 }
 
 }  // extern "C"
@@ -285,7 +321,7 @@ sdv_status sdv_verify_forward(const sdv_model* m, const sdv_kv* kv, const sdv_ve
 namespace {
 
 sdv_status verify_forward_impl(const sdv_model* m, const sdv_kv* kv, const sdv_verify_in* in, sdv_verify_out* out,
-                               void* ws, size_t ws_bytes, void* stream) {
+                               void* ws, size_t ws_bytes, void* stream, bool use_scratch) {
   sdv_status st = check_model(m);
   if (st != SDV_OK) return st;
   if (!kv || !in || !out) return fail(SDV_ERR_NULL, "kv/in/out is NULL");
@@ -305,6 +341,14 @@ sdv_status verify_forward_impl(const sdv_model* m, const sdv_kv* kv, const sdv_v
   if (in->head == SDV_HEAD_CODEBOOK && m->n_codebooks < 1) return fail(SDV_ERR_UNSUPPORTED, "model has no codebook heads");
   if (in->head == SDV_HEAD_LM && in->cfg_partner) return fail(SDV_ERR_UNSUPPORTED, "guidance pairs need the codebook head");
   const Plan P = make_plan(m, B, T, R, in->max_ctx);
+  if (use_scratch) {
+    if (P.total > NOALLOC_SCRATCH_BYTES)
+      return fail(SDV_ERR_WORKSPACE, "pass needs %zu bytes of scratch, more than the %zu-byte static scratch of "
+                  "sdv_verify_forward_noalloc (use sdv_verify_forward with a workspace)", P.total,
+                  NOALLOC_SCRATCH_BYTES);
+    if ((st = current_scratch(&ws)) != SDV_OK) return st;
+    ws_bytes = NOALLOC_SCRATCH_BYTES;
+  }
   if (!ws || ws_bytes < P.total) return fail(SDV_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, P.total);
 
   hipStream_t s = (hipStream_t)stream;

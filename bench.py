@@ -6,8 +6,16 @@ One step = one pass of the whole hot path over one batch of synthetic input:
 (the speculative-sampling workload times accept_sample alone).  Inputs are resident
 in HBM before timing.  Prints ONE JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1.7b-bf16|8b-bf16-tree|toy-f32|sample]
-                  [--graph] [--no-cpu-baseline]
+By default every workload runs, largest first: the batched multi-codebook pass (32
+sessions x guidance pairs on the 8B backbone) carries the headline value, and the
+8B tree pass, the 1.7B pass, the sampling acceptance and the toy fp32 pass follow as
+sub-objects of the same line (`configs`), each with the roofline of its dominant
+kernel (timed live with HIP events the library records on its launch stream), the
+roofline of the whole pass and the CPU oracle timed on a bounded sample.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W]
+                  [--workload all|c5-codebook|8b-bf16-tree|1.7b-bf16|toy-f32|sample]
+                  [--scenario silence|random] [--graph] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -23,48 +31,32 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+MFMA_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+MFMA_F32_TFLOPS = 157.3    # MI355X fp32 (the fp32 model's matrix work runs at this rate at best)
 METRIC = "verified tokens/s per verify pass (chunk+draft) at 1 GPU; % of HBM roofline"
 
-
-def pass_bytes(sh, T, R, C, n_branch_rows=0):
-    """Algorithmic HBM bytes of one verify pass: every weight read once (embedding:
-    the T gathered rows), KV read (C cached rows), KV written (T rows), fp32 logits
-    of the R rows acceptance needs."""
-    eb = sh.elem_bytes
-    w = sh.n_layers * (sh.layer_params() - 2 * sh.d) * eb + sh.vocab * sh.d * eb
-    w += sh.n_layers * 2 * sh.d * 4 + sh.d * 4          # fp32 norm gains
-    w += T * sh.d * eb                                   # gathered embedding rows
-    kv_row = sh.n_layers * 2 * sh.kv_dim * eb
-    return w + C * kv_row + T * kv_row + R * sh.vocab * 4
-
-
-def gate_up_launch_bytes(sh, M):
-    """Algorithmic HBM bytes of one gate/up projection launch (the pass's dominant
-    kernel): the gate and up weights read once, the M normed rows read (4 bytes per
-    value) and the M SwiGLU rows written (4 bytes per value)."""
-    return 2 * sh.ffn * sh.d * sh.elem_bytes + M * sh.d * 4 + M * sh.ffn * 4
-
-
-# HBM traffic of the gate/up kernel from rocprofv3 counters (FETCH_SIZE, then WRITE_SIZE
-# in separate runs of `bench.py --steps 5 --warmup 2 --no-cpu-baseline`), per dispatch,
-# each scaled by what the same counter reads for a plain 256 MiB device copy
-# (`bench.py --copy-calibration`).  Valid only for the workload and the kernel sources
-# they were taken on: both are checked at run time, else traffic is null.
-GATE_UP_TRAFFIC = {"workload": "1.7b-bf16", "sha256": "1f2e20b165ea0707cce46f9d32e44eb39ca284dd8af7f3b6fb72fb9ac882fa1e",
-                   "fetch_kib": 34365.5, "fetch_factor": 262144.0 / 131084.0,
-                   "write_kib": 1344.0, "write_factor": 262144.0 / 262144.0}
+# -- stored HBM traffic of dominant kernels -------------------------------------------
+# From two rocprofv3 counter runs of the same bench command (FETCH_SIZE, then WRITE_SIZE,
+# KiB per dispatch averaged over the kernel's dispatches), each scaled by what the same
+# counter reads for a plain 256 MiB device copy (`bench.py --copy-calibration`: FETCH_SIZE
+# reads 131,084 KiB for 262,144 KiB copied, factor 2.000; WRITE_SIZE reads 262,144 KiB,
+# factor 1.000).  An entry counts only for its workload and kernel and while the sha256
+# of the kernel's sources is the one it was taken on; otherwise traffic is null.
+FETCH_FACTOR = 262144.0 / 131084.0
+WRITE_FACTOR = 1.0
 GEMM_SOURCES = ("speculative_decoding_verify_amd/csrc/gemm.hip", "speculative_decoding_verify_amd/csrc/common.h",
                 "speculative_decoding_verify_amd/csrc/kernels.h")
-
-
-# the same for the row-statistics launch of the speculative-sampling acceptance
-# (64 x 7 drafts, V = 151936)
-ROW_STATS_TRAFFIC = {"workload": "sample", "sha256": "fbfca9f7a64e4cc888b3ebe1372631ccdd6ee92218f7685a8541ddb198a3834f",
-                     "fetch_kib": 284937.3, "fetch_factor": 262144.0 / 131084.0,
-                     "write_kib": 60.0, "write_factor": 262144.0 / 262144.0}
+ATTN_SOURCES = ("speculative_decoding_verify_amd/csrc/attention.hip", "speculative_decoding_verify_amd/csrc/common.h",
+                "speculative_decoding_verify_amd/csrc/kernels.h")
 SAMPLE_SOURCES = ("speculative_decoding_verify_amd/csrc/accept.hip", "speculative_decoding_verify_amd/csrc/common.h",
                   "speculative_decoding_verify_amd/csrc/kernels.h")
+KERNEL_SOURCES = {"qkv": GEMM_SOURCES, "o": GEMM_SOURCES, "gate_up": GEMM_SOURCES, "down": GEMM_SOURCES,
+                  "lm_head": GEMM_SOURCES, "codebook_head": GEMM_SOURCES, "attention": ATTN_SOURCES,
+                  "row_stats": SAMPLE_SOURCES}
+TRAFFIC = [
+    # {"workload": ..., "kernel": ..., "sha256": ..., "fetch_kib": ..., "write_kib": ...}
+]
 
 
 def source_sha(files):
@@ -76,99 +68,228 @@ def source_sha(files):
     return h.hexdigest()
 
 
-def gemm_source_sha():
-    return source_sha(GEMM_SOURCES)
-
-
-def counter_traffic(t, workload, files):
-    """HBM bytes per launch from stored counter readings, or None once the kernel's
-    sources differ from those the counters were taken on."""
-    if not t or t["workload"] != workload or t["sha256"] != source_sha(files):
+def counter_traffic(entry, workload, kernel):
+    """HBM bytes per launch from a stored counter reading, or None when the entry is for
+    another workload or kernel or the kernel's sources have changed since."""
+    if not entry or entry["workload"] != workload or entry["kernel"] != kernel:
         return None
-    return (t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"]) * 1024.0
+    if entry["sha256"] != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    return (entry["fetch_kib"] * FETCH_FACTOR + entry["write_kib"] * WRITE_FACTOR) * 1024.0
 
 
-def gate_up_traffic(workload):
-    return counter_traffic(GATE_UP_TRAFFIC, workload, GEMM_SOURCES)
+def stored_traffic(workload, kernel):
+    for e in TRAFFIC:
+        t = counter_traffic(e, workload, kernel)
+        if t is not None:
+            return t
+    return None
 
 
-def cpu_threads():
+# -- host description for the CPU baselines --------------------------------------------
+
+def host_info():
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        info = threadpool_info()
-        n = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-        return int(n)
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
-        return len(os.sched_getaffinity(0))
+        pass
+    return {"cores": cores, "cpu_model": model, "blas_threads": blas}
 
 
-def draft_under_silence(sdv, model, kv, C, L_a, gamma, silence_id=0):
-    """Greedy drafting on the GPU path (untimed setup): feed L_a silence tokens, then
-    decode gamma tokens one at a time; roll the cache back to C afterwards."""
+def cpu_record(value, unit, sample):
+    h = host_info()
+    return {"value": value, "unit": unit, "cores": h["cores"], "kind": "oracle", "sample": sample,
+            "cpu_model": h["cpu_model"], "blas_threads": h["blas_threads"]}
+
+
+# -- algorithmic work of a verify pass ---------------------------------------------------
+
+def pass_bytes(sh, T, R, ctx, head_rows=None, head_cols=None):
+    """Algorithmic HBM bytes of one verify pass: every weight read once (embedding: the
+    gathered rows), KV read (the cached rows), KV written (the chunk rows), fp32 logits of
+    the rows acceptance needs.  ctx: cached length per sequence.  head_rows / head_cols:
+    the logit matrix (default R rows per sequence over the full vocabulary)."""
+    eb = sh.elem_bytes
+    B = len(ctx)
+    head_cols = sh.vocab if head_cols is None else head_cols
+    head_rows = B * R if head_rows is None else head_rows
+    w = sh.n_layers * (sh.layer_params() - 2 * sh.d) * eb + head_cols * sh.d * eb
+    w += sh.n_layers * 2 * sh.d * 4 + sh.d * 4          # fp32 norm gains
+    w += B * T * sh.d * eb                               # gathered embedding rows
+    kv_row = sh.n_layers * 2 * sh.kv_dim * eb
+    return w + sum(ctx) * kv_row + B * T * kv_row + head_rows * head_cols * 4
+
+
+def attn_visible_keys(T, C, parent):
+    """sum over chunk rows j of the keys row j attends to: C cached + its ancestors-or-self."""
+    depth = np.zeros(T, dtype=np.int64)
+    for j in range(1, T):
+        depth[j] = depth[parent[j] if parent is not None else j - 1] + 1
+    return int(T * C + (depth + 1).sum())
+
+
+def launch_work(sh, B, T, R, ctx, parent, head="lm"):
+    """Algorithmic bytes and FLOPs of one launch of each kernel kind (per layer for the
+    decoder kinds): weights read once, activation rows in and out at 4 bytes per value
+    (the bf16 hi/lo pair or fp32), K/V read once per (sequence, kv head)."""
+    eb = sh.elem_bytes
+    d, F, H, Hkv, dh = sh.d, sh.ffn, sh.n_heads, sh.n_kv_heads, sh.head_dim
+    M, Mr = B * T, B * R
+    qd, kd = H * dh, Hkv * dh
+    work = {
+        "qkv": (( qd + 2 * kd) * d * eb + M * d * 4 + M * qd * 4 + M * 2 * kd * eb, 2.0 * M * (qd + 2 * kd) * d),
+        "attention": (sum(C + T for C in ctx) * 2 * kd * eb + 2 * M * qd * 4,
+                      4.0 * H * dh * sum(attn_visible_keys(T, C, parent) for C in ctx)),
+        "o": (d * qd * eb + M * qd * 4 + M * d * 4, 2.0 * M * d * qd),
+        "gate_up": (2 * F * d * eb + M * d * 4 + M * F * 4, 2.0 * M * 2 * F * d),
+        "down": (d * F * eb + M * F * 4 + M * d * 4, 2.0 * M * d * F),
+    }
+    if head == "lm":
+        work["lm_head"] = (sh.vocab * d * eb + Mr * d * 4 + Mr * sh.vocab * 4, 2.0 * Mr * sh.vocab * d)
+    else:
+        S, Vc = sh.n_codebooks, sh.codebook_size
+        work["codebook_head"] = (Vc * d * eb + (Mr + S) * d * 4 + (Mr + S) * Vc * 4, 2.0 * (Mr + S) * Vc * d)
+    return work
+
+
+def mfma_peak(sh):
+    return MFMA_BF16_TFLOPS if sh.dtype == "bf16" else MFMA_F32_TFLOPS
+
+
+def roofline_of(kind, nbytes, flops, us, sh, workload, launches):
+    """Roofline of one kernel kind from its algorithmic bytes and FLOPs per launch and
+    its average launch duration: bound by HBM when its arithmetic intensity is below
+    the ridge (peak FLOP/s over peak bytes/s), by the matrix cores otherwise."""
+    peak_tf = mfma_peak(sh)
+    ridge = peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if flops / nbytes > ridge:
+        achieved = flops / (us * 1e-6) / 1e12
+        r = {"bound": "mfma", "achieved": achieved, "peak": peak_tf, "unit": "TFLOP/s", "frac": achieved / peak_tf}
+    else:
+        achieved = nbytes / (us * 1e-6) / 1e9
+        r = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": achieved / HBM_PEAK_GBS}
+    r.update({"traffic": stored_traffic(workload, kind), "kernel": kind, "bytes_per_launch": int(nbytes),
+              "flops_per_launch": flops, "avg_launch_us": us, "launches_per_pass": launches})
+    return r
+
+
+GEMM_KINDS = ("qkv", "o", "gate_up", "down")
+
+
+def live_kernel_times(sdv, ver, sh, step, steps, head_kind):
+    """Average launch duration (us) of each kernel kind over `steps` passes, from HIP
+    events the library records on the launch stream around each GEMM launch and each
+    layer's attention."""
     import torch
-    ver = sdv.Verifier(model, kv, L_a, L_a, [L_a - 1], max_ctx=C, want_logits=False)
-    ver.set_tokens(np.full((1, L_a), silence_id))
-    res = ver.forward()
-    keep = torch.tensor([C + L_a], dtype=torch.int32, device="cuda")
-    sdv.kv_rollback(model, kv, keep)
-    drafts = [int(res.argmax[0, 0])]
-    step = sdv.Verifier(model, kv, 1, 1, [0], max_ctx=C + L_a + gamma, want_logits=False)
-    for i in range(gamma - 1):
-        step.set_tokens(np.array([[drafts[-1]]]))
-        r = step.forward()
-        keep = torch.tensor([C + L_a + i + 1], dtype=torch.int32, device="cuda")
-        sdv.kv_rollback(model, kv, keep)
-        drafts.append(int(r.argmax[0, 0]))
-    sdv.kv_rollback(model, kv, torch.tensor([C], dtype=torch.int32, device="cuda"))
+    L = sh.n_layers
+    n_gemm = 4 * L + 1
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_gemm)]
+    aev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * L)]
+    ver.set_profile_events(ev, aev)
+    g, a = [], []
+    for _ in range(steps):
+        step()
+        torch.cuda.synchronize()
+        g.append([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n_gemm)])
+        a.append([aev[2 * i].elapsed_time(aev[2 * i + 1]) for i in range(L)])
+    ver.set_profile_events(None)
+    g = np.asarray(g) * 1e3
+    a = np.asarray(a) * 1e3
+    per_layer = g[:, :4 * L].reshape(steps, L, 4)
+    us = {k: float(per_layer[:, :, i].mean()) for i, k in enumerate(GEMM_KINDS)}
+    us["attention"] = float(a.mean())
+    us[head_kind] = float(g[:, -1].mean())
+    return us
+
+
+def kernel_table(sh, us, work, workload, head_kind):
+    """Roofline of every kernel kind plus the dominant one (largest time per pass)."""
+    L = sh.n_layers
+    table = {}
+    for kind, t in us.items():
+        nb, fl = work[kind]
+        table[kind] = roofline_of(kind, nb, fl, t, sh, workload, 1 if kind == head_kind else L)
+    dom = max(table, key=lambda k: table[k]["avg_launch_us"] * table[k]["launches_per_pass"])
+    return table, dom
+
+
+def timed_steps(step, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step()
     torch.cuda.synchronize()
-    return drafts
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
 
 
-def bench_verify(args, wl):
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# -- drafting (untimed set-up) ----------------------------------------------------------
+
+def draft_under_silence(sdv, model, kv, C, L_a, gamma, silence_id=0, n_branch=0):
+    """Greedy drafting on the GPU path (untimed set-up): sdv_draft_tree with the chunk
+    under silence gives the main draft (gamma tokens) and, with n_branch > 0, the
+    runner-up branch (the second-best first token continued greedily).  The cache is left
+    at C."""
+    import torch
+    drafter = sdv.Drafter(model, kv, L_a, [gamma] + ([n_branch] if n_branch else []), max_ctx=C)
+    drafter.set_chunk(np.full((kv.batch, L_a), silence_id, dtype=np.int32))
+    out = drafter.run()
+    torch.cuda.synchronize()
+    d = out["drafts"].cpu().numpy()[0]
+    main = [int(x) for x in d[0, :gamma]]
+    branch = [int(x) for x in d[1, :n_branch]] if n_branch else []
+    return main, branch
+
+
+# -- the single-sequence verify workloads (toy, 1.7B, 8B tree) ----------------------------
+
+def bench_verify(args, wl, w=None, model=None):
     import torch
     import speculative_decoding_verify_amd as sdv
     from synth import make_weights, make_random_kv, uniform_tokens
 
-    sh = wl.shape
+    sh = wl.shape if w is None else w.shape
     C = wl.ctx[0]
     T, L_a, gamma = wl.T, wl.L_a, wl.gamma
     t0 = time.time()
-    w = make_weights(sh, seed=wl.seed)
-    if wl.kv_init == "prefill":
-        kv_host = None
-    else:
-        kv_host = make_random_kv(sh, [C], capacity=C + T, seed=wl.seed + 1000)
-    model = sdv.DeviceModel(w)
+    if w is None:
+        w = make_weights(sh, seed=wl.seed)
+    if model is None:
+        model = sdv.DeviceModel(w)
+    kv_host = None if wl.kv_init == "prefill" else make_random_kv(sh, [C], capacity=C + T, seed=wl.seed + 1000)
     kv = sdv.PagedKV(sh, 1, C + T + 64)
     if kv_host is not None:
         kv.load(kv_host)
     else:
         # prefill the context through the model itself (chunks of 128 rows)
-        ctx = uniform_tokens(C, sh.vocab, wl.seed + 2000, "ctx")
-        done = 0
-        while done < C:
-            n = min(128, C - done)
-            pv = sdv.Verifier(model, kv, n, n, [n - 1], max_ctx=done, want_logits=False)
-            pv.set_tokens(ctx[None, done:done + n])
-            pv.forward()
-            done += n
-            sdv.kv_rollback(model, kv, torch.tensor([done], dtype=torch.int32, device="cuda"))
+        sdv.prefill(model, kv, uniform_tokens(C, sh.vocab, wl.seed + 2000, "ctx")[None, :])
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
-    # drafts: greedy under silence on the GPU path; main draft + runner-up branch
-    drafts = draft_under_silence(sdv, model, kv, C, L_a, gamma, wl.silence_id)
+    drafts, branch = draft_under_silence(sdv, model, kv, C, L_a, gamma, wl.silence_id, wl.n_branch)
     parent = wl.parent()
-    branch = []
-    if wl.n_branch:
-        # runner-up first token: the second-best token of the first draft position,
-        # continued greedily (untimed setup; uses the GPU path's logits)
-        ver0 = sdv.Verifier(model, kv, L_a, L_a, [L_a - 1], max_ctx=C, want_logits=True)
-        ver0.set_tokens(np.full((1, L_a), wl.silence_id))
-        lg = ver0.forward().logits[0, 0].clone()
-        lg[drafts[0]] = -float("inf")
-        branch = [int(torch.argmax(lg))] + list(uniform_tokens(wl.n_branch - 1, sh.vocab, wl.seed + 3000, "br"))
-        sdv.kv_rollback(model, kv, torch.tensor([C], dtype=torch.int32, device="cuda"))
     audio = np.full(L_a, wl.silence_id, dtype=np.int32) if args.scenario == "silence" else \
         uniform_tokens(L_a, sh.vocab, wl.seed + 4000, "audio")
     tokens = np.concatenate([audio, np.asarray(drafts, np.int32), np.asarray(branch, np.int32)]).astype(np.int32)
@@ -188,11 +309,11 @@ def bench_verify(args, wl):
         sdv.kv_rollback(model, kv, acc_out["keep"], acc_out["move_src"], acc_out["move_dst"], acc_out["err"],
                         stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
     graph = None
     if args.graph:
+        for _ in range(max(1, args.warmup)):
+            step()
+        torch.cuda.synchronize()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
@@ -203,58 +324,22 @@ def bench_verify(args, wl):
         with torch.cuda.graph(graph):
             step()
         torch.cuda.synchronize()
-
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for _ in range(args.steps):
-        if graph is not None:
-            graph.replay()
-        else:
-            step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    ms = elapsed / args.steps * 1e3
+    ms = timed_steps(graph.replay if graph is not None else step, args.steps, args.warmup)
     n_acc = int(acc_out["n"][0])
     assert int(acc_out["err"][0]) == 0 and int(ver.err[0]) == 0, "device error during bench"
 
-    # live per-launch timing of the GEMMs with HIP events that the library records on
-    # the launch stream around each GEMM launch (per layer: q/k/v, o, gate/up, down;
-    # then the LM head), over K more steps of the same pass
-    n_gemm = 4 * sh.n_layers + 1
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_gemm)]
-    ver.set_profile_events(ev)
-    gemm_ms = []
-    for _ in range(args.steps):
-        step()
-        torch.cuda.synchronize()
-        per = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n_gemm)]
-        gemm_ms.append(per)
-    ver.set_profile_events(None)
-    gemm_ms = np.asarray(gemm_ms)                      # [steps, launches]
-    per_layer = gemm_ms[:, :4 * sh.n_layers].reshape(args.steps, sh.n_layers, 4)
-    launch_us = {name: float(per_layer[:, :, i].mean()) * 1e3 for i, name in enumerate(("qkv", "o", "gate_up", "down"))}
-    launch_us["lm_head"] = float(gemm_ms[:, -1].mean()) * 1e3
-    gu_us = launch_us["gate_up"]
-    gu_bytes = gate_up_launch_bytes(sh, T)
-    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
-    traffic = gate_up_traffic(args.workload)
-    lm_bytes = sh.vocab * sh.d * sh.elem_bytes
-
-    nbytes = pass_bytes(sh, T, R, C)
+    us = live_kernel_times(sdv, ver, sh, step, args.steps, "lm_head")
+    work = launch_work(sh, 1, T, R, [C], parent, "lm")
+    table, dom = kernel_table(sh, us, work, wl.shape.name, "lm_head")
+    nbytes = pass_bytes(sh, T, R, [C])
+    flops = sum(fl * (1 if k == "lm_head" else sh.n_layers) for k, (nb, fl) in work.items())
     passes_s = 1e3 / ms
     out = {
         "metric": METRIC,
         "value": T * passes_s,
         "unit": "verified tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": "bf16" if sh.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded N(0,0.02) weights, unit-variance synthetic KV, drafts greedy under silence)",
         "config": {"workload": f"{wl.shape.name} verify: {sh.n_layers} layers d={sh.d} {sh.n_heads}x{sh.head_dim} "
                                f"q heads / {sh.n_kv_heads} kv heads FFN {sh.ffn} V={sh.vocab}; C={C}; "
                                f"{L_a} audio + {gamma} drafts" + (f" + {wl.n_branch}-token branch (tree mask)"
@@ -264,51 +349,51 @@ def bench_verify(args, wl):
         "passes_per_s": passes_s,
         "committed_tokens_per_pass": n_acc + 1,
         "committed_tokens_per_s": (n_acc + 1) * passes_s,
+        "roofline": table[dom],
         "pass_roofline": {"bound": "hbm", "bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
-                          "peak_GBs": HBM_PEAK_GBS, "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "roofline": {"bound": "hbm", "kernel": "gemm_stream, SwiGLU epilogue (gate/up projection)",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "bytes_per_launch": gu_bytes, "avg_launch_us": gu_us,
-                     "launches_per_pass": sh.n_layers},
-        "gemm_launch_us": launch_us,
-        "lm_head": {"avg_launch_us": launch_us["lm_head"], "GBs": lm_bytes / (launch_us["lm_head"] * 1e-6) / 1e9},
+                          "peak_GBs": HBM_PEAK_GBS, "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "flops": flops, "mfma_frac": flops / (ms * 1e-3) / 1e12 / mfma_peak(sh)},
+        "kernels": {k: {"avg_launch_us": v["avg_launch_us"], "launches_per_pass": v["launches_per_pass"],
+                        "bound": v["bound"], "frac": v["frac"]} for k, v in table.items()},
         "setup_s": setup_s,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_verify(w, kv_host, wl, tokens, parent, rows, T)
+        out["cpu_baseline"] = cpu_baseline_verify(w, kv_host, wl, sh, tokens, parent, rows, T)
     return out
 
 
-def cpu_baseline_verify(w, kv_host, wl, tokens, parent, rows, T):
-    """The oracle (fp64 NumPy, bf16 rounding mode for bf16 models) timed on the host:
-    one full pass (verify + greedy acceptance + commit plan)."""
+def cpu_baseline_verify(w, kv_host, wl, sh, tokens, parent, rows, T):
+    """The oracle (fp64 NumPy; bf16 rounding mode for bf16 models) timed on the host: full
+    passes (verify + greedy acceptance + commit plan) of the same workload, repeated
+    until about 10 s of CPU time (at least one pass, at most 20)."""
     from oracle import BF16_KV, EXACT
     from oracle import accept as oacc
     from oracle import decoder as odec
     from synth import make_random_kv
-    sh = wl.shape
     C = wl.ctx[0]
-    if kv_host is None:  # prefilled context: use synthetic KV of the same shape for the timing sample
+    if kv_host is None:  # prefilled context: synthetic KV of the same shape for the timing sample
         kv_host = make_random_kv(sh, [C], capacity=C + T, seed=wl.seed + 1000)
     mode = BF16_KV if sh.dtype == "bf16" else EXACT
     cache = odec.Cache(kv_host.k, kv_host.v)
-    reps = 0
-    t0 = time.perf_counter()
+    times = []
     while True:
+        t0 = time.perf_counter()
         res = odec.verify_forward(w, cache, tokens[None, :], parent, rows, mode)
         am = [oacc.argmax_lowest(r) for r in res["logits"][0]]
         n, nxt, path = oacc.accept_greedy(list(tokens), parent, wl.L_a, rows, am)
         oacc.commit_plan(C, wl.L_a, path)
-        reps += 1
-        if time.perf_counter() - t0 > 10.0 or reps >= 3:
+        times.append(time.perf_counter() - t0)
+        if sum(times) > 10.0 or len(times) >= 20:
             break
-    dt = (time.perf_counter() - t0) / reps
-    return {"value": T / dt, "unit": "verified tokens/s", "cores": cpu_threads(), "kind": "oracle",
-            "sample": f"{reps} full verify pass(es) of the same workload, fp64 oracle ({mode} mode), "
-                      f"{dt:.2f} s per pass"}
+    dt = float(np.median(times))
+    return cpu_record(T / dt, "verified tokens/s",
+                      f"{len(times)} full verify pass(es) of the same workload (median {dt:.3f} s), fp64 oracle "
+                      f"({mode} mode)")
 
 
-def bench_c5(args, wl):
+# -- the batched multi-codebook workload --------------------------------------------------
+
+def bench_c5(args, wl, w=None, model=None):
     """Batched multi-codebook verify: 32 sessions x (conditional, unconditional) rows on
     the 8B-shape backbone with 8 codebook heads, guidance w = 2, acceptance on codebook 0.
     One step = kv_rollback(C) -> verify_forward -> accept_greedy -> kv_rollback."""
@@ -321,16 +406,19 @@ def bench_c5(args, wl):
     base = sh.vocab - S * Vc
     ctx = list(wl.ctx)
     t0 = time.time()
-    w = make_weights(sh, seed=wl.seed)
-    model = sdv.DeviceModel(w)
-    del w
+    if w is None:
+        w = make_weights(sh, seed=wl.seed)
+    if model is None:
+        model = sdv.DeviceModel(w)
     table, n_blocks = page_table(ctx, T + 16, 16, seed=wl.seed + 7)
     kv = sdv.PagedKV(sh, B, 0, table=table, n_blocks=n_blocks)
-    kv.load(HashedKV(sh, ctx, 0, seed=wl.seed + 1000, device=kv.device))
+    kv_seed = wl.seed + 1000
+    kv.load(HashedKV(sh, ctx, 0, seed=kv_seed, device=kv.device))
     tokens = np.empty((B, T), dtype=np.int32)
     for s_ in range(B // 2):   # uniform codes; both rows of a session get the same ids
         tokens[2 * s_] = tokens[2 * s_ + 1] = base + uniform_tokens(T, Vc, wl.seed * 1000 + s_, "c5codes") - 1
     rows = wl.logit_rows()
+    R = len(rows)
     ver = sdv.Verifier(model, kv, T, L_a, rows, max_ctx=max(ctx), want_logits=False, head=sdv.HEAD_CODEBOOK,
                        cfg_partner=[b ^ 1 for b in range(B)], cfg_w=wl.cfg_w)
     ver.set_tokens(tokens)
@@ -347,54 +435,82 @@ def bench_c5(args, wl):
                                     out=acc_out)
         sdv.kv_rollback(model, kv, acc_out["keep"], acc_out["move_src"], acc_out["move_dst"], acc_out["err"])
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t_start) / args.steps * 1e3
+    ms = timed_steps(step, args.steps, args.warmup)
     assert int(acc_out["err"].abs().sum()) == 0 and int(ver.err.abs().sum()) == 0, "device error during bench"
-    n_gemm = 4 * sh.n_layers + 1
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_gemm)]
-    ver.set_profile_events(ev)
-    step()
-    torch.cuda.synchronize()
-    per = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n_gemm)]
-    ver.set_profile_events(None)
-    per_layer = np.asarray(per[:4 * sh.n_layers]).reshape(sh.n_layers, 4)
-    launch_us = {name: float(per_layer[:, i].mean()) * 1e3 for i, name in enumerate(("qkv", "o", "gate_up", "down"))}
-    launch_us["codebook_head"] = per[-1] * 1e3
+    us = live_kernel_times(sdv, ver, sh, step, max(3, args.steps // 4), "codebook_head")
+    work = launch_work(sh, B, T, R, ctx, None, "codebook")
+    ktable, dom = kernel_table(sh, us, work, "c5-codebook", "codebook_head")
     M = B * T
-    gu_flops = 2.0 * M * (2 * sh.ffn) * sh.d
-    achieved = gu_flops / (launch_us["gate_up"] * 1e-6) / 1e12
-    kv_bytes = sum(ctx) * sh.n_layers * 2 * sh.kv_dim * sh.elem_bytes
-    # weights read once (decoder, codebook matrix, gathered embedding rows)
-    w_bytes = (sh.n_layers * (sh.layer_params() - 2 * sh.d) + Vc * sh.d + B * T * sh.d) * sh.elem_bytes
-    nbytes = w_bytes + kv_bytes + M * sh.n_layers * 2 * sh.kv_dim * sh.elem_bytes
+    nbytes = pass_bytes(sh, T, R, ctx, head_rows=B * R * S, head_cols=Vc)
+    flops = sum(fl * (1 if k == "codebook_head" else sh.n_layers) for k, (nb, fl) in work.items())
     passes_s = 1e3 / ms
     n_acc = acc_out["n"].cpu().numpy()
-    return {
-        "metric": METRIC, "value": (B // 2) * T * passes_s, "unit": "verified session tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0,0.02) weights, coordinate-hashed unit-variance KV generated on the device, "
-                "uniform draft codes)",
+    del kv
+    out = {
+        "metric": METRIC, "value": (B // 2) * T * passes_s, "unit": "verified session tokens/s",
+        "ms_per_step": ms, "dtype": "bf16",
         "config": {"workload": f"batched multi-codebook verify: {B // 2} sessions x 2 guidance rows, 8B-shape "
                                f"backbone, {S} codebooks x {Vc}, contexts {min(ctx)}..{max(ctx)}, "
                                f"{L_a} audio + {wl.gamma} drafts, w={wl.cfg_w}",
-                   "rows": B, "T": T, "R": len(rows), "cached_tokens": sum(ctx)},
+                   "rows": B, "T": T, "R": R, "cached_tokens": sum(ctx)},
         "passes_per_s": passes_s, "row_tokens_per_s": B * T * passes_s,
         "committed_tokens_per_pass": int((n_acc + 1).sum()) // 2,
-        "pass_roofline": {"bound": "hbm", "bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
-                          "peak_GBs": HBM_PEAK_GBS, "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "roofline": {"bound": "mfma", "kernel": "gemm_tiled, SwiGLU epilogue (gate/up projection), 2624 rows",
-                     "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s", "frac": achieved / 2500.0,
-                     "traffic": None, "flops_per_launch": gu_flops, "avg_launch_us": launch_us["gate_up"]},
-        "gemm_launch_us": launch_us, "setup_s": setup_s,
+        "roofline": ktable[dom],
+        "pass_roofline": {"bound": "mfma", "bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
+                          "peak_GBs": HBM_PEAK_GBS, "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "flops": flops, "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_TFLOPS,
+                          "note": "the pass is MFMA-bound (HBM roof 12.7 ms < MFMA roof 20.3 ms): frac is the "
+                                  "HBM fraction, mfma_frac the matrix-core fraction"},
+        "kernels": {k: {"avg_launch_us": v["avg_launch_us"], "launches_per_pass": v["launches_per_pass"],
+                        "bound": v["bound"], "frac": v["frac"]} for k, v in ktable.items()},
+        "setup_s": setup_s,
     }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_c5(w, wl, tokens, rows, kv_seed, work_per_row=_c5_row_flops(sh, T, ctx))
+    return out
 
+
+def _c5_row_flops(sh, T, ctx):
+    """Oracle work per row of the batched pass: decoder GEMMs (same for every row) plus
+    attention over its own cached length, in FLOPs."""
+    gemm = 2.0 * T * (sh.n_layers * (sh.layer_params() - 2 * sh.d))
+    attn = [4.0 * sh.n_layers * sh.n_heads * sh.head_dim * attn_visible_keys(T, C, None) for C in ctx]
+    return [gemm + a for a in attn]
+
+
+def cpu_baseline_c5(w, wl, tokens, rows, kv_seed, work_per_row):
+    """The oracle (cfg.verify_codebook, BF16_KV mode) on one guidance pair, the session
+    with the shortest context, timed on the host (verify + merge + greedy acceptance);
+    the time of the whole 64-row pass is extrapolated linearly in the rows' FLOPs."""
+    from oracle import BF16_KV
+    from oracle import accept as oacc
+    from oracle import cfg
+    from oracle import decoder as odec
+    from synth import HashedKV
+    sh = wl.shape
+    ctx = list(wl.ctx)
+    S, Vc = sh.n_codebooks, sh.codebook_size
+    base = sh.vocab - S * Vc
+    s = min(range(len(ctx) // 2), key=lambda i: ctx[2 * i])
+    r2 = [2 * s, 2 * s + 1]
+    hk = HashedKV(sh, [ctx[b] for b in r2], 0, seed=kv_seed, streams=r2)
+    cache = odec.Cache([[hk.block(i, l, 0) for l in range(sh.n_layers)] for i in range(2)],
+                       [[hk.block(i, l, 1) for l in range(sh.n_layers)] for i in range(2)])
+    t0 = time.perf_counter()
+    o = cfg.verify_codebook(w, cache, tokens[r2], None, rows, [1, 0], wl.cfg_w, base, BF16_KV)
+    for i in range(2):
+        oacc.accept_greedy(list(tokens[r2[i]]), None, wl.L_a, rows, list(o["token"][i]))
+    dt = time.perf_counter() - t0
+    scale = sum(work_per_row) / (work_per_row[r2[0]] + work_per_row[r2[1]])
+    pass_s = dt * scale
+    B, T = wl.batch, wl.T
+    return cpu_record((B // 2) * T / pass_s, "verified session tokens/s",
+                      f"1 guidance pair (session {s}, context {ctx[2 * s]}) of the same pass in {dt:.1f} s, fp64 "
+                      f"oracle (bf16-kv mode); the 64-row pass extrapolated linearly in the rows' FLOPs "
+                      f"(x{scale:.1f}: {pass_s:.0f} s per pass)")
+
+
+# -- speculative-sampling acceptance ------------------------------------------------------
 
 def bench_sample(args):
     import torch
@@ -406,27 +522,19 @@ def bench_sample(args):
     B, k, V = wl.batch, wl.k, wl.vocab
     # two resident copies of the inputs, alternated, so consecutive steps do not hit
     # the 256 MB last-level cache with the previous step's data
-    copies = []
-    for c in range(2):
-        copies.append(dict(tgt=torch.from_numpy(si.target_logits).cuda(), drf=torch.from_numpy(si.draft_logits).cuda(),
-                           drafts=torch.from_numpy(si.drafts).cuda()))
+    copies = [dict(tgt=torch.from_numpy(si.target_logits).cuda(), drf=torch.from_numpy(si.draft_logits).cuda(),
+                   drafts=torch.from_numpy(si.drafts).cuda()) for _ in range(2)]
     smp = sdv.Sampler(B, k, V)
     setup_s = time.time() - t0
+    it = [0]
 
-    def step(i):
-        c = copies[i & 1]
+    def step():
+        c = copies[it[0] & 1]
+        it[0] += 1
         smp(c["tgt"], c["drf"], c["drafts"], si.seed)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t_start) / args.steps * 1e3
+    ms = timed_steps(step, args.steps, args.warmup)
     nbytes = si.target_logits.nbytes + si.draft_logits.nbytes
-
     # live duration of the row-statistics launch (it reads every logit once), from two
     # HIP events the library records on the launch stream, over K more steps
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -441,15 +549,14 @@ def bench_sample(args):
     stats_bytes = nbytes + rows * (4 + 8)           # logits in; row maximum (fp32) and sum (fp64) out
     achieved = stats_bytes / (stats_us * 1e-6) / 1e9
     out = {
-        "metric": METRIC, "value": B * k / (ms * 1e-3), "unit": "draft positions/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"speculative-sampling acceptance: {B} seqs x {k} drafts, V={V}, fp32"},
+        "metric": METRIC, "value": B * k / (ms * 1e-3), "unit": "draft positions/s", "ms_per_step": ms,
+        "dtype": "f32",
+        "config": {"workload": f"speculative-sampling acceptance: {B} seqs x {k} drafts, V={V}, fp32, "
+                               f"Philox4x32-10 uniforms drawn in the kernel"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": counter_traffic(ROW_STATS_TRAFFIC, "sample", SAMPLE_SOURCES),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": stored_traffic("sample", "row_stats"),
                      "kernel": "spec_row_stats_kernel (maximum and exponential sum of every logit row)",
-                     "bytes_per_launch": stats_bytes, "avg_launch_us": stats_us},
+                     "bytes_per_launch": stats_bytes, "avg_launch_us": stats_us, "launches_per_pass": 1},
         "pass_roofline": {"bound": "hbm", "bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
                           "peak_GBs": HBM_PEAK_GBS, "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "setup_s": setup_s,
@@ -457,17 +564,49 @@ def bench_sample(args):
     if not args.no_cpu_baseline:
         from oracle import spec_sampling as ss
         tgt64, drf64 = si.target_logits.astype(np.float64), si.draft_logits.astype(np.float64)
-        # repeat the full batch until about 10 s of CPU work have been timed
         reps, dt = 0, 0.0
-        while dt < 10.0 and reps < 100:
+        while dt < 10.0 and reps < 100:      # full batches until about 10 s of CPU work
             t0 = time.perf_counter()
             ss.accept_sample(tgt64, drf64, si.drafts, si.u_accept, si.u_sample)
             dt += time.perf_counter() - t0
             reps += 1
-        out["cpu_baseline"] = {"value": reps * B * k / dt, "unit": "draft positions/s", "cores": cpu_threads(),
-                               "kind": "oracle",
-                               "sample": f"{reps} full batches ({B}x{k}, V={V}) in {dt:.1f} s"}
+        out["cpu_baseline"] = cpu_record(reps * B * k / dt, "draft positions/s",
+                                         f"{reps} full batches ({B}x{k}, V={V}) in {dt:.1f} s")
     return out
+
+
+# -- everything in one line ----------------------------------------------------------------
+
+def bench_all(args):
+    """Every workload, largest first.  The 8B backbone (with its codebook heads) is
+    generated once and serves the batched pass and the 8B tree pass."""
+    import torch
+    import speculative_decoding_verify_amd as sdv
+    from synth import make_weights
+    from synth.configs import WORKLOADS
+    c5wl = WORKLOADS["c5-codebook"]()
+    t0 = time.time()
+    w8 = make_weights(c5wl.shape, seed=c5wl.seed)
+    model8 = sdv.DeviceModel(w8)
+    _log(f"8B weights ready ({time.time() - t0:.0f} s)")
+    head = bench_c5(args, c5wl, w8, model8)
+    torch.cuda.empty_cache()
+    _log(f"c5-codebook done ({time.time() - t0:.0f} s): {head['ms_per_step']:.2f} ms/pass")
+    subs = {}
+    subs["8b-bf16-tree"] = bench_verify(args, WORKLOADS["8b-bf16-tree"](), w8, model8)
+    _log(f"8b-bf16-tree done ({time.time() - t0:.0f} s): {subs['8b-bf16-tree']['ms_per_step']:.3f} ms/pass")
+    del model8, w8
+    torch.cuda.empty_cache()
+    subs["1.7b-bf16"] = bench_verify(args, WORKLOADS["1.7b-bf16"]())
+    _log(f"1.7b-bf16 done ({time.time() - t0:.0f} s): {subs['1.7b-bf16']['ms_per_step']:.3f} ms/pass")
+    torch.cuda.empty_cache()
+    subs["sample"] = bench_sample(args)
+    _log(f"sample done ({time.time() - t0:.0f} s)")
+    subs["toy-f32"] = bench_verify(args, WORKLOADS["toy-f32"]())
+    _log(f"toy-f32 done ({time.time() - t0:.0f} s)")
+    head["configs"] = subs
+    head["wall_s"] = time.time() - t0
+    return head
 
 
 def copy_calibration(nbytes=256 << 20, reps=10):
@@ -488,10 +627,10 @@ def copy_calibration(nbytes=256 << 20, reps=10):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="1.7b-bf16",
-                    choices=["1.7b-bf16", "8b-bf16-tree", "toy-f32", "sample", "c5-codebook"])
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "c5-codebook", "8b-bf16-tree", "1.7b-bf16", "toy-f32", "sample"])
     ap.add_argument("--scenario", default="silence", choices=["silence", "random"])
     ap.add_argument("--graph", action="store_true", help="replay the step from a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -511,13 +650,21 @@ def main():
     import speculative_decoding_verify_amd as sdv
     sdv.lib()  # fail loudly if the HIP library is not built
     from synth.configs import WORKLOADS
-    if args.workload == "sample":
+    if args.workload == "all":
+        out = bench_all(args)
+    elif args.workload == "sample":
         out = bench_sample(args)
     elif args.workload == "c5-codebook":
         out = bench_c5(args, WORKLOADS[args.workload]())
     else:
         out = bench_verify(args, WORKLOADS[args.workload]())
-    print(json.dumps(out), flush=True)
+    line = {"metric": out.pop("metric"), "value": out.pop("value"), "unit": out.pop("unit"), "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": out.pop("ms_per_step"),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": out.pop("dtype"),
+            "data": "synthetic (seeded N(0,0.02) weights, unit-variance synthetic KV, drafts greedy under silence "
+                    "or uniform codes)"}
+    line.update(out)
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SDV_ABI_VERSION 5   /* 5: sdv_accept_sample draws Philox uniforms itself and reports flags */
+#define SDV_ABI_VERSION 7   /* 7: sdv_draft_tree (idle-window drafting) */
 #define SDV_PAGE 16          /* tokens per KV-cache page */
 #define SDV_MAX_T 128        /* rows per verify pass (chunk + drafts + branches) */
 #define SDV_SAMPLE_MAX_K 1024  /* draft positions per sequence of sdv_accept_sample */
@@ -193,7 +193,11 @@ typedef struct {
  *           (decoder projections in order q/k/v, o, gate/up, down per layer, then the
  *           LM head) records event 2i when the kernel starts and event 2i+1 when it
  *           ends (hipExtLaunchKernel), for as many launches as there are event pairs;
- *           the interval is the kernel's execution time. */
+ *           the interval is the kernel's execution time.
+ *   attn_prof_events  nullable host array of n_attn_prof_events caller-created events:
+ *           layer l's attention records event 2l when its kernel starts and event
+ *           2l + 1 when the last kernel of that layer's attention (the split merge, when
+ *           it runs as a kernel of its own) ends, for the layers that have a pair. */
 typedef struct {
   float* logits;
   int32_t* argmax;
@@ -204,6 +208,8 @@ typedef struct {
   void* const* prof_events;
   int32_t n_prof_events;
   int32_t* cb_argmax;          /* codebook head: int32 [B, R, S] argmax code per codebook, nullable */
+  void* const* attn_prof_events;
+  int32_t n_attn_prof_events;
 } sdv_verify_out;
 
 /* Bytes of workspace sdv_verify_forward needs for this model and pass shape. */
@@ -295,6 +301,34 @@ sdv_status sdv_accept_sample(int32_t batch, int32_t k, int32_t vocab, const floa
  * [B, n_pos] fp64, either nullable), s = seq_ids[b] or b. */
 sdv_status sdv_philox_uniforms(uint64_t seed, const int32_t* seq_ids, int32_t batch, int32_t n_pos,
                                double* u0_out, double* u1_out, void* stream);
+
+/* Drafting in the idle window ("Method steps", steps 1 and 2; the top-k first-token
+ * tree of page 1's weaknesses and future directions).  With the cache of every
+ * sequence at its committed length C_b (seq_len), the hypothesised chunk
+ * chunk [B, L_a] (e.g. L_a silence tokens) is run once; from its last row's
+ * distribution p_1, branch k (k < n_branches) starts with the (k+1)-th ranked token
+ * (larger logit first, lower index on ties: branch 0 is the greedy draft, branch 1 the
+ * runner-up argmax over V minus the greedy token) and is continued greedily to
+ * branch_len[k] tokens: token i+1 = argmax p(. | x_{<t}, chunk, branch tokens 0..i),
+ * lowest index on ties.  Every draft position of all branches is one verify forward
+ * (the branches as a tree under the chunk's last row), enqueued on `stream` without
+ * a host round trip.
+ *   branch_len  HOST [n_branches], each in [1, SDV_MAX_T]; 1 <= n_branches <= 16;
+ *               1 + s * (branches longer than s) <= SDV_MAX_T for every s.
+ *   drafts      [B, n_branches, max_k branch_len] int32 out, -1 past a branch's end.
+ *   err         [B] device error bits (as sdv_verify_forward; OR-ed in).
+ * The drafting rows' K/V are written to slots C_b.. and discarded: seq_len is back at
+ * C_b when the call's work completes.  max_ctx bounds every C_b;
+ * max_ctx + L_a - 1 + (rows of the widest pass) must fit the cache. */
+typedef struct {
+  int32_t batch, L_a, n_branches, max_ctx;
+  const int32_t* chunk;        /* [B, L_a] device */
+  const int32_t* branch_len;   /* HOST [n_branches] */
+} sdv_draft_in;
+size_t sdv_draft_workspace_size(const sdv_model* m, int32_t batch, int32_t L_a, int32_t n_branches,
+                                const int32_t* branch_len, int32_t max_ctx);
+sdv_status sdv_draft_tree(const sdv_model* m, const sdv_kv* kv, const sdv_draft_in* in, int32_t* drafts,
+                          int32_t* err, void* workspace, size_t workspace_bytes, void* stream);
 
 /* KV commit / rollback (step 4: roll the cache back to x_{<t}; commit n + 1 tokens).
  *   keep_len [B]: new committed length per sequence (seq_len[b] := keep_len[b]).

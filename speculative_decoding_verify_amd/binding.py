@@ -60,7 +60,13 @@ class SdvVerifyIn(ctypes.Structure):
 class SdvVerifyOut(ctypes.Structure):
     _fields_ = [("logits", _vp), ("argmax", _vp), ("margin", _vp), ("lse", _vp),
                 ("hidden", _vp), ("err", _vp), ("prof_events", ctypes.POINTER(_vp)),
-                ("n_prof_events", _i32), ("cb_argmax", _vp)]
+                ("n_prof_events", _i32), ("cb_argmax", _vp),
+                ("attn_prof_events", ctypes.POINTER(_vp)), ("n_attn_prof_events", _i32)]
+
+
+class SdvDraftIn(ctypes.Structure):
+    _fields_ = [("batch", _i32), ("L_a", _i32), ("n_branches", _i32), ("max_ctx", _i32),
+                ("chunk", _vp), ("branch_len", ctypes.POINTER(_i32))]
 
 
 class SdvError(RuntimeError):
@@ -68,7 +74,7 @@ class SdvError(RuntimeError):
 
 
 _LIB = None
-ABI_VERSION = 5   # SDV_ABI_VERSION of include/sdv.h that these signatures follow
+ABI_VERSION = 7   # SDV_ABI_VERSION of include/sdv.h that these signatures follow
 
 
 def lib():
@@ -92,6 +98,11 @@ def lib():
         L.sdv_verify_forward_noalloc.restype = ctypes.c_int
         L.sdv_verify_forward_noalloc.argtypes = [ctypes.POINTER(SdvModel), ctypes.POINTER(SdvKV),
                                                  ctypes.POINTER(SdvVerifyIn), ctypes.POINTER(SdvVerifyOut), _vp]
+        L.sdv_draft_workspace_size.restype = ctypes.c_size_t
+        L.sdv_draft_workspace_size.argtypes = [ctypes.POINTER(SdvModel), _i32, _i32, _i32, ctypes.POINTER(_i32), _i32]
+        L.sdv_draft_tree.restype = ctypes.c_int
+        L.sdv_draft_tree.argtypes = [ctypes.POINTER(SdvModel), ctypes.POINTER(SdvKV), ctypes.POINTER(SdvDraftIn),
+                                     _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.sdv_accept_greedy.restype = ctypes.c_int
         L.sdv_accept_greedy.argtypes = [_i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp,
                                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -315,22 +326,25 @@ class Verifier:
                                self.logit_rows.data_ptr(), head, _ptr(self.cfg_partner), float(cfg_w))
         self.out = SdvVerifyOut(_ptr(self.logits), self.argmax.data_ptr(), self.margin.data_ptr(),
                                 self.lse.data_ptr(), _ptr(self.hidden), self.err.data_ptr(), None, 0,
-                                _ptr(self.cb_argmax))
+                                _ptr(self.cb_argmax), None, 0)
 
-    def set_profile_events(self, events) -> None:
+    def set_profile_events(self, events, attn_events=None) -> None:
         """events: list of torch.cuda.Event (enable_timing=True), recorded by the library
-        in pairs around its GEMM launches; None disables."""
-        if not events:
-            self._prof = None
-            self.out.prof_events = None
-            self.out.n_prof_events = 0
-            return
-        for e in events:          # torch creates the underlying event on first record
-            e.record()
-        arr = (_vp * len(events))(*[e.cuda_event for e in events])
-        self._prof = (events, arr)
-        self.out.prof_events = ctypes.cast(arr, ctypes.POINTER(_vp))
-        self.out.n_prof_events = len(events)
+        in pairs around its GEMM launches; attn_events likewise around each layer's
+        attention; None disables."""
+        self._prof = []
+        for evs, fp, fn in ((events, "prof_events", "n_prof_events"),
+                            (attn_events, "attn_prof_events", "n_attn_prof_events")):
+            if not evs:
+                setattr(self.out, fp, None)
+                setattr(self.out, fn, 0)
+                continue
+            for e in evs:          # torch creates the underlying event on first record
+                e.record()
+            arr = (_vp * len(evs))(*[e.cuda_event for e in evs])
+            self._prof.append((evs, arr))
+            setattr(self.out, fp, ctypes.cast(arr, ctypes.POINTER(_vp)))
+            setattr(self.out, fn, len(evs))
 
     def set_tokens(self, tokens) -> None:
         t = torch.as_tensor(np.asarray(tokens, dtype=np.int32).reshape(self.B, self.T))
@@ -349,6 +363,53 @@ class Verifier:
                                             ctypes.c_void_p(self.workspace.data_ptr()), self.workspace.numel(),
                                             _stream(stream)), "sdv_verify_forward")
         return VerifyResult(self.argmax, self.margin, self.lse, self.err, self.logits, self.hidden, self.cb_argmax)
+
+
+class Drafter:
+    """Idle-window drafting (sdv_draft_tree) with reusable buffers: branch k of the tree
+    starts from the (k+1)-th ranked first token under the hypothesised chunk and is
+    continued greedily to branch_len[k] tokens."""
+
+    def __init__(self, model: DeviceModel, kv: PagedKV, L_a: int, branch_len: Sequence[int],
+                 max_ctx: Optional[int] = None):
+        self.model, self.kv = model, kv
+        dev = model.device
+        B = kv.batch
+        self.B, self.L_a, self.K = B, L_a, len(branch_len)
+        self.branch_len = list(int(x) for x in branch_len)
+        self.max_len = max(self.branch_len)
+        self._len = (_i32 * self.K)(*self.branch_len)
+        self.max_ctx = int(max_ctx if max_ctx is not None else kv.max_blocks * PAGE - L_a - 1)
+        self.chunk = torch.zeros((B, L_a), dtype=torch.int32, device=dev)
+        self.drafts = torch.empty((B, self.K, self.max_len), dtype=torch.int32, device=dev)
+        self.err = torch.zeros(B, dtype=torch.int32, device=dev)
+        nbytes = lib().sdv_draft_workspace_size(ctypes.byref(model.desc), B, L_a, self.K, self._len, self.max_ctx)
+        if nbytes == 0:
+            raise SdvError("unsupported drafting shape: " + lib().sdv_last_error().decode())
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.inp = SdvDraftIn(B, L_a, self.K, self.max_ctx, self.chunk.data_ptr(), self._len)
+
+    def set_chunk(self, tokens) -> None:
+        self.chunk.copy_(torch.as_tensor(np.asarray(tokens, dtype=np.int32).reshape(self.B, self.L_a)))
+
+    def run(self, stream=None) -> dict:
+        _check(lib().sdv_draft_tree(ctypes.byref(self.model.desc), ctypes.byref(self.kv.desc), ctypes.byref(self.inp),
+                                    _ptr(self.drafts), _ptr(self.err), _ptr(self.workspace), self.workspace.numel(),
+                                    _stream(stream)), "sdv_draft_tree")
+        return {"drafts": self.drafts, "err": self.err}
+
+
+def tree_parent(L_a: int, branch_lens: Sequence[int]) -> List[int]:
+    """Parents of a verify chunk [audio (L_a rows); branch 0; branch 1; ...]: the audio
+    rows form a chain, every branch is a chain whose first row hangs under the last
+    audio row."""
+    par = [j - 1 for j in range(L_a)]
+    at = L_a
+    for n in branch_lens:
+        for i in range(n):
+            par.append(L_a - 1 if i == 0 else at + i - 1)
+        at += n
+    return par
 
 
 def accept_greedy(B: int, T: int, L_a: int, tokens: torch.Tensor, parent: Optional[torch.Tensor],

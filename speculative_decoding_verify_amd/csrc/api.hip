@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/sdv.h"
 #include "kernels.h"
@@ -320,6 +321,74 @@ sdv_status sdv_verify_forward_noalloc(const sdv_model* m, const sdv_kv* kv, cons
 
 namespace {
 
+// The passes of a draft tree: pass 0 runs the chunk (T = L_a, one logit row); pass
+// s >= 1 runs the root row plus the first s tokens of every branch longer than s.
+struct DraftPass {
+  int T, R, max_ctx, n_act;
+  int act[DRAFT_MAX_BRANCHES];
+};
+
+struct DraftPlan {
+  int K, max_len, T_max;
+  std::vector<DraftPass> passes;
+  size_t verify_ws;
+  size_t off_tokens, off_parent, off_rows, off_argmax, off_margin, off_lse, off_logits, off_saved, off_keep, total;
+};
+
+sdv_status make_draft_plan(const sdv_model* m, int B, int L_a, int K, const int32_t* len, int max_ctx,
+                           DraftPlan* out) {
+  sdv_status st = check_model(m);
+  if (st != SDV_OK) return st;
+  if (B < 1) return fail(SDV_ERR_SHAPE, "batch %d", B);
+  if (L_a < 1 || L_a > SDV_MAX_T) return fail(SDV_ERR_SHAPE, "L_a = %d outside [1, %d]", L_a, SDV_MAX_T);
+  if (K < 1 || K > DRAFT_MAX_BRANCHES) return fail(SDV_ERR_SHAPE, "%d branches outside [1, %d]", K, DRAFT_MAX_BRANCHES);
+  if (K > m->vocab) return fail(SDV_ERR_SHAPE, "more branches than vocabulary entries");
+  if (!len) return fail(SDV_ERR_NULL, "branch_len is NULL");
+  if (max_ctx < 0) return fail(SDV_ERR_SHAPE, "max_ctx < 0");
+  DraftPlan& P = *out;
+  P.K = K;
+  P.max_len = 0;
+  for (int k = 0; k < K; ++k) {
+    if (len[k] < 1 || len[k] > SDV_MAX_T) return fail(SDV_ERR_SHAPE, "branch_len[%d] = %d", k, len[k]);
+    P.max_len = std::max(P.max_len, (int)len[k]);
+  }
+  P.passes.clear();
+  DraftPass p0{};
+  p0.T = L_a;
+  p0.R = 1;
+  p0.max_ctx = max_ctx;
+  P.passes.push_back(p0);
+  P.T_max = L_a;
+  for (int s = 1; s < P.max_len; ++s) {
+    DraftPass p{};
+    for (int k = 0; k < K; ++k)
+      if (len[k] > s) p.act[p.n_act++] = k;
+    p.T = 1 + s * p.n_act;
+    p.R = p.n_act;
+    p.max_ctx = max_ctx + L_a - 1;
+    if (p.T > SDV_MAX_T)
+      return fail(SDV_ERR_SHAPE, "drafting pass %d would take %d rows (at most %d)", s, p.T, SDV_MAX_T);
+    P.T_max = std::max(P.T_max, p.T);
+    P.passes.push_back(p);
+  }
+  P.verify_ws = 0;
+  for (const DraftPass& p : P.passes) P.verify_ws = std::max(P.verify_ws, make_plan(m, B, p.T, p.R, p.max_ctx).total);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+  take(P.verify_ws);
+  P.off_tokens = take((size_t)B * P.T_max * 4);
+  P.off_parent = take((size_t)P.T_max * 4);
+  P.off_rows = take((size_t)K * 4);
+  P.off_argmax = take((size_t)B * K * 4);
+  P.off_margin = take((size_t)B * K * 4);
+  P.off_lse = take((size_t)B * K * 4);
+  P.off_logits = take((size_t)B * m->vocab * 4);
+  P.off_saved = take((size_t)B * 4);
+  P.off_keep = take((size_t)B * 4);
+  P.total = o;
+  return SDV_OK;
+}
+
 sdv_status verify_forward_impl(const sdv_model* m, const sdv_kv* kv, const sdv_verify_in* in, sdv_verify_out* out,
                                void* ws, size_t ws_bytes, void* stream, bool use_scratch) {
   sdv_status st = check_model(m);
@@ -404,10 +473,15 @@ sdv_status verify_forward_impl(const sdv_model* m, const sdv_kv* kv, const sdv_v
       AttnArgs a{q, kp, vp, kv->block_table, kv->max_blocks, kv->n_blocks, kv->seq_len, anc, B, T, H, Hkv,
                  P.split_keys, P.n_splits, po, pml, P.nq_pad, P.n_qg, in->max_ctx,
                  P.attn_fused ? sem + (size_t)l * B * Hkv * P.n_qg : nullptr, o};
-      SDV_LAUNCH(launch_attention(P.bf, dh, a, s));
+      // with attention events: event 2l at the attention kernel's start, 2l + 1 at the
+      // end of the kernel that finishes the layer's attention (the combine, if any)
+      const bool aprof = out->attn_prof_events && 2 * l + 1 < out->n_attn_prof_events;
+      hipEvent_t ae0 = aprof ? (hipEvent_t)out->attn_prof_events[2 * l] : nullptr;
+      hipEvent_t ae1 = aprof ? (hipEvent_t)out->attn_prof_events[2 * l + 1] : nullptr;
+      SDV_LAUNCH(launch_attention(P.bf, dh, a, s, ae0, P.attn_fused ? ae1 : nullptr));
       if (!P.attn_fused) {
         CombineArgs c{po, pml, o, B, T, H, Hkv, dh, P.n_splits, P.nq_pad};
-        SDV_LAUNCH(launch_combine(P.bf, c, s));
+        SDV_LAUNCH(launch_combine(P.bf, c, s, ae1));
       }
     }
     {
@@ -595,6 +669,108 @@ sdv_status sdv_accept_sample(int32_t B, int32_t k, int32_t V, const float* tgt, 
   SDV_LAUNCH(launch_accept_sample(a, (hipStream_t)stream, prof_events ? (hipEvent_t)prof_events[0] : nullptr,
                                   prof_events ? (hipEvent_t)prof_events[1] : nullptr));
   return SDV_OK;
+}
+
+size_t sdv_draft_workspace_size(const sdv_model* m, int32_t batch, int32_t L_a, int32_t n_branches,
+                                const int32_t* branch_len, int32_t max_ctx) {
+  DraftPlan P;
+  if (make_draft_plan(m, batch, L_a, n_branches, branch_len, max_ctx, &P) != SDV_OK) return 0;
+  return P.total;
+}
+
+sdv_status sdv_draft_tree(const sdv_model* m, const sdv_kv* kv, const sdv_draft_in* in, int32_t* drafts,
+                          int32_t* err, void* ws, size_t ws_bytes, void* stream) {
+  if (!kv || !in || !drafts || !err) return fail(SDV_ERR_NULL, "kv/in/drafts/err is NULL");
+  if (!in->chunk) return fail(SDV_ERR_NULL, "chunk is NULL");
+  if (!kv->k_pages || !kv->v_pages || !kv->block_table || !kv->seq_len) return fail(SDV_ERR_NULL, "kv pointer NULL");
+  DraftPlan P;
+  sdv_status st = make_draft_plan(m, in->batch, in->L_a, in->n_branches, in->branch_len, in->max_ctx, &P);
+  if (st != SDV_OK) return st;
+  const int B = in->batch, K = P.K, L_a = in->L_a;
+  if (B != kv->batch) return fail(SDV_ERR_SHAPE, "batch %d (kv batch %d)", B, kv->batch);
+  const long long cap = (long long)kv->max_blocks * SDV_PAGE;
+  for (const DraftPass& p : P.passes)
+    if ((long long)p.max_ctx + p.T > cap) return fail(SDV_ERR_SHAPE, "max_ctx + drafting rows exceed the cache capacity");
+  if (!ws || ws_bytes < P.total) return fail(SDV_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, P.total);
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  int32_t* tokens = (int32_t*)(w + P.off_tokens);
+  int32_t* parent = (int32_t*)(w + P.off_parent);
+  int32_t* rows = (int32_t*)(w + P.off_rows);
+  int32_t* argmax = (int32_t*)(w + P.off_argmax);
+  int32_t* saved = (int32_t*)(w + P.off_saved);
+  int32_t* keep = (int32_t*)(w + P.off_keep);
+  float* logits = (float*)(w + P.off_logits);
+
+  DraftStepArgs d;
+  memset(&d, 0, sizeof d);
+  d.B = B;
+  d.K = K;
+  d.max_len = P.max_len;
+  d.drafts = drafts;
+  d.seq_len = kv->seq_len;
+  d.saved = saved;
+  d.argmax = argmax;
+  d.root = in->chunk + (L_a - 1);
+  d.root_stride = L_a;
+  d.tokens = tokens;
+  d.parent = parent;
+  d.logit_rows = rows;
+  // remember C, clear the drafts, set the first pass's logit row; keep = C + L_a - 1
+  d.save = 1;
+  d.first_row = L_a - 1;
+  d.keep_out = keep;
+  d.keep_delta = L_a - 1;
+  SDV_LAUNCH(launch_draft_step(d, s));
+  d.save = 0;
+  d.keep_out = nullptr;
+
+  sdv_verify_out vo;
+  memset(&vo, 0, sizeof vo);
+  vo.argmax = argmax;
+  vo.margin = (float*)(w + P.off_margin);
+  vo.lse = (float*)(w + P.off_lse);
+  vo.err = err;
+  // pass 0: the hypothesised chunk; the first tokens of all branches from its last row
+  {
+    sdv_verify_in vi{B, L_a, L_a, 1, in->max_ctx, in->chunk, nullptr, rows, SDV_HEAD_LM, nullptr, 1.f};
+    vo.logits = logits;
+    if ((st = verify_forward_impl(m, kv, &vi, &vo, ws, P.verify_ws, stream, false)) != SDV_OK) return st;
+    vo.logits = nullptr;
+    DraftTopkArgs t{logits, B, m->vocab, K, drafts, P.max_len};
+    SDV_LAUNCH(launch_draft_topk(t, s));
+  }
+  // commit the chunk rows but the last, which is the root of the following passes
+  if ((st = sdv_kv_rollback(m, kv, keep, nullptr, nullptr, 0, err, stream)) != SDV_OK) return st;
+  for (size_t pi = 1; pi < P.passes.size(); ++pi) {
+    const DraftPass& p = P.passes[pi];
+    const int sx = (int)pi;
+    if (pi >= 2) {
+      const DraftPass& q = P.passes[pi - 1];
+      d.n_prev = q.n_act;
+      d.prev_pos = sx - 1;
+      for (int r = 0; r < q.n_act; ++r) d.prev_branch[r] = q.act[r];
+    }
+    d.n_act = p.n_act;
+    d.s = sx;
+    for (int r = 0; r < p.n_act; ++r) d.act_branch[r] = p.act[r];
+    SDV_LAUNCH(launch_draft_step(d, s));
+    sdv_verify_in vi{B, p.T, 1, p.R, p.max_ctx, tokens, parent, rows, SDV_HEAD_LM, nullptr, 1.f};
+    if ((st = verify_forward_impl(m, kv, &vi, &vo, ws, P.verify_ws, stream, false)) != SDV_OK) return st;
+  }
+  // the last pass's tokens, and the cache back at C
+  d.n_prev = 0;
+  if (P.passes.size() >= 2) {
+    const DraftPass& q = P.passes.back();
+    d.n_prev = q.n_act;
+    d.prev_pos = (int)P.passes.size() - 1;
+    for (int r = 0; r < q.n_act; ++r) d.prev_branch[r] = q.act[r];
+  }
+  d.n_act = 0;
+  d.keep_out = keep;
+  d.keep_delta = 0;
+  SDV_LAUNCH(launch_draft_step(d, s));
+  return sdv_kv_rollback(m, kv, keep, nullptr, nullptr, 0, err, stream);
 }
 
 sdv_status sdv_philox_uniforms(uint64_t seed, const int32_t* seq_ids, int32_t B, int32_t n_pos, double* u0_out,

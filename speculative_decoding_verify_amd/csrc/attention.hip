@@ -23,6 +23,8 @@
 // per query row with log-sum-exp weights by the workgroup that finishes last (the
 // hand-off of common.h), or, where a group's merge would not fit its LDS scratch, by
 // the separate combine kernel.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -862,20 +864,28 @@ int attn_query_groups(bool is_bf16, int dh, int T, int G, int heads, int* rows_p
   return n_qg;
 }
 
+// A launch that records ev0 when the kernel starts and ev1 when it ends (both
+// nullable: a plain launch).
+template <typename K, typename Arg>
+static void launch_ev(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1, const Arg& a) {
+  if (ev0 || ev1) hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev0, ev1, 0, a);
+  else kernel<<<grid, block, 0, s>>>(a);
+}
+
 template <typename T, int DH>
-static hipError_t launch_attn_t(AttnArgs a, hipStream_t s) {
+static hipError_t launch_attn_t(AttnArgs a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   const int G = a.H / a.Hkv;
   const int NQT = (a.T * G + 15) / 16;
   if (attn_uses_reg_path(sizeof(T) == 2, DH, NQT)) {
     dim3 grid(a.n_splits, a.Hkv, a.B);
     a.n_qg = 1;
     if constexpr (DH == 128) {
-      attn_reg<T, DH, 1><<<grid, 256, 0, s>>>(a);   // the register path takes one query tile at dh 128
+      launch_ev(attn_reg<T, DH, 1>, grid, 256, s, ev0, ev1, a);   // the register path takes one query tile at dh 128
     } else {
       switch (NQT) {
-        case 1: attn_reg<T, DH, 1><<<grid, 256, 0, s>>>(a); break;
-        case 2: attn_reg<T, DH, 2><<<grid, 256, 0, s>>>(a); break;
-        default: attn_reg<T, DH, 3><<<grid, 256, 0, s>>>(a); break;
+        case 1: launch_ev(attn_reg<T, DH, 1>, grid, 256, s, ev0, ev1, a); break;
+        case 2: launch_ev(attn_reg<T, DH, 2>, grid, 256, s, ev0, ev1, a); break;
+        default: launch_ev(attn_reg<T, DH, 3>, grid, 256, s, ev0, ev1, a); break;
       }
     }
     return hipGetLastError();
@@ -885,34 +895,35 @@ static hipError_t launch_attn_t(AttnArgs a, hipStream_t s) {
   dim3 grid(a.n_splits, a.Hkv, a.B * a.n_qg);
   dim3 block(64 * nw);
   switch (nqw) {
-    case 1: attn_chunk<T, DH, 1><<<grid, block, 0, s>>>(a); break;
-    case 2: attn_chunk<T, DH, 2><<<grid, block, 0, s>>>(a); break;
+    case 1: launch_ev(attn_chunk<T, DH, 1>, grid, block, s, ev0, ev1, a); break;
+    case 2: launch_ev(attn_chunk<T, DH, 2>, grid, block, s, ev0, ev1, a); break;
     case 3:
-      if constexpr (attn_cap<T, DH>() >= 3) { attn_chunk<T, DH, 3><<<grid, block, 0, s>>>(a); break; }
+      if constexpr (attn_cap<T, DH>() >= 3) { launch_ev(attn_chunk<T, DH, 3>, grid, block, s, ev0, ev1, a); break; }
       return hipErrorInvalidValue;
     case 4:
-      if constexpr (attn_cap<T, DH>() >= 4) { attn_chunk<T, DH, 4><<<grid, block, 0, s>>>(a); break; }
+      if constexpr (attn_cap<T, DH>() >= 4) { launch_ev(attn_chunk<T, DH, 4>, grid, block, s, ev0, ev1, a); break; }
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_attention(bool is_bf16, int dh, const AttnArgs& a, hipStream_t s) {
-  if (is_bf16) return dh == 64 ? launch_attn_t<bf16, 64>(a, s) : launch_attn_t<bf16, 128>(a, s);
-  return dh == 64 ? launch_attn_t<float, 64>(a, s) : launch_attn_t<float, 128>(a, s);
+hipError_t launch_attention(bool is_bf16, int dh, const AttnArgs& a, hipStream_t s, hipEvent_t ev0,
+                            hipEvent_t ev1) {
+  if (is_bf16) return dh == 64 ? launch_attn_t<bf16, 64>(a, s, ev0, ev1) : launch_attn_t<bf16, 128>(a, s, ev0, ev1);
+  return dh == 64 ? launch_attn_t<float, 64>(a, s, ev0, ev1) : launch_attn_t<float, 128>(a, s, ev0, ev1);
 }
 
-hipError_t launch_combine(bool is_bf16, const CombineArgs& a, hipStream_t s) {
+hipError_t launch_combine(bool is_bf16, const CombineArgs& a, hipStream_t s, hipEvent_t ev1) {
   if (a.n_splits > 32) return hipErrorInvalidValue;
   const int items = a.B * a.T * a.H;
   const int grid = (items + 256 / (a.dh / 4) - 1) / (256 / (a.dh / 4));
   if (is_bf16) {
-    if (a.dh == 64) attn_combine<bf16, 64><<<grid, 256, 0, s>>>(a);
-    else attn_combine<bf16, 128><<<grid, 256, 0, s>>>(a);
+    if (a.dh == 64) launch_ev(attn_combine<bf16, 64>, grid, 256, s, nullptr, ev1, a);
+    else launch_ev(attn_combine<bf16, 128>, grid, 256, s, nullptr, ev1, a);
   } else {
-    if (a.dh == 64) attn_combine<float, 64><<<grid, 256, 0, s>>>(a);
-    else attn_combine<float, 128><<<grid, 256, 0, s>>>(a);
+    if (a.dh == 64) launch_ev(attn_combine<float, 64>, grid, 256, s, nullptr, ev1, a);
+    else launch_ev(attn_combine<float, 128>, grid, 256, s, nullptr, ev1, a);
   }
   return hipGetLastError();
 }

@@ -102,7 +102,9 @@ int attn_query_groups(bool is_bf16, int dh, int T, int G, int heads, int* rows_p
 constexpr int ATTN_MERGE_FLOATS = 4096;
 constexpr int ATTN_MAX_SPLITS = 32;
 
-hipError_t launch_attention(bool is_bf16, int dh, const AttnArgs& a, hipStream_t s);
+// ev0 / ev1 (nullable): recorded when the attention kernel starts and ends
+hipError_t launch_attention(bool is_bf16, int dh, const AttnArgs& a, hipStream_t s, hipEvent_t ev0 = nullptr,
+                            hipEvent_t ev1 = nullptr);
 bool attn_uses_reg_path(bool bf, int dh, int NQT);  // keys per tile: 32 bf16 / 16 fp32 either way
 
 struct CombineArgs {
@@ -111,7 +113,8 @@ struct CombineArgs {
   void* o;                  // [B*T, H*dh] activation tile format
   int B, T, H, Hkv, dh, n_splits, nq_pad;
 };
-hipError_t launch_combine(bool is_bf16, const CombineArgs& a, hipStream_t s);
+// ev1 (nullable): recorded when the combine kernel ends
+hipError_t launch_combine(bool is_bf16, const CombineArgs& a, hipStream_t s, hipEvent_t ev1 = nullptr);
 
 struct PrologueArgs {
   const int32_t* parent;    // nullable
@@ -265,5 +268,40 @@ struct PhiloxArgs {
   double* u1;
 };
 hipError_t launch_philox_uniforms(const PhiloxArgs& a, hipStream_t s);
+
+// drafting: the K best first tokens of each row (larger logit first, lower index on ties)
+constexpr int DRAFT_MAX_BRANCHES = 16;
+struct DraftTopkArgs {
+  const float* logits;      // [B, V]
+  int B, V, K;
+  int32_t* drafts;          // [B, K, max_len]: writes position 0 of each branch
+  int max_len;
+};
+hipError_t launch_draft_topk(const DraftTopkArgs& a, hipStream_t s);
+
+// one drafting step's bookkeeping (draft.hip)
+struct DraftStepArgs {
+  int B, K, max_len;
+  int32_t* drafts;          // [B, K, max_len]
+  int save;                 // first call: saved = seq_len, drafts = -1, logit_rows[0] = first_row
+  int first_row;
+  const int32_t* seq_len;   // [B]
+  int32_t* saved;           // [B]
+  int32_t* keep_out;        // [B] nullable: saved + keep_delta
+  int keep_delta;
+  // scatter of the previous step's argmax (one per active branch of that step)
+  const int32_t* argmax;    // [B, n_prev]
+  int n_prev, prev_pos;
+  int prev_branch[DRAFT_MAX_BRANCHES];
+  // the next chunk: root row + the first s tokens of each active branch
+  const int32_t* root;      // root token of sequence b at root[b * root_stride]
+  int root_stride;
+  int n_act, s;
+  int act_branch[DRAFT_MAX_BRANCHES];
+  int32_t* tokens;          // [B, 1 + n_act * s]
+  int32_t* parent;          // [1 + n_act * s]
+  int32_t* logit_rows;      // [n_act]
+};
+hipError_t launch_draft_step(const DraftStepArgs& a, hipStream_t s);
 
 }  // namespace sdv

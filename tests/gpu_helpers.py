@@ -62,8 +62,12 @@ def run_pair(w, kv_host, tokens, L_a, parent=None, logit_rows=None, perm_seed=No
     return g, o, ver, kv
 
 
-def compare_logits(sh, g, o):
-    """Returns (max row rel err, n flagged, n compared) and asserts parity."""
+def compare_logits(sh, g, o, max_flag_frac=0.05):
+    """Returns (max row rel err, n flagged, n compared) and asserts parity.  Rows whose
+    oracle top-2 margin is below 1e-3 are flagged (excluded from the argmax check); at
+    most max_flag_frac of the rows (and at least one) may be flagged: random-weight
+    logits put about 1 % of rows below the band on the small shapes, and none of the
+    full-size rows of the seeded workloads."""
     tol = logit_tol(sh)
     gl, ol = g["logits"], o["logits"]
     B, R, V = ol.shape
@@ -81,6 +85,7 @@ def compare_logits(sh, g, o):
             # margin and log-sum-exp of the GPU agree with its own logits' definition
             srt = np.sort(ol[b, r])
             assert abs(g["margin"][b, r] - (srt[-1] - srt[-2])) <= tol * np.max(np.abs(ol[b, r])) * 2 + 1e-6
+    assert flagged <= max(1, int(max_flag_frac * B * R)), f"{flagged} of {B * R} rows flagged"
     lse = np.log(np.sum(np.exp(ol - ol.max(axis=2, keepdims=True)), axis=2)) + ol.max(axis=2)
     assert np.max(np.abs(g["lse"] - lse)) <= max(1e-4, 4 * tol * np.max(np.abs(ol))), "lse mismatch"
     return float(err.max()), flagged, B * R

@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for f in ("sdv_verify_forward", "sdv_accept_greedy", "sdv_accept_sample", "sdv_kv_rollback",
               "sdv_verify_workspace_size", "sdv_sample_workspace_size", "sdv_pack_weights",
-              "sdv_packed_bytes", "sdv_last_error", "sdv_abi_version", "sdv_philox_uniforms"):
+              "sdv_packed_bytes", "sdv_last_error", "sdv_abi_version", "sdv_philox_uniforms",
+              "sdv_draft_tree", "sdv_draft_workspace_size", "sdv_verify_forward_noalloc"):
         assert f in names, f
 
 
@@ -45,7 +46,7 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_packed_sizes():
     L = sdv.lib()
-    assert L.sdv_abi_version() == 5
+    assert L.sdv_abi_version() == binding.ABI_VERSION == 7
     # rows round up to 16, 2 bytes (bf16) / 4 bytes (fp32) per value
     assert L.sdv_packed_bytes(1, 6144, 2048) == 6144 * 2048 * 2
     assert L.sdv_packed_bytes(0, 17, 64) == 32 * 64 * 4

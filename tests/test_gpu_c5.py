@@ -8,9 +8,11 @@ coordinate-hashed recipe), 25 audio + 16 draft codes per session.
 
 Checked for every row: no device error; both rows of a pair see bit-identical guided
 logits and accept the same count.  Checked against the oracle (BF16_KV mode) on the
-two sessions with the shortest contexts: guided logits per (row, codebook) within 2e-2
-of the largest oracle logit, argmax codes bit-exact where the oracle's top-2 margin is
-at least 1e-3, committed token and accepted count where no deciding row is flagged.
+sessions with the shortest and the longest context and two seeded random sessions:
+guided logits per (row, codebook) within 2e-2 of the largest oracle logit, argmax codes
+bit-exact where the oracle's top-2 margin is at least 1e-3 (at most 2 % of the
+(row, codebook) pairs flagged), committed token and accepted count where no deciding
+row is flagged.
 The draft codes are uniform (the recipe's greedy drafts change only how many are
 accepted, not what the pass computes).
 """
@@ -39,6 +41,7 @@ def _log(msg):
     print(msg, flush=True)
 
 
+@pytest.mark.timeout(1500)
 def test_c5_full_size_codebook_guidance():
     wl = c5_workload()
     sh = wl.shape
@@ -93,8 +96,12 @@ def test_c5_full_size_codebook_guidance():
         assert np.array_equal(g_logits[2 * s], g_logits[2 * s + 1]), s
         assert g_n[2 * s] == g_n[2 * s + 1], s
 
-    # oracle on the two sessions with the shortest contexts
-    sessions = sorted(range(B // 2), key=lambda s: ctx[2 * s])[:2]
+    # oracle on the sessions with the shortest and the longest context and two seeded
+    # random ones (the longest merges two non-empty key splits over ~1000 pages)
+    by_len = sorted(range(B // 2), key=lambda s: ctx[2 * s])
+    rest = [s for s in range(B // 2) if s not in (by_len[0], by_len[-1])]
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, 0xC5C5])))
+    sessions = [by_len[0], by_len[-1]] + [int(x) for x in rng.choice(rest, size=2, replace=False)]
     for s in sessions:
         r2 = [2 * s, 2 * s + 1]
         _log(f"oracle: session {s}, context {ctx[2 * s]}")
@@ -120,3 +127,4 @@ def test_c5_full_size_codebook_guidance():
             if all(o["margin"][i, rows.index(row)] >= MARGIN_FLAG for row in deciding):
                 assert g_n[b] == n, (b, g_n[b], n)
         _log(f"session {s}: flagged {flagged}/{2 * len(rows) * S}")
+        assert flagged <= max(1, 2 * len(rows) * S // 50)

@@ -7,7 +7,9 @@
     audio + 16 drafts: random chunk, and audio = silence with drafts = greedy decoding
     under silence (full acceptance);
   * 8B-shape bf16 decoder (36 layers, d=4096, 32/8 heads x 128, V=151936), C=8192,
-    25 audio + 32 drafts + an 8-token runner-up branch under the tree mask.
+    25 audio + 32 drafts + an 8-token runner-up branch under the tree mask, and a
+    top-4 sibling tree; in both a non-first branch carries the oracle's next token, so
+    the walk takes it and the commit compacts its rows.
 The oracle runs the same pass in fp64 (bf16 rounding mode for bf16 models); logits,
 argmax (flags below 1e-3 top-2 margin), layer-0 keys/values and greedy acceptance are
 compared (tests/gpu_helpers.py).
@@ -133,8 +135,28 @@ def test_full_1p7b_random_and_silence():
                 assert on == gamma
 
 
-@pytest.mark.timeout(900)
+def _commit_and_check_moves(sh, ver, kv, acc, C, L_a, T):
+    """Commit with the plan of accept_greedy: accepted row path[i] must land in slot
+    C + L_a + i of every layer (bit-identical K/V)."""
+    n = int(acc["n"][0])
+    path = acc["path"][0, :n].cpu().tolist()
+    before = [kv.gather(0, l, C, C + T) for l in range(sh.n_layers)]
+    sdv.kv_rollback(ver.model, kv, acc["keep"], acc["move_src"], acc["move_dst"], acc["err"])
+    torch.cuda.synchronize()
+    assert int(kv.seq_len[0]) == C + L_a + n and int(acc["err"][0]) == 0
+    for l in range(sh.n_layers):
+        k, v = kv.gather(0, l, C + L_a, C + L_a + n)
+        assert torch.equal(k, before[l][0][path]) and torch.equal(v, before[l][1][path])
+    return n, path
+
+
+@pytest.mark.timeout(1200)
 def test_full_8b_tree():
+    """The 8B tree workload (25 audio + 32 drafts + an 8-token branch forking at the last
+    audio row), and a top-k tree of 4 siblings (8 + 3 x 4 tokens) on the same model.  In
+    both, one non-first branch starts with the oracle's argmax at the last audio row (from
+    an oracle pass over the audio alone) and the main draft does not, so the walk takes
+    that branch and the commit moves its rows at 36 layers, 8 kv heads, dh 128."""
     wl = w8b_tree_workload()
     sh = wl.shape
     C, L_a, gamma, nb, T = wl.ctx[0], wl.L_a, wl.gamma, wl.n_branch, wl.T
@@ -144,24 +166,47 @@ def test_full_8b_tree():
     model = sdv.DeviceModel(w)
     kv = sdv.PagedKV(sh, 1, C + T + 64)
     kv.load(kvh)
-    parent = wl.parent()
-    rows = wl.logit_rows()
-    main = uniform_tokens(gamma, sh.vocab, 81, "m")
-    branch = uniform_tokens(nb, sh.vocab, 82, "b")
-    branch[0] = (main[0] + 1) % sh.vocab   # siblings carry distinct tokens
-    toks = np.concatenate([uniform_tokens(L_a, sh.vocab, 80, "a"), main, branch]).astype(np.int32)
-    ver = sdv.Verifier(model, kv, T, L_a, rows, parent=parent, max_ctx=C, want_logits=True)
-    ver.set_tokens(toks[None, :])
-    res = ver.forward()
-    torch.cuda.synchronize()
-    g = dict(logits=res.logits.cpu().numpy().astype(np.float64), argmax=res.argmax.cpu().numpy(),
-             margin=res.margin.cpu().numpy(), lse=res.lse.cpu().numpy())
-    _say("oracle verify pass (8B tree)")
-    o = odec.verify_forward(w, odec.Cache(kvh.k, kvh.v), toks[None, :], parent, rows, BF16_KV)
-    err, flagged, n = compare_logits(sh, g, o)
-    _say(f"8b tree: rel err {err:.2e}, flagged {flagged}/{n}")
-    compare_kv_layer0(sh, kv, o, C, T)
-    on, onext, _, fl = greedy_expectation(toks, parent, L_a, rows, o["logits"][0])
-    gn, gnext = _accept(ver, kv, T, L_a, ver.parent)
-    if not fl:
-        assert (gn, gnext) == (on, onext)
+    cache = odec.Cache(kvh.k, kvh.v)
+    audio = uniform_tokens(L_a, sh.vocab, 80, "a")
+    keep_c = torch.tensor([C], dtype=torch.int32, device="cuda")
+    with memoize_f64():
+        _say("oracle pass over the audio alone")
+        a1 = int(np.argmax(odec.verify_forward(w, cache, audio[None, :], None, [L_a - 1], BF16_KV)["logits"][0, 0]))
+        cases = []
+        main = uniform_tokens(gamma, sh.vocab, 81, "m")
+        branch = uniform_tokens(nb, sh.vocab, 82, "b")
+        branch[0] = a1
+        if main[0] == a1:
+            main[0] = (a1 + 1) % sh.vocab
+        cases.append(("C3 tree", wl.parent(), [main, branch]))
+        sib = [uniform_tokens(n, sh.vocab, 90 + k, "s") for k, n in enumerate([8, 4, 4, 4])]
+        firsts = [(a1 + 1 + 17 * k) % sh.vocab for k in range(4)]
+        firsts[2] = a1
+        for k in range(4):
+            sib[k][0] = firsts[k]
+        cases.append(("top-4 tree", sdv.tree_parent(L_a, [8, 4, 4, 4]), sib))
+        for name, parent, branches in cases:
+            toks = np.concatenate([audio] + [np.asarray(b, np.int32) for b in branches]).astype(np.int32)
+            Tc = len(toks)
+            rows = list(range(L_a - 1, Tc))
+            sdv.kv_rollback(model, kv, keep_c)
+            ver = sdv.Verifier(model, kv, Tc, L_a, rows, parent=parent, max_ctx=C, want_logits=True)
+            ver.set_tokens(toks[None, :])
+            res = ver.forward()
+            torch.cuda.synchronize()
+            g = dict(logits=res.logits.cpu().numpy().astype(np.float64), argmax=res.argmax.cpu().numpy(),
+                     margin=res.margin.cpu().numpy(), lse=res.lse.cpu().numpy())
+            _say(f"oracle verify pass ({name}, T={Tc})")
+            o = odec.verify_forward(w, cache, toks[None, :], parent, rows, BF16_KV)
+            err, flagged, n_rows = compare_logits(sh, g, o, max_flag_frac=0.02)
+            _say(f"8b {name}: rel err {err:.2e}, flagged {flagged}/{n_rows}")
+            compare_kv_layer0(sh, kv, o, C, Tc)
+            on, onext, opath, fl = greedy_expectation(toks, parent, L_a, rows, o["logits"][0])
+            acc = sdv.accept_greedy(1, Tc, L_a, ver.tokens, ver.parent, ver.logit_rows, ver.argmax,
+                                    base_len=kv.seq_len)
+            torch.cuda.synchronize()
+            if not fl:
+                assert (int(acc["n"][0]), int(acc["next"][0])) == (on, onext)
+                assert on >= 1 and toks[opath[0]] == a1 and opath[0] != L_a     # a non-first branch won
+            n, path = _commit_and_check_moves(sh, ver, kv, acc, C, L_a, Tc)
+            _say(f"8b {name}: accepted {n} rows {path}")

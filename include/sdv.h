@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SDV_ABI_VERSION 7   /* 7: sdv_draft_tree (idle-window drafting) */
+#define SDV_ABI_VERSION 8   /* 8: hypothesis pool (sdv_pool_*) */
 #define SDV_PAGE 16          /* tokens per KV-cache page */
 #define SDV_MAX_T 128        /* rows per verify pass (chunk + drafts + branches) */
 #define SDV_SAMPLE_MAX_K 1024  /* draft positions per sequence of sdv_accept_sample */
@@ -329,6 +329,51 @@ size_t sdv_draft_workspace_size(const sdv_model* m, int32_t batch, int32_t L_a, 
                                 const int32_t* branch_len, int32_t max_ctx);
 sdv_status sdv_draft_tree(const sdv_model* m, const sdv_kv* kv, const sdv_draft_in* in, int32_t* drafts,
                           int32_t* err, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Hypothesis pool ("Method steps", steps 3 and 5): every draft of a session is stored
+ * and indexed by its n-grams (n = 1..max_n); after a verify pass, the longest n-gram at
+ * the end of the output found in the pool gives the continuation the next pass
+ * verifies.  The caller owns the arrays (device):
+ *   tokens, seg_end  [capacity] int32: stored draft tokens in insertion order, and for
+ *                    each the end position (exclusive) of its draft;
+ *   keys [n_slots] uint64, vals [n_slots] int32: the hash index (n_slots a power of two,
+ *                    at least about twice the n-grams stored; sdv_pool_clear empties it);
+ *   count [1] int32: tokens stored.
+ * An indexed n-gram is one followed by at least one token of its own draft; its entry
+ * holds the position after its most recent occurrence (later drafts, and later
+ * positions inside a draft, win).  Keys are 64-bit hashes of (n, tokens); a lookup
+ * also compares the stored tokens, so a hash collision can only lose a match
+ * (probability about (n-grams)^2 / 2^64), never return a wrong one. */
+#define SDV_POOL_MAX_N 16
+#define SDV_POOL_EFULL_STORE 0x1   /* err bit: storage full, the draft was not stored */
+#define SDV_POOL_EFULL_INDEX 0x2   /* err bit: hash table full, some n-gram not indexed */
+typedef struct {
+  int32_t* tokens;
+  int32_t* seg_end;
+  uint64_t* keys;
+  int32_t* vals;
+  int32_t* count;
+  int32_t capacity, n_slots, max_n;
+} sdv_pool;
+
+/* Empty the pool (count = 0, every slot free). */
+sdv_status sdv_pool_clear(const sdv_pool* pool, void* stream);
+
+/* Append one draft (device [len] int32) and index its n-grams.  err: [1] device error
+ * bits (SDV_POOL_EFULL_*), nullable. */
+sdv_status sdv_pool_insert(const sdv_pool* pool, const int32_t* draft, int32_t len, int32_t* err,
+                           void* stream);
+
+/* For each query q < batch: the output suffix suffix[q, 0..suffix_len[q]-1] (device
+ * [batch, suffix_cap], lengths [batch]; lengths beyond suffix_cap count as suffix_cap).
+ * The longest n <= min(max_n, length) whose last-n-token n-gram is indexed is matched;
+ * cont[q] (device [batch, max_out]) gets the tokens after its most recent occurrence up
+ * to the end of that draft or max_out tokens (-1 padded), cont_len[q] their number and
+ * match_n[q] (nullable) the n matched (0 and an empty continuation when nothing
+ * matches). */
+sdv_status sdv_pool_lookup(const sdv_pool* pool, int32_t batch, const int32_t* suffix, const int32_t* suffix_len,
+                           int32_t suffix_cap, int32_t max_out, int32_t* cont, int32_t* cont_len,
+                           int32_t* match_n, void* stream);
 
 /* KV commit / rollback (step 4: roll the cache back to x_{<t}; commit n + 1 tokens).
  *   keep_len [B]: new committed length per sequence (seq_len[b] := keep_len[b]).

@@ -69,12 +69,17 @@ class SdvDraftIn(ctypes.Structure):
                 ("chunk", _vp), ("branch_len", ctypes.POINTER(_i32))]
 
 
+class SdvPool(ctypes.Structure):
+    _fields_ = [("tokens", _vp), ("seg_end", _vp), ("keys", _vp), ("vals", _vp), ("count", _vp),
+                ("capacity", _i32), ("n_slots", _i32), ("max_n", _i32)]
+
+
 class SdvError(RuntimeError):
     pass
 
 
 _LIB = None
-ABI_VERSION = 7   # SDV_ABI_VERSION of include/sdv.h that these signatures follow
+ABI_VERSION = 8   # SDV_ABI_VERSION of include/sdv.h that these signatures follow
 
 
 def lib():
@@ -103,6 +108,12 @@ def lib():
         L.sdv_draft_tree.restype = ctypes.c_int
         L.sdv_draft_tree.argtypes = [ctypes.POINTER(SdvModel), ctypes.POINTER(SdvKV), ctypes.POINTER(SdvDraftIn),
                                      _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.sdv_pool_clear.restype = ctypes.c_int
+        L.sdv_pool_clear.argtypes = [ctypes.POINTER(SdvPool), _vp]
+        L.sdv_pool_insert.restype = ctypes.c_int
+        L.sdv_pool_insert.argtypes = [ctypes.POINTER(SdvPool), _vp, _i32, _vp, _vp]
+        L.sdv_pool_lookup.restype = ctypes.c_int
+        L.sdv_pool_lookup.argtypes = [ctypes.POINTER(SdvPool), _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp]
         L.sdv_accept_greedy.restype = ctypes.c_int
         L.sdv_accept_greedy.argtypes = [_i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp,
                                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -397,6 +408,44 @@ class Drafter:
                                     _ptr(self.drafts), _ptr(self.err), _ptr(self.workspace), self.workspace.numel(),
                                     _stream(stream)), "sdv_draft_tree")
         return {"drafts": self.drafts, "err": self.err}
+
+
+class HypothesisPool:
+    """Device-resident hypothesis pool (sdv_pool_*): drafts stored in insertion order and
+    indexed by their n-grams, n = 1..max_n."""
+
+    def __init__(self, capacity: int, n_slots: int, max_n: int = 8, device="cuda"):
+        dev = torch.device(device)
+        self.tokens = torch.empty(capacity, dtype=torch.int32, device=dev)
+        self.seg_end = torch.empty(capacity, dtype=torch.int32, device=dev)
+        self.keys = torch.empty(n_slots, dtype=torch.int64, device=dev)
+        self.vals = torch.empty(n_slots, dtype=torch.int32, device=dev)
+        self.count = torch.empty(1, dtype=torch.int32, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.max_n = max_n
+        self.desc = SdvPool(self.tokens.data_ptr(), self.seg_end.data_ptr(), self.keys.data_ptr(),
+                            self.vals.data_ptr(), self.count.data_ptr(), capacity, n_slots, max_n)
+        self.clear()
+
+    def clear(self, stream=None) -> None:
+        _check(lib().sdv_pool_clear(ctypes.byref(self.desc), _stream(stream)), "sdv_pool_clear")
+
+    def insert(self, draft: torch.Tensor, stream=None) -> None:
+        """draft: int32 device tensor [len]."""
+        _check(lib().sdv_pool_insert(ctypes.byref(self.desc), _ptr(draft), int(draft.numel()), _ptr(self.err),
+                                     _stream(stream)), "sdv_pool_insert")
+
+    def lookup(self, suffix: torch.Tensor, suffix_len: torch.Tensor, max_out: int, stream=None):
+        """suffix int32 [B, cap], suffix_len int32 [B] (device).  Returns (cont [B, max_out],
+        cont_len [B], match_n [B]) device tensors."""
+        B, cap = suffix.shape
+        dev = suffix.device
+        cont = torch.empty((B, max_out), dtype=torch.int32, device=dev)
+        clen = torch.empty(B, dtype=torch.int32, device=dev)
+        mn = torch.empty(B, dtype=torch.int32, device=dev)
+        _check(lib().sdv_pool_lookup(ctypes.byref(self.desc), B, _ptr(suffix), _ptr(suffix_len), cap, max_out,
+                                     _ptr(cont), _ptr(clen), _ptr(mn), _stream(stream)), "sdv_pool_lookup")
+        return cont, clen, mn
 
 
 def tree_parent(L_a: int, branch_lens: Sequence[int]) -> List[int]:

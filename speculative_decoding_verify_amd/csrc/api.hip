@@ -773,6 +773,63 @@ sdv_status sdv_draft_tree(const sdv_model* m, const sdv_kv* kv, const sdv_draft_
   return sdv_kv_rollback(m, kv, keep, nullptr, nullptr, 0, err, stream);
 }
 
+namespace {
+
+sdv_status pool_args(const sdv_pool* p, PoolArgs* a) {
+  if (!p) return fail(SDV_ERR_NULL, "pool is NULL");
+  if (!p->tokens || !p->seg_end || !p->keys || !p->vals || !p->count) return fail(SDV_ERR_NULL, "pool pointer NULL");
+  if (p->capacity < 1) return fail(SDV_ERR_SHAPE, "pool capacity %d", p->capacity);
+  if (p->n_slots < 1 || (p->n_slots & (p->n_slots - 1))) return fail(SDV_ERR_SHAPE, "n_slots %d is not a power of two", p->n_slots);
+  if (p->max_n < 1 || p->max_n > SDV_POOL_MAX_N) return fail(SDV_ERR_SHAPE, "max_n %d outside [1, %d]", p->max_n, SDV_POOL_MAX_N);
+  memset(a, 0, sizeof *a);
+  a->tokens = p->tokens;
+  a->seg_end = p->seg_end;
+  a->keys = (unsigned long long*)p->keys;
+  a->vals = p->vals;
+  a->count = p->count;
+  a->capacity = p->capacity;
+  a->n_slots = p->n_slots;
+  a->max_n = p->max_n;
+  return SDV_OK;
+}
+
+}  // namespace
+
+sdv_status sdv_pool_clear(const sdv_pool* pool, void* stream) {
+  PoolArgs a;
+  sdv_status st = pool_args(pool, &a);
+  if (st != SDV_OK) return st;
+  SDV_LAUNCH(launch_pool_clear(a, (hipStream_t)stream));
+  return SDV_OK;
+}
+
+sdv_status sdv_pool_insert(const sdv_pool* pool, const int32_t* draft, int32_t len, int32_t* err, void* stream) {
+  PoolArgs a;
+  sdv_status st = pool_args(pool, &a);
+  if (st != SDV_OK) return st;
+  if (!draft) return fail(SDV_ERR_NULL, "draft is NULL");
+  if (len < 1 || len > pool->capacity) return fail(SDV_ERR_SHAPE, "draft length %d", len);
+  a.draft = draft;
+  a.len = len;
+  a.err = err;
+  SDV_LAUNCH(launch_pool_insert(a, (hipStream_t)stream));
+  return SDV_OK;
+}
+
+sdv_status sdv_pool_lookup(const sdv_pool* pool, int32_t batch, const int32_t* suffix, const int32_t* suffix_len,
+                           int32_t suffix_cap, int32_t max_out, int32_t* cont, int32_t* cont_len, int32_t* match_n,
+                           void* stream) {
+  PoolArgs pa;
+  sdv_status st = pool_args(pool, &pa);
+  if (st != SDV_OK) return st;
+  if (!suffix || !suffix_len || !cont || !cont_len) return fail(SDV_ERR_NULL, "NULL argument");
+  if (batch < 1 || suffix_cap < 1 || max_out < 1) return fail(SDV_ERR_SHAPE, "batch/suffix_cap/max_out out of range");
+  PoolLookupArgs a{pa.tokens, pa.seg_end, pa.keys, pa.vals, pa.count, pa.n_slots, pa.max_n, batch, suffix, suffix_len,
+                   suffix_cap, max_out, cont, cont_len, match_n};
+  SDV_LAUNCH(launch_pool_lookup(a, (hipStream_t)stream));
+  return SDV_OK;
+}
+
 sdv_status sdv_philox_uniforms(uint64_t seed, const int32_t* seq_ids, int32_t B, int32_t n_pos, double* u0_out,
                                double* u1_out, void* stream) {
   if (!u0_out && !u1_out) return fail(SDV_ERR_NULL, "both outputs are NULL");

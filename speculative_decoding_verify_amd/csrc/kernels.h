@@ -304,4 +304,37 @@ struct DraftStepArgs {
 };
 hipError_t launch_draft_step(const DraftStepArgs& a, hipStream_t s);
 
+// hypothesis pool (pool.hip)
+constexpr int POOL_EFULL_STORE = 0x1;       // storage capacity exceeded: draft not stored
+constexpr int POOL_EFULL_INDEX = 0x2;       // hash table full: an n-gram not indexed
+struct PoolArgs {
+  int32_t* tokens;          // [capacity]
+  int32_t* seg_end;         // [capacity]
+  unsigned long long* keys; // [n_slots]
+  int32_t* vals;            // [n_slots]
+  int32_t* count;           // [1]
+  int capacity, n_slots, max_n;
+  const int32_t* draft;     // [len]
+  int len;
+  int32_t* err;             // [1] nullable
+};
+hipError_t launch_pool_insert(const PoolArgs& a, hipStream_t s);
+hipError_t launch_pool_clear(const PoolArgs& a, hipStream_t s);
+struct PoolLookupArgs {
+  const int32_t* tokens;
+  const int32_t* seg_end;
+  const unsigned long long* keys;
+  const int32_t* vals;
+  const int32_t* count;
+  int n_slots, max_n;
+  int B;
+  const int32_t* suffix;    // [B, suffix_cap]
+  const int32_t* suffix_len;// [B]
+  int suffix_cap, max_out;
+  int32_t* cont;            // [B, max_out]
+  int32_t* cont_len;        // [B]
+  int32_t* match_n;         // [B] nullable
+};
+hipError_t launch_pool_lookup(const PoolLookupArgs& a, hipStream_t s);
+
 }  // namespace sdv

@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
     for f in ("sdv_verify_forward", "sdv_accept_greedy", "sdv_accept_sample", "sdv_kv_rollback",
               "sdv_verify_workspace_size", "sdv_sample_workspace_size", "sdv_pack_weights",
               "sdv_packed_bytes", "sdv_last_error", "sdv_abi_version", "sdv_philox_uniforms",
-              "sdv_draft_tree", "sdv_draft_workspace_size", "sdv_verify_forward_noalloc"):
+              "sdv_draft_tree", "sdv_draft_workspace_size", "sdv_verify_forward_noalloc",
+              "sdv_pool_clear", "sdv_pool_insert", "sdv_pool_lookup"):
         assert f in names, f
 
 
@@ -46,7 +47,8 @@ def test_library_exports_every_declared_function():
 
 def test_abi_version_and_packed_sizes():
     L = sdv.lib()
-    assert L.sdv_abi_version() == binding.ABI_VERSION == 7
+    hdr = int(re.search(r"#define SDV_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert L.sdv_abi_version() == binding.ABI_VERSION == hdr
     # rows round up to 16, 2 bytes (bf16) / 4 bytes (fp32) per value
     assert L.sdv_packed_bytes(1, 6144, 2048) == 6144 * 2048 * 2
     assert L.sdv_packed_bytes(0, 17, 64) == 32 * 64 * 4
@@ -95,3 +97,17 @@ def test_sampling_arguments_are_checked_on_the_host():
                                None) == -4
     assert L.sdv_philox_uniforms(1, None, 4, 3, None, None, None) == -1
     assert L.sdv_philox_uniforms(1, None, 0, 3, p, None, None) == -2
+
+
+def test_pool_arguments_are_checked_on_the_host():
+    L = sdv.lib()
+    p = 256
+    bad_slots = binding.SdvPool(p, p, p, p, p, 100, 1000, 4)      # n_slots not a power of two
+    assert L.sdv_pool_clear(ctypes.byref(bad_slots), None) == -2
+    bad_n = binding.SdvPool(p, p, p, p, p, 100, 1024, 17)         # max_n above the maximum
+    assert L.sdv_pool_clear(ctypes.byref(bad_n), None) == -2
+    ok = binding.SdvPool(p, p, p, p, p, 100, 1024, 4)
+    assert L.sdv_pool_insert(ctypes.byref(ok), None, 3, None, None) == -1
+    assert L.sdv_pool_insert(ctypes.byref(ok), ctypes.c_void_p(p), 0, None, None) == -2
+    assert L.sdv_pool_lookup(ctypes.byref(ok), 0, ctypes.c_void_p(p), ctypes.c_void_p(p), 4, 4,
+                             ctypes.c_void_p(p), ctypes.c_void_p(p), None, None) == -2

@@ -247,20 +247,42 @@ def _log(msg):
 
 # -- drafting (untimed set-up) ----------------------------------------------------------
 
-def draft_under_silence(sdv, model, kv, C, L_a, gamma, silence_id=0, n_branch=0):
-    """Greedy drafting on the GPU path (untimed set-up): sdv_draft_tree with the chunk
-    under silence gives the main draft (gamma tokens) and, with n_branch > 0, the
-    runner-up branch (the second-best first token continued greedily).  The cache is left
-    at C."""
+def draft_under_silence(sdv, model, kv, C, L_a, gamma, silence_id=0, n_branch=0, reps=0):
+    """Greedy drafting on the GPU path: sdv_draft_tree with the chunk under silence gives
+    the main draft (gamma tokens) and, with n_branch > 0, the runner-up branch (the
+    second-best first token continued greedily).  The cache is left at C.  With reps > 0
+    the call is also timed (median of reps calls)."""
     import torch
-    drafter = sdv.Drafter(model, kv, L_a, [gamma] + ([n_branch] if n_branch else []), max_ctx=C)
+    lens = [gamma] + ([n_branch] if n_branch else [])
+    drafter = sdv.Drafter(model, kv, L_a, lens, max_ctx=C)
     drafter.set_chunk(np.full((kv.batch, L_a), silence_id, dtype=np.int32))
     out = drafter.run()
     torch.cuda.synchronize()
     d = out["drafts"].cpu().numpy()[0]
     main = [int(x) for x in d[0, :gamma]]
     branch = [int(x) for x in d[1, :n_branch]] if n_branch else []
-    return main, branch
+    timing = None
+    if reps:
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            drafter.run()
+            torch.cuda.synchronize()
+            times.append(time.perf_counter() - t0)
+        ms = float(np.median(times)) * 1e3
+        # every pass streams all weights and reads the cache: pass 0 the L_a chunk rows,
+        # pass s the root plus s rows of each branch longer than s
+        sh = model.shape
+        passes = [(L_a, 1, C)] + [(1 + s * sum(1 for n in lens if n > s), sum(1 for n in lens if n > s), C + L_a - 1)
+                                  for s in range(1, max(lens))]
+        nbytes = sum(pass_bytes(sh, T, R, [c]) for T, R, c in passes)
+        timing = {"ms": ms, "passes": len(passes), "draft_tokens": sum(lens), "tokens_per_s": sum(lens) / ms * 1e3,
+                  "chunk_budget_frac": ms / 1000.0,
+                  "note": "sdv_draft_tree under a silent chunk: one verify forward per draft position, the branches "
+                          "as a tree under the chunk's last row; chunk_budget_frac = time / the 1 s chunk",
+                  "roofline": {"bound": "hbm", "bytes": nbytes, "achieved_GBs": nbytes / (ms * 1e-3) / 1e9,
+                               "peak_GBs": HBM_PEAK_GBS, "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+    return main, branch, timing
 
 
 # -- the single-sequence verify workloads (toy, 1.7B, 8B tree) ----------------------------
@@ -288,7 +310,8 @@ def bench_verify(args, wl, w=None, model=None):
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
-    drafts, branch = draft_under_silence(sdv, model, kv, C, L_a, gamma, wl.silence_id, wl.n_branch)
+    drafts, branch, drafting = draft_under_silence(sdv, model, kv, C, L_a, gamma, wl.silence_id, wl.n_branch,
+                                                   reps=5)
     parent = wl.parent()
     audio = np.full(L_a, wl.silence_id, dtype=np.int32) if args.scenario == "silence" else \
         uniform_tokens(L_a, sh.vocab, wl.seed + 4000, "audio")
@@ -355,6 +378,7 @@ def bench_verify(args, wl, w=None, model=None):
                           "flops": flops, "mfma_frac": flops / (ms * 1e-3) / 1e12 / mfma_peak(sh)},
         "kernels": {k: {"avg_launch_us": v["avg_launch_us"], "launches_per_pass": v["launches_per_pass"],
                         "bound": v["bound"], "frac": v["frac"]} for k, v in table.items()},
+        "drafting": drafting,
         "setup_s": setup_s,
     }
     if not args.no_cpu_baseline:
@@ -575,6 +599,49 @@ def bench_sample(args):
     return out
 
 
+# -- hypothesis pool ------------------------------------------------------------------
+
+def bench_pool(args, n_drafts=2000, draft_len=32, vocab=151936, B=64, max_n=8, max_out=32):
+    """A session's hypothesis pool: n_drafts drafts of draft_len tokens inserted one by
+    one, then batches of B longest-suffix lookups (suffixes of 16 tokens, half of them
+    ending inside a stored draft)."""
+    import torch
+    import speculative_decoding_verify_amd as sdv
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([9, 0x9001])))
+    drafts = rng.integers(0, vocab, size=(n_drafts, draft_len)).astype(np.int32)
+    dev = torch.from_numpy(drafts).cuda()
+    pool = sdv.HypothesisPool(capacity=n_drafts * draft_len, n_slots=1 << 20, max_n=max_n)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_drafts):
+        pool.insert(dev[i])
+    torch.cuda.synchronize()
+    insert_us = (time.perf_counter() - t0) / n_drafts * 1e6
+    cap = 16
+    suf = rng.integers(0, vocab, size=(B, cap)).astype(np.int32)
+    for q in range(0, B, 2):
+        d, e = int(rng.integers(0, n_drafts)), int(rng.integers(4, draft_len))
+        suf[q, cap - 4:] = drafts[d, e - 4:e]
+    suf_t, len_t = torch.from_numpy(suf).cuda(), torch.full((B,), cap, dtype=torch.int32, device="cuda")
+    ms = timed_steps(lambda: pool.lookup(suf_t, len_t, max_out), args.steps * 10, args.warmup)
+    out = {"workload": f"hypothesis pool: {n_drafts} drafts x {draft_len} tokens indexed by n-grams n <= {max_n}, "
+                       f"batches of {B} longest-suffix lookups (continuation <= {max_out})",
+           "lookup_batch_us": ms * 1e3, "lookups_per_s": B / (ms * 1e-3), "insert_us_per_draft": insert_us,
+           "pool_err": int(pool.err[0])}
+    if not args.no_cpu_baseline:
+        from oracle.pool import Pool
+        op = Pool(max_n)
+        for d in drafts:
+            op.insert(d)
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < 5.0 and n < B:
+            op.lookup(list(suf[n]), max_out)
+            n += 1
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = cpu_record(n / dt, "lookups/s", f"{n} oracle lookups (a scan of every stored position)")
+    return out
+
+
 # -- everything in one line ----------------------------------------------------------------
 
 def bench_all(args):
@@ -604,6 +671,8 @@ def bench_all(args):
     _log(f"sample done ({time.time() - t0:.0f} s)")
     subs["toy-f32"] = bench_verify(args, WORKLOADS["toy-f32"]())
     _log(f"toy-f32 done ({time.time() - t0:.0f} s)")
+    subs["hypothesis-pool"] = bench_pool(args)
+    _log(f"hypothesis-pool done ({time.time() - t0:.0f} s)")
     head["configs"] = subs
     head["wall_s"] = time.time() - t0
     return head

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SDV_ABI_VERSION 8   /* 8: hypothesis pool (sdv_pool_*) */
+#define SDV_ABI_VERSION 9   /* 9: multi-codebook streams (sdv_phase_mask, sdv_stream_commit) */
 #define SDV_PAGE 16          /* tokens per KV-cache page */
 #define SDV_MAX_T 128        /* rows per verify pass (chunk + drafts + branches) */
 #define SDV_SAMPLE_MAX_K 1024  /* draft positions per sequence of sdv_accept_sample */
@@ -374,6 +374,75 @@ sdv_status sdv_pool_insert(const sdv_pool* pool, const int32_t* draft, int32_t l
 sdv_status sdv_pool_lookup(const sdv_pool* pool, int32_t batch, const int32_t* suffix, const int32_t* suffix_len,
                            int32_t suffix_cap, int32_t max_out, int32_t* cont, int32_t* cont_len,
                            int32_t* match_n, void* stream);
+
+/* Multi-codebook streams ("An Efficient vLLM-Based Inference Pipeline for Unified Audio
+ * Understanding and Generation", page 2): the delay pattern (stream s of S codebooks is
+ * shifted by s steps, so frame f of stream s is produced at audio step f + s) and its
+ * de-interleave into an S x frames code matrix; the primary stream (codebook 0, the
+ * backbone token) and the S - 1 auxiliary streams buffered per session; and the phase
+ * state machine with its dynamic vocabulary mask: text (text ids only) -> transition
+ * (the fixed bridge tokens) -> audio (codebook-0 ids; ends with the end-of-audio code)
+ * -> drain (S - 1 pad codes, which flush the delay buffer) -> text.  The modality of a
+ * row is the partition of its UNMASKED argmax: ids below text_end are text, ids
+ * [codebook_base, codebook_base + Vc) are codebook 0.  A verify pass keeps the phase it
+ * starts in; a row that leaves it stops acceptance (argmax -1): a text row whose
+ * unmasked argmax is a codebook-0 id (the model switches to audio), a transition row
+ * past the bridge, a drain row past its S - 1 steps. */
+#define SDV_PHASE_TEXT 0
+#define SDV_PHASE_TRANSITION 1
+#define SDV_PHASE_AUDIO 2
+#define SDV_PHASE_DRAIN 3
+#define SDV_MOD_TEXT 0
+#define SDV_MOD_AUDIO 1
+#define SDV_MOD_OTHER 2
+typedef struct {
+  int32_t n_codebooks, codebook_size, codebook_base, text_end;
+  int32_t eoa_code;            /* codebook-0 code that ends the audio phase */
+  int32_t pad_code;            /* codebook-0 code the drain steps carry */
+  int32_t n_bridge;
+  int32_t max_frames;          /* frames the code matrix holds */
+  const int32_t* bridge;       /* [n_bridge] device backbone ids of the transition */
+} sdv_stream_cfg;
+/* Per-session state, device arrays the caller owns (phase SDV_PHASE_TEXT, the others 0
+ * and frames -1 at the start; matrix entries the caller pre-fills, e.g. -1):
+ *   phase, phase_pos [B]  the phase and the tokens taken in it (transition / drain);
+ *   step [B]              audio steps of the current segment;
+ *   frames [B]            frames of the segment once its end-of-audio code arrived, -1 before;
+ *   matrix [B, S, max_frames]  codes: matrix[b, s, f] = code of frame f of stream s. */
+typedef struct {
+  int32_t* phase;
+  int32_t* phase_pos;
+  int32_t* step;
+  int32_t* frames;
+  int32_t* matrix;
+} sdv_stream_state;
+
+/* The phase mask of a pass: for logit row r of session b (row at logits + (b R + r)
+ * row_stride, holding ids id_offset .. id_offset + n_ids - 1; the LM head's rows, or
+ * codebook 0's with id_offset = codebook_base) and its prediction depth k = depth[r]
+ * within the pass: modality_out = partition of the unmasked argmax (nullable output);
+ * argmax_out = argmax under the phase's mask (lowest index on ties), -1 where the row
+ * leaves the phase (text: modality audio; transition: bridge[pos + k], -1 past it;
+ * audio: codebook-0 ids; drain: the pad code while pos + k < S - 1, then -1).  Feed
+ * argmax_out to sdv_accept_greedy. */
+sdv_status sdv_phase_mask(const sdv_stream_cfg* cfg, int32_t batch, int32_t R, const float* logits,
+                          int64_t row_stride, int32_t id_offset, int32_t n_ids, const int32_t* depth,
+                          const sdv_stream_state* state, int32_t* argmax_out, int32_t* modality_out,
+                          void* stream);
+
+/* Commit of a pass: the accepted path (tokens of path rows 0..n-1, then next unless it
+ * is -1) of every session, in order, through the phase machine; in the audio and drain
+ * phases step i's codes (cb_argmax of the logit row that predicted it: row L_a - 1 for
+ * i = 0, path[i - 1] after; [B, R, S], nullable outside audio passes) are written with
+ * the delay pattern: at audio step t, stream s's code is frame t - s (frames >= 0, below
+ * max_frames and, once the end-of-audio code has arrived at step F, below F).  A text
+ * pass whose walk stopped at a row of modality audio (modality [B, R] from
+ * sdv_phase_mask) switches to the transition phase (the audio phase when there are no
+ * bridge tokens). */
+sdv_status sdv_stream_commit(const sdv_stream_cfg* cfg, int32_t batch, int32_t T, int32_t L_a, int32_t R,
+                             const int32_t* tokens, const int32_t* logit_rows, const int32_t* n_acc,
+                             const int32_t* next, const int32_t* path, const int32_t* cb_argmax,
+                             const int32_t* modality, const sdv_stream_state* state, void* stream);
 
 /* KV commit / rollback (step 4: roll the cache back to x_{<t}; commit n + 1 tokens).
  *   keep_len [B]: new committed length per sequence (seq_len[b] := keep_len[b]).

@@ -74,12 +74,21 @@ class SdvPool(ctypes.Structure):
                 ("capacity", _i32), ("n_slots", _i32), ("max_n", _i32)]
 
 
+class SdvStreamCfg(ctypes.Structure):
+    _fields_ = [("n_codebooks", _i32), ("codebook_size", _i32), ("codebook_base", _i32), ("text_end", _i32),
+                ("eoa_code", _i32), ("pad_code", _i32), ("n_bridge", _i32), ("max_frames", _i32), ("bridge", _vp)]
+
+
+class SdvStreamState(ctypes.Structure):
+    _fields_ = [("phase", _vp), ("phase_pos", _vp), ("step", _vp), ("frames", _vp), ("matrix", _vp)]
+
+
 class SdvError(RuntimeError):
     pass
 
 
 _LIB = None
-ABI_VERSION = 8   # SDV_ABI_VERSION of include/sdv.h that these signatures follow
+ABI_VERSION = 9   # SDV_ABI_VERSION of include/sdv.h that these signatures follow
 
 
 def lib():
@@ -114,6 +123,12 @@ def lib():
         L.sdv_pool_insert.argtypes = [ctypes.POINTER(SdvPool), _vp, _i32, _vp, _vp]
         L.sdv_pool_lookup.restype = ctypes.c_int
         L.sdv_pool_lookup.argtypes = [ctypes.POINTER(SdvPool), _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp]
+        L.sdv_phase_mask.restype = ctypes.c_int
+        L.sdv_phase_mask.argtypes = [ctypes.POINTER(SdvStreamCfg), _i32, _i32, _vp, ctypes.c_int64, _i32, _i32, _vp,
+                                     ctypes.POINTER(SdvStreamState), _vp, _vp, _vp]
+        L.sdv_stream_commit.restype = ctypes.c_int
+        L.sdv_stream_commit.argtypes = [ctypes.POINTER(SdvStreamCfg), _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
+                                        _vp, _vp, ctypes.POINTER(SdvStreamState), _vp]
         L.sdv_accept_greedy.restype = ctypes.c_int
         L.sdv_accept_greedy.argtypes = [_i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp,
                                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -446,6 +461,46 @@ class HypothesisPool:
         _check(lib().sdv_pool_lookup(ctypes.byref(self.desc), B, _ptr(suffix), _ptr(suffix_len), cap, max_out,
                                      _ptr(cont), _ptr(clen), _ptr(mn), _stream(stream)), "sdv_pool_lookup")
         return cont, clen, mn
+
+
+PHASE_TEXT, PHASE_TRANSITION, PHASE_AUDIO, PHASE_DRAIN = 0, 1, 2, 3
+MOD_TEXT, MOD_AUDIO, MOD_OTHER = 0, 1, 2
+
+
+class Streams:
+    """Per-session multi-codebook stream state (phase machine and delay-pattern code
+    matrix) with the phase mask and the commit of sdv_stream_commit."""
+
+    def __init__(self, B: int, n_codebooks: int, codebook_size: int, codebook_base: int, text_end: int,
+                 eoa_code: int, pad_code: int, bridge: Sequence[int], max_frames: int, device="cuda"):
+        dev = torch.device(device)
+        self.B, self.S, self.max_frames = B, n_codebooks, max_frames
+        self.bridge = torch.tensor(list(bridge) or [0], dtype=torch.int32, device=dev)
+        self.cfg = SdvStreamCfg(n_codebooks, codebook_size, codebook_base, text_end, eoa_code, pad_code,
+                                len(bridge), max_frames, self.bridge.data_ptr())
+        self.phase = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.phase_pos = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.step = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.frames = torch.full((B,), -1, dtype=torch.int32, device=dev)
+        self.matrix = torch.full((B, n_codebooks, max_frames), -1, dtype=torch.int32, device=dev)
+        self.state = SdvStreamState(self.phase.data_ptr(), self.phase_pos.data_ptr(), self.step.data_ptr(),
+                                    self.frames.data_ptr(), self.matrix.data_ptr())
+
+    def mask(self, logits: torch.Tensor, depth: torch.Tensor, id_offset: int = 0, stream=None):
+        """logits fp32 [B, R, n_ids] (contiguous rows); returns (argmax [B, R], modality [B, R])."""
+        B, R, n = logits.shape
+        am = torch.empty((B, R), dtype=torch.int32, device=logits.device)
+        mod = torch.empty((B, R), dtype=torch.int32, device=logits.device)
+        _check(lib().sdv_phase_mask(ctypes.byref(self.cfg), B, R, _ptr(logits), n, id_offset, n, _ptr(depth),
+                                    ctypes.byref(self.state), _ptr(am), _ptr(mod), _stream(stream)), "sdv_phase_mask")
+        return am, mod
+
+    def commit(self, T: int, L_a: int, tokens: torch.Tensor, logit_rows: torch.Tensor, acc: dict,
+               cb_argmax: Optional[torch.Tensor], modality: Optional[torch.Tensor], stream=None) -> None:
+        _check(lib().sdv_stream_commit(ctypes.byref(self.cfg), self.B, T, L_a, logit_rows.numel(), _ptr(tokens),
+                                       _ptr(logit_rows), _ptr(acc["n"]), _ptr(acc["next"]), _ptr(acc["path"]),
+                                       _ptr(cb_argmax), _ptr(modality), ctypes.byref(self.state), _stream(stream)),
+               "sdv_stream_commit")
 
 
 def tree_parent(L_a: int, branch_lens: Sequence[int]) -> List[int]:

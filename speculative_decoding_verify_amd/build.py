@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libsdv.so")
-SOURCES = ["api.hip", "gemm.hip", "attention.hip", "elementwise.hip", "accept.hip", "draft.hip", "pool.hip"]
+SOURCES = ["api.hip", "gemm.hip", "attention.hip", "elementwise.hip", "accept.hip", "draft.hip", "pool.hip", "streams.hip"]
 
 
 def hipcc() -> str:

@@ -830,6 +830,79 @@ sdv_status sdv_pool_lookup(const sdv_pool* pool, int32_t batch, const int32_t* s
   return SDV_OK;
 }
 
+namespace {
+
+sdv_status stream_cfg(const sdv_stream_cfg* c, StreamCfgDev* d) {
+  if (!c) return fail(SDV_ERR_NULL, "stream cfg is NULL");
+  if (c->n_codebooks < 1 || c->codebook_size < 2 || c->codebook_base < 0 || c->text_end < 0 ||
+      c->text_end > c->codebook_base || c->max_frames < 1)
+    return fail(SDV_ERR_SHAPE, "stream cfg sizes out of range");
+  if (c->eoa_code < 0 || c->eoa_code >= c->codebook_size || c->pad_code < 0 || c->pad_code >= c->codebook_size)
+    return fail(SDV_ERR_SHAPE, "end-of-audio / pad code outside the codebook");
+  if (c->n_bridge < 0 || (c->n_bridge > 0 && !c->bridge)) return fail(SDV_ERR_NULL, "bridge tokens NULL");
+  *d = StreamCfgDev{c->n_codebooks, c->codebook_size, c->codebook_base, c->text_end, c->eoa_code, c->pad_code,
+                    c->n_bridge, c->max_frames, c->bridge};
+  return SDV_OK;
+}
+
+}  // namespace
+
+sdv_status sdv_phase_mask(const sdv_stream_cfg* cfg, int32_t batch, int32_t R, const float* logits,
+                          int64_t row_stride, int32_t id_offset, int32_t n_ids, const int32_t* depth,
+                          const sdv_stream_state* state, int32_t* argmax_out, int32_t* modality_out, void* stream) {
+  PhaseMaskArgs a;
+  sdv_status st = stream_cfg(cfg, &a.cfg);
+  if (st != SDV_OK) return st;
+  if (!logits || !depth || !state || !state->phase || !state->phase_pos || !argmax_out)
+    return fail(SDV_ERR_NULL, "NULL argument");
+  if (batch < 1 || R < 1 || n_ids < 1 || id_offset < 0 || row_stride < n_ids) return fail(SDV_ERR_SHAPE, "sizes out of range");
+  a.B = batch;
+  a.R = R;
+  a.logits = logits;
+  a.row_stride = row_stride;
+  a.id_offset = id_offset;
+  a.n_ids = n_ids;
+  a.depth = depth;
+  a.phase = state->phase;
+  a.phase_pos = state->phase_pos;
+  a.argmax_out = argmax_out;
+  a.modality_out = modality_out;
+  SDV_LAUNCH(launch_phase_mask(a, (hipStream_t)stream));
+  return SDV_OK;
+}
+
+sdv_status sdv_stream_commit(const sdv_stream_cfg* cfg, int32_t batch, int32_t T, int32_t L_a, int32_t R,
+                             const int32_t* tokens, const int32_t* logit_rows, const int32_t* n_acc,
+                             const int32_t* next, const int32_t* path, const int32_t* cb_argmax,
+                             const int32_t* modality, const sdv_stream_state* state, void* stream) {
+  StreamCommitArgs a;
+  sdv_status st = stream_cfg(cfg, &a.cfg);
+  if (st != SDV_OK) return st;
+  if (!tokens || !logit_rows || !n_acc || !next || !path || !state) return fail(SDV_ERR_NULL, "NULL argument");
+  if (!state->phase || !state->phase_pos || !state->step || !state->frames || !state->matrix)
+    return fail(SDV_ERR_NULL, "stream state pointer NULL");
+  if (batch < 1 || T < 1 || T > SDV_MAX_T || R < 1 || R > T || L_a < 1 || L_a > T)
+    return fail(SDV_ERR_SHAPE, "B/T/R/L_a out of range");
+  a.B = batch;
+  a.T = T;
+  a.L_a = L_a;
+  a.R = R;
+  a.tokens = tokens;
+  a.logit_rows = logit_rows;
+  a.n = n_acc;
+  a.next = next;
+  a.path = path;
+  a.cb_argmax = cb_argmax;
+  a.modality = modality;
+  a.phase = state->phase;
+  a.phase_pos = state->phase_pos;
+  a.step = state->step;
+  a.frames = state->frames;
+  a.matrix = state->matrix;
+  SDV_LAUNCH(launch_stream_commit(a, (hipStream_t)stream));
+  return SDV_OK;
+}
+
 sdv_status sdv_philox_uniforms(uint64_t seed, const int32_t* seq_ids, int32_t B, int32_t n_pos, double* u0_out,
                                double* u1_out, void* stream) {
   if (!u0_out && !u1_out) return fail(SDV_ERR_NULL, "both outputs are NULL");

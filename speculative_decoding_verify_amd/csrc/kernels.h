@@ -337,4 +337,40 @@ struct PoolLookupArgs {
 };
 hipError_t launch_pool_lookup(const PoolLookupArgs& a, hipStream_t s);
 
+// multi-codebook stream bookkeeping (streams.hip); phase and modality values follow the
+// ABI's SDV_PHASE_* / SDV_MOD_*
+constexpr int STREAM_TEXT = 0, STREAM_TRANSITION = 1, STREAM_AUDIO = 2, STREAM_DRAIN = 3;
+constexpr int STREAM_MOD_TEXT = 0, STREAM_MOD_AUDIO = 1, STREAM_MOD_OTHER = 2;
+struct StreamCfgDev {
+  int S, Vc, base, text_end, eoa_code, pad_code, n_bridge, max_frames;
+  const int32_t* bridge;    // [n_bridge] device
+};
+struct PhaseMaskArgs {
+  StreamCfgDev cfg;
+  int B, R;
+  const float* logits;      // row (b, r) at logits + (b * R + r) * row_stride
+  long long row_stride;
+  int id_offset, n_ids;     // the row holds ids id_offset .. id_offset + n_ids - 1
+  const int32_t* depth;     // [R] prediction depth of each logit row in the pass
+  const int32_t* phase;     // [B]
+  const int32_t* phase_pos; // [B]
+  int32_t* argmax_out;      // [B, R]
+  int32_t* modality_out;    // [B, R] nullable
+};
+hipError_t launch_phase_mask(const PhaseMaskArgs& a, hipStream_t s);
+struct StreamCommitArgs {
+  StreamCfgDev cfg;
+  int B, T, L_a, R;
+  const int32_t* tokens;    // [B, T]
+  const int32_t* logit_rows;// [R]
+  const int32_t* n;         // [B]
+  const int32_t* next;      // [B]
+  const int32_t* path;      // [B, T]
+  const int32_t* cb_argmax; // [B, R, S] nullable
+  const int32_t* modality;  // [B, R] nullable
+  int32_t *phase, *phase_pos, *step, *frames;   // [B] state
+  int32_t* matrix;          // [B, S, max_frames]
+};
+hipError_t launch_stream_commit(const StreamCommitArgs& a, hipStream_t s);
+
 }  // namespace sdv

@@ -45,7 +45,10 @@ int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 // target workgroups per launch (256 compute units)
 constexpr int TARGET_WG_GEMM = 256;
-constexpr int TARGET_WG_ATTN = 256;  // measured: one workgroup per CU beats two rounds
+#ifndef SDV_ATTN_TARGET_WG
+#define SDV_ATTN_TARGET_WG 256
+#endif
+constexpr int TARGET_WG_ATTN = SDV_ATTN_TARGET_WG;  // measured: one workgroup per CU beats two rounds
 constexpr long long ATTN_MERGE_MAX_READ = 32768;  // floats of partial output one merging workgroup reads
 
 struct GemmPlan {

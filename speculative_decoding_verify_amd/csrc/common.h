@@ -155,6 +155,32 @@ SDV_DEV u32x2 ld_dev8(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buff
 // vector-memory counter at zero; export and LDS counters left alone).
 SDV_DEV void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// LDS DMA: 16 bytes from global address g (per lane) land in LDS at lds + 16 * lane
+// (lds uniform across the wave), without passing through registers; completion is
+// counted by the vector-memory counter.
+SDV_DEV void lds_dma16(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#endif
+}
+// wait until at most N vector memory operations of the wave are outstanding
+template <int N> SDV_DEV void vmem_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// the same, and every LDS access of the wave complete
+template <int N> SDV_DEV void vmem_lds_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+// a bare workgroup barrier (no counter waits); the fences keep the compiler from moving
+// memory accesses across it
+SDV_DEV void bare_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Every thread's stores are complete, then thread 0 counts the workgroup in on
 // `counter` (zero before the launch).  True in all threads of the workgroup that
 // arrives n-th (last).  `flag` is an int in LDS.

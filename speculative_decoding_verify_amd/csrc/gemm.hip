@@ -325,16 +325,6 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs a) {
 // the weights come from HBM once), y = splits of K (split-partials epilogue only), z =
 // column groups.  The finished tile goes through LDS (the ring's memory) to the shared
 // epilogues.
-SDV_DEV void lds_dma16(const void* g, void* lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-#endif
-}
-// wait until at most N vector memory operations of the wave are outstanding
-template <int N> SDV_DEV void vmem_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 template <typename T, int WN, int R>
 constexpr int tiled_lds_bytes() {

@@ -48,7 +48,12 @@ constexpr int TARGET_WG_GEMM = 256;
 #ifndef SDV_ATTN_TARGET_WG
 #define SDV_ATTN_TARGET_WG 256
 #endif
-constexpr int TARGET_WG_ATTN = SDV_ATTN_TARGET_WG;  // measured: one workgroup per CU beats two rounds
+constexpr int TARGET_WG_ATTN = SDV_ATTN_TARGET_WG;  // register path, measured: one workgroup per CU beats two rounds
+// the bf16 LDS-DMA path keeps three workgroups per CU
+#ifndef SDV_ATTN_DMA_TARGET_WG
+#define SDV_ATTN_DMA_TARGET_WG 768
+#endif
+constexpr int TARGET_WG_ATTN_DMA = SDV_ATTN_DMA_TARGET_WG;
 constexpr long long ATTN_MERGE_MAX_READ = 32768;  // floats of partial output one merging workgroup reads
 
 struct GemmPlan {
@@ -189,7 +194,8 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
   const int NQT = cdiv(T * p.G, 16);
   int rows_per_group = 0;
   p.n_qg = attn_query_groups(p.bf, dh, T, p.G, B * Hkv, &rows_per_group);
-  int ns = cdiv(TARGET_WG_ATTN, (long long)B * Hkv * p.n_qg);
+  const int target = (p.bf && !attn_uses_reg_path(true, dh, NQT)) ? TARGET_WG_ATTN_DMA : TARGET_WG_ATTN;
+  int ns = cdiv(target, (long long)B * Hkv * p.n_qg);
   ns = std::max(1, std::min({ns, ATTN_MAX_SPLITS, cdiv(nkeys, KT)}));
   ns = std::max(ns, cdiv(nkeys, 255 * KT));  // a split spans at most 511 pages (staged in LDS)
   p.split_keys = cdiv(cdiv(nkeys, ns), KT) * KT;

@@ -1125,6 +1125,15 @@ template <typename T, int DH> constexpr int attn_cap() {
 #ifndef SDV_ATTN_WIDE_GROUP_TILES
 #define SDV_ATTN_WIDE_GROUP_TILES 4
 #endif
+// (sequence, kv head) pairs from which groups are limited to SDV_ATTN_WIDE_GROUP_TILES
+#ifndef SDV_ATTN_WIDE_HEADS
+#define SDV_ATTN_WIDE_HEADS 256
+#endif
+// query tiles per group of the bf16 (LDS DMA) path below that: small groups and more
+// key splits keep three workgroups resident per CU (8B tree pass: 51 -> 42 us)
+#ifndef SDV_ATTN_FEW_GROUP_TILES
+#define SDV_ATTN_FEW_GROUP_TILES 3
+#endif
 // tiles in the LDS ring of attn_dma
 #ifndef SDV_ATTN_RING
 #define SDV_ATTN_RING 3
@@ -1143,7 +1152,9 @@ int attn_shape(int NQT, int heads, int* nqw_out, int* nw_out) {
   // the fewest query tiles per key tile, then the fewest tiles per wave (registers),
   // then the fewest waves; at least 4 waves (waves without query tiles still stage K/V)
   constexpr int WG = SDV_ATTN_WIDE_GROUP_TILES;
-  const int n_qg = std::max((NQT + 8 * CAP - 1) / (8 * CAP), heads >= 256 ? (NQT + WG - 1) / WG : 1);
+  constexpr int FG = SDV_ATTN_FEW_GROUP_TILES;
+  const int n_qg = std::max((NQT + 8 * CAP - 1) / (8 * CAP), heads >= SDV_ATTN_WIDE_HEADS ? (NQT + WG - 1) / WG
+                                                             : DMA ? (NQT + FG - 1) / FG : 1);
   const int Q = (NQT + n_qg - 1) / n_qg;
   int best_nw = 8, best_nqw = CAP, best_load = 1 << 30;
   for (int nqw = 1; nqw <= CAP; ++nqw)

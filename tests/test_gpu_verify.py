@@ -20,8 +20,9 @@ from oracle import decoder as odec  # noqa: E402
 from synth import (MINI_BF16, MINI_BF16_D128, MINI_BF16_D2048, MINI_F32, MINI_F32_D2048,  # noqa: E402
                    MINI_BF16_FFN12K, MINI_F32_FFN12K, MINI_BF16_V70K, MINI_F32_V70K, make_weights,
                    make_random_kv, uniform_tokens)
+from synth.configs import ModelShape  # noqa: E402
 from tests.gpu_helpers import (run_pair, compare_logits, compare_kv, greedy_expectation,  # noqa: E402
-                               mode_of)
+                               mode_of, logit_tol as logit_tol_of)
 
 
 def _tokens(B, T, V, seed):
@@ -400,3 +401,30 @@ def test_rollback_idempotent_and_ordered_moves():
         k, v = kv.gather(0, l, 0, C)
         assert torch.equal(k[3], ref[l][0][5]) and torch.equal(k[5], ref[l][0][10])
         assert torch.equal(v[3], ref[l][1][5]) and torch.equal(k[4], ref[l][0][4])
+
+
+# d = 256 with 32 MHA heads of 64 (6144 q/k/v rows) and FFN 12288: with 11 sequences x 120
+# rows (1320 rows, 11 row blocks) the tiled GEMM takes 8 MFMA column tiles per wave for the
+# q/k/v projection (rotary + paged append epilogue) and gate/up (SwiGLU epilogue), whose
+# epilogues run on 64-row halves of the 128-row block
+WIDE_MHA_BF16 = ModelShape("mini-bf16-wide-mha", n_layers=1, d=256, n_heads=32, n_kv_heads=32, head_dim=64,
+                           ffn=12288, vocab=1000, dtype="bf16")
+WIDE_MHA_F32 = ModelShape("mini-f32-wide-mha", n_layers=1, d=256, n_heads=32, n_kv_heads=32, head_dim=64,
+                          ffn=12288, vocab=1000, dtype="f32")
+
+
+@pytest.mark.parametrize("shape", [WIDE_MHA_BF16, WIDE_MHA_F32], ids=lambda s: s.name)
+def test_tiled_gemm_eight_column_epilogues(shape):
+    w = make_weights(shape, seed=701)
+    B, L_a, gamma = 11, 100, 20
+    T = L_a + gamma
+    lens = [int(x) for x in np.random.default_rng(702).integers(5, 61, size=B)]
+    kvh = make_random_kv(shape, lens, capacity=max(lens) + T, seed=703)
+    toks = _tokens(B, T, shape.vocab, 704)
+    g, o, ver, kv = run_pair(w, kvh, toks, L_a, perm_seed=705)
+    assert np.all(g["err"] == 0)
+    err, flagged, n = compare_logits(shape, g, o)
+    print(f"  1320 rows, tiled 8-column epilogues: logits rel err {err:.2e}; flagged {flagged}/{n}", flush=True)
+    compare_kv(shape, kv, o, lens, T)
+    hd = np.max(np.abs(g["hidden"] - o["hidden"]), axis=2) / np.max(np.abs(o["hidden"]), axis=2)
+    assert hd.max() <= logit_tol_of(shape), hd.max()

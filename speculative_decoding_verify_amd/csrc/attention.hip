@@ -116,6 +116,27 @@ SDV_DEV void split_probs_fast(const float (&p)[8], u32x4& hi, u32x4& lo) {
   lo.z = __builtin_amdgcn_perm(l[5], l[4], 0x07060302u); lo.w = __builtin_amdgcn_perm(l[7], l[6], 0x07060302u);
 }
 
+// The same hi/lo pair with gfx950's packed conversion: hi = p rounded to nearest even
+// bf16, lo = (p - hi) rounded likewise (p - hi is exact in fp32), so |p - hi - lo| <=
+// 2^-18 |p|; one conversion covers two values and yields the operand word directly.
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+SDV_DEV uint32_t cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_v){a, b}, bf16x2_v));
+}
+SDV_DEV void split_probs_pk(const float (&p)[8], u32x4& hi, u32x4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = cvt_pk_bf16(p[2 * e], p[2 * e + 1]);
+    const float r0 = p[2 * e] - __uint_as_float(h[e] << 16);
+    const float r1 = p[2 * e + 1] - __uint_as_float(h[e] & 0xFFFF0000u);
+    l[e] = cvt_pk_bf16(r0, r1);
+  }
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  lo = u32x4{l[0], l[1], l[2], l[3]};
+}
+
 // Merge of the split partial states of query rows [qi0, qi1) of (sequence b, kv head
 // g), run by the last workgroup of the group to finish; splits are taken in order:
 //   M = max_s m_s,  w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s',  o = sum_s w_s o_s.
@@ -508,6 +529,9 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
 // layout; the key rows are 256 (dh 128) or 128 (dh 64) bytes, so inside LDS the
 // 16-byte chunks of a key are permuted (chunk index XOR bits of the key), which a
 // wave-load can do where padding would not fit.
+// how far (log2 units) a row's running maximum may rise above the reference point of
+// its probabilities before O and l are rescaled to it
+constexpr float ATTN_RESCALE_LAG = 8.f;
 template <int DH> struct DmaTile {
   static constexpr int PAGE_B = 16 * DH * 2;   // one page of one kv head, K or V
   static constexpr int TILE_B = 4 * PAGE_B;    // K pages 0, 1, then V pages 0, 1
@@ -574,7 +598,7 @@ void attn_dma(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt) acc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int pg0 = stage_pages(a, bt, k_begin, sPage);
+  stage_pages(a, bt, k_begin, sPage);   // sPage[i]: page k_begin / 16 + i
 
   // this wave's wave-loads of a tile: u = w + NW * i; the LDS offset inside the tile and
   // this lane's offset inside the source page (the inverse of the chunk permutation)
@@ -593,11 +617,11 @@ void attn_dma(AttnArgs a) {
       ld_src[i] = o;   // values keep the page's layout
     }
   }
-  auto issue = [&](int kt0, int slot) {
+  // the two physical pages of tile t of the split in one LDS read (k_begin is a
+  // multiple of 32, so the pair is 8-byte aligned)
+  auto pages_of = [&](int t) { return *(const int2*)&sPage[2 * t]; };
+  auto issue = [&](int2 ph, int slot) {
     char* dst = ring + slot * G::TILE_B;
-    // the tile's two pages in one LDS read (kt0 and k_begin are multiples of 32, so the
-    // pair is 8-byte aligned)
-    const int2 ph = *(const int2*)&sPage[(kt0 >> 4) - pg0];
     const int ph0 = __builtin_amdgcn_readfirstlane(ph.x), ph1 = __builtin_amdgcn_readfirstlane(ph.y);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
@@ -659,13 +683,18 @@ void attn_dma(AttnArgs a) {
   vmem_wait_all();   // the query loads are complete before the ring starts
 #pragma unroll
   for (int u = 0; u < R - 1; ++u)
-    if (u < n_tiles) issue(k_begin + u * KT, u);
+    if (u < n_tiles) issue(pages_of(u), u);
+  // pages of the tile the loop issues next, read a whole tile ahead so the read's
+  // latency is never waited on
+  int2 ph_next = pages_of(min(R - 1, max(n_tiles - 1, 0)));
   for (int it = 0; it < n_tiles; ++it) {
     const int kt0 = k_begin + it * KT;
     // issued so far: tiles up to min(it + R - 2, n_tiles - 1)
     land(it, it + R - 2 <= n_tiles - 1 ? R - 2 : 0);
     // the slot of tile it - 1 is free: refill it with tile it + R - 1
-    if (it + R - 1 < n_tiles) issue(kt0 + (R - 1) * KT, (it + R - 1) % R);
+    if (it + R - 1 < n_tiles) issue(ph_next, (it + R - 1) % R);
+    ph_next = pages_of(min(it + R, n_tiles - 1));
+    if (nj == 0) continue;   // a wave without query tiles only stages K/V
     const char* sl = ring + (it % R) * G::TILE_B;
 
     // ---- scores S^T of all this wave's query tiles: every K operand of the tile is
@@ -681,13 +710,19 @@ void attn_dma(AttnArgs a) {
     for (int j = 0; j < NQW; ++j) {
 #pragma unroll
       for (int hv = 0; hv < NH; ++hv) sc[j][hv] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (j < nj) {
+      if (j == 0 || j < nj) {
 #pragma unroll
         for (int ks = 0; ks < DH / KS; ++ks)
 #pragma unroll
           for (int qp = 0; qp < QP; ++qp)
 #pragma unroll
             for (int hv = 0; hv < NH; ++hv) sc[j][hv] = mma16<T>(kk[ks][hv], qreg[j][ks][qp], sc[j][hv]);
+        if (j == 0) {
+          // every K read of the tile goes out before the first MFMA (one LDS latency
+          // per tile, not one per k step)
+          __builtin_amdgcn_sched_group_barrier(0x100, DH / KS * NH, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, DH / KS * QP * NH, 0);
+        }
       }
     }
     // the V operands of the tile, read while the softmax below runs
@@ -715,7 +750,11 @@ void attn_dma(AttnArgs a) {
         }
       }
     }
-    // ---- online softmax; rescale only when some row's maximum rises
+    // ---- online softmax.  The reference point mrun of a row moves up to the row's
+    //      maximum only when that maximum exceeds it by more than RESCALE_LAG (log2
+    //      units); until then the probabilities are taken against the old reference
+    //      and stay below 2^RESCALE_LAG, so most tiles skip the rescale of O and l.
+    //      O / l and the split merge are the same for any reference point.
     float mnew[NQW];
     bool rise = false;
 #pragma unroll
@@ -725,7 +764,7 @@ void attn_dma(AttnArgs a) {
       for (int e = 1; e < PE; ++e) mx = fmaxf(mx, sv[j][e]);
       mx = pair32_max(pair16_max(mx));
       mnew[j] = fmaxf(mrun[j], mx);
-      rise |= mnew[j] > mrun[j];
+      rise |= mnew[j] > mrun[j] + ATTN_RESCALE_LAG;
     }
     if (__any(rise)) {
 #pragma unroll
@@ -740,19 +779,16 @@ void attn_dma(AttnArgs a) {
     u32x4 pop[NQW][QP];
 #pragma unroll
     for (int j = 0; j < NQW; ++j) {
-      float pj[PE], ps = 0.f;
+      float pj[PE];
 #pragma unroll
-      for (int e = 0; e < PE; ++e) {
-        pj[e] = __builtin_amdgcn_exp2f(sv[j][e] - mrun[j]);
-        ps += pj[e];
-      }
-      lrun[j] += ps;
-      split_probs_fast(pj, pop[j][0], pop[j][1]);
+      for (int e = 0; e < PE; ++e) pj[e] = __builtin_amdgcn_exp2f(sv[j][e] - mrun[j]);
+      lrun[j] += ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7]));
+      split_probs_pk(pj, pop[j][0], pop[j][1]);
     }
     // ---- O^T += V^T P^T
 #pragma unroll
     for (int j = 0; j < NQW; ++j)
-      if (j < nj)
+      if (j == 0 || j < nj)
 #pragma unroll
         for (int dt = 0; dt < DH / 16; ++dt)
 #pragma unroll

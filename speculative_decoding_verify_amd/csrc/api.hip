@@ -419,6 +419,8 @@ sdv_status verify_forward_impl(const sdv_model* m, const sdv_kv* kv, const sdv_v
   if (in->head == SDV_HEAD_CODEBOOK && m->n_codebooks < 1) return fail(SDV_ERR_UNSUPPORTED, "model has no codebook heads");
   if (in->head == SDV_HEAD_LM && in->cfg_partner) return fail(SDV_ERR_UNSUPPORTED, "guidance pairs need the codebook head");
   const Plan P = make_plan(m, B, T, R, in->max_ctx);
+  if ((long long)B * P.n_qg > 65535)
+    return fail(SDV_ERR_UNSUPPORTED, "batch %d x %d query groups exceeds the attention grid", B, P.n_qg);
   if (use_scratch) {
     if (P.total > NOALLOC_SCRATCH_BYTES)
       return fail(SDV_ERR_WORKSPACE, "pass needs %zu bytes of scratch, more than the %zu-byte static scratch of "

@@ -270,11 +270,11 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
   T* const ldsK = (T*)lds_raw;
   T* const ldsV = (T*)(lds_raw + KBYTES);
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z / a.n_qg;
+  const int split = blockIdx.z, g = blockIdx.x, b = blockIdx.y / a.n_qg;
   const int lane = threadIdx.x & 63, NW = blockDim.x >> 6;
   // this wave's query tiles: q_base + w + j*NW, q_base = (query group) * NW * NQW
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-  const int q_base = (blockIdx.z % a.n_qg) * NW * NQW;
+  const int q_base = (blockIdx.y % a.n_qg) * NW * NQW;
   const int r = lane & 15, lg = lane >> 4;
   const int G = a.H / a.Hkv;
   const int C = min(max(a.seq_len[b], 0), a.max_ctx);
@@ -511,7 +511,7 @@ __global__ __launch_bounds__(512) void attn_chunk(AttnArgs a) {
   }
   if (!fused || direct) return;
   __shared__ int is_last;
-  const int qg = blockIdx.z % a.n_qg;
+  const int qg = blockIdx.y % a.n_qg;
   if (!arrive_last(a.sem + ((size_t)b * a.Hkv + g) * a.n_qg + qg, a.n_splits, &is_last)) return;
   if (a.n_splits <= 8) attn_merge8<T, DH>(a, b, g, q_base * 16, min(nq, (q_base + NW * NQW) * 16));
   else attn_merge<T, DH>(a, b, g, q_base * 16, min(nq, (q_base + NW * NQW) * 16), (float*)lds_raw);
@@ -563,10 +563,10 @@ void attn_dma(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char ring[RING_B > ATTN_MERGE_FLOATS * 4 ? RING_B : ATTN_MERGE_FLOATS * 4];
   __shared__ __attribute__((aligned(8))) int sPage[ATTN_MAX_PAGES];
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z / a.n_qg;
+  const int split = blockIdx.z, g = blockIdx.x, b = blockIdx.y / a.n_qg;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int q_base = (blockIdx.z % a.n_qg) * NW * NQW;
+  const int q_base = (blockIdx.y % a.n_qg) * NW * NQW;
   const int r = lane & 15, lg = lane >> 4;
   const int Gq = a.H / a.Hkv;
   const int C = min(max(a.seq_len[b], 0), a.max_ctx);
@@ -696,103 +696,116 @@ void attn_dma(AttnArgs a) {
     ph_next = pages_of(min(it + R, n_tiles - 1));
     if (nj == 0) continue;   // a wave without query tiles only stages K/V
     const char* sl = ring + (it % R) * G::TILE_B;
+    const bool edge = kt0 + KT > C || kt0 + KT > k_end;   // the tile reaches the chunk rows or the split end
 
-    // ---- scores S^T of all this wave's query tiles: every K operand of the tile is
-    //      read from LDS first, then the MFMAs run back to back (one branch per query
-    //      tile, not per MFMA)
     u32x4 kk[DH / KS][NH];
-#pragma unroll
-    for (int ks = 0; ks < DH / KS; ++ks)
-#pragma unroll
-      for (int hv = 0; hv < NH; ++hv) kk[ks][hv] = *(const u32x4*)(sl + koff[hv][ks]);
     f32x4 sc[NQW][NH];
+    float sv[NQW][PE];
+    float mnew[NQW];
+    u32x4 pop[NQW][QP];
+    u32x4 va[DH / 16];
+    auto read_k = [&]() {
 #pragma unroll
-    for (int j = 0; j < NQW; ++j) {
+      for (int ks = 0; ks < DH / KS; ++ks)
+#pragma unroll
+        for (int hv = 0; hv < NH; ++hv) kk[ks][hv] = *(const u32x4*)(sl + koff[hv][ks]);
+    };
+    auto read_v = [&]() {
+#pragma unroll
+      for (int dt = 0; dt < DH / 16; ++dt) va[dt] = *(const u32x4*)(sl + voff[dt]);
+    };
+    // S^T of query tile j
+    auto scores = [&](int j) {
 #pragma unroll
       for (int hv = 0; hv < NH; ++hv) sc[j][hv] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (j == 0 || j < nj) {
 #pragma unroll
-        for (int ks = 0; ks < DH / KS; ++ks)
+      for (int ks = 0; ks < DH / KS; ++ks)
 #pragma unroll
-          for (int qp = 0; qp < QP; ++qp)
+        for (int qp = 0; qp < QP; ++qp)
 #pragma unroll
-            for (int hv = 0; hv < NH; ++hv) sc[j][hv] = mma16<T>(kk[ks][hv], qreg[j][ks][qp], sc[j][hv]);
-        if (j == 0) {
-          // every K read of the tile goes out before the first MFMA (one LDS latency
-          // per tile, not one per k step)
-          __builtin_amdgcn_sched_group_barrier(0x100, DH / KS * NH, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, DH / KS * QP * NH, 0);
-        }
-      }
-    }
-    // the V operands of the tile, read while the softmax below runs
-    u32x4 va[DH / 16];
-#pragma unroll
-    for (int dt = 0; dt < DH / 16; ++dt) va[dt] = *(const u32x4*)(sl + voff[dt]);
-    float sv[NQW][PE];
-#pragma unroll
-    for (int j = 0; j < NQW; ++j)
+          for (int hv = 0; hv < NH; ++hv) sc[j][hv] = mma16<T>(kk[ks][hv], qreg[j][ks][qp], sc[j][hv]);
+    };
+    // the lane's 8 scores of tile j, masked where the tile needs it (wave-uniform test);
+    // the row maxima; true where a row's maximum leaves the reference point behind.
+    // The reference point mrun of a row moves up to the row's maximum only when that
+    // maximum exceeds it by more than ATTN_RESCALE_LAG (log2 units); until then the
+    // probabilities are taken against the old reference and stay below
+    // 2^ATTN_RESCALE_LAG, so most tiles skip the rescale of O and l.  O / l and the
+    // split merge are the same for any reference point.
+    auto row_max = [&](int j) {
 #pragma unroll
       for (int hv = 0; hv < NH; ++hv)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sv[j][4 * hv + i] = sc[j][hv][i];
-    // ---- mask only tiles that reach the chunk rows or the split end (wave-uniform)
-    if (kt0 + KT > C || kt0 + KT > k_end) {
+      if (edge) {
 #pragma unroll
-      for (int e = 0; e < PE; ++e) {
-        const int sl_ = kt0 + PE * lg + e;
-        const bool live = sl_ < k_end;
-        const int jr = max(sl_ - C, 0);
-#pragma unroll
-        for (int j = 0; j < NQW; ++j) {
+        for (int e = 0; e < PE; ++e) {
+          const int sl_ = kt0 + PE * lg + e;
+          const bool live = sl_ < k_end;
+          const int jr = max(sl_ - C, 0);
           const bool vis = live & ((sl_ < C) | (((anc_word(anc[j], jr >> 5) >> (jr & 31)) & 1u) != 0u));
           sv[j][e] = vis ? sv[j][e] : -INFINITY;
         }
       }
-    }
-    // ---- online softmax.  The reference point mrun of a row moves up to the row's
-    //      maximum only when that maximum exceeds it by more than RESCALE_LAG (log2
-    //      units); until then the probabilities are taken against the old reference
-    //      and stay below 2^RESCALE_LAG, so most tiles skip the rescale of O and l.
-    //      O / l and the split merge are the same for any reference point.
-    float mnew[NQW];
-    bool rise = false;
-#pragma unroll
-    for (int j = 0; j < NQW; ++j) {
       float mx = sv[j][0];
 #pragma unroll
       for (int e = 1; e < PE; ++e) mx = fmaxf(mx, sv[j][e]);
       mx = pair32_max(pair16_max(mx));
       mnew[j] = fmaxf(mrun[j], mx);
-      rise |= mnew[j] > mrun[j] + ATTN_RESCALE_LAG;
-    }
-    if (__any(rise)) {
+      return mnew[j] > mrun[j] + ATTN_RESCALE_LAG;
+    };
+    auto rescale = [&](int j) {
+      const float alpha = __builtin_amdgcn_exp2f(mrun[j] - mnew[j]);
+      mrun[j] = mnew[j];
+      lrun[j] *= alpha;
 #pragma unroll
-      for (int j = 0; j < NQW; ++j) {
-        const float alpha = __builtin_amdgcn_exp2f(mrun[j] - mnew[j]);
-        mrun[j] = mnew[j];
-        lrun[j] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DH / 16; ++dt) acc[j][dt] *= alpha;
-      }
-    }
-    u32x4 pop[NQW][QP];
-#pragma unroll
-    for (int j = 0; j < NQW; ++j) {
+      for (int dt = 0; dt < DH / 16; ++dt) acc[j][dt] *= alpha;
+    };
+    // probabilities of tile j as the hi/lo operand pair; the row sums
+    auto probs = [&](int j) {
       float pj[PE];
 #pragma unroll
       for (int e = 0; e < PE; ++e) pj[e] = __builtin_amdgcn_exp2f(sv[j][e] - mrun[j]);
       lrun[j] += ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7]));
       split_probs_pk(pj, pop[j][0], pop[j][1]);
+    };
+    // O^T += V^T P^T of tile j
+    auto pv = [&](int j) {
+#pragma unroll
+      for (int dt = 0; dt < DH / 16; ++dt)
+#pragma unroll
+        for (int qp = 0; qp < QP; ++qp) acc[j][dt] = mma16<T>(va[dt], pop[j][qp], acc[j][dt]);
+    };
+
+    // scores of every query tile of the wave with all K operands read first, the V
+    // operands read while the softmax runs, then P V
+    read_k();
+#pragma unroll
+    for (int j = 0; j < NQW; ++j) {
+      if (j == 0 || j < nj) {
+        scores(j);
+        if (j == 0) {
+          __builtin_amdgcn_sched_group_barrier(0x100, DH / KS * NH, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, DH / KS * QP * NH, 0);
+        }
+      } else {
+#pragma unroll
+        for (int hv = 0; hv < NH; ++hv) sc[j][hv] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
-    // ---- O^T += V^T P^T
+    read_v();
+    bool rise = false;
+#pragma unroll
+    for (int j = 0; j < NQW; ++j) rise |= row_max(j);
+    if (__any(rise)) {
+#pragma unroll
+      for (int j = 0; j < NQW; ++j) rescale(j);
+    }
+#pragma unroll
+    for (int j = 0; j < NQW; ++j) probs(j);
 #pragma unroll
     for (int j = 0; j < NQW; ++j)
-      if (j == 0 || j < nj)
-#pragma unroll
-        for (int dt = 0; dt < DH / 16; ++dt)
-#pragma unroll
-          for (int qp = 0; qp < QP; ++qp) acc[j][dt] = mma16<T>(va[dt], pop[j][qp], acc[j][dt]);
+      if (j == 0 || j < nj) pv(j);
   }
   __syncthreads();   // every wave is done with the ring (its memory is the merge scratch)
 
@@ -830,7 +843,7 @@ void attn_dma(AttnArgs a) {
   }
   if (!fused || direct) return;
   __shared__ int is_last;
-  const int qg = blockIdx.z % a.n_qg;
+  const int qg = blockIdx.y % a.n_qg;
   if (!arrive_last(a.sem + ((size_t)b * a.Hkv + g) * a.n_qg + qg, a.n_splits, &is_last)) return;
   if (a.n_splits <= 8) attn_merge8<T, DH>(a, b, g, q_base * 16, min(nq, (q_base + NW * NQW) * 16));
   else attn_merge<T, DH>(a, b, g, q_base * 16, min(nq, (q_base + NW * NQW) * 16), (float*)ring);
@@ -1255,7 +1268,11 @@ static hipError_t launch_attn_t(AttnArgs a, hipStream_t s, hipEvent_t ev0, hipEv
   }
   int nqw, nw;
   a.n_qg = attn_shape<T, DH>(NQT, a.B * a.Hkv, &nqw, &nw);
-  dim3 grid(a.n_splits, a.Hkv, a.B * a.n_qg);
+  // workgroups go out in order of their linear index, x fastest: kv heads, then
+  // (sequence, query group), then key splits, so every sequence's first split (the
+  // longest) starts before any later split and the short ones fill the tail; the
+  // workgroups of one kv head land on one XCD (index mod 8) and share its L2
+  dim3 grid(a.Hkv, a.B * a.n_qg, a.n_splits);
   if constexpr (sizeof(T) == 2) {
     constexpr int R = SDV_ATTN_RING;
     if (nw == 4) {

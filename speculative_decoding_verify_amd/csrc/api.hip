@@ -54,6 +54,13 @@ constexpr int TARGET_WG_ATTN = SDV_ATTN_TARGET_WG;  // register path, measured: 
 #define SDV_ATTN_DMA_TARGET_WG 768
 #endif
 constexpr int TARGET_WG_ATTN_DMA = SDV_ATTN_DMA_TARGET_WG;
+// ... and when the (sequence, kv head, query group) triples alone fill those slots: the
+// grid goes out split by split, longest first, so more (shorter) splits make the tail
+// finer (batched 64-row pass: 987 -> 960 us per layer at four splits instead of three)
+#ifndef SDV_ATTN_DMA_WIDE_TARGET_WG
+#define SDV_ATTN_DMA_WIDE_TARGET_WG 6144
+#endif
+constexpr int TARGET_WG_ATTN_DMA_WIDE = SDV_ATTN_DMA_WIDE_TARGET_WG;
 constexpr long long ATTN_MERGE_MAX_READ = 32768;  // floats of partial output one merging workgroup reads
 
 struct GemmPlan {
@@ -194,7 +201,9 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
   const int NQT = cdiv(T * p.G, 16);
   int rows_per_group = 0;
   p.n_qg = attn_query_groups(p.bf, dh, T, p.G, B * Hkv, &rows_per_group);
-  const int target = (p.bf && !attn_uses_reg_path(true, dh, NQT)) ? TARGET_WG_ATTN_DMA : TARGET_WG_ATTN;
+  const bool dma = p.bf && !attn_uses_reg_path(true, dh, NQT);
+  const long long groups = (long long)B * Hkv * p.n_qg;
+  const int target = !dma ? TARGET_WG_ATTN : groups >= TARGET_WG_ATTN_DMA ? TARGET_WG_ATTN_DMA_WIDE : TARGET_WG_ATTN_DMA;
   int ns = cdiv(target, (long long)B * Hkv * p.n_qg);
   ns = std::max(1, std::min({ns, ATTN_MAX_SPLITS, cdiv(nkeys, KT)}));
   ns = std::max(ns, cdiv(nkeys, 255 * KT));  // a split spans at most 511 pages (staged in LDS)

@@ -55,7 +55,21 @@ KERNEL_SOURCES = {"qkv": GEMM_SOURCES, "o": GEMM_SOURCES, "gate_up": GEMM_SOURCE
                   "lm_head": GEMM_SOURCES, "codebook_head": GEMM_SOURCES, "attention": ATTN_SOURCES,
                   "row_stats": SAMPLE_SOURCES}
 TRAFFIC = [
-    # {"workload": ..., "kernel": ..., "sha256": ..., "fetch_kib": ..., "write_kib": ...}
+    # rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, on `bench.py --workload <w> --steps 2
+    # --warmup 1 --no-cpu-baseline` (--no-drafting for the single-sequence passes);
+    # means over every dispatch of the kernel
+    {"workload": "c5-codebook", "kernel": "attention",   # sdv::attn_dma<128, 1, 4, 3>, 216 dispatches
+     "sha256": "099fb39744e8f394cfc7a3792db9dfb1c4bb2ebf894110f2e49d424fc5e22f97",
+     "fetch_kib": 1854498.87, "write_kib": 250548.06},
+    {"workload": "8b-bf16", "kernel": "gate_up",         # sdv::gemm_stream<bf16, 5, 6, 2, SWIGLU>, 180 dispatches
+     "sha256": "912e85a8171080bdcace0b39cc145c6cc40889028083e0dc5599734cc4adba9c",
+     "fetch_kib": 103030.12, "write_kib": 3168.0},
+    {"workload": "1.7b-bf16", "kernel": "gate_up",       # sdv::gemm_stream<bf16, 3, 4, 2, SWIGLU>, 120 dispatches
+     "sha256": "912e85a8171080bdcace0b39cc145c6cc40889028083e0dc5599734cc4adba9c",
+     "fetch_kib": 34365.67, "write_kib": 1344.0},
+    {"workload": "sample", "kernel": "row_stats",        # sdv::spec_row_stats_kernel, 5 dispatches
+     "sha256": "ab157bca86e5d987d8d1460d146bd1c7c5e72e6835f776c196cdb54791f3ee28",
+     "fetch_kib": 284713.35, "write_kib": 60.03},
 ]
 
 
@@ -310,8 +324,14 @@ def bench_verify(args, wl, w=None, model=None):
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
-    drafts, branch, drafting = draft_under_silence(sdv, model, kv, C, L_a, gamma, wl.silence_id, wl.n_branch,
-                                                   reps=5)
+    if args.no_drafting:
+        # uniform draft tokens: the verify pass has the same shapes and kernels
+        drafts = uniform_tokens(gamma, sh.vocab, wl.seed + 5000, "draft")
+        branch = uniform_tokens(wl.n_branch, sh.vocab, wl.seed + 5001, "branch") if wl.n_branch else []
+        drafting = None
+    else:
+        drafts, branch, drafting = draft_under_silence(sdv, model, kv, C, L_a, gamma, wl.silence_id, wl.n_branch,
+                                                       reps=5)
     parent = wl.parent()
     audio = np.full(L_a, wl.silence_id, dtype=np.int32) if args.scenario == "silence" else \
         uniform_tokens(L_a, sh.vocab, wl.seed + 4000, "audio")
@@ -703,6 +723,9 @@ def main():
     ap.add_argument("--scenario", default="silence", choices=["silence", "random"])
     ap.add_argument("--graph", action="store_true", help="replay the step from a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-drafting", action="store_true",
+                    help="verify uniform draft tokens instead of drafting them on the GPU first (same pass shapes; "
+                         "for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 256 MiB device-to-device copy (counter calibration) and exit")
     args = ap.parse_args()

@@ -545,15 +545,14 @@ template <int DH> SDV_DEV int kswz(int k) {
   else return ((k >> 1) & 1) | (((k >> 3) & 3) << 1);
 }
 
-// waves per SIMD the register budget of attn_dma aims at: one query tile per wave keeps
-// three (dh 128) or four (dh 64) waves resident, more tiles fewer
-template <int DH, int NQW> constexpr int dma_waves() {
-  return DH == 128 ? (NQW == 1 ? 3 : 2) : (NQW == 1 ? 4 : NQW == 2 ? 3 : 2);
-}
+// waves per SIMD the register budget of attn_dma aims at (one query tile per wave):
+// three at dh 128, four at dh 64
+template <int DH> constexpr int dma_waves() { return DH == 128 ? 3 : 4; }
 
 template <int DH, int NQW, int NW, int R>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(dma_waves<DH, NQW>())))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(dma_waves<DH>())))
 void attn_dma(AttnArgs a) {
+  static_assert(NQW == 1, "one query tile per wave");
   using T = bf16;
   using G = DmaTile<DH>;
   constexpr int KT = 32, VE = 8, KS = 32, PE = 8, NH = 2, QP = 2;
@@ -620,9 +619,13 @@ void attn_dma(AttnArgs a) {
   // the two physical pages of tile t of the split in one LDS read (k_begin is a
   // multiple of 32, so the pair is 8-byte aligned)
   auto pages_of = [&](int t) { return *(const int2*)&sPage[2 * t]; };
+  // bit k set: the k-th newest issued tile had a page outside the table, so the wave
+  // issued fewer loads for it than LPW and the counter waits must not count on them
+  uint32_t short_tiles = 0;
   auto issue = [&](int2 ph, int slot) {
     char* dst = ring + slot * G::TILE_B;
     const int ph0 = __builtin_amdgcn_readfirstlane(ph.x), ph1 = __builtin_amdgcn_readfirstlane(ph.y);
+    short_tiles = (short_tiles << 1) | ((ph0 < 0 || ph1 < 0) ? 1u : 0u);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int part = ld_part[i];
@@ -661,9 +664,10 @@ void attn_dma(AttnArgs a) {
   // tile t - 1 (with the dead values of the tile holding the sequence end zeroed).
   // `later` tiles issued after t may stay in flight: their loads are the wave's newest,
   // so waiting until at most later * LPW loads are outstanding leaves exactly those
-  // (later = R - 2, else 0: wait for all)
+  // (later = R - 2, else 0: wait for all; also 0 when one of those tiles had a page
+  // outside the table, whose loads were not issued)
   auto land = [&](int t, int later) {
-    if (later == R - 2) vmem_lds_wait<(R - 2) * LPW>();
+    if (later == R - 2 && (short_tiles & ((1u << (R - 2)) - 1u)) == 0u) vmem_lds_wait<(R - 2) * LPW>();
     else vmem_lds_wait<0>();
     bare_barrier();
     const int kt0 = k_begin + t * KT;
@@ -1190,9 +1194,10 @@ template <typename T, int DH> constexpr int attn_cap() {
 
 template <typename T, int DH>
 int attn_shape(int NQT, int heads, int* nqw_out, int* nw_out) {
-  constexpr int CAP = attn_cap<T, DH>();
-  // bf16 stages K/V by LDS DMA, whose wave-loads split evenly over 4 or 8 waves
+  // bf16 stages K/V by LDS DMA, whose wave-loads split evenly over 4 or 8 waves, one
+  // query tile per wave (its registers leave room for three waves per SIMD)
   constexpr bool DMA = sizeof(T) == 2;
+  constexpr int CAP = DMA ? 1 : attn_cap<T, DH>();
   // query groups of at most 8 waves x CAP tiles -- of at most 4 tiles (one per SIMD)
   // when the (sequence, kv head) pairs alone fill the GPU (heads >= 256: no key splits
   // are needed, and a shorter busiest SIMD beats reading the keys and values once per
@@ -1275,27 +1280,10 @@ static hipError_t launch_attn_t(AttnArgs a, hipStream_t s, hipEvent_t ev0, hipEv
   dim3 grid(a.Hkv, a.B * a.n_qg, a.n_splits);
   if constexpr (sizeof(T) == 2) {
     constexpr int R = SDV_ATTN_RING;
-    if (nw == 4) {
-      switch (nqw) {
-        case 1: launch_ev(attn_dma<DH, 1, 4, R>, grid, 256, s, ev0, ev1, a); break;
-        case 2: launch_ev(attn_dma<DH, 2, 4, R>, grid, 256, s, ev0, ev1, a); break;
-        case 3:
-          if constexpr (attn_cap<T, DH>() >= 3) { launch_ev(attn_dma<DH, 3, 4, R>, grid, 256, s, ev0, ev1, a); break; }
-          return hipErrorInvalidValue;
-        default: return hipErrorInvalidValue;
-      }
-    } else if (nw == 8) {
-      switch (nqw) {
-        case 1: launch_ev(attn_dma<DH, 1, 8, R>, grid, 512, s, ev0, ev1, a); break;
-        case 2: launch_ev(attn_dma<DH, 2, 8, R>, grid, 512, s, ev0, ev1, a); break;
-        case 3:
-          if constexpr (attn_cap<T, DH>() >= 3) { launch_ev(attn_dma<DH, 3, 8, R>, grid, 512, s, ev0, ev1, a); break; }
-          return hipErrorInvalidValue;
-        default: return hipErrorInvalidValue;
-      }
-    } else {
-      return hipErrorInvalidValue;
-    }
+    if (nqw != 1) return hipErrorInvalidValue;
+    if (nw == 4) launch_ev(attn_dma<DH, 1, 4, R>, grid, 256, s, ev0, ev1, a);
+    else if (nw == 8) launch_ev(attn_dma<DH, 1, 8, R>, grid, 512, s, ev0, ev1, a);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
   }
   dim3 block(64 * nw);

@@ -352,6 +352,28 @@ def test_paged_placement_is_bit_identical():
         assert np.array_equal(g["hidden"], outs[0]["hidden"])
 
 
+@pytest.mark.parametrize("shape", [MINI_BF16_D128, MINI_BF16], ids=["dh128", "dh64"])
+def test_tight_block_table_tail_tile(shape):
+    """LDS-DMA attention (more query tiles than the register path takes) where the
+    longest sequence ends in the first page of its last 32-key tile and the block table
+    has no entry for that tile's second page: the staging copies the missing page from
+    the zero page, so every wave issues the same loads for every tile and the
+    load-counter waits stay exact.  The logits match the oracle, and a table with room
+    to spare gives the same results bit for bit."""
+    w = make_weights(shape, seed=631)
+    lens, T, L_a = (40, 75), 30, 6          # 75 + 30 = 105 = 3 * 32 + 9 keys: page 7 of 7 is missing
+    print(f"case {shape.name} lens={lens} T={T}", flush=True)
+    kvh = make_random_kv(shape, list(lens), capacity=max(lens) + T, seed=632)
+    toks = _tokens(2, T, shape.vocab, 633)
+    model = sdv.DeviceModel(w)
+    g, o, ver, kv = run_pair(w, kvh, toks, L_a, model=model, extra_capacity=0)
+    assert 2 * ((max(lens) + T - 1) // 32) + 1 == kv.max_blocks   # the last tile's second page has no entry
+    compare_logits(shape, g, o)
+    g2, _, _, _ = run_pair(w, kvh, toks, L_a, model=model, extra_capacity=48)
+    assert np.array_equal(g["logits"], g2["logits"])
+    assert np.array_equal(g["hidden"], g2["hidden"])
+
+
 def test_device_errors_are_reported():
     shape = MINI_BF16
     w = make_weights(shape, seed=701)

@@ -59,8 +59,8 @@ TRAFFIC = [
     # --warmup 1 --no-cpu-baseline` (--no-drafting for the single-sequence passes);
     # means over every dispatch of the kernel
     {"workload": "c5-codebook", "kernel": "attention",   # sdv::attn_dma<128, 1, 4, 3>, 216 dispatches
-     "sha256": "099fb39744e8f394cfc7a3792db9dfb1c4bb2ebf894110f2e49d424fc5e22f97",
-     "fetch_kib": 1854498.87, "write_kib": 250548.06},
+     "sha256": "475915ce153a3072d06ece9e77468f799e98269fb817377e149bf333992c8ef8",
+     "fetch_kib": 1829124.76, "write_kib": 249954.30},
     {"workload": "8b-bf16", "kernel": "gate_up",         # sdv::gemm_stream<bf16, 5, 6, 2, SWIGLU>, 180 dispatches
      "sha256": "912e85a8171080bdcace0b39cc145c6cc40889028083e0dc5599734cc4adba9c",
      "fetch_kib": 103030.12, "write_kib": 3168.0},

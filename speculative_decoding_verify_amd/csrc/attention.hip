@@ -29,6 +29,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace sdv {
 
@@ -1121,9 +1122,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 // the chunk takes DH / 4 threads, each owning 4 consecutive output values; a thread
 // loads every split's (m, l) pair and 16-byte output chunk in one round, then sums
 // the splits in order.
-template <typename T, int DH>
+// MAXS: registers for that many splits (the launch takes the smallest of 8, 16, 32
+// that holds n_splits; room for 32 would cost two waves per SIMD)
+template <typename T, int DH, int MAXS>
 __global__ __launch_bounds__(256) void attn_combine(CombineArgs a) {
-  constexpr int MAXS = 32;
   constexpr int TPI = DH / 4;   // threads per item
   const int item = blockIdx.x * (256 / TPI) + threadIdx.x / TPI;
   const int c4 = threadIdx.x % TPI;
@@ -1311,12 +1313,21 @@ hipError_t launch_combine(bool is_bf16, const CombineArgs& a, hipStream_t s, hip
   if (a.n_splits > 32) return hipErrorInvalidValue;
   const int items = a.B * a.T * a.H;
   const int grid = (items + 256 / (a.dh / 4) - 1) / (256 / (a.dh / 4));
+  auto go = [&](auto t_tag, auto dh_tag) {
+    using T = decltype(t_tag);
+    constexpr int DH = decltype(dh_tag)::value;
+    if (a.n_splits <= 8) launch_ev(attn_combine<T, DH, 8>, grid, 256, s, nullptr, ev1, a);
+    else if (a.n_splits <= 16) launch_ev(attn_combine<T, DH, 16>, grid, 256, s, nullptr, ev1, a);
+    else launch_ev(attn_combine<T, DH, 32>, grid, 256, s, nullptr, ev1, a);
+  };
+  using D64 = std::integral_constant<int, 64>;
+  using D128 = std::integral_constant<int, 128>;
   if (is_bf16) {
-    if (a.dh == 64) launch_ev(attn_combine<bf16, 64>, grid, 256, s, nullptr, ev1, a);
-    else launch_ev(attn_combine<bf16, 128>, grid, 256, s, nullptr, ev1, a);
+    if (a.dh == 64) go(bf16{}, D64{});
+    else go(bf16{}, D128{});
   } else {
-    if (a.dh == 64) launch_ev(attn_combine<float, 64>, grid, 256, s, nullptr, ev1, a);
-    else launch_ev(attn_combine<float, 128>, grid, 256, s, nullptr, ev1, a);
+    if (a.dh == 64) go(float{}, D64{});
+    else go(float{}, D128{});
   }
   return hipGetLastError();
 }

@@ -99,3 +99,49 @@ def test_non_mutual_partner_is_reported_and_row_uses_its_own_head():
     assert (g["err"] & 0x20).all()
     w2, tokens2, rows2, base2, kv2, g_own = _run(shape, [-1, -1, -1], [6, 6, 6], seed=51)
     assert np.array_equal(g["logits"], g_own["logits"])
+
+
+@pytest.mark.parametrize("shape", [CB_BF16, CB_F32], ids=lambda s: s.name)
+def test_guided_greedy_drafts_are_accepted_in_full(shape):
+    """Drafts that are the guided greedy continuation (the oracle's codebook-0 argmax of
+    the merged logits, one token at a time from the audio chunk) are accepted in full on
+    both rows of every pair, with the corrected token equal to the oracle's next one."""
+    partner = [1, 0, 3, 2]
+    ctx = [9, 9, 20, 20]
+    L_a, gamma, seed = 4, 5, 61
+    w = make_weights(shape, seed=seed)
+    B = len(partner)
+    base = shape.vocab - shape.n_codebooks * shape.codebook_size
+    kv_host = make_random_kv(shape, ctx, capacity=max(ctx) + L_a + gamma, seed=seed + 1)
+    tokens = np.empty((B, L_a), dtype=np.int32)
+    for b in range(B):
+        tokens[b] = base + uniform_tokens(L_a, shape.codebook_size, seed * 100 + min(b, partner[b]), "cbt")
+    mode = mode_of(shape)
+    near = np.zeros(B, dtype=bool)   # a guided decision along the drafts within the margin band
+    for i in range(gamma + 1):
+        o = cfg.verify_codebook(w, odec.Cache(kv_host.k, kv_host.v), tokens, None, [tokens.shape[1] - 1], partner,
+                                2.0, base, mode)
+        near |= o["margin"][:, 0] < MARGIN_FLAG
+        nxt = o["token"][:, 0].astype(np.int32)
+        if i == gamma:
+            break
+        tokens = np.concatenate([tokens, nxt[:, None]], axis=1)
+    T = L_a + gamma
+    rows = list(range(L_a - 1, T))
+    model = sdv.DeviceModel(w)
+    kv = sdv.PagedKV(shape, B, max(ctx) + T + 16)
+    kv.load(kv_host)
+    ver = sdv.Verifier(model, kv, T, L_a, rows, max_ctx=max(ctx), want_logits=True, head=sdv.HEAD_CODEBOOK,
+                       cfg_partner=partner, cfg_w=2.0)
+    ver.set_tokens(tokens)
+    res = ver.forward()
+    acc = sdv.accept_greedy(B, T, L_a, ver.tokens, None, ver.logit_rows, res.argmax)
+    torch.cuda.synchronize()
+    n, nx = acc["n"].cpu().numpy(), acc["next"].cpu().numpy()
+    assert near.sum() <= 1, f"{near.sum()} rows of {B} within the margin band"
+    for c, u in ((0, 1), (2, 3)):
+        assert n[c] == n[u] and nx[c] == nx[u]
+        if not (near[c] or near[u]):
+            assert n[c] == gamma, (c, n[c])
+            assert nx[c] == nxt[c], (c, nx[c], nxt[c])
+    print(f"{shape.name}: accepted {list(n)} of {gamma}, near {list(near)}")

@@ -1009,7 +1009,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       for (int e = 1; e < PE; ++e) mx = fmaxf(mx, sv[j][e]);
       mx = pair32_max(pair16_max(mx));
       mnew[j] = fmaxf(mrun[j], mx);
-      rise |= mnew[j] > mrun[j];
+      rise |= mnew[j] > mrun[j] + ATTN_RESCALE_LAG;   // the lazy reference point of attn_dma
     }
     if (__any(rise)) {
 #pragma unroll
@@ -1023,16 +1023,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     }
 #pragma unroll
     for (int j = 0; j < NQT; ++j) {
-      float p[PE], ps = 0.f;
+      float p[PE];
 #pragma unroll
-      for (int e = 0; e < PE; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(sv[j][e] - mrun[j]);
-        ps += p[e];
+      for (int e = 0; e < PE; ++e) p[e] = __builtin_amdgcn_exp2f(sv[j][e] - mrun[j]);
+      if constexpr (PE == 8) lrun[j] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      else {
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < PE; ++e) ps += p[e];
+        lrun[j] += ps;
       }
-      lrun[j] += ps;
       if constexpr (BF) {
         u32x4 phi, plo;
-        split_probs_fast(p, phi, plo);
+        split_probs_pk(p, phi, plo);
 #pragma unroll
         for (int dt = 0; dt < DH / 16; ++dt) {
           acc[j][dt] = mma16<T>(vo[dt], phi, acc[j][dt]);

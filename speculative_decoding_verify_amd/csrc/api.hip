@@ -45,6 +45,18 @@ int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 // target workgroups per launch (256 compute units)
 constexpr int TARGET_WG_GEMM = 256;
+// workgroups of the column-split GEMM resident at once
+#ifndef SDV_WIDE_SLOTS
+#define SDV_WIDE_SLOTS 256
+#endif
+constexpr int WIDE_SLOTS = SDV_WIDE_SLOTS;
+// row tiles from which the column-split kernel replaces gemm_stream (at 3 row tiles,
+// 41 rows of the 1.7B shape, gemm_stream measured faster on every projection; at 5,
+// 65 rows of the 8B shape, the column-split kernel on o, down and q/k/v)
+#ifndef SDV_WIDE_MIN_MT
+#define SDV_WIDE_MIN_MT 4
+#endif
+constexpr int WIDE_MIN_MT = SDV_WIDE_MIN_MT;
 #ifndef SDV_ATTN_TARGET_WG
 #define SDV_ATTN_TARGET_WG 256
 #endif
@@ -105,6 +117,43 @@ GemmPlan plan_gemm(int M, int N, int K, bool bf, int epi) {
   }
   p.MT = std::max(1, cdiv(M, 16));
   p.row_blocks = 1;
+#ifndef SDV_GEMM_STREAM_ONLY
+  if (p.MT >= WIDE_MIN_MT && epi != EPI_LOGITS) {
+    // the column-split kernel (4 NT tiles per workgroup, the activation steps fetched
+    // once per workgroup): take the tiles per wave, the K splits and the way the splits
+    // meet that minimise an estimate of the launch time.  A compute unit moves its
+    // workgroups' weight tiles, activation steps and partial tiles at about 50 GB/s
+    // (the measured rate of the weight-streaming kernels through one CU's vector memory
+    // path), the whole launch at most at the weights' HBM rate.  Split partials are
+    // read back once: by the residual-norm kernel after o and down, by gemm_finish
+    // (one dependent launch more) after q/k/v and SwiGLU, whose epilogues otherwise
+    // run in the workgroup (one split).
+    const int NB = p.MT * (bf ? 2 : 1);   // KB of activations per k step
+    const bool fin = epi == EPI_QKV || epi == EPI_SWIGLU;
+    const double cu_bw = 50e3, hbm_bw = 7.2e6, l2_bw = 5e6, finish_us = 5.0;   // bytes per us
+    double best = 1e300;
+    for (int nt = fin ? 2 : 1; nt <= 4; ++nt) {
+      const int ncg = cdiv(ntiles, 4 * nt);
+      const double tile_b = 16.0 * p.MT * 64 * nt * 4;
+      for (int S = 1; S <= 16; ++S) {
+        const int spp = cdiv(steps, S), Se = cdiv(steps, spp);
+        if (Se != S || (S > 1 && spp < 4)) continue;
+        const long long wgs = (long long)ncg * S;
+        const double per_wg = (4.0 * nt * spp + (double)spp * NB) * 1024 + (S > 1 || !fin ? tile_b : 0.0);
+        const double t0 = std::max((double)cdiv(wgs, WIDE_SLOTS) * per_wg / cu_bw, (double)ntiles * 16 * K * (bf ? 2 : 4) / hbm_bw);
+        const double t = t0 + (fin && S == 1 ? 0.0 : (double)S * M * N * 4 / l2_bw + (fin ? finish_us : 0.0));
+        if (t < best - 1e-9) {
+          best = t;
+          p.cfg = GemmCfg{nt, 3, false, true, fin && S > 1 ? 1 : 0};
+          p.ncg = ncg;
+          p.spp = spp;
+          p.S = S;
+        }
+      }
+    }
+    return p;
+  }
+#endif
   // configurations measured on the decoder shapes: few tiles per workgroup and a
   // deeper register ring where the grid would otherwise be small (q/k/v and o
   // projections), more tiles per workgroup as the row tiles grow
@@ -194,6 +243,9 @@ Plan make_plan(const sdv_model* m, int B, int T, int R, int max_ctx) {
   p.S = m->n_codebooks > 0 ? m->n_codebooks : 0;
   if (p.S) p.cb = plan_gemm(p.Mr + p.S, m->codebook_size, d, p.bf, EPI_PARTIAL);
   p.part_floats = std::max((size_t)p.o.S * p.M * d, (size_t)p.dn.S * p.M * d);
+  // column-split q/k/v and SwiGLU launches sum their split partials in the finish
+  if (p.qkv.cfg.wide && p.qkv.S > 1) p.part_floats = std::max(p.part_floats, (size_t)p.qkv.S * p.M * (qd + 2 * kd));
+  if (p.gu.cfg.wide && p.gu.S > 1) p.part_floats = std::max(p.part_floats, (size_t)p.gu.S * p.M * 2 * F);
   // attention: split the keys so that the grid fills the GPU (the register path
   // has four waves per workgroup, each streaming its own key tiles)
   const int KT = p.bf ? 32 : 16;
@@ -258,19 +310,30 @@ struct ProfEvents {
 };
 
 // one weight-streaming GEMM launch; `a` carries the operands and epilogue targets
+// one weight-streaming GEMM launch; `a` carries the operands and epilogue targets (the
+// split-partials buffer in a.out, also for the q/k/v and SwiGLU launches of the
+// column-split kernel, whose finish applies their epilogue)
 sdv_status run_gemm(ProfEvents& pe, const Plan& P, const GemmPlan& g, GemmArgs a, hipStream_t s) {
   a.steps_per_split = g.spp;
   a.out_split_stride = (long long)a.M * a.N;
   a.ldo = a.N;
   a.ldl = a.N;
   a.n_groups = g.ncg;
+  a.n_split = g.S;
   const dim3 grid = g.cfg.tiled ? dim3(g.row_blocks, g.S, g.ncg) : dim3(g.ncg, g.S, g.row_blocks);
   const bool prof = pe.ev && pe.next < pe.n_pairs;
-  if (prof)
-    SDV_LAUNCH(launch_gemm(P.bf, g.cfg, g.MT, g.epi, grid, a, s, (hipEvent_t)pe.ev[2 * pe.next],
-                           (hipEvent_t)pe.ev[2 * pe.next + 1]));
-  else
-    SDV_LAUNCH(launch_gemm(P.bf, g.cfg, g.MT, g.epi, grid, a, s));
+  hipEvent_t e0 = prof ? (hipEvent_t)pe.ev[2 * pe.next] : nullptr;
+  hipEvent_t e1 = prof ? (hipEvent_t)pe.ev[2 * pe.next + 1] : nullptr;
+  if (g.cfg.wide && g.epi != EPI_PARTIAL && g.cfg.NTF == 0 && g.S > 1)
+    return fail(SDV_ERR_LAUNCH, "column-split epilogue %d planned with %d K splits", g.epi, g.S);
+  if (g.cfg.wide && g.cfg.NTF > 0) {
+    if (!a.out) return fail(SDV_ERR_LAUNCH, "split partials buffer missing");
+    SDV_LAUNCH(launch_gemm(P.bf, g.cfg, g.MT, EPI_PARTIAL, grid, a, s, e0, nullptr));
+    const int ntiles = cdiv(a.N, 16);
+    SDV_LAUNCH(launch_gemm_finish(P.bf, g.cfg, g.MT, g.epi, dim3(cdiv(ntiles, g.cfg.NTF)), a, s, e1));
+  } else {
+    SDV_LAUNCH(launch_gemm(P.bf, g.cfg, g.MT, g.epi, grid, a, s, e0, e1));
+  }
   if (pe.ev) ++pe.next;
   return SDV_OK;
 }
@@ -487,6 +550,7 @@ sdv_status verify_forward_impl(const sdv_model* m, const sdv_kv* kv, const sdv_v
       GemmArgs a = gemm_args(act, M, L.wqkv, qd + 2 * kd, d);
       a.pair_n = dh / 2;
       a.qkv = QkvEpi{q, kp, vp, kv_dst, rope, B, T, H, Hkv, (float)(1.4426950408889634 / sqrt((double)dh))};
+      a.out = part;
       if ((st = run_gemm(pe, P, P.qkv, a, s)) != SDV_OK) return st;
     }
     {
@@ -518,6 +582,7 @@ sdv_status verify_forward_impl(const sdv_model* m, const sdv_kv* kv, const sdv_v
       GemmArgs a = gemm_args(act, M, L.wgu, 2 * F, d);
       a.pair_n = F;
       a.out_act = h;
+      a.out = part;
       if ((st = run_gemm(pe, P, P.gu, a, s)) != SDV_OK) return st;
     }
     {

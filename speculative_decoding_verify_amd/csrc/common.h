@@ -181,6 +181,16 @@ SDV_DEV void bare_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// a workgroup barrier after the wave's own LDS accesses have completed (so its LDS
+// writes are visible to the workgroup behind it); vector memory loads stay in flight
+SDV_DEV void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((3 << 14) | (7 << 4) | 15);   // lgkmcnt(0); vmcnt 63 and expcnt 7: no wait
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Every thread's stores are complete, then thread 0 counts the workgroup in on
 // `counter` (zero before the launch).  True in all threads of the workgroup that
 // arrives n-th (last).  `flag` is an int in LDS.

@@ -34,6 +34,8 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -487,6 +489,232 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Column-split weight-streaming GEMM for few rows (M <= 80).  In gemm_stream the four
+// waves of a workgroup split the k range of one weight slice, so every workgroup
+// fetches the activation operand of its whole k range for only NT weight tiles; with
+// bf16 pairs at 65 rows that is 10 KB of activations per 1 KB weight tile step, more
+// bytes through each CU than the weights.  Here the waves split the columns: wave w
+// owns NT packed tiles of the workgroup's 4 NT, over the workgroup's k range, so one
+// copy of a k step's activation blocks serves all four waves.  The threads fetch the
+// step's blocks (16 bytes each, P steps ahead into registers) and store them to an LDS
+// double buffer; each wave reads them back in operand order and streams its own weight
+// tiles through a register ring D steps deep.  One LDS barrier per k step.
+// Grid: x = column groups of 4 NT tiles, y = splits of K.  Epilogues: PARTIAL (the
+// split's fp32 partial sums, stored from the accumulators); the others take the whole
+// K in one workgroup (one split) and go through an LDS tile to the shared epilogue.
+// A q/k/v or SwiGLU launch with K splits writes partials with PARTIAL and gemm_finish
+// sums them.  (Handing the partials to the last workgroup of each column group
+// instead, through device-coherent stores and an arrival counter, measured slower on
+// the 8B gate/up projection: 61 against 51 us with the finish launch.)
+
+template <int... I, typename F>
+SDV_DEV void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+SDV_DEV void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
+constexpr int cgcd(int x, int y) { return y == 0 ? x : cgcd(y, x % y); }
+
+#ifndef SDV_WIDE_P
+#define SDV_WIDE_P 2
+#endif
+constexpr int WIDE_P = SDV_WIDE_P;
+
+template <typename T, int MT, int NT, int D, int EPI>
+__global__ __launch_bounds__(256) void gemm_wide(GemmArgs a) {
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int KS = BF ? 32 : 16;
+  constexpr int AL = BF ? 2 : 1;
+  constexpr int NB = MT * AL;                 // 1 KB activation blocks per k step
+  constexpr int NCH = (NB * 64 + 255) / 256;  // 16-byte chunks of a step per thread
+  constexpr int P = WIDE_P;                   // k steps of activation loads ahead
+  constexpr int TW = 4 * NT;                  // packed tiles of the workgroup
+  // register ring slots, staging slots and LDS buffers are indexed by compile-time
+  // step residues
+  constexpr int U2 = D * 2 / cgcd(D, 2);
+  constexpr int U = U2 * P / cgcd(U2, P);
+  static_assert(U % P == 0, "unroll covers the staging ring");
+  constexpr int E = (D - 1 > P + 1) ? D - 1 : P + 1;   // look-ahead of a step's issues
+  // a buffer holds every thread's NCH chunks: chunks past the NB blocks land in a pad
+  // that is never read, so no load or store of the staging path takes a branch
+  __shared__ __attribute__((aligned(16))) char abuf[2][NCH * 256 * 16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, lg = lane >> 4;
+  const int cg = blockIdx.x, sp = blockIdx.y;
+  const int ksteps = a.K / KS;
+  const int s0 = sp * a.steps_per_split;
+  const int nk = max(0, min(ksteps, s0 + a.steps_per_split) - s0);
+  const int ntiles = (a.N + 15) >> 4;
+  const int row_tiles = (a.M + 15) >> 4;
+
+  // this wave's weight tiles (past the last tile: the last one again; its columns are
+  // not stored): lane's 16 bytes at step s0, steps 1 KB apart
+  const char* wp[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int tile = min(cg * TW + wave * NT + t, ntiles - 1);
+    wp[t] = (const char*)a.W + ((size_t)tile * ksteps + s0) * 1024 + lane * 16;
+  }
+  // this thread's activation chunks c = threadIdx.x + 256 i of a step's NB blocks
+  // (block b = row tile * AL + half; steps 64 * KS bytes apart in a row tile); lanes of
+  // rows past M read the last row's chunk, chunks past the blocks the last chunk
+  const char* cp[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    const int cc = min(c, NB * 64 - 1);
+    const int b = cc >> 6, l = cc & 63;
+    const int rt = min(b / AL, row_tiles - 1), h = b % AL;
+    const int rr = min(l & 15, a.M - 1 - rt * 16);
+    cp[i] = (const char*)a.A + ((size_t)rt * ksteps + s0) * (64 * KS) + h * 1024 + ((l >> 4) * 16 + rr) * 16;
+  }
+
+  u32x4 wb[D][NT];
+  u32x4 st[P][NCH];
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto load_w = [&](int j, u32x4 (&dst)[NT]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) dst[t] = ld16_stream(wp[t] + (size_t)j * 1024);
+  };
+  auto load_a = [&](int j, u32x4 (&dst)[NCH]) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) dst[i] = ld16(cp[i] + (size_t)j * (64 * KS));
+  };
+  auto store_a = [&](const u32x4 (&src)[NCH], int buf) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) *(u32x4*)(&abuf[buf][(threadIdx.x + 256 * i) * 16]) = src[i];
+  };
+  // k step j (j % U == u): issue the loads that run ahead, stage step j + 1 into the
+  // other LDS buffer, multiply step j, then the barrier that publishes step j + 1 and
+  // frees step j's buffer
+  auto step = [&](int j, auto uc, bool guard) {
+    constexpr int u = decltype(uc)::value;
+    if (!guard || j + D - 1 < nk) load_w(j + D - 1, wb[(u + D - 1) % D]);
+    if (!guard || j + 1 < nk) {
+      store_a(st[(u + 1) % P], (u + 1) & 1);
+      if (!guard || j + 1 + P < nk) load_a(j + 1 + P, st[(u + 1) % P]);
+    }
+    // keep the loads ahead of the step's multiplies (the scheduler would sink them
+    // towards their uses, a step later, and shorten the look-ahead)
+    __builtin_amdgcn_sched_barrier(0);
+    // every block of the step read from LDS first, so their latencies overlap
+    const char* blk = &abuf[u & 1][lane * 16];
+    u32x4 av[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) av[b] = *(const u32x4*)(blk + b * 1024);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[b / AL][t] = mma16<T>(av[b], wb[u % D][t], acc[b / AL][t]);
+    lds_barrier();
+  };
+
+#pragma unroll
+  for (int u = 0; u < P; ++u)
+    if (u < nk) load_a(u, st[u]);
+#pragma unroll
+  for (int u = 0; u < D - 1; ++u)
+    if (u < nk) load_w(u, wb[u]);
+  if (nk > 0) {
+    store_a(st[0], 0);
+    if (P < nk) load_a(P, st[0]);
+  }
+  lds_barrier();
+  int j0 = 0;
+  // steady state: every look-ahead of the group is in range, no branches
+  for (; j0 + U - 1 + E < nk; j0 += U) static_for<U>([&](auto uc) { step(j0 + decltype(uc)::value, uc, false); });
+  for (; j0 < nk; j0 += U)
+    static_for<U>([&](auto uc) {
+      if (j0 + decltype(uc)::value < nk) step(j0 + decltype(uc)::value, uc, true);
+    });
+
+  if constexpr (EPI == EPI_PARTIAL) {
+    float* out = a.out + (size_t)sp * a.out_split_stride;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int n = (cg * TW + wave * NT + t) * 16 + r;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = mt * 16 + 4 * lg + v;
+          if (m < a.M && n < a.N) out[(size_t)m * a.ldo + n] = acc[mt][t][v];
+        }
+      }
+  } else {
+    __shared__ float tile[16 * MT][16 * TW + 1];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) tile[mt * 16 + 4 * lg + v][(wave * NT + t) * 16 + r] = acc[mt][t][v];
+    __syncthreads();
+    gemm_epilogue<T, MT, TW, EPI>(a, tile, cg, sp, 0, [&](int, int m, int i) {
+      if constexpr (EPI == EPI_QKV) return QkvItem{a.qkv.rope[(size_t)m * a.pair_n + i], a.qkv.kv_dst[m]};
+      else return QkvItem{};
+    });
+  }
+}
+
+// Split-K finish of a wide q/k/v or SwiGLU launch: rows [0, M) of column group cg (16 NT
+// columns) summed over the a.n_split partials in split order (at most MAXS), then the
+// shared epilogue on the finished tile.  Each thread loads all of its partials before
+// it adds any.  Grid: x = column groups of NT tiles.
+template <typename T, int MT, int NT, int EPI, int MAXS>
+__global__ __launch_bounds__(256) void gemm_finish(GemmArgs a) {
+  constexpr int TC = 16 * NT;
+  constexpr int EPT = MT * NT;   // tile elements per thread (16 MT x 16 NT over 256)
+  __shared__ float tile[16 * MT][TC + 1];
+  const int cg = blockIdx.x;
+  const int S = a.n_split;
+  // q/k/v epilogue inputs of this thread's items (the epilogue's item order), loaded
+  // first so that their latency overlaps the partials'
+  constexpr int QI = EPI == EPI_QKV ? (16 * MT * NT * 8 + 255) / 256 : 1;
+  QkvItem items[QI];
+  if constexpr (EPI == EPI_QKV) {
+    const int half = a.pair_n;
+#pragma unroll
+    for (int u = 0; u < QI; ++u) {
+      const int idx = threadIdx.x + 256 * u;
+      const int m = min(idx / (NT * 8), a.M - 1), pc = idx % (NT * 8);
+      const int i = ((cg * NT + (pc >> 3)) * 8 + (pc & 7)) % half;
+      items[u] = QkvItem{a.qkv.rope[(size_t)m * half + i], a.qkv.kv_dst[m]};
+    }
+  }
+  float v[EPT][MAXS];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int idx = threadIdx.x + 256 * e;
+    const int ml = idx / TC, n = cg * TC + idx % TC;
+    const bool ok = ml < a.M && n < a.N;
+    const float* p = a.out + (size_t)min(ml, a.M - 1) * a.ldo + min(n, a.N - 1);
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) v[e][s] = (ok && s < S) ? p[(size_t)s * a.out_split_stride] : 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int idx = threadIdx.x + 256 * e;
+    float x = v[e][0];
+#pragma unroll
+    for (int s = 1; s < MAXS; ++s) x += v[e][s];
+    tile[idx / TC][idx % TC] = x;
+  }
+  __syncthreads();
+  gemm_epilogue<T, MT, NT, EPI>(a, tile, cg, 0, 0, [&](int u, int, int) { return items[u]; });
+}
+
+// ---------------------------------------------------------------------------
 // Weight packing: packed row n (of n_packed, a multiple of 16) takes source row
 // src_row(n); rows past the sources are zero.  One thread per 16-byte chunk.
 template <typename T>
@@ -584,8 +812,46 @@ static hipError_t launch_tiled(const Launch& L, const GemmArgs& a) {
   return hipGetLastError();
 }
 
+// the column-split kernel: 3 weight steps in flight per wave; NT 1-4 tiles per wave for
+// split partials, 3-4 for the head
+#ifndef SDV_WIDE_D
+#define SDV_WIDE_D 3
+#endif
+constexpr int WIDE_D = SDV_WIDE_D;
+
+template <typename T, int MT, int NT, int EPI>
+static hipError_t launch_wide_one(const Launch& L, const GemmArgs& a) {
+  if (L.ev0 || L.ev1) hipExtLaunchKernelGGL(gemm_wide<T, MT, NT, WIDE_D, EPI>, L.grid, dim3(256), 0, L.s, L.ev0, L.ev1, 0, a);
+  else gemm_wide<T, MT, NT, WIDE_D, EPI><<<L.grid, 256, 0, L.s>>>(a);
+  return hipGetLastError();
+}
+
+template <typename T, int MT, int EPI>
+static hipError_t launch_wide_nt(int NT, const Launch& L, const GemmArgs& a) {
+  if constexpr (EPI == EPI_PARTIAL)
+    if (NT == 1) return launch_wide_one<T, MT, 1, EPI>(L, a);
+  if constexpr (EPI != EPI_LOGITS)
+    if (NT == 2) return launch_wide_one<T, MT, 2, EPI>(L, a);
+  if (NT == 3) return launch_wide_one<T, MT, 3, EPI>(L, a);
+  if (NT == 4) return launch_wide_one<T, MT, 4, EPI>(L, a);
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int EPI>
+static hipError_t launch_wide(int NT, int MT, const Launch& L, const GemmArgs& a) {
+  switch (MT) {
+    case 1: return launch_wide_nt<T, 1, EPI>(NT, L, a);
+    case 2: return launch_wide_nt<T, 2, EPI>(NT, L, a);
+    case 3: return launch_wide_nt<T, 3, EPI>(NT, L, a);
+    case 4: return launch_wide_nt<T, 4, EPI>(NT, L, a);
+    case 5: return launch_wide_nt<T, 5, EPI>(NT, L, a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename T, int EPI>
 static hipError_t launch_cfg(const GemmCfg& c, int MT, const Launch& L, const GemmArgs& a) {
+  if (c.wide) return launch_wide<T, EPI>(c.NT, MT, L, a);
   if (c.tiled) {
     if (c.NT == 4 && c.D == 3) return launch_tiled<T, 4, 3, EPI>(L, a);
     if (c.NT == 8 && c.D == 2) return launch_tiled<T, 8, 2, EPI>(L, a);
@@ -603,9 +869,46 @@ static hipError_t launch_cfg(const GemmCfg& c, int MT, const Launch& L, const Ge
   return hipErrorInvalidValue;
 }
 
+template <typename T, int MT, int EPI, int MAXS>
+static hipError_t launch_finish_one(const Launch& L, const GemmArgs& a) {
+  if (L.ev1) hipExtLaunchKernelGGL(gemm_finish<T, MT, 1, EPI, MAXS>, L.grid, dim3(256), 0, L.s, nullptr, L.ev1, 0, a);
+  else gemm_finish<T, MT, 1, EPI, MAXS><<<L.grid, 256, 0, L.s>>>(a);
+  return hipGetLastError();
+}
+
+template <typename T, int MT, int EPI>
+static hipError_t launch_finish_s(const Launch& L, const GemmArgs& a) {
+  if (a.n_split <= 4) return launch_finish_one<T, MT, EPI, 4>(L, a);
+  if (a.n_split <= 8) return launch_finish_one<T, MT, EPI, 8>(L, a);
+  if (a.n_split <= 16) return launch_finish_one<T, MT, EPI, 16>(L, a);
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int EPI>
+static hipError_t launch_finish_t(int MT, const Launch& L, const GemmArgs& a) {
+  switch (MT) {
+    case 1: return launch_finish_s<T, 1, EPI>(L, a);
+    case 2: return launch_finish_s<T, 2, EPI>(L, a);
+    case 3: return launch_finish_s<T, 3, EPI>(L, a);
+    case 4: return launch_finish_s<T, 4, EPI>(L, a);
+    case 5: return launch_finish_s<T, 5, EPI>(L, a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm_finish(bool is_bf16, const GemmCfg& c, int MT, int epi, dim3 grid, const GemmArgs& a,
+                              hipStream_t s, hipEvent_t ev_stop) {
+  if (c.NTF != 1 || a.n_split < 1) return hipErrorInvalidValue;
+  const Launch L{grid, s, nullptr, ev_stop};
+  if (epi == EPI_QKV) return is_bf16 ? launch_finish_t<bf16, EPI_QKV>(MT, L, a) : launch_finish_t<float, EPI_QKV>(MT, L, a);
+  if (epi == EPI_SWIGLU)
+    return is_bf16 ? launch_finish_t<bf16, EPI_SWIGLU>(MT, L, a) : launch_finish_t<float, EPI_SWIGLU>(MT, L, a);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemm(bool is_bf16, const GemmCfg& c, int MT, int epi, dim3 grid, const GemmArgs& a,
                        hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
-  const Launch L{grid, s, ev_start, ev_start ? ev_stop : nullptr};
+  const Launch L{grid, s, ev_start, (ev_start || c.wide) ? ev_stop : nullptr};
 #define SDV_EPI(E)                                                                          \
   if (epi == E) return is_bf16 ? launch_cfg<bf16, E>(c, MT, L, a) : launch_cfg<float, E>(c, MT, L, a);
   SDV_EPI(EPI_PARTIAL)

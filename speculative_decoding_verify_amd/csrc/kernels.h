@@ -45,14 +45,19 @@ struct GemmArgs {
   int ldl;
   float4* stats;            // LOGITS: stats[m * n_groups + column group]
   int n_groups;
+  int n_split;              // gemm_finish: split partials in `out` to sum
 };
 
 // launch configuration: NT weight tiles per workgroup, D k steps in flight per wave;
 // tiled: the many-row kernel (128-row blocks; NT = MFMA column tiles per wave, D = k
-// steps in its LDS ring)
+// steps in its LDS ring); wide: the column-split few-row kernel (NT tiles per wave,
+// 4 NT per workgroup; q/k/v and SwiGLU launches write split partials that gemm_finish
+// sums over column groups of NTF tiles)
 struct GemmCfg {
   int NT, D;
   bool tiled = false;
+  bool wide = false;
+  int NTF = 0;
 };
 int gemm_lds_ok(int MT, int NT);
 // With ev_start / ev_stop set, the events are recorded by the dispatch itself at the
@@ -60,6 +65,9 @@ int gemm_lds_ok(int MT, int NT);
 // execution time.
 hipError_t launch_gemm(bool is_bf16, const GemmCfg& c, int MT, int epi, dim3 grid, const GemmArgs& a,
                        hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+// the split-K finish of a wide q/k/v or SwiGLU launch (grid: column groups of c.NTF tiles)
+hipError_t launch_gemm_finish(bool is_bf16, const GemmCfg& c, int MT, int epi, dim3 grid, const GemmArgs& a,
+                              hipStream_t s, hipEvent_t ev_stop = nullptr);
 
 // weight packing (one-time, at model load): rows of up to three row-major [rows, K]
 // sources, viewed as one matrix, rearranged into tiles; kind 0 plain, 1 q/k/v rotation

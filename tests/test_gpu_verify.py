@@ -109,6 +109,7 @@ def test_row_tile_boundaries(shape, B, L_a, gamma):
     ((37, 70), 5, 16),           # 42 rows
     ((12,), 1, 0),               # a single row
     ((9, 51, 30, 66), 5, 25),    # 120 rows: the tiled GEMM, K split in 4 for o and down
+    ((40, 58), 5, 28),           # 66 rows: the column-split GEMM, K split on every projection
 ])
 def test_parity_d2048(shape, lens, L_a, gamma):
     """The 1.7B model width (d = 2048, 256 threads x 8 columns in the norms, K = 2048

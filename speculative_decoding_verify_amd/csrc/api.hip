@@ -144,7 +144,7 @@ GemmPlan plan_gemm(int M, int N, int K, bool bf, int epi) {
         const double t = t0 + (fin && S == 1 ? 0.0 : (double)S * M * N * 4 / l2_bw + (fin ? finish_us : 0.0));
         if (t < best - 1e-9) {
           best = t;
-          p.cfg = GemmCfg{nt, 3, false, true, fin && S > 1 ? 1 : 0};
+          p.cfg = GemmCfg{nt, 3, false, true, fin && S > 1 ? gemm_finish_tiles(S) : 0};
           p.ncg = ncg;
           p.spp = spp;
           p.S = S;

@@ -674,7 +674,8 @@ __global__ __launch_bounds__(256) void gemm_wide(GemmArgs a) {
 template <typename T, int MT, int NT, int EPI, int MAXS>
 __global__ __launch_bounds__(256) void gemm_finish(GemmArgs a) {
   constexpr int TC = 16 * NT;
-  constexpr int EPT = MT * NT;   // tile elements per thread (16 MT x 16 NT over 256)
+  constexpr int RC = TC / 4;                  // 16-byte chunks per tile row
+  constexpr int CPT = (16 * MT * RC + 255) / 256;   // chunks per thread
   __shared__ float tile[16 * MT][TC + 1];
   const int cg = blockIdx.x;
   const int S = a.n_split;
@@ -692,23 +693,29 @@ __global__ __launch_bounds__(256) void gemm_finish(GemmArgs a) {
       items[u] = QkvItem{a.qkv.rope[(size_t)m * half + i], a.qkv.kv_dst[m]};
     }
   }
-  float v[EPT][MAXS];
+  // 16-byte chunks (row ml, columns n .. n + 3; N and the row pitch are multiples of
+  // 16): every partial of every chunk of the thread is loaded before any is added
+  f32x4 v[CPT][MAXS];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int idx = threadIdx.x + 256 * e;
-    const int ml = idx / TC, n = cg * TC + idx % TC;
-    const bool ok = ml < a.M && n < a.N;
-    const float* p = a.out + (size_t)min(ml, a.M - 1) * a.ldo + min(n, a.N - 1);
+  for (int c = 0; c < CPT; ++c) {
+    const int idx = threadIdx.x + 256 * c;
+    const int ml = idx / RC, n = cg * TC + (idx % RC) * 4;
+    const bool ok = idx < 16 * MT * RC && ml < a.M && n < a.N;
+    const float* p = a.out + (size_t)min(ml, a.M - 1) * a.ldo + min(n, a.N - 4);
 #pragma unroll
-    for (int s = 0; s < MAXS; ++s) v[e][s] = (ok && s < S) ? p[(size_t)s * a.out_split_stride] : 0.f;
+    for (int s = 0; s < MAXS; ++s)
+      v[c][s] = (ok && s < S) ? *(const f32x4*)(p + (size_t)s * a.out_split_stride) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int idx = threadIdx.x + 256 * e;
-    float x = v[e][0];
+  for (int c = 0; c < CPT; ++c) {
+    const int idx = threadIdx.x + 256 * c;
+    if (idx < 16 * MT * RC) {
+      f32x4 x = v[c][0];
 #pragma unroll
-    for (int s = 1; s < MAXS; ++s) x += v[e][s];
-    tile[idx / TC][idx % TC] = x;
+      for (int s = 1; s < MAXS; ++s) x += v[c][s];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[idx / RC][(idx % RC) * 4 + e] = x[e];
+    }
   }
   __syncthreads();
   gemm_epilogue<T, MT, NT, EPI>(a, tile, cg, 0, 0, [&](int u, int, int) { return items[u]; });
@@ -869,40 +876,45 @@ static hipError_t launch_cfg(const GemmCfg& c, int MT, const Launch& L, const Ge
   return hipErrorInvalidValue;
 }
 
-template <typename T, int MT, int EPI, int MAXS>
+template <typename T, int MT, int NT, int EPI, int MAXS>
 static hipError_t launch_finish_one(const Launch& L, const GemmArgs& a) {
-  if (L.ev1) hipExtLaunchKernelGGL(gemm_finish<T, MT, 1, EPI, MAXS>, L.grid, dim3(256), 0, L.s, nullptr, L.ev1, 0, a);
-  else gemm_finish<T, MT, 1, EPI, MAXS><<<L.grid, 256, 0, L.s>>>(a);
+  if (L.ev1) hipExtLaunchKernelGGL(gemm_finish<T, MT, NT, EPI, MAXS>, L.grid, dim3(256), 0, L.s, nullptr, L.ev1, 0, a);
+  else gemm_finish<T, MT, NT, EPI, MAXS><<<L.grid, 256, 0, L.s>>>(a);
   return hipGetLastError();
 }
 
+// two tiles per workgroup up to 8 splits, one beyond (the partials of a thread's
+// chunks are all in registers at once)
 template <typename T, int MT, int EPI>
-static hipError_t launch_finish_s(const Launch& L, const GemmArgs& a) {
-  if (a.n_split <= 4) return launch_finish_one<T, MT, EPI, 4>(L, a);
-  if (a.n_split <= 8) return launch_finish_one<T, MT, EPI, 8>(L, a);
-  if (a.n_split <= 16) return launch_finish_one<T, MT, EPI, 16>(L, a);
+static hipError_t launch_finish_s(int NTF, const Launch& L, const GemmArgs& a) {
+  if (NTF == 2 && a.n_split <= 4) return launch_finish_one<T, MT, 2, EPI, 4>(L, a);
+  if (NTF == 2 && a.n_split <= 8) return launch_finish_one<T, MT, 2, EPI, 8>(L, a);
+  if (NTF == 1 && a.n_split <= 16) return launch_finish_one<T, MT, 1, EPI, 16>(L, a);
   return hipErrorInvalidValue;
 }
 
 template <typename T, int EPI>
-static hipError_t launch_finish_t(int MT, const Launch& L, const GemmArgs& a) {
+static hipError_t launch_finish_t(int NTF, int MT, const Launch& L, const GemmArgs& a) {
   switch (MT) {
-    case 1: return launch_finish_s<T, 1, EPI>(L, a);
-    case 2: return launch_finish_s<T, 2, EPI>(L, a);
-    case 3: return launch_finish_s<T, 3, EPI>(L, a);
-    case 4: return launch_finish_s<T, 4, EPI>(L, a);
-    case 5: return launch_finish_s<T, 5, EPI>(L, a);
+    case 1: return launch_finish_s<T, 1, EPI>(NTF, L, a);
+    case 2: return launch_finish_s<T, 2, EPI>(NTF, L, a);
+    case 3: return launch_finish_s<T, 3, EPI>(NTF, L, a);
+    case 4: return launch_finish_s<T, 4, EPI>(NTF, L, a);
+    case 5: return launch_finish_s<T, 5, EPI>(NTF, L, a);
     default: return hipErrorInvalidValue;
   }
 }
 
+int gemm_finish_tiles(int n_split) { return n_split <= 8 ? 2 : 1; }
+
 hipError_t launch_gemm_finish(bool is_bf16, const GemmCfg& c, int MT, int epi, dim3 grid, const GemmArgs& a,
                               hipStream_t s, hipEvent_t ev_stop) {
-  if (c.NTF != 1 || a.n_split < 1) return hipErrorInvalidValue;
+  if (c.NTF != gemm_finish_tiles(a.n_split) || a.n_split < 1) return hipErrorInvalidValue;
   const Launch L{grid, s, nullptr, ev_stop};
-  if (epi == EPI_QKV) return is_bf16 ? launch_finish_t<bf16, EPI_QKV>(MT, L, a) : launch_finish_t<float, EPI_QKV>(MT, L, a);
+  if (epi == EPI_QKV)
+    return is_bf16 ? launch_finish_t<bf16, EPI_QKV>(c.NTF, MT, L, a) : launch_finish_t<float, EPI_QKV>(c.NTF, MT, L, a);
   if (epi == EPI_SWIGLU)
-    return is_bf16 ? launch_finish_t<bf16, EPI_SWIGLU>(MT, L, a) : launch_finish_t<float, EPI_SWIGLU>(MT, L, a);
+    return is_bf16 ? launch_finish_t<bf16, EPI_SWIGLU>(c.NTF, MT, L, a) : launch_finish_t<float, EPI_SWIGLU>(c.NTF, MT, L, a);
   return hipErrorInvalidValue;
 }
 

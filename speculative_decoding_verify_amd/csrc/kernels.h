@@ -65,7 +65,9 @@ int gemm_lds_ok(int MT, int NT);
 // execution time.
 hipError_t launch_gemm(bool is_bf16, const GemmCfg& c, int MT, int epi, dim3 grid, const GemmArgs& a,
                        hipStream_t s, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
-// the split-K finish of a wide q/k/v or SwiGLU launch (grid: column groups of c.NTF tiles)
+// the split-K finish of a wide q/k/v or SwiGLU launch (grid: column groups of c.NTF
+// tiles, c.NTF = gemm_finish_tiles(splits))
+int gemm_finish_tiles(int n_split);
 hipError_t launch_gemm_finish(bool is_bf16, const GemmCfg& c, int MT, int epi, dim3 grid, const GemmArgs& a,
                               hipStream_t s, hipEvent_t ev_stop = nullptr);
 

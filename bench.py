@@ -57,19 +57,22 @@ KERNEL_SOURCES = {"qkv": GEMM_SOURCES, "o": GEMM_SOURCES, "gate_up": GEMM_SOURCE
 TRAFFIC = [
     # rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, on `bench.py --workload <w> --steps 2
     # --warmup 1 --no-cpu-baseline` (--no-drafting for the single-sequence passes);
-    # means over every dispatch of the kernel
+    # means over every dispatch of the kernel; a kind of two kernels sums both
     {"workload": "c5-codebook", "kernel": "attention",   # sdv::attn_dma<128, 1, 4, 3>, 216 dispatches
-     "sha256": "475915ce153a3072d06ece9e77468f799e98269fb817377e149bf333992c8ef8",
-     "fetch_kib": 1829124.76, "write_kib": 249954.30},
-    {"workload": "8b-bf16", "kernel": "gate_up",         # sdv::gemm_stream<bf16, 5, 6, 2, SWIGLU>, 180 dispatches
-     "sha256": "912e85a8171080bdcace0b39cc145c6cc40889028083e0dc5599734cc4adba9c",
-     "fetch_kib": 103030.12, "write_kib": 3168.0},
+     "sha256": "ac09b876b9ff28fc5b73c792a15ebdfaa3e47ddeab550c1e32b768b772dfbe47",
+     "fetch_kib": 1833869.36, "write_kib": 248266.91},
+    # gate/up on the 8B shape is two kernels: sdv::gemm_wide<bf16, 5, 3, 3, PARTIAL> (the
+    # gate/up half of that instance's 360 dispatches; the other half is q/k/v) and
+    # sdv::gemm_finish<bf16, 5, 2, SWIGLU, 4> (180 dispatches)
+    {"workload": "8b-bf16", "kernel": "gate_up",
+     "sha256": "50f4bddd617bb4639f91f44c4c2681949f5547e55d52fe9320d6b4d026d3535b",
+     "fetch_kib": 103018.53 + 6263.50, "write_kib": 12480.0 + 3168.0},
     {"workload": "1.7b-bf16", "kernel": "gate_up",       # sdv::gemm_stream<bf16, 3, 4, 2, SWIGLU>, 120 dispatches
-     "sha256": "912e85a8171080bdcace0b39cc145c6cc40889028083e0dc5599734cc4adba9c",
-     "fetch_kib": 34365.67, "write_kib": 1344.0},
+     "sha256": "50f4bddd617bb4639f91f44c4c2681949f5547e55d52fe9320d6b4d026d3535b",
+     "fetch_kib": 34367.48, "write_kib": 1344.0},
     {"workload": "sample", "kernel": "row_stats",        # sdv::spec_row_stats_kernel, 5 dispatches
-     "sha256": "ab157bca86e5d987d8d1460d146bd1c7c5e72e6835f776c196cdb54791f3ee28",
-     "fetch_kib": 284713.35, "write_kib": 60.03},
+     "sha256": "74b3d66b04ee2035b9cfeb0ced0b7b80b10f0007a6fd38cfaff2cc545b9cc7d5",
+     "fetch_kib": 284938.97, "write_kib": 60.03},
 ]
 
 

@@ -215,6 +215,20 @@ SDV_DEV float wave_sum(float v) {
 }
 
 // Sum over a 256-thread block in a fixed order (deterministic).  `red` holds 8 floats.
+// Sum over a block of NW waves in a fixed order (deterministic).  `red` holds NW floats.
+template <int NW>
+SDV_DEV float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float t = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) t += red[i];
+  __syncthreads();
+  return t;
+}
+
 SDV_DEV float block_sum_256(float v, float* red) {
   v = wave_sum(v);
   const int w = threadIdx.x >> 6;

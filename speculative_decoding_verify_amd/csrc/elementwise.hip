@@ -95,7 +95,7 @@ hipError_t launch_prologue(const PrologueArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// RMSNorm of one fp32 row held in registers (256 threads, PER elements each,
+// RMSNorm of one fp32 row held in registers (NTHR threads, PER elements each,
 // element c = threadIdx.x * PER + i), stored as row m of an activation operand.
 // The thread's PER gain values, loaded up front (before the block reduction's
 // barrier, which loads cannot cross).
@@ -109,14 +109,14 @@ SDV_DEV void load_gain(const float* gain, int d, float (&g)[PER]) {
   }
 }
 
-template <typename T, int PER>
+template <typename T, int PER, int NTHR = 256>
 SDV_DEV void norm_store(const float (&v)[PER], int d, const float (&gain)[PER], void* out, int m, float eps,
                         float* red) {
   static_assert(PER % 8 == 0, "whole k groups per thread");
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) ss += v[i] * v[i];
-  ss = block_sum_256(ss, red);
+  ss = NTHR == 256 ? block_sum_256(ss, red) : block_sum<NTHR / 64>(ss, red);
   const float rs = rsqrtf(ss / (float)d + eps);
   const int c0 = threadIdx.x * PER;
   if (c0 < d) {
@@ -159,9 +159,9 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(EmbedArgs a) {
 // batched pass, S = 3: 75 -> 60 us per launch).  Block j:
 // without a.rows, row j (x updated in place); with a.rows, output row j < n_rows
 // normalises source row rows[j], and the blocks after those write hidden rows.
-template <typename T, int PER, int MAXS>
-__global__ __launch_bounds__(256) void resid_norm_kernel(ResidNormArgs a) {
-  __shared__ float red[8];
+template <typename T, int PER, int MAXS, int NTHR = 256>
+__global__ __launch_bounds__(NTHR) void resid_norm_kernel(ResidNormArgs a) {
+  __shared__ float red[NTHR / 64 > 8 ? NTHR / 64 : 8];
   const bool gather = a.rows != nullptr;
   const bool hidden_only = gather && (int)blockIdx.x >= a.n_rows;
   const int m = !gather ? blockIdx.x : hidden_only ? blockIdx.x - a.n_rows : a.rows[blockIdx.x];
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(ResidNormArgs a) {
     for (int i = 0; i < PER; ++i) v[i] = 0.f;
   }
   if (hidden_only) return;   // uniform over the block
-  norm_store<T, PER>(v, a.d, gn, a.a, blockIdx.x, a.eps, red);
+  norm_store<T, PER, NTHR>(v, a.d, gn, a.a, blockIdx.x, a.eps, red);
 }
 
 // PER columns per thread: the smallest of 8, 16, 24, 32 with 256 * PER >= d and
@@ -230,9 +230,23 @@ static hipError_t launch_rows(bool resid, int d, int blocks, const void* args, h
 hipError_t launch_embed_norm(bool is_bf16, const EmbedArgs& a, hipStream_t s) {
   return is_bf16 ? launch_rows<bf16>(false, a.d, a.M, &a, s) : launch_rows<float>(false, a.d, a.M, &a, s);
 }
+// Few rows of a wide model (fewer rows than compute units, d above 2048): 8 columns per
+// thread and d / 8 threads per row, so the partial loads spread over more waves
+template <typename T, int NTHR>
+static hipError_t launch_resid_wide(const ResidNormArgs& a, int blocks, hipStream_t s) {
+  if (a.S <= 4) resid_norm_kernel<T, 8, 4, NTHR><<<blocks, NTHR, 0, s>>>(a);
+  else if (a.S <= 8) resid_norm_kernel<T, 8, 8, NTHR><<<blocks, NTHR, 0, s>>>(a);
+  else resid_norm_kernel<T, 8, 16, NTHR><<<blocks, NTHR, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_resid_norm(bool is_bf16, const ResidNormArgs& a, hipStream_t s) {
   if (a.S > 16 || (a.rows && a.n_rows < 1)) return hipErrorInvalidValue;
   const int blocks = a.rows ? a.n_rows + (a.hidden ? a.M : 0) : a.M;
+  if (blocks <= 256 && a.d > 2048 && a.d % 8 == 0) {
+    if (a.d <= 4096) return is_bf16 ? launch_resid_wide<bf16, 512>(a, blocks, s) : launch_resid_wide<float, 512>(a, blocks, s);
+    if (a.d <= 8192) return is_bf16 ? launch_resid_wide<bf16, 1024>(a, blocks, s) : launch_resid_wide<float, 1024>(a, blocks, s);
+  }
   return is_bf16 ? launch_rows<bf16>(true, a.d, blocks, &a, s) : launch_rows<float>(true, a.d, blocks, &a, s);
 }
 

@@ -59,20 +59,20 @@ TRAFFIC = [
     # --warmup 1 --no-cpu-baseline` (--no-drafting for the single-sequence passes);
     # means over every dispatch of the kernel; a kind of two kernels sums both
     {"workload": "c5-codebook", "kernel": "attention",   # sdv::attn_dma<128, 1, 4, 3>, 216 dispatches
-     "sha256": "ac09b876b9ff28fc5b73c792a15ebdfaa3e47ddeab550c1e32b768b772dfbe47",
-     "fetch_kib": 1833869.36, "write_kib": 248266.91},
+     "sha256": "4b91ba904840a815a57a7fe98b6e71b70ba37aeb75ff5cc09f8f547143c783ee",
+     "fetch_kib": 1831011.10, "write_kib": 249141.81},
     # gate/up on the 8B shape is two kernels: sdv::gemm_wide<bf16, 5, 3, 3, PARTIAL> (the
     # gate/up half of that instance's 360 dispatches; the other half is q/k/v) and
     # sdv::gemm_finish<bf16, 5, 2, SWIGLU, 4> (180 dispatches)
     {"workload": "8b-bf16", "kernel": "gate_up",
-     "sha256": "50f4bddd617bb4639f91f44c4c2681949f5547e55d52fe9320d6b4d026d3535b",
+     "sha256": "81f9aaf1da23a69b19b5205b989ceb65bb3298ce93220beb61b984a75c53443a",
      "fetch_kib": 103018.53 + 6263.50, "write_kib": 12480.0 + 3168.0},
     {"workload": "1.7b-bf16", "kernel": "gate_up",       # sdv::gemm_stream<bf16, 3, 4, 2, SWIGLU>, 120 dispatches
-     "sha256": "50f4bddd617bb4639f91f44c4c2681949f5547e55d52fe9320d6b4d026d3535b",
+     "sha256": "81f9aaf1da23a69b19b5205b989ceb65bb3298ce93220beb61b984a75c53443a",
      "fetch_kib": 34367.48, "write_kib": 1344.0},
     {"workload": "sample", "kernel": "row_stats",        # sdv::spec_row_stats_kernel, 5 dispatches
-     "sha256": "74b3d66b04ee2035b9cfeb0ced0b7b80b10f0007a6fd38cfaff2cc545b9cc7d5",
-     "fetch_kib": 284938.97, "write_kib": 60.03},
+     "sha256": "ee33c89460be84d2d289185241a795a24df0a5df5d52d4ae186a68d2a2729291",
+     "fetch_kib": 284938.95, "write_kib": 60.09},
 ]
 
 

@@ -523,15 +523,17 @@ constexpr int cgcd(int x, int y) { return y == 0 ? x : cgcd(y, x % y); }
 #endif
 constexpr int WIDE_P = SDV_WIDE_P;
 
-template <typename T, int MT, int NT, int D, int EPI>
-__global__ __launch_bounds__(256) void gemm_wide(GemmArgs a) {
+template <typename T, int MT, int NT, int D, int EPI, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void gemm_wide(GemmArgs a) {
+  static_assert(NW == 4 || EPI == EPI_PARTIAL, "the shared epilogues take 256 threads");
+  constexpr int NTHR = 64 * NW;
   constexpr bool BF = sizeof(T) == 2;
   constexpr int KS = BF ? 32 : 16;
   constexpr int AL = BF ? 2 : 1;
   constexpr int NB = MT * AL;                 // 1 KB activation blocks per k step
-  constexpr int NCH = (NB * 64 + 255) / 256;  // 16-byte chunks of a step per thread
+  constexpr int NCH = (NB * 64 + NTHR - 1) / NTHR;  // 16-byte chunks of a step per thread
   constexpr int P = WIDE_P;                   // k steps of activation loads ahead
-  constexpr int TW = 4 * NT;                  // packed tiles of the workgroup
+  constexpr int TW = NW * NT;                 // packed tiles of the workgroup
   // register ring slots, staging slots and LDS buffers are indexed by compile-time
   // step residues
   constexpr int U2 = D * 2 / cgcd(D, 2);
@@ -540,7 +542,7 @@ __global__ __launch_bounds__(256) void gemm_wide(GemmArgs a) {
   constexpr int E = (D - 1 > P + 1) ? D - 1 : P + 1;   // look-ahead of a step's issues
   // a buffer holds every thread's NCH chunks: chunks past the NB blocks land in a pad
   // that is never read, so no load or store of the staging path takes a branch
-  __shared__ __attribute__((aligned(16))) char abuf[2][NCH * 256 * 16];
+  __shared__ __attribute__((aligned(16))) char abuf[2][NCH * NTHR * 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -560,13 +562,13 @@ __global__ __launch_bounds__(256) void gemm_wide(GemmArgs a) {
     const int tile = min(cg * TW + wave * NT + t, ntiles - 1);
     wp[t] = (const char*)a.W + ((size_t)tile * ksteps + s0) * 1024 + lane * 16;
   }
-  // this thread's activation chunks c = threadIdx.x + 256 i of a step's NB blocks
+  // this thread's activation chunks c = threadIdx.x + NTHR i of a step's NB blocks
   // (block b = row tile * AL + half; steps 64 * KS bytes apart in a row tile); lanes of
   // rows past M read the last row's chunk, chunks past the blocks the last chunk
   const char* cp[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int c = threadIdx.x + 256 * i;
+    const int c = threadIdx.x + NTHR * i;
     const int cc = min(c, NB * 64 - 1);
     const int b = cc >> 6, l = cc & 63;
     const int rt = min(b / AL, row_tiles - 1), h = b % AL;
@@ -592,7 +594,7 @@ __global__ __launch_bounds__(256) void gemm_wide(GemmArgs a) {
   };
   auto store_a = [&](const u32x4 (&src)[NCH], int buf) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) *(u32x4*)(&abuf[buf][(threadIdx.x + 256 * i) * 16]) = src[i];
+    for (int i = 0; i < NCH; ++i) *(u32x4*)(&abuf[buf][(threadIdx.x + NTHR * i) * 16]) = src[i];
   };
   // k step j (j % U == u): issue the loads that run ahead, stage step j + 1 into the
   // other LDS buffer, multiply step j, then the barrier that publishes step j + 1 and
@@ -826,15 +828,25 @@ static hipError_t launch_tiled(const Launch& L, const GemmArgs& a) {
 #endif
 constexpr int WIDE_D = SDV_WIDE_D;
 
-template <typename T, int MT, int NT, int EPI>
+template <typename T, int MT, int NT, int EPI, int NW = 4>
 static hipError_t launch_wide_one(const Launch& L, const GemmArgs& a) {
-  if (L.ev0 || L.ev1) hipExtLaunchKernelGGL(gemm_wide<T, MT, NT, WIDE_D, EPI>, L.grid, dim3(256), 0, L.s, L.ev0, L.ev1, 0, a);
-  else gemm_wide<T, MT, NT, WIDE_D, EPI><<<L.grid, 256, 0, L.s>>>(a);
+  if (L.ev0 || L.ev1)
+    hipExtLaunchKernelGGL(gemm_wide<T, MT, NT, WIDE_D, EPI, NW>, L.grid, dim3(64 * NW), 0, L.s, L.ev0, L.ev1, 0, a);
+  else gemm_wide<T, MT, NT, WIDE_D, EPI, NW><<<L.grid, 64 * NW, 0, L.s>>>(a);
   return hipGetLastError();
 }
 
 template <typename T, int MT, int EPI>
-static hipError_t launch_wide_nt(int NT, const Launch& L, const GemmArgs& a) {
+static hipError_t launch_wide_nt(int NT, int NW, const Launch& L, const GemmArgs& a) {
+  if constexpr (EPI == EPI_PARTIAL && MT >= 4) {   // eight waves: split partials from 49 rows
+    if (NW == 8) {
+      if (NT == 1) return launch_wide_one<T, MT, 1, EPI, 8>(L, a);
+      if (NT == 2) return launch_wide_one<T, MT, 2, EPI, 8>(L, a);
+      if (NT == 3) return launch_wide_one<T, MT, 3, EPI, 8>(L, a);
+      return hipErrorInvalidValue;
+    }
+  }
+  if (NW != 4) return hipErrorInvalidValue;
   if constexpr (EPI == EPI_PARTIAL)
     if (NT == 1) return launch_wide_one<T, MT, 1, EPI>(L, a);
   if constexpr (EPI != EPI_LOGITS)
@@ -845,20 +857,20 @@ static hipError_t launch_wide_nt(int NT, const Launch& L, const GemmArgs& a) {
 }
 
 template <typename T, int EPI>
-static hipError_t launch_wide(int NT, int MT, const Launch& L, const GemmArgs& a) {
+static hipError_t launch_wide(int NT, int NW, int MT, const Launch& L, const GemmArgs& a) {
   switch (MT) {
-    case 1: return launch_wide_nt<T, 1, EPI>(NT, L, a);
-    case 2: return launch_wide_nt<T, 2, EPI>(NT, L, a);
-    case 3: return launch_wide_nt<T, 3, EPI>(NT, L, a);
-    case 4: return launch_wide_nt<T, 4, EPI>(NT, L, a);
-    case 5: return launch_wide_nt<T, 5, EPI>(NT, L, a);
+    case 1: return launch_wide_nt<T, 1, EPI>(NT, NW, L, a);
+    case 2: return launch_wide_nt<T, 2, EPI>(NT, NW, L, a);
+    case 3: return launch_wide_nt<T, 3, EPI>(NT, NW, L, a);
+    case 4: return launch_wide_nt<T, 4, EPI>(NT, NW, L, a);
+    case 5: return launch_wide_nt<T, 5, EPI>(NT, NW, L, a);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename T, int EPI>
 static hipError_t launch_cfg(const GemmCfg& c, int MT, const Launch& L, const GemmArgs& a) {
-  if (c.wide) return launch_wide<T, EPI>(c.NT, MT, L, a);
+  if (c.wide) return launch_wide<T, EPI>(c.NT, c.NW, MT, L, a);
   if (c.tiled) {
     if (c.NT == 4 && c.D == 3) return launch_tiled<T, 4, 3, EPI>(L, a);
     if (c.NT == 8 && c.D == 2) return launch_tiled<T, 8, 2, EPI>(L, a);

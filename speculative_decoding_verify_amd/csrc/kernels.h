@@ -58,6 +58,7 @@ struct GemmCfg {
   bool tiled = false;
   bool wide = false;
   int NTF = 0;
+  int NW = 4;               // wide: waves per workgroup (8 only for split partials)
 };
 int gemm_lds_ok(int MT, int NT);
 // With ev_start / ev_stop set, the events are recorded by the dispatch itself at the

@@ -59,20 +59,20 @@ TRAFFIC = [
     # --warmup 1 --no-cpu-baseline` (--no-drafting for the single-sequence passes);
     # means over every dispatch of the kernel; a kind of two kernels sums both
     {"workload": "c5-codebook", "kernel": "attention",   # sdv::attn_dma<128, 1, 4, 3>, 216 dispatches
-     "sha256": "4b91ba904840a815a57a7fe98b6e71b70ba37aeb75ff5cc09f8f547143c783ee",
-     "fetch_kib": 1831011.10, "write_kib": 249141.81},
+     "sha256": "202be0ec9a006cc92dd0a041f3778f24e3f5d77b238d18c2da8ad17aac80500f",
+     "fetch_kib": 1824697.22, "write_kib": 250554.12},
     # gate/up on the 8B shape is two kernels: sdv::gemm_wide<bf16, 5, 3, 3, PARTIAL> (the
     # gate/up half of that instance's 360 dispatches; the other half is q/k/v) and
     # sdv::gemm_finish<bf16, 5, 2, SWIGLU, 4> (180 dispatches)
     {"workload": "8b-bf16", "kernel": "gate_up",
-     "sha256": "81f9aaf1da23a69b19b5205b989ceb65bb3298ce93220beb61b984a75c53443a",
-     "fetch_kib": 103018.53 + 6263.50, "write_kib": 12480.0 + 3168.0},
+     "sha256": "71db19d75368b34d71c408686e6f11789a0cab9453f9fc3125893d488353c55e",
+     "fetch_kib": 103018.54 + 6257.50, "write_kib": 12480.0 + 3168.0},
     {"workload": "1.7b-bf16", "kernel": "gate_up",       # sdv::gemm_stream<bf16, 3, 4, 2, SWIGLU>, 120 dispatches
-     "sha256": "81f9aaf1da23a69b19b5205b989ceb65bb3298ce93220beb61b984a75c53443a",
-     "fetch_kib": 34367.48, "write_kib": 1344.0},
+     "sha256": "71db19d75368b34d71c408686e6f11789a0cab9453f9fc3125893d488353c55e",
+     "fetch_kib": 34367.17, "write_kib": 1344.0},
     {"workload": "sample", "kernel": "row_stats",        # sdv::spec_row_stats_kernel, 5 dispatches
-     "sha256": "ee33c89460be84d2d289185241a795a24df0a5df5d52d4ae186a68d2a2729291",
-     "fetch_kib": 284938.95, "write_kib": 60.09},
+     "sha256": "4bee3d41264a24db90d895fc36caa70c5105b66d46e8d082e43ae4b4f01e1f82",
+     "fetch_kib": 284938.81, "write_kib": 60.00},
 ]
 
 

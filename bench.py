@@ -65,10 +65,10 @@ TRAFFIC = [
     # gate/up half of that instance's 360 dispatches; the other half is q/k/v) and
     # sdv::gemm_finish<bf16, 5, 2, SWIGLU, 4> (180 dispatches)
     {"workload": "8b-bf16", "kernel": "gate_up",
-     "sha256": "71db19d75368b34d71c408686e6f11789a0cab9453f9fc3125893d488353c55e",
+     "sha256": "4a82a96b054f52a8b7a9636cb4895682cea0da3ff6eb2927a181856165c3f2b9",
      "fetch_kib": 103018.54 + 6257.50, "write_kib": 12480.0 + 3168.0},
     {"workload": "1.7b-bf16", "kernel": "gate_up",       # sdv::gemm_stream<bf16, 3, 4, 2, SWIGLU>, 120 dispatches
-     "sha256": "71db19d75368b34d71c408686e6f11789a0cab9453f9fc3125893d488353c55e",
+     "sha256": "4a82a96b054f52a8b7a9636cb4895682cea0da3ff6eb2927a181856165c3f2b9",
      "fetch_kib": 34367.17, "write_kib": 1344.0},
     {"workload": "sample", "kernel": "row_stats",        # sdv::spec_row_stats_kernel, 5 dispatches
      "sha256": "4bee3d41264a24db90d895fc36caa70c5105b66d46e8d082e43ae4b4f01e1f82",

@@ -494,12 +494,13 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmArgs a) {
 // fetches the activation operand of its whole k range for only NT weight tiles; with
 // bf16 pairs at 65 rows that is 10 KB of activations per 1 KB weight tile step, more
 // bytes through each CU than the weights.  Here the waves split the columns: wave w
-// owns NT packed tiles of the workgroup's 4 NT, over the workgroup's k range, so one
-// copy of a k step's activation blocks serves all four waves.  The threads fetch the
-// step's blocks (16 bytes each, P steps ahead into registers) and store them to an LDS
-// double buffer; each wave reads them back in operand order and streams its own weight
-// tiles through a register ring D steps deep.  One LDS barrier per k step.
-// Grid: x = column groups of 4 NT tiles, y = splits of K.  Epilogues: PARTIAL (the
+// owns NT packed tiles of the workgroup's NW NT (NW = 4 waves, or 8 for split
+// partials), over the workgroup's k range, so one copy of a k step's activation blocks
+// serves every wave.  The threads fetch the step's blocks (16 bytes each, P steps ahead
+// into registers) and store them to an LDS double buffer; each wave reads them back in
+// operand order and streams its own weight tiles through a register ring D steps deep.
+// One LDS barrier per k step.
+// Grid: x = column groups of NW NT tiles, y = splits of K.  Epilogues: PARTIAL (the
 // split's fp32 partial sums, stored from the accumulators); the others take the whole
 // K in one workgroup (one split) and go through an LDS tile to the shared epilogue.
 // A q/k/v or SwiGLU launch with K splits writes partials with PARTIAL and gemm_finish

@@ -200,7 +200,13 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmArgs a) {
 
   constexpr int AL = BF ? 2 : 1;
   u32x4 wb[D][NT], ab[D][MT][AL];
-  auto issue = [&](int j, u32x4 (&w)[NT], u32x4 (&av)[MT][AL]) {
+  // SwiGLU launches start each workgroup's walk over its k steps at a different step
+  // (by its place among the workgroups of its XCD), so that the workgroups resident on
+  // an XCD read different activation steps at a time instead of all the same ones
+  // (1.7B gate/up 19.5 -> 18.2 us; on the other epilogues it measured no better)
+  const int rot = (EPI == EPI_SWIGLU && nk > 0) ? (int)(((blockIdx.x >> 3) + blockIdx.y * 5) % (unsigned)nk) : 0;
+  auto issue = [&](int j_, u32x4 (&w)[NT], u32x4 (&av)[MT][AL]) {
+    const int j = j_ + rot < nk ? j_ + rot : j_ + rot - nk;
 #pragma unroll
     for (int t = 0; t < NT; ++t) w[t] = ld16_stream(wp[t] + (size_t)j * 4096);
 #pragma unroll

@@ -65,11 +65,11 @@ TRAFFIC = [
     # gate/up half of that instance's 360 dispatches; the other half is q/k/v) and
     # sdv::gemm_finish<bf16, 5, 2, SWIGLU, 4> (180 dispatches)
     {"workload": "8b-bf16", "kernel": "gate_up",
-     "sha256": "f447bdd4b05ba346743a384aeccfc4576647d5526f5967791564d5cbc53a3499",
-     "fetch_kib": 103018.57 + 6257.50, "write_kib": 12480.0 + 3168.0},
+     "sha256": "68255c2adf92e34f0c9cb1ba0a4d306a4b147dd9fffa684b27a8fc585321d7a5",
+     "fetch_kib": 103018.57 + 6255.50, "write_kib": 12480.0 + 3168.0},
     {"workload": "1.7b-bf16", "kernel": "gate_up",       # sdv::gemm_stream<bf16, 3, 4, 2, SWIGLU>, 120 dispatches
-     "sha256": "f447bdd4b05ba346743a384aeccfc4576647d5526f5967791564d5cbc53a3499",
-     "fetch_kib": 34375.14, "write_kib": 1344.0},
+     "sha256": "68255c2adf92e34f0c9cb1ba0a4d306a4b147dd9fffa684b27a8fc585321d7a5",
+     "fetch_kib": 34376.60, "write_kib": 1344.0},
     {"workload": "sample", "kernel": "row_stats",        # sdv::spec_row_stats_kernel, 5 dispatches
      "sha256": "4bee3d41264a24db90d895fc36caa70c5105b66d46e8d082e43ae4b4f01e1f82",
      "fetch_kib": 284938.81, "write_kib": 60.00},

@@ -118,7 +118,10 @@ GemmPlan plan_gemm(int M, int N, int K, bool bf, int epi) {
   p.MT = std::max(1, cdiv(M, 16));
   p.row_blocks = 1;
 #ifndef SDV_GEMM_STREAM_ONLY
-  if (p.MT >= WIDE_MIN_MT && epi != EPI_LOGITS) {
+  // (also the split-partial launches over a long K at 33-48 rows: the 1.7B down
+  // projection, K = 8192 at 41 rows, 12.9 -> 10.8 us with the residual norm of its
+  // 16 partials; its o projection, K = 2048, measured slower)
+  if ((p.MT >= WIDE_MIN_MT || (p.MT == 3 && epi == EPI_PARTIAL && K >= 4096)) && epi != EPI_LOGITS) {
     // the column-split kernel (4 NT tiles per workgroup, the activation steps fetched
     // once per workgroup): take the tiles per wave, the K splits and the way the splits
     // meet that minimise an estimate of the launch time.  A compute unit moves its

@@ -845,7 +845,7 @@ static hipError_t launch_wide_one(const Launch& L, const GemmArgs& a) {
 
 template <typename T, int MT, int EPI>
 static hipError_t launch_wide_nt(int NT, int NW, const Launch& L, const GemmArgs& a) {
-  if constexpr (EPI == EPI_PARTIAL && MT >= 4) {   // eight waves: split partials from 49 rows
+  if constexpr (EPI == EPI_PARTIAL && MT >= 3) {   // eight waves: split partials from 33 rows
     if (NW == 8) {
       if (NT == 1) return launch_wide_one<T, MT, 1, EPI, 8>(L, a);
       if (NT == 2) return launch_wide_one<T, MT, 2, EPI, 8>(L, a);

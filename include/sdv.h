@@ -189,11 +189,13 @@ typedef struct {
  *   err     int32 [B]: device error bits (OR-ed in; the caller clears it)
  *   cb_argmax  see the field
  *   prof_events  nullable host array of n_prof_events caller-created hipEvent_t
- *           handles: when given, the i-th weight-streaming GEMM launch of the pass
- *           (decoder projections in order q/k/v, o, gate/up, down per layer, then the
- *           LM head) records event 2i when the kernel starts and event 2i+1 when it
- *           ends (hipExtLaunchKernel), for as many launches as there are event pairs;
- *           the interval is the kernel's execution time.
+ *           handles: when given, the i-th projection of the pass (decoder
+ *           projections in order q/k/v, o, gate/up, down per layer, then the LM head)
+ *           records event 2i when its GEMM kernel starts and event 2i+1 when its last
+ *           kernel ends (the GEMM, or the kernel that sums its K-split partials and
+ *           applies the epilogue when it has one), both recorded by the dispatches
+ *           themselves (hipExtLaunchKernel), for as many projections as there are
+ *           event pairs.
  *   attn_prof_events  nullable host array of n_attn_prof_events caller-created events:
  *           layer l's attention records event 2l when its kernel starts and event
  *           2l + 1 when the last kernel of that layer's attention (the split merge, when

@@ -320,7 +320,6 @@ struct ProfEvents {
   int next = 0;
 };
 
-// one weight-streaming GEMM launch; `a` carries the operands and epilogue targets
 // one weight-streaming GEMM launch; `a` carries the operands and epilogue targets (the
 // split-partials buffer in a.out, also for the q/k/v and SwiGLU launches of the
 // column-split kernel, whose finish applies their epilogue)

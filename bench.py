@@ -70,6 +70,9 @@ TRAFFIC = [
     {"workload": "1.7b-bf16", "kernel": "gate_up",       # sdv::gemm_stream<bf16, 3, 4, 2, SWIGLU>, 120 dispatches
      "sha256": "68255c2adf92e34f0c9cb1ba0a4d306a4b147dd9fffa684b27a8fc585321d7a5",
      "fetch_kib": 34376.60, "write_kib": 1344.0},
+    {"workload": "toy-f32", "kernel": "attention",       # sdv::attn_reg<float, 64, 2>, 10 dispatches
+     "sha256": "202be0ec9a006cc92dd0a041f3778f24e3f5d77b238d18c2da8ad17aac80500f",
+     "fetch_kib": 890.11, "write_kib": 583.13},
     {"workload": "sample", "kernel": "row_stats",        # sdv::spec_row_stats_kernel, 5 dispatches
      "sha256": "4bee3d41264a24db90d895fc36caa70c5105b66d46e8d082e43ae4b4f01e1f82",
      "fetch_kib": 284938.81, "write_kib": 60.00},

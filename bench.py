@@ -250,15 +250,28 @@ def kernel_table(sh, us, work, workload, head_kind):
 
 
 def timed_steps(step, steps, warmup):
+    """Mean ms per step over `steps` steps between two host synchronisations, and the
+    distribution of the single steps (median, p10, p90 in ms) from HIP events recorded
+    between them on the launch stream (torch's current stream) in the same region."""
     import torch
     for _ in range(warmup):
         step()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    ev[0].record()
+    for i in range(steps):
         step()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps * 1e3
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    return ms, step_distribution([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+
+
+def step_distribution(per_step_ms):
+    t = np.asarray(per_step_ms, dtype=np.float64)
+    return {"median": float(np.median(t)), "p10": float(np.percentile(t, 10)), "p90": float(np.percentile(t, 90)),
+            "n": int(t.size)}
 
 
 def _log(msg):
@@ -373,7 +386,7 @@ def bench_verify(args, wl, w=None, model=None):
         with torch.cuda.graph(graph):
             step()
         torch.cuda.synchronize()
-    ms = timed_steps(graph.replay if graph is not None else step, args.steps, args.warmup)
+    ms, dist = timed_steps(graph.replay if graph is not None else step, args.steps, args.warmup)
     n_acc = int(acc_out["n"][0])
     assert int(acc_out["err"][0]) == 0 and int(ver.err[0]) == 0, "device error during bench"
 
@@ -388,6 +401,7 @@ def bench_verify(args, wl, w=None, model=None):
         "value": T * passes_s,
         "unit": "verified tokens/s",
         "ms_per_step": ms,
+        "per_step_ms": dist,
         "dtype": "bf16" if sh.dtype == "bf16" else "f32",
         "config": {"workload": f"{wl.shape.name} verify: {sh.n_layers} layers d={sh.d} {sh.n_heads}x{sh.head_dim} "
                                f"q heads / {sh.n_kv_heads} kv heads FFN {sh.ffn} V={sh.vocab}; C={C}; "
@@ -485,7 +499,7 @@ def bench_c5(args, wl, w=None, model=None):
                                     out=acc_out)
         sdv.kv_rollback(model, kv, acc_out["keep"], acc_out["move_src"], acc_out["move_dst"], acc_out["err"])
 
-    ms = timed_steps(step, args.steps, args.warmup)
+    ms, dist = timed_steps(step, args.steps, args.warmup)
     assert int(acc_out["err"].abs().sum()) == 0 and int(ver.err.abs().sum()) == 0, "device error during bench"
     us = live_kernel_times(sdv, ver, sh, step, max(3, args.steps // 4), "codebook_head")
     work = launch_work(sh, B, T, R, ctx, None, "codebook")
@@ -498,7 +512,7 @@ def bench_c5(args, wl, w=None, model=None):
     del kv
     out = {
         "metric": METRIC, "value": (B // 2) * T * passes_s, "unit": "verified session tokens/s",
-        "ms_per_step": ms, "dtype": "bf16",
+        "ms_per_step": ms, "per_step_ms": dist, "dtype": "bf16",
         "config": {"workload": f"batched multi-codebook verify: {B // 2} sessions x 2 guidance rows, 8B-shape "
                                f"backbone, {S} codebooks x {Vc}, contexts {min(ctx)}..{max(ctx)}, "
                                f"{L_a} audio + {wl.gamma} drafts, w={wl.cfg_w}",
@@ -583,7 +597,7 @@ def bench_sample(args):
         it[0] += 1
         smp(c["tgt"], c["drf"], c["drafts"], si.seed)
 
-    ms = timed_steps(step, args.steps, args.warmup)
+    ms, dist = timed_steps(step, args.steps, args.warmup)
     nbytes = si.target_logits.nbytes + si.draft_logits.nbytes
     # live duration of the row-statistics launch (it reads every logit once), from two
     # HIP events the library records on the launch stream, over K more steps
@@ -600,7 +614,7 @@ def bench_sample(args):
     achieved = stats_bytes / (stats_us * 1e-6) / 1e9
     out = {
         "metric": METRIC, "value": B * k / (ms * 1e-3), "unit": "draft positions/s", "ms_per_step": ms,
-        "dtype": "f32",
+        "per_step_ms": dist, "dtype": "f32",
         "config": {"workload": f"speculative-sampling acceptance: {B} seqs x {k} drafts, V={V}, fp32, "
                                f"Philox4x32-10 uniforms drawn in the kernel"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -649,10 +663,10 @@ def bench_pool(args, n_drafts=2000, draft_len=32, vocab=151936, B=64, max_n=8, m
         d, e = int(rng.integers(0, n_drafts)), int(rng.integers(4, draft_len))
         suf[q, cap - 4:] = drafts[d, e - 4:e]
     suf_t, len_t = torch.from_numpy(suf).cuda(), torch.full((B,), cap, dtype=torch.int32, device="cuda")
-    ms = timed_steps(lambda: pool.lookup(suf_t, len_t, max_out), args.steps * 10, args.warmup)
+    ms, dist = timed_steps(lambda: pool.lookup(suf_t, len_t, max_out), args.steps * 10, args.warmup)
     out = {"workload": f"hypothesis pool: {n_drafts} drafts x {draft_len} tokens indexed by n-grams n <= {max_n}, "
                        f"batches of {B} longest-suffix lookups (continuation <= {max_out})",
-           "lookup_batch_us": ms * 1e3, "lookups_per_s": B / (ms * 1e-3), "insert_us_per_draft": insert_us,
+           "lookup_batch_us": ms * 1e3, "per_batch_ms": dist, "lookups_per_s": B / (ms * 1e-3), "insert_us_per_draft": insert_us,
            "pool_err": int(pool.err[0])}
     if not args.no_cpu_baseline:
         from oracle.pool import Pool

@@ -54,3 +54,11 @@ def test_launch_work_of_the_decoder_kinds():
     # attention: every query row of a chain sees C cached keys plus itself and its predecessors
     assert w["attention"][1] == 4.0 * 32 * 64 * (41 * 4096 + 41 * 42 // 2)
     assert bench.attn_visible_keys(3, 10, [-1, 0, 0]) == 3 * 10 + 1 + 2 + 2
+
+
+def test_step_distribution_reports_median_and_tails():
+    """Per-step times of a timed region: median, 10th and 90th percentile, count."""
+    d = bench.step_distribution([4.0, 1.0, 3.0, 2.0, 5.0, 10.0, 6.0, 8.0, 7.0, 9.0])
+    assert d == {"median": 5.5, "p10": pytest.approx(1.9), "p90": pytest.approx(9.1), "n": 10}
+    one = bench.step_distribution([2.5])
+    assert one["median"] == one["p10"] == one["p90"] == 2.5 and one["n"] == 1

@@ -251,20 +251,24 @@ def kernel_table(sh, us, work, workload, head_kind):
 
 def timed_steps(step, steps, warmup):
     """Mean ms per step over `steps` steps between two host synchronisations, and the
-    distribution of the single steps (median, p10, p90 in ms) from HIP events recorded
-    between them on the launch stream (torch's current stream) in the same region."""
+    distribution of single steps (median, p10, p90 in ms) over as many more steps, each
+    between two HIP events on the launch stream (torch's current stream).  The events
+    stay out of the timed region: a marker between steps adds a few us to a small one."""
     import torch
     for _ in range(warmup):
         step()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record()
     for i in range(steps):
         step()
         ev[i + 1].record()
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) / steps * 1e3
     return ms, step_distribution([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
 
 

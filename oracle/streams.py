@@ -31,7 +31,7 @@ Readings where the page is silent (the plainest ones; the verify pass sees one p
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from typing import List, Optional, Sequence
 
 import numpy as np

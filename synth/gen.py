@@ -23,12 +23,12 @@ import math
 import os
 import zlib
 from concurrent.futures import ThreadPoolExecutor
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from typing import Dict, List, Optional
 
 import numpy as np
 
-from .configs import ModelShape, VerifyWorkload, SampleWorkload
+from .configs import ModelShape, SampleWorkload
 
 CHUNK = 1 << 24
 

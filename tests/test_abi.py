@@ -7,7 +7,6 @@ import os
 import re
 import subprocess
 
-import pytest
 
 import speculative_decoding_verify_amd as sdv
 from speculative_decoding_verify_amd import binding

@@ -29,7 +29,7 @@ from oracle import decoder as odec  # noqa: E402
 from oracle.numerics import memoize_f64  # noqa: E402
 from synth import (make_weights, make_random_kv, uniform_tokens, toy_workload, w1p7b_workload,  # noqa: E402
                    w8b_tree_workload)
-from tests.gpu_helpers import compare_logits, compare_kv, greedy_expectation  # noqa: E402
+from tests.gpu_helpers import compare_logits, greedy_expectation  # noqa: E402
 
 
 def _say(msg):

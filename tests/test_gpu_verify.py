@@ -15,7 +15,6 @@ if not torch.cuda.is_available():  # pragma: no cover
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import speculative_decoding_verify_amd as sdv  # noqa: E402
-from oracle import accept as oacc  # noqa: E402
 from oracle import decoder as odec  # noqa: E402
 from synth import (MINI_BF16, MINI_BF16_D128, MINI_BF16_D2048, MINI_F32, MINI_F32_D2048,  # noqa: E402
                    MINI_BF16_FFN12K, MINI_F32_FFN12K, MINI_BF16_V70K, MINI_F32_V70K, make_weights,

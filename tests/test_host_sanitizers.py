@@ -4,7 +4,6 @@ the sanitizers on its host side only (the device code is the normal build), link
 with the other objects into a driver that calls every host path that returns before
 a launch (tests/sanitize/host_checks.cpp), and run."""
 import os
-import shutil
 import subprocess
 import tempfile
 

@@ -767,7 +767,7 @@ def main():
                     help="time a plain 256 MiB device-to-device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "bench.py runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
